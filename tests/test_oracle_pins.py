@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test names what it pins: a count the pages print, a closed form, an
+invariant, a hand-derived fixture under tests/golden/, brute force on tiny
+inputs, or an independent 50-digit evaluation.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import moe_synth as ms
+from oracle import bucket as obucket
+from oracle import layer as olayer
+from oracle import lfu as olfu
+from oracle import quant as oquant
+import golden_io
+import pins_mpmath
+
+TINY = ms.CONFIGS["tiny"]
+
+
+def _tiny_experts(cfg):
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = ms.expert_raw(cfg, e)
+        return cache[e]
+    return get
+
+
+# ---- P1: the fan-out the pages print (10 of 512, 8 of 256) ----------------
+@pytest.mark.parametrize("name,k,E", [("decode80b", 10, 512), ("decode35b", 8, 256)])
+def test_topk_counts_pages(name, k, E):
+    cfg = ms.CONFIGS[name]
+    assert (cfg.k, cfg.E) == (k, E)
+    Wr = ms.router_weight(cfg)
+    for step in range(3):
+        idx, w, s, _ = olayer.route(ms.x_bits(cfg, step), Wr, ms.logit_bias(cfg), cfg.k)
+        assert idx.shape == (1, k)
+        assert len(set(idx[0].tolist())) == k
+        assert idx.min() >= 0 and idx.max() < E
+
+
+# ---- P2: selection vs subset enumeration -----------------------------------
+def test_selection_bruteforce():
+    g = np.random.default_rng(7)
+    for trial in range(40):
+        E, k = 9, 3
+        l = g.standard_normal(E)
+        if trial % 3 == 0:          # plant exact ties, incl. at the boundary
+            l[g.integers(E)] = l[g.integers(E)]
+            l[:4] = np.round(l[:4])
+        got = olayer.select_topk(l[None, :], k)[0].tolist()
+        ref = pins_mpmath.brute_subset([float(v) for v in l], k)
+        assert got == list(ref)
+        chosen = set(got)
+        assert min(l[e] for e in chosen) >= max(l[e] for e in range(E) if e not in chosen)
+
+
+# ---- P14: equal logits go to the lower index --------------------------------
+def test_tie_rule_identical_rows():
+    cfg = TINY
+    Wr = ms.router_weight(cfg).copy()
+    Wr[11] = Wr[4]           # experts 4 and 11 now have identical logits
+    x = ms.x_bits(cfg, 0)
+    l, _ = olayer.router_logits(olayer.bf16_to_f64(x), Wr, None)
+    assert np.array_equal(l[:, 4], l[:, 11])
+    # force both to the top
+    Wr2 = Wr.copy()
+    Wr2[4] *= 0
+    Wr2[11] *= 0
+    b = np.zeros(cfg.E, np.float32)
+    b[4] = b[11] = 50.0
+    idx, _, _, _ = olayer.route(x, Wr2, b, 1)
+    assert (idx[:, 0] == 4).all()
+
+
+# ---- P3: weights -------------------------------------------------------------
+def test_weights_sum_and_ratio():
+    g = np.random.default_rng(3)
+    l = g.standard_normal((5, 16)) * 3
+    for k in (1, 2, 5, 16):
+        idx = olayer.select_topk(l, k)
+        w = olayer.topk_weights(l, idx)
+        assert np.allclose(w.sum(1), 1.0, atol=1e-15)
+        if k == 1:
+            assert (w == 1.0).all()
+        sel = np.take_along_axis(l, idx.astype(np.int64), 1)
+        # ratio of two weights is exp of the logit difference
+        assert np.allclose(w[:, 0] / w[:, -1], np.exp(sel[:, 0] - sel[:, -1]), rtol=1e-12)
+        assert (np.diff(w, axis=1) <= 1e-15).all()     # rank order = weight order
+
+
+# ---- P15: shared gate --------------------------------------------------------
+def test_shared_gate_closed_form():
+    cfg = TINY
+    Wr = ms.router_weight(cfg).copy()
+    Wr[cfg.E] = 0.0
+    _, _, s, _ = olayer.route(ms.x_bits(cfg, 0), Wr, None, cfg.k)
+    assert (s == 0.5).all()
+    # one-hot x picks a single router element: s = 1 / (1 + e^-w)
+    xb = np.zeros((1, cfg.d), np.uint16)
+    xb[0, 5] = 0x3F80                       # bf16 1.0
+    Wr[cfg.E, 5] = np.float32(math.log(3.0))
+    _, _, s, _ = olayer.route(xb, Wr, None, cfg.k)
+    assert abs(s[0] - 0.75) < 1e-7          # sigmoid(ln 3) = 3/4 (w rounded to fp32)
+
+
+# ---- P5: whole tiny layer vs 50-digit brute force ---------------------------
+def test_layer_vs_mpmath_bruteforce():
+    cfg = TINY
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 0)
+    ex = _tiny_experts(cfg)
+    sh = ms.shared_raw(cfg)
+    res = olayer.moe_layer(xb, Wr, None, cfg.k, ex, sh)
+    for t in (0, 3):
+        y, S, w, s = pins_mpmath.layer_token(xb[t], Wr, None, cfg.k, ex, sh)
+        assert res["idx"][t].tolist() == list(S)
+        assert np.allclose(res["w"][t], [float(v) for v in w], rtol=1e-13, atol=0)
+        assert abs(res["s"][t] - float(s)) < 1e-15
+        yr = np.array([float(v) for v in y])
+        assert np.max(np.abs(res["y"][t] - yr)) <= 1e-12 * np.max(np.abs(yr))
+
+
+# ---- P4: k = E reduces to the dense all-experts softmax sum -----------------
+def test_k_equals_E_dense():
+    cfg = ms.scaled(TINY, E=6, k=6)
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 1)
+    ex = _tiny_experts(cfg)
+    sh = ms.shared_raw(cfg)
+    res = olayer.moe_layer(xb, Wr, None, cfg.k, ex, sh)
+    # dense formula: stacked weights, full softmax, einsum over experts
+    x = olayer.bf16_to_f64(xb)
+    W = Wr.astype(np.float64)
+    L = np.einsum("td,ed->te", x, W[:cfg.E])
+    P = np.exp(L - L.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    Gs = np.stack([oquant.dequant(ex(e)["gate"]) for e in range(cfg.E)])
+    Us = np.stack([oquant.dequant(ex(e)["up"]) for e in range(cfg.E)])
+    Ds = np.stack([oquant.dequant(ex(e)["down"]) for e in range(cfg.E)])
+    G = np.einsum("eid,td->tei", Gs, x)
+    U = np.einsum("eid,td->tei", Us, x)
+    H = G / (1 + np.exp(-G)) * U
+    O = np.einsum("edi,tei->ted", Ds, H)
+    dense = np.einsum("te,ted->td", P, O)
+    gs = 1 / (1 + np.exp(-(x @ W[cfg.E])))
+    Gsh = x @ oquant.dequant(sh["gate"]).T
+    Ush = x @ oquant.dequant(sh["up"]).T
+    dense += gs[:, None] * ((Gsh / (1 + np.exp(-Gsh)) * Ush) @ oquant.dequant(sh["down"]).T)
+    assert np.allclose(res["y"], dense, rtol=1e-11, atol=1e-12 * np.abs(dense).max())
+
+
+# ---- closed form: identical constant experts ---------------------------------
+def test_constant_experts_closed_form():
+    """All codes of a matrix equal, one scale/bias per matrix: every weight is a
+    constant c, so g_o = c_g Sx, u_o = c_u Sx, h = silu(g) u for every o,
+    o_j = c_d * I * h, and y_j = (sum_r w_r) o + s o = (1 + s) o."""
+    cfg = TINY
+    d, I = cfg.d, cfg.I
+
+    def const(out, inp, q, sc, bi):
+        return {"codes": np.full((out, inp), q, np.uint8),
+                "scales": np.full((out, inp // 64), sc, np.float16),
+                "biases": np.full((out, inp // 64), bi, np.float16)}
+    raw = {"gate": const(I, d, 11, 0.0078125, -0.0625),
+           "up": const(I, d, 3, 0.015625, 0.0),
+           "down": const(d, I, 9, 0.001953125, -0.015625)}
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 2)
+    res = olayer.moe_layer(xb, Wr, None, cfg.k, lambda e: raw, raw)
+    x = olayer.bf16_to_f64(xb)
+    Sx = x.sum(1)
+    cg = 0.0078125 * 11 - 0.0625
+    cu = 0.015625 * 3
+    cd = 0.001953125 * 9 - 0.015625
+    g = cg * Sx
+    h = g / (1 + np.exp(-g)) * (cu * Sx)
+    o = cd * I * h
+    s = 1 / (1 + np.exp(-(x @ Wr[cfg.E].astype(np.float64))))
+    ref = ((1 + s) * o)[:, None] * np.ones((1, d))
+    assert np.allclose(res["y"], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---- P10 / P11: zero expert, power-of-two scaling ---------------------------
+def test_zero_expert_and_power_of_two():
+    cfg = TINY
+    raw = ms.expert_raw(cfg, 3)
+    z = {k: dict(v) for k, v in raw.items()}
+    z["down"] = {"codes": np.full_like(raw["down"]["codes"], 8),
+                 "scales": raw["down"]["scales"], "biases": raw["down"]["biases"]}
+    x = olayer.bf16_to_f64(ms.x_bits(cfg, 0))
+    assert (olayer.expert_ffn(z, x) == 0).all()      # bias = -8 scale -> W = 0
+    dbl = {k: dict(v) for k, v in raw.items()}
+    dbl["down"] = {"codes": raw["down"]["codes"],
+                   "scales": (raw["down"]["scales"] * 2).astype(np.float16),
+                   "biases": (raw["down"]["biases"] * 2).astype(np.float16)}
+    assert np.array_equal(olayer.expert_ffn(dbl, x), 2 * olayer.expert_ffn(raw, x))
+
+
+def test_dequant_exact_in_fp32():
+    """s*q + b with fp16 s, b = -8 s and q in 0..15 has <= 15 significant bits:
+    exactly representable in fp32 (so an fp32 device loses nothing there)."""
+    raw = ms.expert_raw(ms.CONFIGS["decode80b"], 5)
+    for m in raw.values():
+        W = oquant.dequant(m)
+        assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
+
+
+# ---- P7: blob layout ---------------------------------------------------------
+@pytest.mark.parametrize("case", range(2))
+def test_blob_layout_golden(case):
+    d, I, nbytes, stride, codes, sbs = golden_io.blob_layout()[case]
+    assert oquant.blob_bytes(d, I) == nbytes == 27 * d * I // 16
+    assert oquant.blob_stride(d, I) == stride
+    dims = oquant.mat_dims(d, I)
+    for mat, row, col, val, off, byte in codes:
+        raw = {m: {"codes": np.zeros(dims[m], np.uint8),
+                   "scales": np.zeros((dims[m][0], dims[m][1] // 64), np.float16),
+                   "biases": np.zeros((dims[m][0], dims[m][1] // 64), np.float16)}
+               for m in oquant.MATS}
+        raw[mat]["codes"][row, col] = val
+        blob = oquant.pack_expert(raw, d, I)
+        assert blob.size == stride
+        nz = np.nonzero(blob)[0]
+        assert nz.tolist() == [off] and blob[off] == byte
+    for mat, row, g, soff, boff in sbs:
+        raw = {m: {"codes": np.zeros(dims[m], np.uint8),
+                   "scales": np.zeros((dims[m][0], dims[m][1] // 64), np.float16),
+                   "biases": np.zeros((dims[m][0], dims[m][1] // 64), np.float16)}
+               for m in oquant.MATS}
+        raw[mat]["scales"][row, g] = np.float16(0.5)      # 0x3800
+        raw[mat]["biases"][row, g] = np.float16(-2.0)     # 0xC000
+        blob = oquant.pack_expert(raw, d, I)
+        assert blob[soff:soff + 2].tobytes() == b"\x00\x38"
+        assert blob[boff:boff + 2].tobytes() == b"\x00\xc0"
+        assert np.count_nonzero(blob) == 2
+
+
+def test_pack_roundtrip():
+    for cfg in (TINY, ms.CONFIGS["decode80b"]):
+        raw = ms.expert_raw(cfg, 9)
+        blob = oquant.pack_expert(raw, cfg.d, cfg.I)
+        assert blob.size == oquant.blob_stride(cfg.d, cfg.I)
+        assert not blob[oquant.blob_bytes(cfg.d, cfg.I):].any()
+        back = oquant.unpack_expert(blob, cfg.d, cfg.I)
+        for m in oquant.MATS:
+            for f in ("codes", "scales", "biases"):
+                assert np.array_equal(back[m][f], raw[m][f])
+        assert np.array_equal(oquant.pack_expert(back, cfg.d, cfg.I), blob)
+    assert oquant.blob_bytes(2048, 512) == 1769472 == oquant.blob_stride(2048, 512)
+
+
+# ---- P8: placement invariance (oracle reading blobs through a slot table) ---
+def test_placement_invariance_oracle():
+    cfg = TINY
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 0)
+    stride = oquant.blob_stride(cfg.d, cfg.I)
+    blobs = [oquant.pack_expert(ms.expert_raw(cfg, e), cfg.d, cfg.I) for e in range(cfg.E)]
+    sh = ms.shared_raw(cfg)
+    ys = []
+    for perm_seed in (None, 1, 2):
+        table = np.arange(cfg.E) if perm_seed is None else \
+            np.random.default_rng(perm_seed).permutation(cfg.E)
+        pool = np.zeros(cfg.E * stride, np.uint8)
+        for e in range(cfg.E):
+            pool[table[e] * stride:(table[e] + 1) * stride] = blobs[e]
+
+        def fetch(e, pool=pool, table=table):
+            s = int(table[e])
+            return oquant.unpack_expert(pool[s * stride:(s + 1) * stride], cfg.d, cfg.I)
+        ys.append(olayer.moe_layer(xb, Wr, None, cfg.k, fetch, sh)["y"])
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+# ---- P9: token independence (incremental vs whole) --------------------------
+def test_token_independence():
+    cfg = TINY
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 4)
+    ex = _tiny_experts(cfg)
+    sh = ms.shared_raw(cfg)
+    whole = olayer.moe_layer(xb, Wr, None, cfg.k, ex, sh)
+    for t in range(cfg.T):
+        one = olayer.moe_layer(xb[t:t + 1], Wr, None, cfg.k, ex, sh)
+        assert one["idx"][0].tolist() == whole["idx"][t].tolist()
+        assert np.allclose(one["y"][0], whole["y"][t], rtol=1e-13, atol=1e-15)
+
+
+# ---- P12: bucketing = stable counting sort -----------------------------------
+def test_bucketing_bruteforce():
+    g = np.random.default_rng(11)
+    for T, k, E in ((1, 10, 512), (64, 10, 512), (7, 3, 5), (33, 4, 1024)):
+        idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        counts, offsets, pair_ids = obucket.bucket(idx, E)
+        flat = idx.ravel()
+        ref = sorted(range(T * k), key=lambda i: (flat[i], i))
+        assert pair_ids.tolist() == ref
+        assert counts.sum() == T * k and offsets[-1] == T * k and offsets[0] == 0
+        for e in range(E):
+            seg = pair_ids[offsets[e]:offsets[e + 1]]
+            assert len(seg) == counts[e] == (flat == e).sum()
+            assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()
+
+
+# ---- P13 (oracle side): LFU + recency vs hand-derived traces -----------------
+def test_lfu_golden_traces():
+    for name, E, slots, steps in golden_io.lfu_traces():
+        sim = olfu.SlotPoolSim(E, slots)
+        for sel, loads, hits in steps:
+            h0 = sim.hits
+            got = sim.plan(sel)
+            assert got == loads, (name, sel)
+            assert sim.hits - h0 == hits, (name, sel)
+
+
+def test_lfu_pool_too_small():
+    sim = olfu.SlotPoolSim(4, 1)
+    with pytest.raises(ValueError):
+        sim.plan([0, 1])
+
+
+# ---- certified near-tie bound is a true bound ---------------------------------
+def test_logit_error_bound_holds_for_fp32_sums():
+    cfg = ms.CONFIGS["decode80b"]
+    Wr = ms.router_weight(cfg)
+    b = ms.logit_bias(cfg)
+    xb = ms.x_bits(cfg, 0)
+    x32 = ms.bf16_bits_to_f32(xb)
+    exact, _ = olayer.router_logits(olayer.bf16_to_f64(xb), Wr, b)
+    # a plain sequential fp32 sum has depth d; bound must cover it
+    seq = np.zeros(cfg.E, np.float32)
+    for j in range(cfg.d):
+        seq = (seq + x32[0, j] * Wr[:cfg.E, j]).astype(np.float32)
+    seq = (seq + b).astype(np.float32)
+    r = olayer.logit_error_bound(xb, Wr, b, depth=cfg.d)
+    assert np.max(np.abs(seq - exact[0])) <= r[0]
