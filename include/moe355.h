@@ -1,0 +1,282 @@
+/*
+ * libmoe355 — routed-expert Mixture-of-Experts layer for MI355X (gfx950).
+ *
+ * The layer (Swiftlet pages, "How it works"): every token is routed to k of E
+ * experts (10 of 512 for the 80B model, 8 of 256 for the 35B model); the
+ * router and a shared expert stay resident; routed experts are 4-bit MLX
+ * affine group-quantised weights, each repacked as one fixed-stride blob so a
+ * fetch is one read, cached in a bounded slot pool evicted by LFU + recency
+ * (relationship-to-TurboFieldfare section).  Placement never changes the
+ * answer (correctness section).
+ *
+ * Readings where the pages are silent (all calls follow them):
+ *   router   l[t,e] = x_t . W_r[e] + b[e]; top-k largest logits, ties to the
+ *            lower index, emitted in rank order (logit desc, index asc);
+ *            w = softmax over the k chosen logits; shared gate
+ *            s_t = sigmoid(x_t . W_r[E]).
+ *   expert   SwiGLU: h = silu(W_gate x) * (W_up x), o = W_down h,
+ *            W = scale * q + bias per group of 64 inputs, q in 0..15.
+ *   layer    y_t = sum_{r<k} w[t,r] o_{e_r}(x_t) + s_t o_shared(x_t), summed in
+ *            that order, in fp32.
+ *
+ * Conventions
+ *   - Every pointer named *_dev / documented "device" is device memory; every
+ *     other pointer is host memory.  The caller owns all buffers except a
+ *     pool's slab, slot table, usage counters and error word, which the pool
+ *     owns.  No call allocates device memory except moe_pool_create.
+ *   - Device work is enqueued asynchronously on the given stream; results are
+ *     valid once the stream reaches that point.  Calls that also take host
+ *     data (moe_pool_plan, moe_pool_refill) say so.
+ *   - Every call returns a status: MOE_OK or a negative MOE_ERR_*.  No call
+ *     aborts or throws; kernels report an expert that is selected but not
+ *     resident through the pool's device error word (moe_pool_check_error).
+ *   - Workspaces: device buffers of the size the *_workspace_bytes call
+ *     returns, 256-byte aligned, zero-filled by the caller before their first
+ *     use; every call leaves them reusable without another fill.  One
+ *     workspace must not be used by two calls in flight at once.
+ *   - x is bf16 (uint16 bit patterns) row-major [T][d]; router weights fp32
+ *     row-major [E+1][d]; outputs fp32.
+ *   - Not thread-safe per pool or per workspace.
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,    /* null pointer, bad size, misaligned buffer   */
+  MOE_ERR_UNSUPPORTED = -2,    /* shape outside the kernels' envelope         */
+  MOE_ERR_NOT_RESIDENT = -3,   /* a selected expert had no slot               */
+  MOE_ERR_POOL_TOO_SMALL = -4, /* one step needs more distinct experts than slots */
+  MOE_ERR_HIP = -5             /* HIP runtime error; see moe_last_hip_error   */
+};
+
+/* Flags for moe_expert_ffn_int4 / moe_layer_forward. */
+enum {
+  MOE_PATH_AUTO = 0,       /* choose by tokens per expert                     */
+  MOE_PATH_DECODE = 1,     /* per-(token, rank) GEMV, fused combine (T <= 8)  */
+  MOE_PATH_BATCHED = 2,    /* bucketed GEMV, partials + combine               */
+  MOE_PATH_PREFILL = 3     /* bucketed bf16 MFMA grouped GEMM + combine       */
+};
+
+/* Expert FFN shape.  group must be 64; d and I multiples of 64. */
+typedef struct moe_ffn_shape {
+  int32_t d;      /* hidden size (input of gate/up, output of down)          */
+  int32_t I;      /* intermediate size                                       */
+  int32_t group;  /* quantisation group along the input dimension (64)       */
+} moe_ffn_shape;
+
+/* ---------------------------------------------------------------- errors */
+const char* moe_status_string(int status);
+/* Text of the last HIP error seen by any call of this thread ("" if none). */
+const char* moe_last_hip_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/* ----------------------------------------------------------- blob layout
+ * One expert = one fixed-stride blob ("How it works": one fetch is one read).
+ * For m in gate [I x d], up [I x d], down [d x I] (out x in):
+ *   codes_m [in/32][out][16 B]: q[o][32c+2b] in the low nibble and
+ *           q[o][32c+2b+1] in the high nibble of byte b of (c, o)
+ *   sb_m    [in/64][out][2] fp16: (scale, bias) of group g of row o
+ * in the order gate codes, gate sb, up codes, up sb, down codes, down sb.
+ * bytes = 27/16 * d * I; stride = bytes rounded up to 4096, zero padded.
+ * Offsets are 64-bit (multi-GB pools; MLX affine kernels with 64-bit offsets
+ * in the relationship-to-TurboFieldfare section). */
+size_t moe_blob_bytes(const moe_ffn_shape* sh);   /* 0 if sh is invalid */
+size_t moe_blob_stride(const moe_ffn_shape* sh);  /* 0 if sh is invalid */
+
+/* Pack one expert (host).  codes[m]: [out][in] bytes, one code (0..15) each,
+ * MLX orientation; scales[m], biases[m]: [out][in/64] fp16 bit patterns;
+ * m = 0 gate, 1 up, 2 down.  blob_out: moe_blob_stride bytes, written whole
+ * (padding zeroed).  Codes above 15: MOE_ERR_INVALID_ARG. */
+int moe_pack_expert_int4(const moe_ffn_shape* sh,
+                         const uint8_t* const codes[3],
+                         const uint16_t* const scales[3],
+                         const uint16_t* const biases[3],
+                         void* blob_out);
+/* Inverse of moe_pack_expert_int4 (host). */
+int moe_unpack_expert_int4(const moe_ffn_shape* sh, const void* blob,
+                           uint8_t* const codes[3], uint16_t* const scales[3],
+                           uint16_t* const biases[3]);
+
+/* ------------------------------------------------------------ slot pool
+ * Bounded pool of n_slots blobs in HBM ("How it works": hot experts cached in
+ * a bounded pool), a device slot table slot_table[e] (-1 = not resident),
+ * device usage counters usage[e] (selections, cumulative) and a device error
+ * word.  Host-side LFU + recency state decides refills (moe_pool_plan). */
+typedef struct moe_pool moe_pool;
+
+typedef struct moe_pool_stats {
+  uint64_t steps, hits, misses, loads, evictions, bytes_loaded;
+} moe_pool_stats;
+
+/* LFU + recency policy on its own (host only; a pool embeds one).
+ * moe_lfu_plan follows the rules of moe_pool_plan below. */
+typedef struct moe_lfu moe_lfu;
+int moe_lfu_create(int32_t E, int32_t n_slots, moe_lfu** out);
+int moe_lfu_destroy(moe_lfu* lfu);
+int moe_lfu_plan(moe_lfu* lfu, const int32_t* selected, int32_t n,
+                 int32_t* load_expert, int32_t* load_slot, int32_t* load_victim,
+                 int32_t* n_loads);
+int moe_lfu_get_stats(const moe_lfu* lfu, moe_pool_stats* st);
+
+/* Allocates slab (n_slots * stride bytes), slot table (all -1), usage (0) and
+ * error word (0) on the current device. */
+int moe_pool_create(int32_t E, int32_t n_slots, const moe_ffn_shape* sh,
+                    moe_pool** out);
+int moe_pool_destroy(moe_pool* pool);
+void* moe_pool_slab(const moe_pool* pool);              /* device */
+size_t moe_pool_stride(const moe_pool* pool);
+int32_t* moe_pool_slot_table(const moe_pool* pool);     /* device, [E] */
+uint32_t* moe_pool_usage(const moe_pool* pool);         /* device, [E] */
+int32_t moe_pool_num_experts(const moe_pool* pool);
+int32_t moe_pool_num_slots(const moe_pool* pool);
+
+/* Copy one blob into a slot and make `expert` resident there (evicting any
+ * previous holder of the slot).  blob is host memory (pinned for a truly
+ * asynchronous copy; it must stay valid until the stream passes the copy)
+ * for moe_pool_load, device memory for moe_pool_load_device. */
+int moe_pool_load(moe_pool* pool, int32_t expert, int32_t slot,
+                  const void* blob, hipStream_t stream);
+int moe_pool_load_device(moe_pool* pool, int32_t expert, int32_t slot,
+                         const void* blob_dev, hipStream_t stream);
+
+/* LFU + recency plan for one step (host only, no device work).  selected: the
+ * step's rank-ordered selections (host, n entries, duplicates allowed).  Each
+ * selection adds 1 to the expert's count and stamps it with the step number.
+ * Distinct experts are taken in first-appearance order; a resident one is a
+ * hit; a missing one goes to the lowest free slot, else replaces the resident
+ * expert not needed this step with the smallest (count, last step, id).
+ * Writes loads (expert, slot, evicted expert or -1) to the three arrays
+ * (capacity n each) and their number to *n_loads, and updates the pool's host
+ * residency map.  MOE_ERR_POOL_TOO_SMALL if the distinct experts exceed
+ * n_slots (nothing is changed then). */
+int moe_pool_plan(moe_pool* pool, const int32_t* selected, int32_t n,
+                  int32_t* load_expert, int32_t* load_slot,
+                  int32_t* load_victim, int32_t* n_loads);
+
+/* Plan (as above) and carry it out: copy each missing blob from
+ * host_blobs + expert * host_stride (pinned host memory holding all E blobs)
+ * into its slot and publish the new slot-table entries, all on `stream`. */
+int moe_pool_refill(moe_pool* pool, const int32_t* selected, int32_t n,
+                    const void* host_blobs, size_t host_stride,
+                    hipStream_t stream);
+
+/* Set the whole slot table (host array [E], -1 = absent) and the host map;
+ * blobs must already sit in those slots (placement tests, replicas). */
+int moe_pool_set_slot_table(moe_pool* pool, const int32_t* table,
+                            hipStream_t stream);
+int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* st);
+/* Synchronises the stream, reads and clears the device error word:
+ * *err = MOE_OK or MOE_ERR_NOT_RESIDENT. */
+int moe_pool_check_error(moe_pool* pool, hipStream_t stream, int32_t* err);
+/* Synchronises the stream and copies the device slot table ([E] int32) and
+ * usage counters ([E] uint32) to host arrays (either may be NULL). */
+int moe_pool_read_state(const moe_pool* pool, int32_t* table, uint32_t* usage,
+                        hipStream_t stream);
+/* Zero the device usage counters (async). */
+int moe_pool_reset_usage(moe_pool* pool, hipStream_t stream);
+
+/* --------------------------------------------------------------- router
+ * Router logits, top-k, renormalised weights, shared gate, usage counters.
+ * x_dev [T][d] bf16; w_router_dev [E+1][d] fp32 (row E = shared-expert gate);
+ * logit_bias_dev [E] fp32 or NULL; outputs topk_idx_dev [T][k] int32 and
+ * topk_w_dev [T][k] fp32 in rank order, shared_gate_dev [T] fp32 (may be
+ * NULL); usage_dev [E] uint32 or NULL (+1 per selection, atomically).
+ * 1 <= k <= E <= 1024, d a multiple of 64 and <= 8192.
+ * Each logit is an fp32 sum of the d products (plus the bias) in a fixed
+ * tree, so the result is deterministic; moe_router_sum_depth gives the
+ * largest number of additions on any path of that tree for (T, d), which
+ * bounds the rounding error (gamma_n * sum|x_j W_ej|). */
+int32_t moe_router_sum_depth(int32_t T, int32_t d);
+size_t moe_router_workspace_bytes(int32_t T, int32_t d, int32_t E);
+int moe_router_topk(const uint16_t* x_dev, int32_t T, int32_t d,
+                    const float* w_router_dev, const float* logit_bias_dev,
+                    int32_t E, int32_t k, int32_t* topk_idx_dev,
+                    float* topk_w_dev, float* shared_gate_dev,
+                    uint32_t* usage_dev, void* workspace_dev,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ bucketing
+ * Stable counting sort of the T*k (token, rank) pairs by expert:
+ * counts_dev[E], offsets_dev[E+1] (exclusive prefix, offsets[E] = T*k),
+ * pair_ids_dev[T*k] (pair i = t*k + r, ascending within each bucket).
+ * Indices outside [0, E) make the call fail on the host side only if it can
+ * see them; on the device they are counted into no bucket. */
+size_t moe_bucket_workspace_bytes(int32_t T, int32_t k, int32_t E);
+int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
+                      int32_t E, int32_t* counts_dev, int32_t* offsets_dev,
+                      int32_t* pair_ids_dev, void* workspace_dev,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------- expert FFN
+ * Apply the selected int4 experts (read from `pool` through its slot table)
+ * and the shared expert (shared_blob_dev, shape shared_sh with the same d).
+ *   MOE_PATH_DECODE : out_dev = y [T][d], combine fused (needs topk_w and
+ *                     shared_gate).  offsets/pair_ids ignored.  T <= 8.
+ *   MOE_PATH_BATCHED/PREFILL : needs offsets_dev/pair_ids_dev from
+ *                     moe_bucket_tokens; writes the unweighted expert outputs
+ *                     partial_dev [T*k][d] (pair order) and shared_out_dev
+ *                     [T][d]; combine with moe_combine (out_dev unused).
+ *   MOE_PATH_AUTO   : DECODE for T <= 4, BATCHED for T*k/E < 16, else PREFILL
+ *                     (the caller must then supply every buffer).
+ * A selected expert with slot_table[e] < 0 sets the pool's error word and
+ * contributes zero. */
+size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh,
+                               const moe_ffn_shape* shared_sh, int32_t T,
+                               int32_t k, int32_t E, int32_t path);
+int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh,
+                        const void* shared_blob_dev,
+                        const moe_ffn_shape* shared_sh,
+                        const uint16_t* x_dev, int32_t T, int32_t k,
+                        const int32_t* topk_idx_dev, const float* topk_w_dev,
+                        const float* shared_gate_dev,
+                        const int32_t* offsets_dev, const int32_t* pair_ids_dev,
+                        float* out_dev, float* partial_dev,
+                        float* shared_out_dev, int32_t path,
+                        void* workspace_dev, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* -------------------------------------------------------------- combine
+ * y[t] = sum_{r<k} w[t,r] * partial[t*k+r] + s_t * shared_out[t], in that
+ * order, fp32.  shared_out_dev / shared_gate_dev may both be NULL. */
+int moe_combine(const float* partial_dev, const float* shared_out_dev,
+                const float* topk_w_dev, const float* shared_gate_dev,
+                int32_t T, int32_t k, int32_t d, float* y_dev,
+                hipStream_t stream);
+
+/* ---------------------------------------------------------- whole layer
+ * Router -> (bucketing) -> experts -> combine, one call, all on `stream`. */
+typedef struct moe_layer_desc {
+  moe_ffn_shape sh;            /* routed expert shape                       */
+  moe_ffn_shape shared_sh;     /* shared expert shape (same d)              */
+  int32_t E, k;
+  const float* w_router_dev;   /* [E+1][d]                                  */
+  const float* logit_bias_dev; /* [E] or NULL                               */
+  const moe_pool* pool;        /* routed experts                            */
+  const void* shared_blob_dev; /* one blob of shape shared_sh               */
+  uint32_t* usage_dev;         /* [E] or NULL                               */
+} moe_layer_desc;
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int32_t T,
+                                 int32_t path);
+/* Outputs: y_dev [T][d]; topk_idx_dev [T][k], topk_w_dev [T][k],
+ * shared_gate_dev [T] (all required: later stages read them). */
+int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x_dev,
+                      int32_t T, float* y_dev, int32_t* topk_idx_dev,
+                      float* topk_w_dev, float* shared_gate_dev, int32_t path,
+                      void* workspace_dev, size_t workspace_bytes,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE355_H */

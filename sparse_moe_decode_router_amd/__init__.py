@@ -1,0 +1,431 @@
+"""Python binding for libmoe355 (routed-expert MoE layer on MI355X / gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe355.so`` behind the C ABI declared in ``include/moe355.h``.  torch is
+used for device memory and streams.  Importing this package does not need a
+GPU; calling the device entry points does.  If the shared library has not
+been built the import fails loudly (there is no fallback path).
+
+Names follow the C ABI (``moe_router_topk`` etc.).  Device arguments are
+torch CUDA tensors; host arguments of the pool calls are numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe355.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_NOT_RESIDENT = -3
+MOE_ERR_POOL_TOO_SMALL = -4
+MOE_ERR_HIP = -5
+
+MOE_PATH_AUTO = 0
+MOE_PATH_DECODE = 1
+MOE_PATH_BATCHED = 2
+MOE_PATH_PREFILL = 3
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmoe355.so not built at {LIB_PATH}; run "
+        "`python sparse_moe_decode_router_amd/build.py` (the HIP library is required; "
+        "there is no CPU fallback)")
+
+_lib = C.CDLL(LIB_PATH)
+
+
+class moe_ffn_shape(C.Structure):
+    _fields_ = [("d", C.c_int32), ("I", C.c_int32), ("group", C.c_int32)]
+
+
+class moe_pool_stats(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in ("steps", "hits", "misses", "loads", "evictions", "bytes_loaded")]
+
+
+class moe_layer_desc(C.Structure):
+    _fields_ = [("sh", moe_ffn_shape), ("shared_sh", moe_ffn_shape),
+                ("E", C.c_int32), ("k", C.c_int32),
+                ("w_router_dev", C.c_void_p), ("logit_bias_dev", C.c_void_p),
+                ("pool", C.c_void_p), ("shared_blob_dev", C.c_void_p),
+                ("usage_dev", C.c_void_p)]
+
+
+_P = C.c_void_p
+_I = C.c_int32
+_S = C.c_size_t
+_SIGS = {
+    "moe_status_string": (C.c_char_p, [C.c_int]),
+    "moe_last_hip_error": (C.c_char_p, []),
+    "moe_version": (C.c_char_p, []),
+    "moe_blob_bytes": (_S, [_P]),
+    "moe_blob_stride": (_S, [_P]),
+    "moe_pack_expert_int4": (C.c_int, [_P, _P, _P, _P, _P]),
+    "moe_unpack_expert_int4": (C.c_int, [_P, _P, _P, _P, _P]),
+    "moe_lfu_create": (C.c_int, [_I, _I, _P]),
+    "moe_lfu_destroy": (C.c_int, [_P]),
+    "moe_lfu_plan": (C.c_int, [_P, _P, _I, _P, _P, _P, _P]),
+    "moe_lfu_get_stats": (C.c_int, [_P, _P]),
+    "moe_pool_create": (C.c_int, [_I, _I, _P, _P]),
+    "moe_pool_destroy": (C.c_int, [_P]),
+    "moe_pool_slab": (_P, [_P]),
+    "moe_pool_stride": (_S, [_P]),
+    "moe_pool_slot_table": (_P, [_P]),
+    "moe_pool_usage": (_P, [_P]),
+    "moe_pool_num_experts": (_I, [_P]),
+    "moe_pool_num_slots": (_I, [_P]),
+    "moe_pool_load": (C.c_int, [_P, _I, _I, _P, _P]),
+    "moe_pool_load_device": (C.c_int, [_P, _I, _I, _P, _P]),
+    "moe_pool_plan": (C.c_int, [_P, _P, _I, _P, _P, _P, _P]),
+    "moe_pool_refill": (C.c_int, [_P, _P, _I, _P, _S, _P]),
+    "moe_pool_set_slot_table": (C.c_int, [_P, _P, _P]),
+    "moe_pool_get_stats": (C.c_int, [_P, _P]),
+    "moe_pool_check_error": (C.c_int, [_P, _P, _P]),
+    "moe_pool_reset_usage": (C.c_int, [_P, _P]),
+    "moe_pool_read_state": (C.c_int, [_P, _P, _P, _P]),
+    "moe_router_sum_depth": (_I, [_I, _I]),
+    "moe_router_workspace_bytes": (_S, [_I, _I, _I]),
+    "moe_router_topk": (C.c_int, [_P, _I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_bucket_workspace_bytes": (_S, [_I, _I, _I]),
+    "moe_bucket_tokens": (C.c_int, [_P, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "moe_ffn_workspace_bytes": (_S, [_P, _P, _I, _I, _I, _I]),
+    "moe_expert_ffn_int4": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, _I, _P, _S, _P]),
+    "moe_combine": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_layer_workspace_bytes": (_S, [_P, _I, _I]),
+    "moe_layer_forward": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.moe_status_string(status).decode()
+        if status == MOE_ERR_HIP:
+            msg += f" ({_lib.moe_last_hip_error().decode()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+        self.status = status
+
+
+def _check(st: int, where: str):
+    if st != MOE_OK:
+        raise MoeError(st, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def version() -> str:
+    return _lib.moe_version().decode()
+
+
+def shape(d: int, I: int) -> moe_ffn_shape:
+    return moe_ffn_shape(d, I, 64)
+
+
+# -------------------------------------------------------------- blob layout
+def moe_blob_bytes(d: int, I: int) -> int:
+    return int(_lib.moe_blob_bytes(C.byref(shape(d, I))))
+
+
+def moe_blob_stride(d: int, I: int) -> int:
+    return int(_lib.moe_blob_stride(C.byref(shape(d, I))))
+
+
+_MATS = ("gate", "up", "down")
+
+
+def moe_pack_expert_int4(raw, d: int, I: int) -> np.ndarray:
+    """Blob bytes (uint8[stride]) of one expert from raw MLX-orientation arrays."""
+    keep = []
+    cp, sp, bp = (C.c_void_p * 3)(), (C.c_void_p * 3)(), (C.c_void_p * 3)()
+    for m, name in enumerate(_MATS):
+        c = np.ascontiguousarray(raw[name]["codes"], dtype=np.uint8)
+        s = np.ascontiguousarray(np.asarray(raw[name]["scales"], np.float16)).view(np.uint16)
+        b = np.ascontiguousarray(np.asarray(raw[name]["biases"], np.float16)).view(np.uint16)
+        keep += [c, s, b]
+        cp[m], sp[m], bp[m] = c.ctypes.data, s.ctypes.data, b.ctypes.data
+    out = np.empty(moe_blob_stride(d, I), dtype=np.uint8)
+    _check(_lib.moe_pack_expert_int4(C.byref(shape(d, I)), cp, sp, bp, out.ctypes.data),
+           "moe_pack_expert_int4")
+    return out
+
+
+def moe_unpack_expert_int4(blob: np.ndarray, d: int, I: int):
+    dims = {"gate": (I, d), "up": (I, d), "down": (d, I)}
+    raw = {}
+    cp, sp, bp = (C.c_void_p * 3)(), (C.c_void_p * 3)(), (C.c_void_p * 3)()
+    for m, name in enumerate(_MATS):
+        o, i = dims[name]
+        raw[name] = {"codes": np.empty((o, i), np.uint8),
+                     "scales": np.empty((o, i // 64), np.float16),
+                     "biases": np.empty((o, i // 64), np.float16)}
+        cp[m] = raw[name]["codes"].ctypes.data
+        sp[m] = raw[name]["scales"].ctypes.data
+        bp[m] = raw[name]["biases"].ctypes.data
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    _check(_lib.moe_unpack_expert_int4(C.byref(shape(d, I)), blob.ctypes.data, cp, sp, bp),
+           "moe_unpack_expert_int4")
+    return raw
+
+
+# --------------------------------------------------------------------- pool
+def _plan(fn, handle, selected):
+    sel = np.ascontiguousarray(np.asarray(selected, dtype=np.int32))
+    n = sel.size
+    le = np.empty(max(n, 1), np.int32)
+    ls = np.empty(max(n, 1), np.int32)
+    lv = np.empty(max(n, 1), np.int32)
+    nl = C.c_int32()
+    _check(fn(handle, sel.ctypes.data, n, le.ctypes.data, ls.ctypes.data, lv.ctypes.data, C.byref(nl)),
+           fn.__name__)
+    return [(int(le[q]), int(ls[q]), int(lv[q])) for q in range(nl.value)]
+
+
+class Lfu:
+    """Host-only LFU + recency slot policy (no device needed)."""
+
+    def __init__(self, E: int, n_slots: int):
+        h = C.c_void_p()
+        _check(_lib.moe_lfu_create(E, n_slots, C.byref(h)), "moe_lfu_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _lib.moe_lfu_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def plan(self, selected):
+        return _plan(_lib.moe_lfu_plan, self.handle, selected)
+
+    def stats(self) -> dict:
+        st = moe_pool_stats()
+        _check(_lib.moe_lfu_get_stats(self.handle, C.byref(st)), "moe_lfu_get_stats")
+        return {n: int(getattr(st, n)) for n, _ in moe_pool_stats._fields_}
+
+
+class Pool:
+    """A bounded HBM slot pool of expert blobs (owns its device memory)."""
+
+    def __init__(self, E: int, n_slots: int, d: int, I: int):
+        self.E, self.n_slots, self.d, self.I = E, n_slots, d, I
+        h = C.c_void_p()
+        _check(_lib.moe_pool_create(E, n_slots, C.byref(shape(d, I)), C.byref(h)), "moe_pool_create")
+        self.handle = h
+        self.stride = int(_lib.moe_pool_stride(h))
+
+    def close(self):
+        if self.handle:
+            _lib.moe_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def slab_ptr(self) -> int:
+        return int(_lib.moe_pool_slab(self.handle))
+
+    @property
+    def slot_table_ptr(self) -> int:
+        return int(_lib.moe_pool_slot_table(self.handle))
+
+    @property
+    def usage_ptr(self) -> int:
+        return int(_lib.moe_pool_usage(self.handle))
+
+    def load(self, expert: int, slot: int, blob, stream=None):
+        """blob: a torch CUDA uint8 tensor (device copy) or a numpy/pinned host array."""
+        if hasattr(blob, "is_cuda") and blob.is_cuda:
+            st = _lib.moe_pool_load_device(self.handle, expert, slot, blob.data_ptr(), _stream(stream))
+        else:
+            ptr = blob.data_ptr() if hasattr(blob, "data_ptr") else blob.ctypes.data
+            st = _lib.moe_pool_load(self.handle, expert, slot, ptr, _stream(stream))
+        _check(st, "moe_pool_load")
+
+    def plan(self, selected: Sequence[int]):
+        return _plan(_lib.moe_pool_plan, self.handle, selected)
+
+    def refill(self, selected, host_blobs, host_stride: int, stream=None):
+        sel = np.ascontiguousarray(np.asarray(selected, dtype=np.int32))
+        _check(_lib.moe_pool_refill(self.handle, sel.ctypes.data, sel.size, host_blobs.data_ptr(),
+                                    host_stride, _stream(stream)), "moe_pool_refill")
+
+    def set_slot_table(self, table, stream=None):
+        t = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+        _check(_lib.moe_pool_set_slot_table(self.handle, t.ctypes.data, _stream(stream)),
+               "moe_pool_set_slot_table")
+
+    def stats(self) -> dict:
+        st = moe_pool_stats()
+        _check(_lib.moe_pool_get_stats(self.handle, C.byref(st)), "moe_pool_get_stats")
+        return {n: int(getattr(st, n)) for n, _ in moe_pool_stats._fields_}
+
+    def check_error(self, stream=None) -> int:
+        e = C.c_int32()
+        _check(_lib.moe_pool_check_error(self.handle, _stream(stream), C.byref(e)), "moe_pool_check_error")
+        return e.value
+
+    def reset_usage(self, stream=None):
+        _check(_lib.moe_pool_reset_usage(self.handle, _stream(stream)), "moe_pool_reset_usage")
+
+    def read_state(self, stream=None):
+        """(slot_table int32[E], usage uint32[E]) copied to host."""
+        table = np.empty(self.E, np.int32)
+        usage = np.empty(self.E, np.uint32)
+        _check(_lib.moe_pool_read_state(self.handle, table.ctypes.data, usage.ctypes.data,
+                                        _stream(stream)), "moe_pool_read_state")
+        return table, usage
+
+
+def _ws(nbytes: int):
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
+
+
+# ------------------------------------------------------------------- router
+def moe_router_sum_depth(T: int, d: int) -> int:
+    return int(_lib.moe_router_sum_depth(T, d))
+
+
+def moe_router_workspace_bytes(T: int, d: int, E: int) -> int:
+    return int(_lib.moe_router_workspace_bytes(T, d, E))
+
+
+def moe_router_topk(x, w_router, logit_bias, k: int, usage_ptr: Optional[int] = None,
+                    workspace=None, out=None, stream=None):
+    """x: bf16 [T, d] CUDA; w_router fp32 [E+1, d]; logit_bias fp32 [E] or None.
+    Returns (topk_idx int32 [T,k], topk_w fp32 [T,k], shared_gate fp32 [T])."""
+    import torch
+    T, d = x.shape
+    E = w_router.shape[0] - 1
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=x.device),
+               torch.empty((T, k), dtype=torch.float32, device=x.device),
+               torch.empty((T,), dtype=torch.float32, device=x.device))
+    idx, w, s = out
+    if workspace is None:
+        workspace = _ws(moe_router_workspace_bytes(T, d, E))
+    st = _lib.moe_router_topk(_ptr(x), T, d, _ptr(w_router), _ptr(logit_bias), E, k, _ptr(idx), _ptr(w),
+                              _ptr(s), usage_ptr, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "moe_router_topk")
+    return idx, w, s
+
+
+# ---------------------------------------------------------------- bucketing
+def moe_bucket_tokens(topk_idx, E: int, workspace=None, stream=None):
+    import torch
+    T, k = topk_idx.shape
+    counts = torch.empty(E, dtype=torch.int32, device=topk_idx.device)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=topk_idx.device)
+    pair_ids = torch.empty(max(T * k, 1), dtype=torch.int32, device=topk_idx.device)
+    if workspace is None:
+        workspace = _ws(_lib.moe_bucket_workspace_bytes(T, k, E))
+    st = _lib.moe_bucket_tokens(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(pair_ids),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "moe_bucket_tokens")
+    return counts, offsets, pair_ids[:T * k]
+
+
+# --------------------------------------------------------------- expert FFN
+def moe_ffn_workspace_bytes(d, I, Ish, T, k, E, path) -> int:
+    return int(_lib.moe_ffn_workspace_bytes(C.byref(shape(d, I)), C.byref(shape(d, Ish)), T, k, E, path))
+
+
+def moe_expert_ffn_int4(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, shared_gate,
+                        path: int = MOE_PATH_DECODE, offsets=None, pair_ids=None,
+                        workspace=None, stream=None):
+    """DECODE: returns y [T, d].  BATCHED/PREFILL: returns (partial [T*k, d], shared_out [T, d])."""
+    import torch
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    if workspace is None:
+        workspace = _ws(moe_ffn_workspace_bytes(d, pool.I, Ish, T, k, pool.E, path))
+    y = partial = shared_out = None
+    if path == MOE_PATH_DECODE:
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    else:
+        partial = torch.empty((T * k, d), dtype=torch.float32, device=x.device)
+        shared_out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    st = _lib.moe_expert_ffn_int4(pool.handle, C.byref(shape(d, pool.I)), _ptr(shared_blob),
+                                  C.byref(shape(d, Ish)), _ptr(x), T, k, _ptr(topk_idx), _ptr(topk_w),
+                                  _ptr(shared_gate), _ptr(offsets), _ptr(pair_ids), _ptr(y), _ptr(partial),
+                                  _ptr(shared_out), path, _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check(st, "moe_expert_ffn_int4")
+    return y if path == MOE_PATH_DECODE else (partial, shared_out)
+
+
+def moe_combine(partial, shared_out, topk_w, shared_gate, stream=None):
+    import torch
+    T, k = topk_w.shape
+    d = partial.shape[1]
+    y = torch.empty((T, d), dtype=torch.float32, device=partial.device)
+    st = _lib.moe_combine(_ptr(partial), _ptr(shared_out), _ptr(topk_w), _ptr(shared_gate), T, k, d,
+                          _ptr(y), _stream(stream))
+    _check(st, "moe_combine")
+    return y
+
+
+# -------------------------------------------------------------- whole layer
+class Layer:
+    """Descriptor of one MoE layer (router, pool of routed experts, shared expert)."""
+
+    def __init__(self, w_router, logit_bias, pool: Pool, shared_blob, Ish: int, k: int,
+                 usage: bool = True):
+        self.w_router, self.logit_bias, self.pool, self.shared_blob = w_router, logit_bias, pool, shared_blob
+        self.k, self.Ish = k, Ish
+        self.desc = moe_layer_desc(shape(pool.d, pool.I), shape(pool.d, Ish), pool.E, k,
+                                   _ptr(w_router), _ptr(logit_bias), pool.handle.value,
+                                   _ptr(shared_blob), pool.usage_ptr if usage else None)
+
+    def workspace_bytes(self, T: int, path: int = MOE_PATH_AUTO) -> int:
+        return int(_lib.moe_layer_workspace_bytes(C.byref(self.desc), T, path))
+
+
+def moe_layer_forward(layer: Layer, x, path: int = MOE_PATH_AUTO, workspace=None, out=None,
+                      stream=None):
+    """Returns (y fp32 [T,d], topk_idx [T,k], topk_w [T,k], shared_gate [T])."""
+    import torch
+    T, d = x.shape
+    k = layer.k
+    if out is None:
+        out = (torch.empty((T, d), dtype=torch.float32, device=x.device),
+               torch.empty((T, k), dtype=torch.int32, device=x.device),
+               torch.empty((T, k), dtype=torch.float32, device=x.device),
+               torch.empty((T,), dtype=torch.float32, device=x.device))
+    y, idx, w, s = out
+    if workspace is None:
+        workspace = _ws(layer.workspace_bytes(T, path))
+    st = _lib.moe_layer_forward(C.byref(layer.desc), _ptr(x), T, _ptr(y), _ptr(idx), _ptr(w), _ptr(s),
+                                path, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "moe_layer_forward")
+    return y, idx, w, s

@@ -1,0 +1,504 @@
+// Int4 expert FFN as GEMVs (decode and batched decode).
+//
+// Experts are MLX affine int4 group-quantised (relationship-to-TurboFieldfare
+// section of the Swiftlet pages), fetched from the slot pool through the slot
+// table with 64-bit offsets; the SwiGLU form and group 64 are this library's
+// readings.  With W = s*q + b per group of 64 inputs, a group's dot product
+// is  s * sum(q x) + b * sum(x).  The kernels form sum((128 + q) x) with
+// v_dot2c_f32_bf16 on bf16 pairs built by OR-ing nibbles into 0x4300 (exact
+// 128 + q), and fold the offset into the bias term:
+//     group = s * sum((128+q) x) + (b - 128 s) * sum(x).
+// Products of bf16 values are exact in fp32; accumulation is fp32.
+//
+// gate/up: one work item = (instance, 8 rows).  Lane (row r, group g) loads
+// the 2 x 16 B codes of its group for gate and up (8 rows x 8 groups per
+// wave-load = eight 128 B segments), activations come from LDS, partial sums
+// meet through a 3-step butterfly and LDS.  h = silu(g) * u is stored as bf16
+// (hi, lo) pairs in the (x[8m+i], x[8m+i+4]) order plus per-8 sums, ready
+// for the down GEMV.
+// down (decode): one block = 8 output rows for every instance of every token,
+// so the weighted combine sum_r w_r o_r + s o_shared runs in rank order in
+// the block (no float atomics; bit-reproducible, independent of placement).
+// down (batched): one work item = (instance, 32 rows), unweighted outputs
+// written per (token, rank) pair for moe_combine.
+#include "internal.h"
+#include "device.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTC = 4;          // tokens per batched instance
+constexpr int kXPad = 36;       // LDS dwords per 32-dword group (bank spread)
+
+struct Inst {                   // batched instance
+  int32_t expert;               // -1 = shared expert
+  int32_t start;                // routed: offset into pair_ids; shared: first token
+  int32_t n;                    // tokens (1..kTC)
+};
+
+struct GateUpArgs {
+  PoolView pool;
+  const uint8_t* shared_blob;
+  int d, I, Ish, Imax, T, k;
+  const int32_t* idx;           // decode: [T*k]
+  const uint32_t* xq;           // [T][d/2]
+  const float* xs;              // [T][d/64]
+  const Inst* inst;             // batched: instances
+  const int32_t* n_routed;      // batched: device count of routed instances
+  int n_shared_inst;            // batched
+  const int32_t* pair_ids;
+  uint32_t* hq;                 // [hrows][Imax]: hi pairs then lo pairs
+  float* hs8;                   // [hrows][Imax/8]
+  int batched;
+};
+
+// Resolve instance -> (blob, I, tokens, hrows).  Returns ntok (0 = skip).
+__device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, const uint8_t** blob,
+                                       int* Iinst, int* tok, int* hrow, bool* missing) {
+  *missing = false;
+  if (!a.batched) {
+    if (routed) {
+      const int e = a.idx[i];
+      const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
+      *missing = slot < 0;
+      *blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
+      *Iinst = a.I;
+      tok[0] = i / a.k;
+      hrow[0] = i;
+    } else {
+      *blob = a.shared_blob;
+      *Iinst = a.Ish;
+      tok[0] = i;
+      hrow[0] = a.T * a.k + i;
+    }
+    return 1;
+  }
+  const Inst in = a.inst[routed ? i : *a.n_routed + i];
+  if (routed) {
+    const int e = in.expert;
+    const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
+    *missing = slot < 0;
+    *blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
+    *Iinst = a.I;
+    for (int j = 0; j < in.n; ++j) {
+      const int p = a.pair_ids[in.start + j];
+      tok[j] = p / a.k;
+      hrow[j] = p;
+    }
+  } else {
+    *blob = a.shared_blob;
+    *Iinst = a.Ish;
+    for (int j = 0; j < in.n; ++j) {
+      tok[j] = in.start + j;
+      hrow[j] = a.T * a.k + in.start + j;
+    }
+  }
+  return in.n;
+}
+
+template <int TC>
+__global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
+  extern __shared__ uint32_t xlds[];            // [TC][G][kXPad]
+  __shared__ float red[4][2][TC][8];
+  __shared__ float gu[2][TC][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = tid & 7, cpl = tid >> 3;        // row in block, group lane (0..31)
+  const int G = a.d / 64;
+  const int rbR = a.I / 8, rbS = a.Ish / 8;
+  const int nR = a.batched ? *a.n_routed : a.T * a.k;
+  const int nS = a.batched ? a.n_shared_inst : a.T;
+  const int items = nR * rbR + nS * rbS;
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const bool routed = item < nR * rbR;
+    const int rel = routed ? item : item - nR * rbR;
+    const int rb_per = routed ? rbR : rbS;
+    const int i = rel / rb_per, rb = rel % rb_per;
+    const uint8_t* blob;
+    int Iinst, tok[TC], hrow[TC];
+    bool missing;
+    const int ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
+    const BlobLayout L = blob_layout(a.d, Iinst);
+    const int o0 = rb * 8;
+
+    // stage activations (bf16 pairs) and group sums
+    for (int q = tid; q < ntok * (a.d / 8); q += 256) {
+      const int tt = q / (a.d / 8), c4 = q % (a.d / 8);           // c4: 4-dword piece
+      const uint4 v = reinterpret_cast<const uint4*>(a.xq + (size_t)tok[tt] * (a.d / 2))[c4];
+      const int g = c4 >> 3, w4 = c4 & 7;
+      *reinterpret_cast<uint4*>(&xlds[(tt * G + g) * kXPad + 4 * w4]) = v;
+    }
+    __syncthreads();
+
+    float vg[TC], vu[TC];
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) { vg[tt] = 0.f; vu[tt] = 0.f; }
+    if (!missing) {
+      const uint8_t* gc = blob + L.m[0].codes;
+      const uint8_t* uc = blob + L.m[1].codes;
+      const uint8_t* gs = blob + L.m[0].sb;
+      const uint8_t* us = blob + L.m[1].sb;
+      for (int g = cpl; g < G; g += 32) {
+        const uint64_t o = (uint64_t)(o0 + r);
+        const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
+        const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
+        const uint4 g0 = *reinterpret_cast<const uint4*>(gc + c0);
+        const uint4 g1 = *reinterpret_cast<const uint4*>(gc + c1);
+        const uint4 u0 = *reinterpret_cast<const uint4*>(uc + c0);
+        const uint4 u1 = *reinterpret_cast<const uint4*>(uc + c1);
+        const uint32_t sbg = *reinterpret_cast<const uint32_t*>(gs + ((uint64_t)g * Iinst + o) * 4);
+        const uint32_t sbu = *reinterpret_cast<const uint32_t*>(us + ((uint64_t)g * Iinst + o) * 4);
+        const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const float sg = f16_to_f32(sbg);
+        const float bg = f16_to_f32(sbg >> 16);
+        const float su = f16_to_f32(sbu);
+        const float bu = f16_to_f32(sbu >> 16);
+#pragma unroll
+        for (int tt = 0; tt < TC; ++tt) {
+          if (tt < ntok) {
+            const uint32_t* xp = &xlds[(tt * G + g) * kXPad];
+            float ag = 0.f, au = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+              const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * w);
+              const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                ag = dot2_bf16(nib_pair(gw[w], ii), xw[ii], ag);
+                au = dot2_bf16(nib_pair(uw[w], ii), xw[ii], au);
+              }
+            }
+            const float sx = a.xs[(size_t)tok[tt] * G + g];
+            vg[tt] += sg * ag + (bg - 128.0f * sg) * sx;
+            vu[tt] += su * au + (bu - 128.0f * su) * sx;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) {
+      float x1 = vg[tt], x2 = vu[tt];
+      x1 += __shfl_xor(x1, 8, 64);  x2 += __shfl_xor(x2, 8, 64);
+      x1 += __shfl_xor(x1, 16, 64); x2 += __shfl_xor(x2, 16, 64);
+      x1 += __shfl_xor(x1, 32, 64); x2 += __shfl_xor(x2, 32, 64);
+      if (lane < 8) { red[wave][0][tt][lane] = x1; red[wave][1][tt][lane] = x2; }
+    }
+    __syncthreads();
+    if (tid < 2 * TC * 8) {
+      const int m = tid / (TC * 8), tt = (tid / 8) % TC, rr = tid % 8;
+      gu[m][tt][rr] = ((red[0][m][tt][rr] + red[1][m][tt][rr]) + red[2][m][tt][rr]) + red[3][m][tt][rr];
+    }
+    __syncthreads();
+    if (tid < ntok) {
+      const int tt = tid;
+      float h[8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const float g = gu[0][tt][rr], u = gu[1][tt][rr];
+        h[rr] = missing ? 0.0f : g / (1.0f + expf(-g)) * u;
+      }
+      uint32_t hi[4], lo[4];
+      float s8 = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t a0 = f32_to_bf16(h[ii]), a1 = f32_to_bf16(h[ii + 4]);
+        const float r0 = h[ii] - __uint_as_float(a0 << 16);
+        const float r1 = h[ii + 4] - __uint_as_float(a1 << 16);
+        const uint32_t b0 = f32_to_bf16(r0), b1 = f32_to_bf16(r1);
+        hi[ii] = a0 | (a1 << 16);
+        lo[ii] = b0 | (b1 << 16);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const int p = ii & 3;
+        const float hv = ii < 4 ? __uint_as_float(hi[p] << 16) + __uint_as_float(lo[p] << 16)
+                                : __uint_as_float(hi[p] & 0xFFFF0000u) + __uint_as_float(lo[p] & 0xFFFF0000u);
+        s8 += hv;
+      }
+      uint32_t* dst = a.hq + (size_t)hrow[tt] * a.Imax;
+      *reinterpret_cast<uint4*>(dst + 4 * rb) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(dst + a.Imax / 2 + 4 * rb) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      a.hs8[(size_t)hrow[tt] * (a.Imax / 8) + rb] = s8;
+    }
+    if (missing && tid == 0) atomicOr(a.pool.err, 1);
+    __syncthreads();
+  }
+}
+
+// One group (64 inputs) of one down row against h: s*sum((128+q)h) + (b-128s)*sum(h).
+__device__ __forceinline__ float down_group(const uint8_t* blob, const BlobLayout& L, int d, int j,
+                                            int g, const uint32_t* __restrict__ hrec, int Imax,
+                                            const float* __restrict__ hs) {
+  const uint64_t c0 = ((uint64_t)(2 * g) * d + j) * 16;
+  const uint4 q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
+  const uint4 q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)d * 16);
+  const uint32_t sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * d + j) * 4);
+  const float s = f16_to_f32(sb);
+  const float b = f16_to_f32(sb >> 16);
+  const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint4* hh = reinterpret_cast<const uint4*>(hrec + 32 * g);
+  const uint4* hl = reinterpret_cast<const uint4*>(hrec + Imax / 2 + 32 * g);
+  float acc = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint4 vh = hh[w], vl = hl[w];
+    const uint32_t ph[4] = {vh.x, vh.y, vh.z, vh.w};
+    const uint32_t pl[4] = {vl.x, vl.y, vl.z, vl.w};
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t q = nib_pair(qw[w], ii);
+      acc = dot2_bf16(q, ph[ii], acc);
+      acc = dot2_bf16(q, pl[ii], acc);
+    }
+  }
+  float sh = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) sh += hs[8 * g + m];
+  return s * acc + (b - 128.0f * s) * sh;
+}
+
+struct DownArgs {
+  PoolView pool;
+  const uint8_t* shared_blob;
+  int d, I, Ish, Imax, T, k;
+  const int32_t* idx;
+  const float* w;
+  const float* sgate;
+  const uint32_t* hq;
+  const float* hs8;
+  float* y;
+  // batched
+  const Inst* inst;
+  const int32_t* n_routed;
+  int n_shared_inst;
+  const int32_t* pair_ids;
+  float* partial;
+  float* shared_out;
+};
+
+// Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order combine.
+__global__ __launch_bounds__(256) void down_decode_kernel(DownArgs a) {
+  extern __shared__ float oi[];                 // [n_inst][8]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 7, gl = lane >> 3;
+  const int j = blockIdx.x * 8 + r;
+  const int nR = a.T * a.k, nI = nR + a.T;
+  for (int i = wave; i < nI; i += 4) {
+    const uint8_t* blob;
+    int Iinst;
+    bool missing = false;
+    if (i < nR) {
+      const int e = a.idx[i];
+      const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
+      missing = slot < 0;
+      blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
+      Iinst = a.I;
+    } else {
+      blob = a.shared_blob;
+      Iinst = a.Ish;
+    }
+    const BlobLayout L = blob_layout(a.d, Iinst);
+    const uint32_t* hrec = a.hq + (size_t)i * a.Imax;
+    const float* hs = a.hs8 + (size_t)i * (a.Imax / 8);
+    float acc = 0.f;
+    if (!missing)
+      for (int g = gl; g < Iinst / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
+    acc += __shfl_xor(acc, 8, 64);
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (lane < 8) oi[i * 8 + lane] = acc;
+    if (missing && lane == 0) atomicOr(a.pool.err, 1);
+  }
+  __syncthreads();
+  if (tid < 8 * a.T) {
+    const int t = tid / 8, rr = tid % 8;
+    float y = 0.f;
+    for (int q = 0; q < a.k; ++q) y += a.w[t * a.k + q] * oi[(t * a.k + q) * 8 + rr];
+    y += a.sgate[t] * oi[(nR + t) * 8 + rr];
+    a.y[(size_t)t * a.d + blockIdx.x * 8 + rr] = y;
+  }
+}
+
+// Batched: item = (instance, 32 rows); wave = 8 rows x 8 group lanes.
+__global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 7, gl = lane >> 3;
+  const int rbs = a.d / 32;
+  const int nR = *a.n_routed;
+  const int items = (nR + a.n_shared_inst) * rbs;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int ii = item / rbs, rb = item % rbs;
+    const bool routed = ii < nR;
+    const Inst in = a.inst[ii];
+    const uint8_t* blob;
+    int Iinst;
+    bool missing = false;
+    if (routed) {
+      const int e = in.expert;
+      const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
+      missing = slot < 0;
+      blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
+      Iinst = a.I;
+    } else {
+      blob = a.shared_blob;
+      Iinst = a.Ish;
+    }
+    const BlobLayout L = blob_layout(a.d, Iinst);
+    const int j = rb * 32 + wave * 8 + r;
+    for (int tt = 0; tt < in.n; ++tt) {
+      const int hrow = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
+      const uint32_t* hrec = a.hq + (size_t)hrow * a.Imax;
+      const float* hs = a.hs8 + (size_t)hrow * (a.Imax / 8);
+      float acc = 0.f;
+      if (!missing)
+        for (int g = gl; g < Iinst / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
+      acc += __shfl_xor(acc, 8, 64);
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      if (lane < 8) {
+        if (routed) a.partial[(size_t)hrow * a.d + j] = acc;
+        else a.shared_out[(size_t)(in.start + tt) * a.d + j] = acc;
+      }
+    }
+    if (missing && tid == 0) atomicOr(a.pool.err, 1);
+  }
+}
+
+// Batched instance list: per expert ceil(count/kTC) chunks in expert order,
+// then ceil(T/kTC) shared chunks.  One block.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int T,
+                                                    Inst* __restrict__ inst, int32_t* __restrict__ n_routed) {
+  __shared__ int sums[1024];
+  const int tid = threadIdx.x;
+  // E <= 1024: one expert per thread
+  const int c = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
+  const int nch = (c + kTC - 1) / kTC;
+  sums[tid] = nch;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? sums[tid - off] : 0;
+    __syncthreads();
+    sums[tid] += v;
+    __syncthreads();
+  }
+  const int base = sums[tid] - nch;
+  for (int q = 0; q < nch; ++q) {
+    Inst in;
+    in.expert = tid;
+    in.start = offsets[tid] + q * kTC;
+    in.n = min(kTC, c - q * kTC);
+    inst[base + q] = in;
+  }
+  const int total = sums[1023];
+  if (tid == 0) *n_routed = total;
+  const int nsh = (T + kTC - 1) / kTC;
+  for (int q = tid; q < nsh; q += 1024) {
+    Inst in;
+    in.expert = -1;
+    in.start = q * kTC;
+    in.n = min(kTC, T - q * kTC);
+    inst[total + q] = in;
+  }
+}
+
+struct FfnWs {
+  uint32_t* xq; float* xs;
+  uint32_t* hq; float* hs8;
+  Inst* inst; int32_t* n_routed;
+};
+
+bool carve_ffn(Carver& c, int d, int Imax, int T, int k, int path, FfnWs* w) {
+  const size_t hrows = (size_t)T * k + T;
+  w->xq = c.take<uint32_t>((size_t)T * d / 2);
+  w->xs = c.take<float>((size_t)T * d / 64);
+  w->hq = c.take<uint32_t>(hrows * Imax);
+  w->hs8 = c.take<float>(hrows * Imax / 8);
+  w->inst = nullptr;
+  w->n_routed = nullptr;
+  if (path != MOE_PATH_DECODE) {
+    w->inst = c.take<Inst>((size_t)T * k + (T + kTC - 1) / kTC);
+    w->n_routed = c.take<int32_t>(64);
+  }
+  return c.ok();
+}
+
+int grid_for(int items_upper) {
+  return items_upper < 8192 ? (items_upper > 0 ? items_upper : 1) : 8192;
+}
+
+}  // namespace
+
+int resolve_path(int path, int T, int k, int E) {
+  if (path != MOE_PATH_AUTO) return path;
+  if (T <= 4) return MOE_PATH_DECODE;
+  return MOE_PATH_BATCHED;
+}
+
+size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
+  (void)E;
+  Carver c(nullptr, (size_t)-1);
+  FfnWs w;
+  carve_ffn(c, d, I > Ish ? I : Ish, T, k, path, &w);
+  return c.off + 256;
+}
+
+int xprep_launch(const uint16_t* x, int T, int d, uint32_t* xq, float* xs, hipStream_t s);
+
+int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int Imax = f.I > f.Ish ? f.I : f.Ish;
+  Carver c(ws, ws_bytes);
+  FfnWs w;
+  if (!carve_ffn(c, f.d, Imax, f.T, f.k, path, &w)) return MOE_ERR_INVALID_ARG;
+  const uint32_t* xq = f.xq;
+  const float* xs = f.xs;
+  if (!xq) {
+    MOE_TRY(xprep_launch(f.x, f.T, f.d, w.xq, w.xs, s));
+    xq = w.xq;
+    xs = w.xs;
+  }
+  const int G = f.d / 64;
+  GateUpArgs g{};
+  g.pool = f.pool; g.shared_blob = f.shared_blob;
+  g.d = f.d; g.I = f.I; g.Ish = f.Ish; g.Imax = Imax; g.T = f.T; g.k = f.k;
+  g.idx = f.idx; g.xq = xq; g.xs = xs;
+  g.hq = w.hq; g.hs8 = w.hs8;
+  DownArgs dn{};
+  dn.pool = f.pool; dn.shared_blob = f.shared_blob;
+  dn.d = f.d; dn.I = f.I; dn.Ish = f.Ish; dn.Imax = Imax; dn.T = f.T; dn.k = f.k;
+  dn.idx = f.idx; dn.w = f.w; dn.sgate = f.sgate; dn.hq = w.hq; dn.hs8 = w.hs8; dn.y = f.y;
+
+  if (path == MOE_PATH_DECODE) {
+    g.batched = 0;
+    const int items = f.T * f.k * (f.I / 8) + f.T * (f.Ish / 8);
+    const size_t lds = (size_t)1 * G * kXPad * 4;
+    void* args[] = {&g};
+    MOE_HIP(hipLaunchKernel((void*)gate_up_kernel<1>, dim3(items), dim3(256), args, lds, s));
+    const int nI = f.T * (f.k + 1);
+    void* dargs[] = {&dn};
+    MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(256), dargs,
+                            (size_t)nI * 8 * sizeof(float), s));
+    return MOE_OK;
+  }
+  // batched: bucketed instances of up to kTC tokens
+  if (!f.offsets || !f.pair_ids || !f.partial || !f.shared_out) return MOE_ERR_INVALID_ARG;
+  const int nsh = (f.T + kTC - 1) / kTC;
+  plan_kernel<<<1, 1024, 0, s>>>(f.offsets, f.pool.E, f.T, w.inst, w.n_routed);
+  MOE_HIP(hipGetLastError());
+  g.batched = 1;
+  g.inst = w.inst; g.n_routed = w.n_routed; g.n_shared_inst = nsh; g.pair_ids = f.pair_ids;
+  const long upper = ((long)f.T * f.k + nsh) * (Imax / 8);
+  const size_t lds = (size_t)kTC * G * kXPad * 4;
+  void* args[] = {&g};
+  MOE_HIP(hipLaunchKernel((void*)gate_up_kernel<kTC>, dim3(grid_for((int)(upper < 65536 ? upper : 65536))),
+                          dim3(256), args, lds, s));
+  dn.inst = w.inst; dn.n_routed = w.n_routed; dn.n_shared_inst = nsh; dn.pair_ids = f.pair_ids;
+  dn.partial = f.partial; dn.shared_out = f.shared_out;
+  const long dupper = ((long)f.T * f.k + nsh) * (f.d / 32);
+  void* dargs[] = {&dn};
+  MOE_HIP(hipLaunchKernel((void*)down_batched_kernel, dim3(grid_for((int)(dupper < 65536 ? dupper : 65536))),
+                          dim3(256), dargs, 0, s));
+  return MOE_OK;
+}
+
+}  // namespace moe

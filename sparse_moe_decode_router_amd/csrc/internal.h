@@ -1,0 +1,123 @@
+// Internal declarations shared by the libmoe355 translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe355.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- errors
+int hip_fail(hipError_t e);            // records the HIP error, returns MOE_ERR_HIP
+#define MOE_HIP(call)                                    \
+  do {                                                   \
+    hipError_t moe_e_ = (call);                          \
+    if (moe_e_ != hipSuccess) return ::moe::hip_fail(moe_e_); \
+  } while (0)
+#define MOE_CHECK(cond) \
+  do { if (!(cond)) return MOE_ERR_INVALID_ARG; } while (0)
+#define MOE_TRY(call) \
+  do { int moe_s_ = (call); if (moe_s_ != MOE_OK) return moe_s_; } while (0)
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// -------------------------------------------------------------- layout
+// Byte offsets of the six sections of an expert blob (see moe355.h).
+struct MatLayout {
+  uint64_t codes;   // [in/32][out][16]
+  uint64_t sb;      // [in/64][out][2] fp16 (scale, bias)
+};
+struct BlobLayout {
+  MatLayout m[3];   // gate, up, down
+  uint64_t bytes, stride;
+};
+
+__host__ __device__ inline BlobLayout blob_layout(int d, int I) {
+  BlobLayout L;
+  uint64_t off = 0;
+  const int outs[3] = {I, I, d};
+  const int ins[3] = {d, d, I};
+  for (int m = 0; m < 3; ++m) {
+    L.m[m].codes = off;
+    off += (uint64_t)outs[m] * (uint64_t)ins[m] / 2;
+    L.m[m].sb = off;
+    off += (uint64_t)(ins[m] / 64) * (uint64_t)outs[m] * 4;
+  }
+  L.bytes = off;
+  L.stride = (off + 4095) & ~(uint64_t)4095;
+  return L;
+}
+
+bool shape_ok(const moe_ffn_shape* sh);
+
+// Device view of a pool, passed to kernels by value.
+struct PoolView {
+  const uint8_t* slab;
+  uint64_t stride;
+  const int32_t* slot_table;
+  int32_t* err;
+  int32_t E;
+};
+bool pool_view(const moe_pool* p, PoolView* v);
+
+// ------------------------------------------------------------ workspace
+// Carves a caller workspace into 256-byte aligned pieces.
+struct Carver {
+  uint8_t* base;
+  size_t size, off;
+  explicit Carver(void* b, size_t s) : base((uint8_t*)b), size(s), off(0) {}
+  template <class T> T* take(size_t n) {
+    size_t at = (off + 255) & ~(size_t)255;
+    off = at + n * sizeof(T);
+    return (base && off <= size) ? (T*)(base + at) : nullptr;
+  }
+  bool ok() const { return off <= size; }
+};
+
+// -------------------------------------------------------- internal entry
+// Router pieces used by the layer driver (router.hip).
+struct RouterWs {
+  float* logits;      // [T][E+1]
+  uint32_t* ticket;   // one counter, zero between calls
+  uint32_t* xq;       // [T][d/2]  bf16 pairs (x[8m+i], x[8m+i+4])
+  float* xs;          // [T][d/64] group sums of x
+};
+size_t router_ws_bytes(int T, int d, int E);
+bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws);
+int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias,
+                  int E, int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
+                  const RouterWs& ws, hipStream_t s);
+
+int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts,
+                  int32_t* offsets, int32_t* pair_ids, void* ws, size_t ws_bytes,
+                  hipStream_t s);
+size_t bucket_ws_bytes(int T, int k, int E);
+
+int combine_launch(const float* partial, const float* shared_out, const float* w,
+                   const float* sgate, int T, int k, int d, float* y, hipStream_t s);
+
+// Expert FFN with x already prepared (xq/xs from the router workspace).
+struct FfnArgs {
+  PoolView pool;
+  int d, I, Ish;
+  const uint8_t* shared_blob;
+  const uint16_t* x;        // bf16 [T][d]
+  const uint32_t* xq;       // [T][d/2]
+  const float* xs;          // [T][d/64]
+  int T, k;
+  const int32_t* idx;       // [T][k]
+  const float* w;           // [T][k]
+  const float* sgate;       // [T]
+  const int32_t* offsets;   // [E+1]
+  const int32_t* pair_ids;  // [T*k]
+  float* y;                 // decode: [T][d]
+  float* partial;           // batched: [T*k][d]
+  float* shared_out;        // batched: [T][d]
+};
+size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
+int ffn_launch(const FfnArgs& a, int path, void* ws, size_t ws_bytes, hipStream_t s);
+int resolve_path(int path, int T, int k, int E);
+
+}  // namespace moe

@@ -1,0 +1,256 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Bars: routing indices, bucket offsets and pair lists bit-exact (up to
+certified near-ties of fp32 logits, where any correct choice is accepted and
+the output is compared with the oracle run on the device's choice); weights
+and gates within fp32 rounding; layer outputs within
+max|y - y_ref| <= 2e-3 * max|y_ref| per step; runs that differ only in expert
+placement bit-identical.
+"""
+import numpy as np
+import pytest
+
+import moe_synth as ms
+from oracle import bucket as obucket
+from oracle import layer as olayer
+from gpu_support import DeviceLayer, certify_routing, assert_close_y
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("sparse_moe_decode_router_amd")
+
+TINY = ms.CONFIGS["tiny"]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return DeviceLayer(TINY)
+
+
+@pytest.fixture(scope="module")
+def l35():
+    return DeviceLayer(ms.CONFIGS["decode35b"])
+
+
+@pytest.fixture(scope="module")
+def l80():
+    return DeviceLayer(ms.scaled(ms.CONFIGS["decode80b"], n_slots=512))
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _check_layer_step(L, step, path=moe.MOE_PATH_AUTO, T=None):
+    xb, x = L.x(step, T)
+    y, idx, w, s = moe.moe_layer_forward(L.layer, x, path=path)
+    torch.cuda.synchronize()
+    idx_np = _np(idx)
+    depth = moe.moe_router_sum_depth(xb.shape[0], L.cfg.d)
+    namb, amb = certify_routing(xb, L.Wr_np, L.bias_np, L.cfg.k, idx_np, depth)
+    ref = L.oracle(xb, idx=idx_np if namb else None)
+    assert np.array_equal(idx_np, ref["idx"])
+    assert np.allclose(_np(w), ref["w"], rtol=0, atol=2e-5)
+    assert np.allclose(_np(s), ref["s"], rtol=0, atol=2e-6)
+    rel = [assert_close_y(_np(y)[t:t + 1], ref["y"][t:t + 1]) for t in range(xb.shape[0])]
+    return max(rel), namb, _np(y), idx_np
+
+
+# ------------------------------------------------------------------ router
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode35b", 1), ("decode80b", 1), ("decode80b", 3),
+                                    ("decode80b", 64), ("decode80b", 300)])
+def test_router_parity(name, T):
+    cfg = ms.CONFIGS[name]
+    Wr = ms.router_weight(cfg)
+    bias = ms.logit_bias(cfg)
+    Wd = torch.from_numpy(Wr).cuda()
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    usage = torch.zeros(cfg.E, dtype=torch.int32, device="cuda")
+    total = np.zeros(cfg.E, np.int64)
+    namb_all = 0
+    for step in range(3):
+        xb = ms.x_bits(cfg, step, T)
+        x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        idx, w, s = moe.moe_router_topk(x, Wd, bd, cfg.k, usage_ptr=usage.data_ptr())
+        torch.cuda.synchronize()
+        idx = _np(idx)
+        namb, amb = certify_routing(xb, Wr, bias, cfg.k, idx, moe.moe_router_sum_depth(T, cfg.d))
+        namb_all += namb
+        ref_idx, ref_w, ref_s, _ = olayer.route(xb, Wr, bias, cfg.k)
+        l, _ = olayer.router_logits(olayer.bf16_to_f64(xb), Wr, bias)
+        w_ref = olayer.topk_weights(l, idx)        # weights of the device's own choice
+        assert np.allclose(_np(w), w_ref, rtol=0, atol=2e-5)
+        assert np.allclose(_np(w).sum(1), 1.0, atol=1e-5)
+        assert np.allclose(_np(s), ref_s, rtol=0, atol=2e-6)
+        total += np.bincount(idx.ravel(), minlength=cfg.E)
+    assert np.array_equal(_np(usage).astype(np.int64), total)
+    assert namb_all <= max(1, 3 * T // 50)
+
+
+def test_router_tie_rule_on_device():
+    """Identical router rows give identical fp32 logits; the lower index wins."""
+    cfg = TINY
+    Wr = ms.router_weight(cfg).copy()
+    Wr[9] = Wr[2]
+    b = np.zeros(cfg.E, np.float32)
+    b[2] = b[9] = 40.0
+    x = torch.from_numpy(ms.x_bits(cfg, 0).view(np.int16)).cuda().view(torch.bfloat16)
+    idx, w, _ = moe.moe_router_topk(x, torch.from_numpy(Wr).cuda(), torch.from_numpy(b).cuda(), 2)
+    idx = _np(idx)
+    assert (idx[:, 0] == 2).all() and (idx[:, 1] == 9).all()
+    assert np.allclose(_np(w), 0.5, atol=1e-6)
+
+
+@pytest.mark.parametrize("k", [1, 16])
+def test_router_k_extremes(k):
+    cfg = TINY
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 1)
+    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    idx, w, _ = moe.moe_router_topk(x, torch.from_numpy(Wr).cuda(), None, k)
+    idx, w = _np(idx), _np(w)
+    certify_routing(xb, Wr, None, k, idx, moe.moe_router_sum_depth(cfg.T, cfg.d))
+    if k == 1:
+        assert (w == 1.0).all()
+    else:                                    # k = E: the full softmax
+        l, _ = olayer.router_logits(olayer.bf16_to_f64(xb), Wr, None)
+        p = np.exp(l - l.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        assert np.allclose(np.take_along_axis(p, idx.astype(np.int64), 1), w, atol=2e-6)
+
+
+# ---------------------------------------------------------------- bucketing
+@pytest.mark.parametrize("T,k,E", [(1, 10, 512), (4, 2, 16), (64, 10, 512), (100, 10, 512),
+                                   (700, 3, 1024), (4096, 10, 512), (5, 7, 7)])
+def test_bucket_bit_exact(T, k, E):
+    g = np.random.default_rng(T * 1000 + k)
+    idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    if T >= 64:   # skew: many pairs in a few buckets
+        hot = g.random(idx.shape) < 0.3
+        idx[hot] = np.minimum(idx[hot] % 5, E - 1)
+        for t in range(T):       # restore distinctness within a token
+            seen = set()
+            for r in range(k):
+                while int(idx[t, r]) in seen:
+                    idx[t, r] = (idx[t, r] + 7) % E
+                seen.add(int(idx[t, r]))
+    c, o, p = moe.moe_bucket_tokens(torch.from_numpy(idx).cuda(), E)
+    rc, ro, rp = obucket.bucket(idx, E)
+    assert np.array_equal(_np(c), rc) and np.array_equal(_np(o), ro) and np.array_equal(_np(p), rp)
+
+
+# ------------------------------------------------------------ decode layer
+def test_tiny_layer_parity(tiny):
+    worst = 0
+    for step in range(TINY.steps):
+        rel, _, _, _ = _check_layer_step(tiny, step)
+        worst = max(worst, rel)
+    print(f"tiny worst rel err {worst:.2e}")
+
+
+def test_decode35b_parity(l35):
+    worst = max(_check_layer_step(l35, s)[0] for s in range(4))
+    print(f"35B decode worst rel err {worst:.2e}")
+
+
+def test_decode80b_parity(l80):
+    worst = max(_check_layer_step(l80, s)[0] for s in range(4))
+    print(f"80B decode worst rel err {worst:.2e}")
+
+
+def test_decode80b_small_T(l80):
+    for T in (2, 4, 8):
+        _check_layer_step(l80, 10 + T, path=moe.MOE_PATH_DECODE, T=T)
+
+
+def test_batched80b_parity(l80):
+    rel, namb, y, idx = _check_layer_step(l80, 0, path=moe.MOE_PATH_BATCHED, T=64)
+    print(f"80B batched T=64 rel err {rel:.2e}, ambiguous {namb}")
+
+
+def test_token_independence(l80):
+    """Row t of a T=64 batched call vs a T=1 decode call on x_t: routing
+    bit-identical, outputs within tolerance of each other."""
+    xb, x = l80.x(5, 64)
+    yb, ib, _, _ = moe.moe_layer_forward(l80.layer, x, path=moe.MOE_PATH_BATCHED)
+    for t in (0, 17, 63):
+        y1, i1, _, _ = moe.moe_layer_forward(l80.layer, x[t:t + 1].contiguous(), path=moe.MOE_PATH_DECODE)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(i1)[0], _np(ib)[t])
+        assert_close_y(_np(y1)[0], _np(yb)[t].astype(np.float64))
+
+
+# ------------------------------------------------------ placement invariance
+def test_placement_invariance_bit_identical():
+    """Two pools holding the same experts at different slots, and a smaller
+    pool refilled step by step through LFU + recency: identical bits."""
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], E=64, k=6, steps=12)
+    A = DeviceLayer(cfg, table=np.arange(cfg.E))
+    B = DeviceLayer(cfg, table=np.random.default_rng(3).permutation(cfg.E))
+    C_ = DeviceLayer(cfg, table=None, n_slots=16)        # starts empty
+    host = torch.from_numpy(np.stack([A.blob(e) for e in range(cfg.E)])).pin_memory()
+    for step in range(cfg.steps):
+        xb, x = A.x(step)
+        ya, ia, _, _ = moe.moe_layer_forward(A.layer, x)
+        yb, ib, _, _ = moe.moe_layer_forward(B.layer, x)
+        # partial residency: route, refill the pool, then run the experts
+        idx, w, s = moe.moe_router_topk(x, C_.Wr, C_.bias, cfg.k)
+        torch.cuda.synchronize()
+        C_.pool.refill(_np(idx).ravel(), host, A.pool.stride)
+        yc = moe.moe_expert_ffn_int4(C_.pool, C_.shared_blob, cfg.I_shared, x, idx, w, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(ia), _np(ib)) and np.array_equal(_np(ia), _np(idx))
+        assert np.array_equal(_np(ya), _np(yb))
+        assert np.array_equal(_np(ya), _np(yc))
+    st = C_.pool.stats()
+    assert st["misses"] > 0 and st["hits"] > 0
+    assert C_.pool.check_error() == moe.MOE_OK
+
+
+def test_pool_state_after_refill():
+    cfg = ms.scaled(TINY, E=16, k=2)
+    L = DeviceLayer(cfg, table=None, n_slots=4)
+    host = torch.from_numpy(np.stack([L.blob(e) for e in range(cfg.E)])).pin_memory()
+    sel_steps = [[3, 5], [3, 9], [1, 2], [5, 3]]
+    from oracle import lfu as olfu
+    sim = olfu.SlotPoolSim(cfg.E, 4)
+    for sel in sel_steps:
+        L.pool.refill(sel, host, L.pool.stride)
+        sim.plan(sel)
+    table, _ = L.pool.read_state()
+    assert table.tolist() == sim.slot_of
+
+
+def test_not_resident_sets_error_word():
+    cfg = ms.scaled(TINY, E=16, k=2)
+    L = DeviceLayer(cfg, table=np.arange(16), resident=[0, 1, 2])    # most experts absent
+    _, x = L.x(0)
+    moe.moe_layer_forward(L.layer, x)
+    assert L.pool.check_error() == moe.MOE_ERR_NOT_RESIDENT
+    assert L.pool.check_error() == moe.MOE_OK        # cleared by the read
+
+
+def test_shared_intermediate_differs():
+    cfg = ms.scaled(TINY, I=64, I_shared=128, d=512)
+    L = DeviceLayer(cfg)
+    for path in (moe.MOE_PATH_DECODE, moe.MOE_PATH_BATCHED):
+        _check_layer_step(L, 1, path=path)
+
+
+def test_usage_counters_match_selections(l35):
+    l35.pool.reset_usage()
+    tot = np.zeros(l35.cfg.E, np.int64)
+    for step in range(5):
+        _, x = l35.x(100 + step)
+        _, idx, _, _ = moe.moe_layer_forward(l35.layer, x)
+        torch.cuda.synchronize()
+        tot += np.bincount(_np(idx).ravel(), minlength=l35.cfg.E)
+    _, usage = l35.pool.read_state()
+    assert np.array_equal(usage.astype(np.int64), tot)
+
+
+def test_zero_tokens_is_noop(tiny):
+    x = torch.empty((0, TINY.d), dtype=torch.bfloat16, device="cuda")
+    y, idx, w, s = moe.moe_layer_forward(tiny.layer, x)
+    assert y.shape == (0, TINY.d)
