@@ -166,27 +166,33 @@ def main():
     ms_step = ms_total / K
     assert torch.equal(y, y_eager) and torch.equal(idx, idx_eager), "graph replay differs from eager"
 
-    # dominant kernels: the expert FFN of each step (gate/up + down), timed
-    # with events on the launch stream around the FFN call alone
-    ffn_ev = []
-    wsr = torch.zeros(moe.moe_router_workspace_bytes(1, cfg.d, cfg.E), dtype=torch.uint8, device="cuda")
+    # dominant kernels: the expert FFN of each step (gate/up + down, two
+    # launches), replayed alone from a graph over the same steps with the
+    # routing the layer produced; HIP events on the launch stream
     wsf = torch.zeros(moe.moe_ffn_workspace_bytes(cfg.d, cfg.I, cfg.I_shared, 1, cfg.k, cfg.E,
                                                   moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
-    nf = min(K, 200)
+    yf = torch.empty((nsteps, 1, cfg.d), dtype=torch.float32, device="cuda")
+
+    def ffn(i):
+        L = layers[i % R]
+        moe.moe_expert_ffn_int4(L.pool, L.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
+                                workspace=wsf, out=yf[i])
+
+    gf = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
-        for i in range(W, W + nf):
-            L = layers[i % R]
-            moe.moe_router_topk(xall[i], L.w_router, L.logit_bias, cfg.k, workspace=wsr,
-                                out=(idx[i], w[i], s[i]))
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            moe.moe_expert_ffn_int4(L.pool, L.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
-                                    workspace=wsf)
-            b.record(stream)
-            ffn_ev.append((a, b))
+        with torch.cuda.graph(gf, stream=stream):
+            for i in range(W, nsteps):
+                ffn(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        gf.replay()
+        f1.record(stream)
         torch.cuda.synchronize()
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ffn_ev]))
+    ffn_ms = f0.elapsed_time(f1) / K
+    assert torch.equal(yf[W:], y[W:]), "FFN-only replay differs from the layer"
     expert_bytes = (cfg.k + 1) * moe.moe_blob_bytes(cfg.d, cfg.I)
     achieved = expert_bytes / (ffn_ms * 1e-3) / 1e9
     layer_gbs = expert_bytes / (ms_step * 1e-3) / 1e9

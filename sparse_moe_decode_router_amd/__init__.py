@@ -362,7 +362,7 @@ def moe_ffn_workspace_bytes(d, I, Ish, T, k, E, path) -> int:
 
 def moe_expert_ffn_int4(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, shared_gate,
                         path: int = MOE_PATH_DECODE, offsets=None, pair_ids=None,
-                        workspace=None, stream=None):
+                        workspace=None, out=None, stream=None):
     """DECODE: returns y [T, d].  BATCHED/PREFILL: returns (partial [T*k, d], shared_out [T, d])."""
     import torch
     T, d = x.shape
@@ -371,7 +371,7 @@ def moe_expert_ffn_int4(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, 
         workspace = _ws(moe_ffn_workspace_bytes(d, pool.I, Ish, T, k, pool.E, path))
     y = partial = shared_out = None
     if path == MOE_PATH_DECODE:
-        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
     else:
         partial = torch.empty((T * k, d), dtype=torch.float32, device=x.device)
         shared_out = torch.empty((T, d), dtype=torch.float32, device=x.device)

@@ -53,6 +53,28 @@ __device__ __forceinline__ float f32_unorder(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// Wave-wide max of a uint32 via DPP (pair, quad, row rotations, row
+// broadcasts); lane 63 ends with the maximum, which is returned to all lanes.
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t t) { return v > t ? v : t; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));
+  v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));
+  v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const int o = __shfl_xor(v, s, 64);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 }  // namespace moe

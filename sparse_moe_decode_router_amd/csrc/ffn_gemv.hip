@@ -23,6 +23,7 @@
 // written per (token, rank) pair for moe_combine.
 #include "internal.h"
 #include "device.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -40,7 +41,13 @@ struct GateUpArgs {
   PoolView pool;
   const uint8_t* shared_blob;
   int d, I, Ish, Imax, T, k;
-  const int32_t* idx;           // decode: [T*k]
+  int32_t* idx;                 // decode: [T*k] (input, or output when routing here)
+  float* w;                     // decode: [T*k] output when routing here
+  float* sgate;                 // decode: [T] output when routing here
+  const float* logits;          // decode: [T][E+1] -> route in-kernel
+  const float* bias;            // [E] or null
+  uint32_t* usage;              // [E] or null
+  int32_t* sel_slot;            // decode: [T*k] slot of each selection, for the down pass
   const uint32_t* xq;           // [T][d/2]
   const float* xs;              // [T][d/64]
   const Inst* inst;             // batched: instances
@@ -96,9 +103,16 @@ __device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, 
   return in.n;
 }
 
-template <int TC>
+constexpr int kGMax = 4;        // groups of 64 inputs per lane (d <= 8192)
+
+// Decode blocks of routed instances select their expert in-kernel: the
+// token's logits (+ bias) and the slot table are staged in LDS, wave 0 runs
+// the top-k, and the block of (rank 0, rows 0..7) publishes the token's
+// indices, weights, shared gate and usage.  This trades a redundant ~1k-cycle
+// selection per block for the dependent global loads of a separate top-k.
+template <int TC, int NK>
 __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
-  extern __shared__ uint32_t xlds[];            // [TC][G][kXPad]
+  extern __shared__ uint32_t xlds[];            // [TC][G][kXPad] | routing area
   __shared__ float red[4][2][TC][8];
   __shared__ float gu[2][TC][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,6 +122,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   const int nR = a.batched ? *a.n_routed : a.T * a.k;
   const int nS = a.batched ? a.n_shared_inst : a.T;
   const int items = nR * rbR + nS * rbS;
+  const int E = a.pool.E;
+  // routing area (decode): scratch | logits | slots | sel_l | sel_e
+  uint32_t* tscr = xlds + TC * G * kXPad;                          // topk scratch
+  float* rl = reinterpret_cast<float*>(tscr + topk_scratch_words(E));   // [E+1] logits
+  int32_t* rslot = reinterpret_cast<int32_t*>(rl + E + 1);       // [E] slot table
+  float* sel_l = reinterpret_cast<float*>(rslot + E);            // [k]
+  int32_t* sel_e = reinterpret_cast<int32_t*>(sel_l + a.k);      // [k]
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const bool routed = item < nR * rbR;
@@ -116,12 +137,60 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     const int i = rel / rb_per, rb = rel % rb_per;
     const uint8_t* blob;
     int Iinst, tok[TC], hrow[TC];
-    bool missing;
-    const int ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
+    bool missing = false;
+    int ntok;
+    if (!a.batched && routed && a.logits) {
+      const int t = i / a.k, rank = i % a.k;
+      const float* lrow = a.logits + (size_t)t * (E + 1);
+      for (int q = tid; q <= E; q += 256) rl[q] = (q < E && a.bias) ? lrow[q] + a.bias[q] : lrow[q];
+      for (int q = tid; q < E; q += 256) rslot[q] = a.pool.slot_table[q];
+      __syncthreads();
+      if (wave == 0) {
+        topk_select<NK>(rl, nullptr, E, a.k, sel_l, sel_e, tscr);
+        if (rank == 0 && rb == 0) {
+          topk_finish(sel_l, sel_e, a.k, a.idx + (size_t)t * a.k, a.w + (size_t)t * a.k, a.usage);
+          if (lane == 0) a.sgate[t] = sigmoidf_(rl[E]);
+        }
+      }
+      __syncthreads();
+      const int e = sel_e[rank];
+      const int slot = rslot[e];
+      missing = slot < 0;
+      blob = a.pool.slab + (uint64_t)(missing ? 0 : slot) * a.pool.stride;
+      Iinst = a.I;
+      tok[0] = t;
+      hrow[0] = i;
+      ntok = 1;
+      if (rb == 0 && tid == 0) a.sel_slot[i] = slot;
+    } else {
+      ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
+      if (!a.batched && routed && rb == 0 && tid == 0)
+        a.sel_slot[i] = missing ? -1 : (int32_t)((blob - a.pool.slab) / a.pool.stride);
+    }
     const BlobLayout L = blob_layout(a.d, Iinst);
     const int o0 = rb * 8;
 
-    // stage activations (bf16 pairs) and group sums
+    // 1. weight loads first: all of this lane's codes and (scale, bias) words
+    uint4 cg[kGMax][2], cu[kGMax][2];
+    uint32_t sbg[kGMax], sbu[kGMax];
+    if (!missing) {
+      const uint64_t o = (uint64_t)(o0 + r);
+#pragma unroll
+      for (int gi = 0; gi < kGMax; ++gi) {
+        const int g = cpl + 32 * gi;
+        if (g < G) {
+          const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
+          const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
+          cg[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c0);
+          cg[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c1);
+          cu[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c0);
+          cu[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c1);
+          sbg[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[0].sb + ((uint64_t)g * Iinst + o) * 4);
+          sbu[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[1].sb + ((uint64_t)g * Iinst + o) * 4);
+        }
+      }
+    }
+    // 2. stage activations (bf16 pairs) while the weights are in flight
     for (int q = tid; q < ntok * (a.d / 8); q += 256) {
       const int tt = q / (a.d / 8), c4 = q % (a.d / 8);           // c4: 4-dword piece
       const uint4 v = reinterpret_cast<const uint4*>(a.xq + (size_t)tok[tt] * (a.d / 2))[c4];
@@ -134,26 +203,16 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TC; ++tt) { vg[tt] = 0.f; vu[tt] = 0.f; }
     if (!missing) {
-      const uint8_t* gc = blob + L.m[0].codes;
-      const uint8_t* uc = blob + L.m[1].codes;
-      const uint8_t* gs = blob + L.m[0].sb;
-      const uint8_t* us = blob + L.m[1].sb;
-      for (int g = cpl; g < G; g += 32) {
-        const uint64_t o = (uint64_t)(o0 + r);
-        const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
-        const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
-        const uint4 g0 = *reinterpret_cast<const uint4*>(gc + c0);
-        const uint4 g1 = *reinterpret_cast<const uint4*>(gc + c1);
-        const uint4 u0 = *reinterpret_cast<const uint4*>(uc + c0);
-        const uint4 u1 = *reinterpret_cast<const uint4*>(uc + c1);
-        const uint32_t sbg = *reinterpret_cast<const uint32_t*>(gs + ((uint64_t)g * Iinst + o) * 4);
-        const uint32_t sbu = *reinterpret_cast<const uint32_t*>(us + ((uint64_t)g * Iinst + o) * 4);
-        const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        const float sg = f16_to_f32(sbg);
-        const float bg = f16_to_f32(sbg >> 16);
-        const float su = f16_to_f32(sbu);
-        const float bu = f16_to_f32(sbu >> 16);
+#pragma unroll
+      for (int gi = 0; gi < kGMax; ++gi) {
+        const int g = cpl + 32 * gi;
+        if (g >= G) continue;
+        const uint32_t gw[8] = {cg[gi][0].x, cg[gi][0].y, cg[gi][0].z, cg[gi][0].w,
+                                cg[gi][1].x, cg[gi][1].y, cg[gi][1].z, cg[gi][1].w};
+        const uint32_t uw[8] = {cu[gi][0].x, cu[gi][0].y, cu[gi][0].z, cu[gi][0].w,
+                                cu[gi][1].x, cu[gi][1].y, cu[gi][1].z, cu[gi][1].w};
+        const float sg = f16_to_f32(sbg[gi]), bg = f16_to_f32(sbg[gi] >> 16);
+        const float su = f16_to_f32(sbu[gi]), bu = f16_to_f32(sbu[gi] >> 16);
 #pragma unroll
         for (int tt = 0; tt < TC; ++tt) {
           if (tt < ntok) {
@@ -226,14 +285,11 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   }
 }
 
-// One group (64 inputs) of one down row against h: s*sum((128+q)h) + (b-128s)*sum(h).
-__device__ __forceinline__ float down_group(const uint8_t* blob, const BlobLayout& L, int d, int j,
-                                            int g, const uint32_t* __restrict__ hrec, int Imax,
-                                            const float* __restrict__ hs) {
-  const uint64_t c0 = ((uint64_t)(2 * g) * d + j) * 16;
-  const uint4 q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
-  const uint4 q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)d * 16);
-  const uint32_t sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * d + j) * 4);
+// One group (64 inputs) of one down row: s*sum((128+q)h) + (b-128s)*sum(h),
+// h given as bf16 (hi, lo) pairs and per-8 sums (hrec: hi pairs at [0, Imax/2),
+// lo pairs at [Imax/2, Imax); hs: per-8 sums).
+__device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint32_t sb, int g,
+                                                 const uint32_t* hrec, int Imax, const float* hs) {
   const float s = f16_to_f32(sb);
   const float b = f16_to_f32(sb >> 16);
   const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
@@ -258,11 +314,21 @@ __device__ __forceinline__ float down_group(const uint8_t* blob, const BlobLayou
   return s * acc + (b - 128.0f * s) * sh;
 }
 
+__device__ __forceinline__ float down_group(const uint8_t* blob, const BlobLayout& L, int d, int j,
+                                            int g, const uint32_t* __restrict__ hrec, int Imax,
+                                            const float* __restrict__ hs) {
+  const uint64_t c0 = ((uint64_t)(2 * g) * d + j) * 16;
+  const uint4 q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
+  const uint4 q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)d * 16);
+  const uint32_t sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * d + j) * 4);
+  return down_group_regs(q0, q1, sb, g, hrec, Imax, hs);
+}
+
 struct DownArgs {
   PoolView pool;
   const uint8_t* shared_blob;
   int d, I, Ish, Imax, T, k;
-  const int32_t* idx;
+  const int32_t* sel_slot;      // decode: slot of each (token, rank) selection
   const float* w;
   const float* sgate;
   const uint32_t* hq;
@@ -277,44 +343,98 @@ struct DownArgs {
   float* shared_out;
 };
 
-// Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order combine.
+// Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order
+// combine.  Instances are taken in rounds of 16 (4 per wave): the round's
+// code loads are issued first, its h records are staged in LDS meanwhile.
+constexpr int kDnRound = 16;
 __global__ __launch_bounds__(256) void down_decode_kernel(DownArgs a) {
-  extern __shared__ float oi[];                 // [n_inst][8]
+  extern __shared__ float dyn[];                // oi[nI][8] | hst[kDnRound][Imax + Imax/8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 7, gl = lane >> 3;
   const int j = blockIdx.x * 8 + r;
   const int nR = a.T * a.k, nI = nR + a.T;
-  for (int i = wave; i < nI; i += 4) {
-    const uint8_t* blob;
-    int Iinst;
-    bool missing = false;
-    if (i < nR) {
-      const int e = a.idx[i];
-      const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
-      missing = slot < 0;
-      blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
-      Iinst = a.I;
-    } else {
-      blob = a.shared_blob;
-      Iinst = a.Ish;
+  const int rec = a.Imax + a.Imax / 8;          // dwords per staged record
+  float* oi = dyn;
+  uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 8 + 3) & ~3));
+  for (int base = 0; base < nI; base += kDnRound) {
+    const int nr = min(kDnRound, nI - base);
+    // 1. code loads for this wave's instances of the round
+    uint4 q[4][2];
+    uint32_t sb[4];
+    bool miss[4];
+    int Iw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + wave + 4 * u;
+      miss[u] = true;
+      Iw[u] = 0;
+      if (wave + 4 * u < nr) {
+        const uint8_t* blob;
+        int Iinst;
+        bool missing = false;
+        if (i < nR) {
+          const int slot = a.sel_slot[i];
+          missing = slot < 0;
+          blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
+          Iinst = a.I;
+        } else {
+          blob = a.shared_blob;
+          Iinst = a.Ish;
+        }
+        miss[u] = missing;
+        Iw[u] = Iinst;
+        if (!missing && gl < Iinst / 64) {       // one group per lane when I <= 512
+          const BlobLayout L = blob_layout(a.d, Iinst);
+          const uint64_t c0 = ((uint64_t)(2 * gl) * a.d + j) * 16;
+          q[u][0] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
+          q[u][1] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
+          sb[u] = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
+        }
+      }
     }
-    const BlobLayout L = blob_layout(a.d, Iinst);
-    const uint32_t* hrec = a.hq + (size_t)i * a.Imax;
-    const float* hs = a.hs8 + (size_t)i * (a.Imax / 8);
-    float acc = 0.f;
-    if (!missing)
-      for (int g = gl; g < Iinst / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
-    acc += __shfl_xor(acc, 8, 64);
-    acc += __shfl_xor(acc, 16, 64);
-    acc += __shfl_xor(acc, 32, 64);
-    if (lane < 8) oi[i * 8 + lane] = acc;
-    if (missing && lane == 0) atomicOr(a.pool.err, 1);
+    // 2. stage the round's h records (pairs + per-8 sums) in LDS
+    for (int q4 = tid; q4 < nr * (rec / 4); q4 += 256) {
+      const int u = q4 / (rec / 4), c = q4 % (rec / 4);
+      const int i = base + u;
+      uint4 v;
+      if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)i * a.Imax)[c];
+      else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)i * (a.Imax / 8))[c - a.Imax / 4];
+      *reinterpret_cast<uint4*>(hst + u * rec + 4 * c) = v;
+    }
+    __syncthreads();
+    // 3. compute
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (wave + 4 * u >= nr) continue;
+      const int i = base + wave + 4 * u;
+      const uint32_t* hrec = hst + (wave + 4 * u) * rec;
+      const float* hs = reinterpret_cast<const float*>(hrec + a.Imax);
+      float acc = 0.f;
+      if (!miss[u]) {
+        if (gl < Iw[u] / 64) acc = down_group_regs(q[u][0], q[u][1], sb[u], gl, hrec, a.Imax, hs);
+        // wider intermediates: remaining groups, loaded here
+        const uint8_t* blob = nullptr;
+        if (Iw[u] > 512) {
+          if (i < nR) {
+            blob = a.pool.slab + (uint64_t)a.sel_slot[i] * a.pool.stride;
+          } else {
+            blob = a.shared_blob;
+          }
+          const BlobLayout L = blob_layout(a.d, Iw[u]);
+          for (int g = gl + 8; g < Iw[u] / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
+        }
+      }
+      acc += __shfl_xor(acc, 8, 64);
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      if (lane < 8) oi[i * 8 + lane] = acc;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (tid < 8 * a.T) {
     const int t = tid / 8, rr = tid % 8;
     float y = 0.f;
-    for (int q = 0; q < a.k; ++q) y += a.w[t * a.k + q] * oi[(t * a.k + q) * 8 + rr];
+    for (int q2 = 0; q2 < a.k; ++q2) y += a.w[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
     y += a.sgate[t] * oi[(nR + t) * 8 + rr];
     a.y[(size_t)t * a.d + blockIdx.x * 8 + rr] = y;
   }
@@ -405,6 +525,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 struct FfnWs {
   uint32_t* xq; float* xs;
   uint32_t* hq; float* hs8;
+  int32_t* sel_slot;
   Inst* inst; int32_t* n_routed;
 };
 
@@ -414,6 +535,7 @@ bool carve_ffn(Carver& c, int d, int Imax, int T, int k, int path, FfnWs* w) {
   w->xs = c.take<float>((size_t)T * d / 64);
   w->hq = c.take<uint32_t>(hrows * Imax);
   w->hs8 = c.take<float>(hrows * Imax / 8);
+  w->sel_slot = c.take<int32_t>((size_t)T * k);
   w->inst = nullptr;
   w->n_routed = nullptr;
   if (path != MOE_PATH_DECODE) {
@@ -461,23 +583,35 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   GateUpArgs g{};
   g.pool = f.pool; g.shared_blob = f.shared_blob;
   g.d = f.d; g.I = f.I; g.Ish = f.Ish; g.Imax = Imax; g.T = f.T; g.k = f.k;
-  g.idx = f.idx; g.xq = xq; g.xs = xs;
+  g.idx = f.idx; g.w = f.w; g.sgate = f.sgate; g.logits = f.logits; g.bias = f.bias; g.usage = f.usage;
+  g.sel_slot = w.sel_slot;
+  g.xq = xq; g.xs = xs;
   g.hq = w.hq; g.hs8 = w.hs8;
   DownArgs dn{};
   dn.pool = f.pool; dn.shared_blob = f.shared_blob;
   dn.d = f.d; dn.I = f.I; dn.Ish = f.Ish; dn.Imax = Imax; dn.T = f.T; dn.k = f.k;
-  dn.idx = f.idx; dn.w = f.w; dn.sgate = f.sgate; dn.hq = w.hq; dn.hs8 = w.hs8; dn.y = f.y;
+  dn.sel_slot = w.sel_slot; dn.w = f.w; dn.sgate = f.sgate; dn.hq = w.hq; dn.hs8 = w.hs8; dn.y = f.y;
 
   if (path == MOE_PATH_DECODE) {
     g.batched = 0;
     const int items = f.T * f.k * (f.I / 8) + f.T * (f.Ish / 8);
-    const size_t lds = (size_t)1 * G * kXPad * 4;
+    const int E = f.pool.E;
+    const size_t lds = (size_t)1 * G * kXPad * 4 +
+                       (f.logits ? (size_t)(topk_scratch_words(E) + 2 * E + 1 + 2 * f.k) * 4 : 0);
+    void* fn;
+    switch (nk_for(E)) {
+      case 1: fn = (void*)gate_up_kernel<1, 1>; break;
+      case 2: fn = (void*)gate_up_kernel<1, 2>; break;
+      case 4: fn = (void*)gate_up_kernel<1, 4>; break;
+      case 8: fn = (void*)gate_up_kernel<1, 8>; break;
+      default: fn = (void*)gate_up_kernel<1, 16>; break;
+    }
     void* args[] = {&g};
-    MOE_HIP(hipLaunchKernel((void*)gate_up_kernel<1>, dim3(items), dim3(256), args, lds, s));
+    MOE_HIP(hipLaunchKernel(fn, dim3(items), dim3(256), args, lds, s));
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
-    MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(256), dargs,
-                            (size_t)nI * 8 * sizeof(float), s));
+    const size_t dlds = (size_t)(((nI * 8 + 3) & ~3) + kDnRound * (Imax + Imax / 8)) * 4;
+    MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(256), dargs, dlds, s));
     return MOE_OK;
   }
   // batched: bucketed instances of up to kTC tokens
@@ -490,7 +624,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   const long upper = ((long)f.T * f.k + nsh) * (Imax / 8);
   const size_t lds = (size_t)kTC * G * kXPad * 4;
   void* args[] = {&g};
-  MOE_HIP(hipLaunchKernel((void*)gate_up_kernel<kTC>, dim3(grid_for((int)(upper < 65536 ? upper : 65536))),
+  MOE_HIP(hipLaunchKernel((void*)gate_up_kernel<kTC, 1>, dim3(grid_for((int)(upper < 65536 ? upper : 65536))),
                           dim3(256), args, lds, s));
   dn.inst = w.inst; dn.n_routed = w.n_routed; dn.n_shared_inst = nsh; dn.pair_ids = f.pair_ids;
   dn.partial = f.partial; dn.shared_out = f.shared_out;

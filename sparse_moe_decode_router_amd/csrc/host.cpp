@@ -438,7 +438,8 @@ extern "C" int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh
   a.d = sh->d; a.I = sh->I; a.Ish = ssh->I;
   a.shared_blob = static_cast<const uint8_t*>(shared_blob);
   a.x = x; a.xq = nullptr; a.xs = nullptr;
-  a.T = T; a.k = k; a.idx = idx; a.w = w; a.sgate = sgate;
+  a.T = T; a.k = k; a.idx = const_cast<int32_t*>(idx); a.w = const_cast<float*>(w);
+  a.sgate = const_cast<float*>(sgate);
   a.offsets = offsets; a.pair_ids = pair_ids;
   a.y = out; a.partial = partial; a.shared_out = shared_out;
   if (path == MOE_PATH_DECODE) {
@@ -514,8 +515,13 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   LayerWs lw;
   if (!carve_layer(c, L, T, path, &lw)) return MOE_ERR_INVALID_ARG;
   const int d = L->sh.d;
-  MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, L->k, idx, w, sgate,
-                        L->usage_dev, lw.r, s));
+  if (path == MOE_PATH_DECODE) {
+    // logits here; the decode FFN selects the experts in-kernel
+    MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s));
+  } else {
+    MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, L->k, idx, w, sgate,
+                          L->usage_dev, lw.r, s));
+  }
   FfnArgs a{};
   pool_view(L->pool, &a.pool);
   a.d = d; a.I = L->sh.I; a.Ish = L->shared_sh.I;
@@ -524,6 +530,9 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   a.T = T; a.k = L->k; a.idx = idx; a.w = w; a.sgate = sgate;
   if (path == MOE_PATH_DECODE) {
     a.y = y;
+    a.logits = lw.r.logits;
+    a.bias = L->logit_bias_dev;
+    a.usage = L->usage_dev;
     return ffn_launch(a, path, lw.ffn_ws, lw.ffn_bytes, s);
   }
   MOE_TRY(bucket_launch(idx, T, L->k, L->E, lw.counts, lw.offsets, lw.pair_ids, lw.bucket_ws,

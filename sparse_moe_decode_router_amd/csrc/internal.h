@@ -89,6 +89,11 @@ bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws);
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias,
                   int E, int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
                   const RouterWs& ws, hipStream_t s);
+// logits [T][E+1] (+ xq/xs) only; the decode FFN selects in-kernel
+int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
+                         const RouterWs& ws, hipStream_t s);
+int topk_launch(const float* logits, const float* bias, int T, int E, int k, int32_t* idx,
+                float* w, float* sgate, uint32_t* usage, hipStream_t s);
 
 int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts,
                   int32_t* offsets, int32_t* pair_ids, void* ws, size_t ws_bytes,
@@ -107,9 +112,12 @@ struct FfnArgs {
   const uint32_t* xq;       // [T][d/2]
   const float* xs;          // [T][d/64]
   int T, k;
-  const int32_t* idx;       // [T][k]
-  const float* w;           // [T][k]
-  const float* sgate;       // [T]
+  int32_t* idx;             // [T][k] (written when logits is set)
+  float* w;                 // [T][k] (written when logits is set)
+  float* sgate;             // [T]    (written when logits is set)
+  const float* logits;      // decode: [T][E+1] router logits -> select in-kernel
+  const float* bias;        // [E] or null (with logits)
+  uint32_t* usage;          // [E] or null (with logits)
   const int32_t* offsets;   // [E+1]
   const int32_t* pair_ids;  // [T*k]
   float* y;                 // decode: [T][d]

@@ -8,6 +8,7 @@
 // ascending.  Weights are the softmax over the k chosen logits.
 #include "internal.h"
 #include "device.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -46,133 +47,57 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
   if (id < T * G) xprep_group(x, d, id / G, id % G, xq, xs);
 }
 
-// ----------------------------------------------------------------- top-k
-// One wave selects the top k of one token's E logits (E <= 64*NK) and writes
-// idx/w in rank order, bumps usage.  sel_l / sel_e: this wave's LDS, k each.
-template <int NK>
-__device__ void topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
-                          int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                          uint32_t* __restrict__ usage, float* sel_l, int32_t* sel_e) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[NK];
-#pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = 0;
-    if (e < E) {
-      float l = lrow[e];
-      if (bias) l += bias[e];
-      key[j] = ((uint64_t)f32_order(l) << 32) | (uint64_t)(~(uint32_t)e);
-    }
-  }
-  for (int r = 0; r < k; ++r) {
-    uint64_t m = key[0];
-#pragma unroll
-    for (int j = 1; j < NK; ++j) m = key[j] > m ? key[j] : m;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const uint64_t o = __shfl_xor(m, s, 64);
-      m = o > m ? o : m;
-    }
-#pragma unroll
-    for (int j = 0; j < NK; ++j) key[j] = (key[j] == m) ? 0 : key[j];
-    if (lane == 0) {
-      sel_e[r] = (int32_t)(~(uint32_t)m);
-      sel_l[r] = f32_unorder((uint32_t)(m >> 32));
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float lmax = sel_l[0];
-  float z = 0.0f;
-  for (int r = lane; r < k; r += 64) z += expf(sel_l[r] - lmax);
-  z = wave_sum(z);
-  for (int r = lane; r < k; r += 64) {
-    const int e = sel_e[r];
-    idx_out[r] = e;
-    w_out[r] = expf(sel_l[r] - lmax) / z;
-    if (usage) atomicAdd(&usage[e], 1u);
-  }
-}
+}  // namespace
+
+namespace {
 
 // --------------------------------------------------------- decode router
-// T <= TMAX tokens.  Block b computes logit rows 2b and 2b+1 (row E is the
-// shared gate); 128 threads per row, each summing d/128 products in column
-// order, then a 64-lane butterfly and one cross-wave add: depth d/128 + 7,
-// plus one for the bias.  Blocks also prepare xq/xs.  The last block to
-// finish (device-scope ticket) runs top-k, one wave per token.
+// Logits for T <= TMAX tokens.  Block b computes logit row b (row E is the
+// shared gate) with 256 threads, each summing d/256 products in column
+// order, then a 64-lane butterfly and a two-level tree over the 4 waves:
+// depth d/256 + 8, plus one for the bias (added by the top-k).  Blocks also
+// prepare xq/xs.  No block waits for another.
 struct DecodeArgs {
   const uint16_t* x; int T, d;
-  const float* W; const float* bias; int E, k;
-  int32_t* idx; float* w; float* sgate; uint32_t* usage;
-  float* logits; uint32_t* ticket; uint32_t* xq; float* xs;
+  const float* W; int E;
+  float* logits; uint32_t* xq; float* xs;
 };
 
-template <int TMAX, int NK>
+template <int TMAX>
 __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArgs a) {
-  extern __shared__ uint8_t dyn_lds[];
-  __shared__ float red[2][2][TMAX];
-  __shared__ int is_last;
-  const int tid = threadIdx.x;
-  const int half = tid >> 7, j = tid & 127, lane = tid & 63, wih = (tid >> 6) & 1;
-  const int row = blockIdx.x * 2 + half;
+  __shared__ float red[4][TMAX];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
   const int d = a.d, T = a.T, E = a.E;
-
-  // x prep, spread over blocks
   {
     const int G = d / 64;
     const int id = blockIdx.x * kRouterThreads + tid;
     if (id < T * G) xprep_group(a.x, d, id / G, id % G, a.xq, a.xs);
   }
-
   float acc[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) acc[t] = 0.0f;
-  if (row <= E) {
-    const float4* Wr = reinterpret_cast<const float4*>(a.W + (size_t)row * d);
-    for (int c = j; c < d / 4; c += 128) {
-      const float4 wv = Wr[c];
+  const float4* Wr = reinterpret_cast<const float4*>(a.W + (size_t)row * d);
+  for (int c = tid; c < d / 4; c += kRouterThreads) {
+    const float4 wv = Wr[c];
 #pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-          const uint2 xv = *reinterpret_cast<const uint2*>(a.x + (size_t)t * d + 4 * c);
-          acc[t] += wv.x * bf16_lo(xv.x);
-          acc[t] += wv.y * bf16_hi(xv.x);
-          acc[t] += wv.z * bf16_lo(xv.y);
-          acc[t] += wv.w * bf16_hi(xv.y);
-        }
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(a.x + (size_t)t * d + 4 * c);
+        acc[t] += wv.x * bf16_lo(xv.x);
+        acc[t] += wv.y * bf16_hi(xv.x);
+        acc[t] += wv.z * bf16_lo(xv.y);
+        acc[t] += wv.w * bf16_hi(xv.y);
       }
     }
   }
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
     const float v = wave_sum(acc[t]);
-    if (lane == 0) red[half][wih][t] = v;
+    if (lane == 0) red[wave][t] = v;
   }
   __syncthreads();
-  if (tid < 2 * TMAX) {
-    const int h = tid / TMAX, t = tid % TMAX;
-    const int r = blockIdx.x * 2 + h;
-    if (t < T && r <= E) a.logits[(size_t)t * (E + 1) + r] = red[h][0][t] + red[h][1][t];
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  const int wave = tid >> 6;
-  float* sel_l = reinterpret_cast<float*>(dyn_lds) + wave * a.k;
-  int32_t* sel_e = reinterpret_cast<int32_t*>(dyn_lds + 4 * a.k * sizeof(float)) + wave * a.k;
-  for (int t = wave; t < T; t += 4) {
-    const float* lrow = a.logits + (size_t)t * (E + 1);
-    topk_wave<NK>(lrow, a.bias, E, a.k, a.idx + (size_t)t * a.k, a.w + (size_t)t * a.k,
-                  a.usage, sel_l, sel_e);
-    if (lane == 0 && a.sgate) a.sgate[t] = sigmoidf_(lrow[E]);
-  }
-  if (tid == 0) atomicExch(a.ticket, 0u);
+  if (tid < T) a.logits[(size_t)tid * (E + 1) + row] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
 }
 
 // ---------------------------------------------------------- batched router
@@ -243,29 +168,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int T, int E, int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ sgate,
                                                    uint32_t* __restrict__ usage) {
-  extern __shared__ uint8_t dyn_lds[];
+  extern __shared__ uint32_t dyn_lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  float* sel_l = reinterpret_cast<float*>(dyn_lds) + wave * k;
-  int32_t* sel_e = reinterpret_cast<int32_t*>(dyn_lds + 4 * k * sizeof(float)) + wave * k;
+  const int k4 = (k + 3) & ~3;
+  uint32_t* base = dyn_lds + wave * (2 * k4 + topk_scratch_words(E));
+  float* sel_l = reinterpret_cast<float*>(base);
+  int32_t* sel_e = reinterpret_cast<int32_t*>(base + k4);
   const float* lrow = logits + (size_t)t * (E + 1);
-  topk_wave<NK>(lrow, bias, E, k, idx + (size_t)t * k, w + (size_t)t * k, usage, sel_l, sel_e);
+  topk_select<NK>(lrow, bias, E, k, sel_l, sel_e, base + 2 * k4);
+  topk_finish(sel_l, sel_e, k, idx + (size_t)t * k, w + (size_t)t * k, usage);
   if (lane == 0 && sgate) sgate[t] = sigmoidf_(lrow[E]);
 }
-
-template <int TMAX>
-void* pick_decode(int nk) {
-  switch (nk) {
-    case 1: return (void*)router_decode_kernel<TMAX, 1>;
-    case 2: return (void*)router_decode_kernel<TMAX, 2>;
-    case 4: return (void*)router_decode_kernel<TMAX, 4>;
-    case 8: return (void*)router_decode_kernel<TMAX, 8>;
-    default: return (void*)router_decode_kernel<TMAX, 16>;
-  }
-}
-
-int nk_for(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
 
 }  // namespace
 
@@ -292,36 +207,44 @@ bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws) {
   return c.ok();
 }
 
-int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias, int E,
-                  int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
-                  const RouterWs& ws, hipStream_t s) {
+int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E, const RouterWs& ws,
+                         hipStream_t s) {
   if (T == 0) return MOE_OK;
-  const int nk = nk_for(E);
-  const size_t lds = (size_t)4 * k * (sizeof(float) + sizeof(int32_t));
   if (T <= 8) {
-    DecodeArgs a{x, T, d, W, bias, E, k, idx, w, sgate, usage, ws.logits, ws.ticket, ws.xq, ws.xs};
-    void* fn = T == 1 ? pick_decode<1>(nk) : T == 2 ? pick_decode<2>(nk)
-             : T <= 4 ? pick_decode<4>(nk) : pick_decode<8>(nk);
-    const int blocks = (E + 1 + 1) / 2;
+    DecodeArgs a{x, T, d, W, E, ws.logits, ws.xq, ws.xs};
+    void* fn = T == 1 ? (void*)router_decode_kernel<1> : T == 2 ? (void*)router_decode_kernel<2>
+             : T <= 4 ? (void*)router_decode_kernel<4> : (void*)router_decode_kernel<8>;
     void* args[] = {&a};
-    MOE_HIP(hipLaunchKernel(fn, dim3(blocks), dim3(kRouterThreads), args, lds, s));
+    MOE_HIP(hipLaunchKernel(fn, dim3(E + 1), dim3(kRouterThreads), args, 0, s));
     return MOE_OK;
   }
-  const int G = d / 64;
-  xprep_kernel<<<(T * G + 255) / 256, 256, 0, s>>>(x, T, d, ws.xq, ws.xs);
-  MOE_HIP(hipGetLastError());
+  MOE_TRY(xprep_launch(x, T, d, ws.xq, ws.xs, s));
   router_gemm_kernel<<<dim3((E + 1 + 63) / 64, (T + 63) / 64), 256, 0, s>>>(x, T, d, W, E + 1, ws.logits);
   MOE_HIP(hipGetLastError());
+  return MOE_OK;
+}
+
+int topk_launch(const float* logits, const float* bias, int T, int E, int k, int32_t* idx, float* w,
+                float* sgate, uint32_t* usage, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  const size_t lds = (size_t)4 * (2 * ((k + 3) & ~3) + topk_scratch_words(E)) * 4;
   const dim3 tg((T + 3) / 4);
-  switch (nk) {
-    case 1: topk_kernel<1><<<tg, 256, lds, s>>>(ws.logits, bias, T, E, k, idx, w, sgate, usage); break;
-    case 2: topk_kernel<2><<<tg, 256, lds, s>>>(ws.logits, bias, T, E, k, idx, w, sgate, usage); break;
-    case 4: topk_kernel<4><<<tg, 256, lds, s>>>(ws.logits, bias, T, E, k, idx, w, sgate, usage); break;
-    case 8: topk_kernel<8><<<tg, 256, lds, s>>>(ws.logits, bias, T, E, k, idx, w, sgate, usage); break;
-    default: topk_kernel<16><<<tg, 256, lds, s>>>(ws.logits, bias, T, E, k, idx, w, sgate, usage); break;
+  switch (nk_for(E)) {
+    case 1: topk_kernel<1><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
+    case 2: topk_kernel<2><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
+    case 4: topk_kernel<4><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
+    case 8: topk_kernel<8><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
+    default: topk_kernel<16><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
   }
   MOE_HIP(hipGetLastError());
   return MOE_OK;
+}
+
+int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias, int E,
+                  int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
+                  const RouterWs& ws, hipStream_t s) {
+  MOE_TRY(router_logits_launch(x, T, d, W, E, ws, s));
+  return topk_launch(ws.logits, bias, T, E, k, idx, w, sgate, usage, s);
 }
 
 }  // namespace moe
@@ -335,7 +258,7 @@ extern "C" size_t moe_router_workspace_bytes(int32_t T, int32_t d, int32_t E) {
 
 extern "C" int32_t moe_router_sum_depth(int32_t T, int32_t d) {
   if (d <= 0) return -1;
-  return T <= 8 ? d / 128 + 8 : 32 + d / 32 + 1;
+  return T <= 8 ? d / 256 + 9 : 32 + d / 32 + 1;
 }
 
 extern "C" int moe_router_topk(const uint16_t* x, int32_t T, int32_t d, const float* W,
