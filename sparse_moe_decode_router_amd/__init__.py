@@ -18,7 +18,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe355.so")
+# MOE355_LIB may name another build of the same library (e.g. an instrumented one)
+LIB_PATH = os.environ.get("MOE355_LIB") or os.path.join(_HERE, "libmoe355.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1

@@ -66,6 +66,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Sum over each aligned group of 8 consecutive lanes (every lane of the
+// group gets the sum): pair swap, quad swap, half-row mirror, all DPP.
+__device__ __forceinline__ float sum8_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ int wave_min_i32(int v) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {

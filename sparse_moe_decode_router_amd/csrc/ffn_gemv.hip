@@ -116,7 +116,9 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   __shared__ float red[4][2][TC][8];
   __shared__ float gu[2][TC][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = tid & 7, cpl = tid >> 3;        // row in block, group lane (0..31)
+  // lane = (row r, group lane): the 8 lanes of one row are consecutive so the
+  // row's partial sums meet by DPP within groups of 8
+  const int r = (tid >> 3) & 7, cpl = (tid & 7) + 8 * (tid >> 6);   // cpl: 0..31
   const int G = a.d / 64;
   const int rbR = a.I / 8, rbS = a.Ish / 8;
   const int nR = a.batched ? *a.n_routed : a.T * a.k;
@@ -173,6 +175,14 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     // 1. weight loads first: all of this lane's codes and (scale, bias) words
     uint4 cg[kGMax][2], cu[kGMax][2];
     uint32_t sbg[kGMax], sbu[kGMax];
+    float sxv[kGMax][TC];                       // group sums of x, loaded up front
+#pragma unroll
+    for (int gi = 0; gi < kGMax; ++gi) {
+      const int g = cpl + 32 * gi;
+#pragma unroll
+      for (int tt = 0; tt < TC; ++tt)
+        sxv[gi][tt] = (g < G && tt < ntok) ? a.xs[(size_t)tok[tt] * G + g] : 0.f;
+    }
     if (!missing) {
       const uint64_t o = (uint64_t)(o0 + r);
 #pragma unroll
@@ -217,18 +227,21 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
         for (int tt = 0; tt < TC; ++tt) {
           if (tt < ntok) {
             const uint32_t* xp = &xlds[(tt * G + g) * kXPad];
-            float ag = 0.f, au = 0.f;
+            float ag0 = 0.f, au0 = 0.f, ag1 = 0.f, au1 = 0.f;   // two chains each
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
               const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * w);
               const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-              for (int ii = 0; ii < 4; ++ii) {
-                ag = dot2_bf16(nib_pair(gw[w], ii), xw[ii], ag);
-                au = dot2_bf16(nib_pair(uw[w], ii), xw[ii], au);
+              for (int ii = 0; ii < 4; ii += 2) {
+                ag0 = dot2_bf16(nib_pair(gw[w], ii), xw[ii], ag0);
+                au0 = dot2_bf16(nib_pair(uw[w], ii), xw[ii], au0);
+                ag1 = dot2_bf16(nib_pair(gw[w], ii + 1), xw[ii + 1], ag1);
+                au1 = dot2_bf16(nib_pair(uw[w], ii + 1), xw[ii + 1], au1);
               }
             }
-            const float sx = a.xs[(size_t)tok[tt] * G + g];
+            const float ag = ag0 + ag1, au = au0 + au1;
+            const float sx = sxv[gi][tt];
             vg[tt] += sg * ag + (bg - 128.0f * sg) * sx;
             vu[tt] += su * au + (bu - 128.0f * su) * sx;
           }
@@ -237,11 +250,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     }
 #pragma unroll
     for (int tt = 0; tt < TC; ++tt) {
-      float x1 = vg[tt], x2 = vu[tt];
-      x1 += __shfl_xor(x1, 8, 64);  x2 += __shfl_xor(x2, 8, 64);
-      x1 += __shfl_xor(x1, 16, 64); x2 += __shfl_xor(x2, 16, 64);
-      x1 += __shfl_xor(x1, 32, 64); x2 += __shfl_xor(x2, 32, 64);
-      if (lane < 8) { red[wave][0][tt][lane] = x1; red[wave][1][tt][lane] = x2; }
+      const float x1 = sum8_dpp(vg[tt]), x2 = sum8_dpp(vu[tt]);
+      if ((lane & 7) == 0) { red[wave][0][tt][r] = x1; red[wave][1][tt][r] = x2; }
     }
     __syncthreads();
     if (tid < 2 * TC * 8) {
@@ -295,19 +305,22 @@ __device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint32_t sb
   const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
   const uint4* hh = reinterpret_cast<const uint4*>(hrec + 32 * g);
   const uint4* hl = reinterpret_cast<const uint4*>(hrec + Imax / 2 + 32 * g);
-  float acc = 0.f;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;      // four independent chains
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const uint4 vh = hh[w], vl = hl[w];
     const uint32_t ph[4] = {vh.x, vh.y, vh.z, vh.w};
     const uint32_t pl[4] = {vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const uint32_t q = nib_pair(qw[w], ii);
-      acc = dot2_bf16(q, ph[ii], acc);
-      acc = dot2_bf16(q, pl[ii], acc);
+    for (int ii = 0; ii < 4; ii += 2) {
+      const uint32_t q0 = nib_pair(qw[w], ii), q1 = nib_pair(qw[w], ii + 1);
+      a0 = dot2_bf16(q0, ph[ii], a0);
+      a1 = dot2_bf16(q0, pl[ii], a1);
+      a2 = dot2_bf16(q1, ph[ii + 1], a2);
+      a3 = dot2_bf16(q1, pl[ii + 1], a3);
     }
   }
+  const float acc = (a0 + a2) + (a1 + a3);
   float sh = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) sh += hs[8 * g + m];
@@ -344,13 +357,15 @@ struct DownArgs {
 };
 
 // Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order
-// combine.  Instances are taken in rounds of 16 (4 per wave): the round's
-// code loads are issued first, its h records are staged in LDS meanwhile.
-constexpr int kDnRound = 16;
-__global__ __launch_bounds__(256) void down_decode_kernel(DownArgs a) {
+// combine.  16 waves; instances are taken in rounds of 16 (one per wave):
+// the round's code loads are issued first, its h records are staged in LDS
+// meanwhile.
+constexpr int kDnWaves = 16;
+constexpr int kDnRound = kDnWaves;
+__global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) {
   extern __shared__ float dyn[];                // oi[nI][8] | hst[kDnRound][Imax + Imax/8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 7, gl = lane >> 3;
+  const int r = lane >> 3, gl = lane & 7;       // group lanes of a row are consecutive
   const int j = blockIdx.x * 8 + r;
   const int nR = a.T * a.k, nI = nR + a.T;
   const int rec = a.Imax + a.Imax / 8;          // dwords per staged record
@@ -358,76 +373,57 @@ __global__ __launch_bounds__(256) void down_decode_kernel(DownArgs a) {
   uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 8 + 3) & ~3));
   for (int base = 0; base < nI; base += kDnRound) {
     const int nr = min(kDnRound, nI - base);
-    // 1. code loads for this wave's instances of the round
-    uint4 q[4][2];
-    uint32_t sb[4];
-    bool miss[4];
-    int Iw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + wave + 4 * u;
-      miss[u] = true;
-      Iw[u] = 0;
-      if (wave + 4 * u < nr) {
-        const uint8_t* blob;
-        int Iinst;
-        bool missing = false;
-        if (i < nR) {
-          const int slot = a.sel_slot[i];
-          missing = slot < 0;
-          blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
-          Iinst = a.I;
-        } else {
-          blob = a.shared_blob;
-          Iinst = a.Ish;
-        }
-        miss[u] = missing;
-        Iw[u] = Iinst;
-        if (!missing && gl < Iinst / 64) {       // one group per lane when I <= 512
-          const BlobLayout L = blob_layout(a.d, Iinst);
-          const uint64_t c0 = ((uint64_t)(2 * gl) * a.d + j) * 16;
-          q[u][0] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
-          q[u][1] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
-          sb[u] = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
-        }
+    const int i = base + wave;
+    const bool active = wave < nr;
+    // 1. this wave's code loads
+    uint4 q0, q1;
+    uint32_t sb = 0;
+    bool miss = true;
+    int Iinst = 0;
+    const uint8_t* blob = nullptr;
+    if (active) {
+      if (i < nR) {
+        const int slot = a.sel_slot[i];
+        miss = slot < 0;
+        blob = a.pool.slab + (uint64_t)(miss ? 0 : slot) * a.pool.stride;
+        Iinst = a.I;
+      } else {
+        miss = false;
+        blob = a.shared_blob;
+        Iinst = a.Ish;
+      }
+      if (!miss && gl < Iinst / 64) {
+        const BlobLayout L = blob_layout(a.d, Iinst);
+        const uint64_t c0 = ((uint64_t)(2 * gl) * a.d + j) * 16;
+        q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
+        q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
+        sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
       }
     }
     // 2. stage the round's h records (pairs + per-8 sums) in LDS
-    for (int q4 = tid; q4 < nr * (rec / 4); q4 += 256) {
+    for (int q4 = tid; q4 < nr * (rec / 4); q4 += 64 * kDnWaves) {
       const int u = q4 / (rec / 4), c = q4 % (rec / 4);
-      const int i = base + u;
+      const int ii = base + u;
       uint4 v;
-      if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)i * a.Imax)[c];
-      else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)i * (a.Imax / 8))[c - a.Imax / 4];
+      if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)ii * a.Imax)[c];
+      else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)ii * (a.Imax / 8))[c - a.Imax / 4];
       *reinterpret_cast<uint4*>(hst + u * rec + 4 * c) = v;
     }
     __syncthreads();
     // 3. compute
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (wave + 4 * u >= nr) continue;
-      const int i = base + wave + 4 * u;
-      const uint32_t* hrec = hst + (wave + 4 * u) * rec;
+    if (active) {
+      const uint32_t* hrec = hst + wave * rec;
       const float* hs = reinterpret_cast<const float*>(hrec + a.Imax);
       float acc = 0.f;
-      if (!miss[u]) {
-        if (gl < Iw[u] / 64) acc = down_group_regs(q[u][0], q[u][1], sb[u], gl, hrec, a.Imax, hs);
-        // wider intermediates: remaining groups, loaded here
-        const uint8_t* blob = nullptr;
-        if (Iw[u] > 512) {
-          if (i < nR) {
-            blob = a.pool.slab + (uint64_t)a.sel_slot[i] * a.pool.stride;
-          } else {
-            blob = a.shared_blob;
-          }
-          const BlobLayout L = blob_layout(a.d, Iw[u]);
-          for (int g = gl + 8; g < Iw[u] / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
+      if (!miss) {
+        if (gl < Iinst / 64) acc = down_group_regs(q0, q1, sb, gl, hrec, a.Imax, hs);
+        if (Iinst > 512) {                      // wider intermediates: further groups
+          const BlobLayout L = blob_layout(a.d, Iinst);
+          for (int g = gl + 8; g < Iinst / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
         }
       }
-      acc += __shfl_xor(acc, 8, 64);
-      acc += __shfl_xor(acc, 16, 64);
-      acc += __shfl_xor(acc, 32, 64);
-      if (lane < 8) oi[i * 8 + lane] = acc;
+      acc = sum8_dpp(acc);
+      if (gl == 0) oi[i * 8 + r] = acc;
     }
     __syncthreads();
   }
@@ -611,7 +607,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 8 + 3) & ~3) + kDnRound * (Imax + Imax / 8)) * 4;
-    MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(256), dargs, dlds, s));
+    MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
     return MOE_OK;
   }
   // batched: bucketed instances of up to kTC tokens
