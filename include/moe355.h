@@ -176,7 +176,9 @@ int moe_pool_set_slot_table(moe_pool* pool, const int32_t* table,
                             hipStream_t stream);
 int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* st);
 /* Synchronises the stream, reads and clears the device error word:
- * *err = MOE_OK or MOE_ERR_NOT_RESIDENT. */
+ * *err = MOE_OK, MOE_ERR_NOT_RESIDENT (a selected expert had no slot) or
+ * MOE_ERR_UNSUPPORTED (the prefill path met an activation or intermediate
+ * beyond the fp16 range, |v| > 65504). */
 int moe_pool_check_error(moe_pool* pool, hipStream_t stream, int32_t* err);
 /* Synchronises the stream and copies the device slot table ([E] int32) and
  * usage counters ([E] uint32) to host arrays (either may be NULL). */
@@ -226,6 +228,11 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
  *                     moe_bucket_tokens; writes the unweighted expert outputs
  *                     partial_dev [T*k][d] (pair order) and shared_out_dev
  *                     [T][d]; combine with moe_combine (out_dev unused).
+ *   MOE_PATH_PREFILL: as BATCHED, on the matrix cores: weights dequantised
+ *                     to fp16 (one rounding of s*q + b), activations and the
+ *                     SwiGLU intermediate in fp16 (|v| <= 65504, else the
+ *                     pool error word reports MOE_ERR_UNSUPPORTED), fp32
+ *                     accumulate.
  *   MOE_PATH_AUTO   : DECODE for T <= 4, BATCHED for T*k/E < 16, else PREFILL
  *                     (the caller must then supply every buffer).
  * A selected expert with slot_table[e] < 0 sets the pool's error word and

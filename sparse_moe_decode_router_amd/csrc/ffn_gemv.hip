@@ -550,11 +550,12 @@ int grid_for(int items_upper) {
 int resolve_path(int path, int T, int k, int E) {
   if (path != MOE_PATH_AUTO) return path;
   if (T <= 4) return MOE_PATH_DECODE;
-  return MOE_PATH_BATCHED;
+  if ((long)T * k < 16L * E) return MOE_PATH_BATCHED;   // < 16 tokens per expert
+  return MOE_PATH_PREFILL;
 }
 
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
-  (void)E;
+  if (path == MOE_PATH_PREFILL) return prefill_ws_bytes(d, I, Ish, T, k, E);
   Carver c(nullptr, (size_t)-1);
   FfnWs w;
   carve_ffn(c, d, I > Ish ? I : Ish, T, k, path, &w);
@@ -564,6 +565,7 @@ size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
 int xprep_launch(const uint16_t* x, int T, int d, uint32_t* xq, float* xs, hipStream_t s);
 
 int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (path == MOE_PATH_PREFILL) return prefill_launch(f, ws, ws_bytes, s);
   const int Imax = f.I > f.Ish ? f.I : f.Ish;
   Carver c(ws, ws_bytes);
   FfnWs w;

@@ -388,7 +388,9 @@ extern "C" int moe_pool_check_error(moe_pool* p, hipStream_t s, int32_t* err) {
   MOE_HIP(hipStreamSynchronize(s));
   MOE_HIP(hipMemcpy(&v, p->err, sizeof(v), hipMemcpyDeviceToHost));
   MOE_HIP(hipMemset(p->err, 0, sizeof(v)));
-  *err = v ? MOE_ERR_NOT_RESIDENT : MOE_OK;
+  // bit 0: a selected expert had no slot; bit 1: a prefill activation or
+  // intermediate fell outside the fp16 range
+  *err = (v & 1) ? MOE_ERR_NOT_RESIDENT : (v & 2) ? MOE_ERR_UNSUPPORTED : MOE_OK;
   return MOE_OK;
 }
 
