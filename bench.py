@@ -1,17 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the routed-expert MoE layer on one MI355X.
 
-Default workload: the 80B-shaped batch-1 decode layer (T=1, d=2048, E=512,
-top-10, expert and shared intermediate 512, int4 group-64 blobs, Zipf-skewed
-router), all 512 experts resident in the HBM slot pool behind a seeded slot
-permutation.  One step = router -> top-k -> expert SwiGLU FFNs -> weighted
-combine with the gated shared expert, for one token.  The layer is replicated
-R times (pools, router weights, shared experts) and step s uses replica
-s mod R so that re-reads do not come from the 256 MB last-level cache.
+Default workload (the headline): the 80B-shaped batch-1 decode layer (T=1,
+d=2048, E=512, top-10, expert and shared intermediate 512, int4 group-64
+blobs, Zipf-skewed router), all 512 experts resident in the HBM slot pool
+behind a seeded slot permutation.  One step = router -> top-k -> expert
+SwiGLU FFNs -> weighted combine with the gated shared expert, for one token.
+The layer is replicated R times (pools, router weights, shared experts) and
+step s uses replica s mod R, so re-reads do not come from the 256 MB
+last-level cache.  Steps are captured in a HIP graph and replayed.
 
 Prints one JSON line: tokens/s of the whole layer (value), the dominant
-kernel's achieved HBM bandwidth on algorithmic expert bytes (roofline), and
+kernels' achieved HBM bandwidth on algorithmic expert bytes (roofline), and
 the CPU oracle timed on a bounded sample of the same steps (cpu_baseline).
+
+--workload selects another configuration (decode35b, refill80b: 256-slot
+pool refilled by LFU + recency from pinned host memory, batch80b: T=64,
+prefill80b / prefill80b_zipf: T=4096 on the matrix cores); --workload all
+prints one line per workload, the headline first.
 """
 from __future__ import annotations
 
@@ -27,22 +33,47 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "routed-MoE layer tokens/s + achieved HBM GB/s on int4 experts (80B shape)"
+DATA = ("synthetic (seeded int4 codes U{0..15}, fp16 scales U[0.002,0.02], bias -8*scale, "
+        "x ~ N(0,1) bf16, router N(0,0.02) fp32, Zipf(1.1) logit offset alpha=0.15 where skewed)")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_layers(cfg, R, torch, moe, ms):
+class Ctx:
+    def __init__(self):
+        import torch
+        import moe_synth as ms
+        import sparse_moe_decode_router_amd as moe
+        from oracle import layer as olayer
+        self.torch, self.ms, self.moe, self.olayer = torch, ms, moe, olayer
+
+
+def packed_experts(c, cfg, pinned=False):
+    """All E blobs packed by the library's packer: [E, stride] uint8."""
+    torch, ms, moe = c.torch, c.ms, c.moe
+    stride = moe.moe_blob_stride(cfg.d, cfg.I)
+    t0 = time.time()
+    if pinned:
+        out = torch.empty((cfg.E, stride), dtype=torch.uint8, pin_memory=True)
+    else:
+        out = torch.empty((cfg.E, stride), dtype=torch.uint8, device="cuda")
+    for e in range(cfg.E):
+        out[e].copy_(torch.from_numpy(moe.moe_pack_expert_int4(ms.expert_raw(cfg, e), cfg.d, cfg.I)))
+        if e % 128 == 127:
+            log(f"packed {e + 1}/{cfg.E} experts ({time.time() - t0:.1f}s)")
+    return out
+
+
+def build_layers(c, cfg, R, staging=None):
+    torch, ms, moe = c.torch, c.ms, c.moe
     d, I, E = cfg.d, cfg.I, cfg.E
     perm = ms.slot_permutation(cfg)
-    t0 = time.time()
-    stride = moe.moe_blob_stride(d, I)
-    staging = torch.empty((E, stride), dtype=torch.uint8, device="cuda")
-    for e in range(E):
-        staging[e].copy_(torch.from_numpy(moe.moe_pack_expert_int4(ms.expert_raw(cfg, e), d, I)))
-        if e % 128 == 127:
-            log(f"packed {e + 1}/{E} experts ({time.time() - t0:.1f}s)")
+    if staging is None:
+        staging = packed_experts(c, cfg)
     Wr = torch.from_numpy(ms.router_weight(cfg)).cuda()
     b = ms.logit_bias(cfg)
     bias = None if b is None else torch.from_numpy(b).cuda()
@@ -58,63 +89,66 @@ def build_layers(cfg, R, torch, moe, ms):
         if r % 8 == 7:
             log(f"replica {r + 1}/{R} ready")
     torch.cuda.synchronize()
-    del staging
     return layers
 
 
-def cpu_baseline(cfg, sample_steps, ms, olayer):
-    """The oracle as it stands, on the first `sample_steps` steps."""
+def x_steps(c, cfg, n, T=None):
+    torch, ms = c.torch, c.ms
+    xs = np.stack([ms.x_bits(cfg, s % cfg.steps, T) for s in range(n)])
+    return torch.from_numpy(xs.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def graph_time(c, fn, lo, hi, stream):
+    """Capture fn(i) for i in [lo, hi) in one graph; replay once; ms per call."""
+    torch = c.torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(lo, hi):
+                fn(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (hi - lo)
+
+
+def cpu_baseline(c, cfg, sample_steps):
+    """The oracle as it stands, on the first `sample_steps` decode steps."""
     import threadpoolctl
+    ms, olayer = c.ms, c.olayer
     Wr = ms.router_weight(cfg)
     bias = ms.logit_bias(cfg)
     sh = ms.shared_raw(cfg)
     xs = [ms.x_bits(cfg, s) for s in range(sample_steps)]
-    # inputs the oracle reads (raw codes of the experts those steps select)
     need = set()
     for xb in xs:
         idx, _, _, _ = olayer.route(xb, Wr, bias, cfg.k)
         need.update(int(e) for e in idx.ravel())
-    raws = {e: ms.expert_raw(cfg, e) for e in sorted(need)}
+    raws = {e: ms.expert_raw(cfg, e) for e in sorted(need)}     # inputs, generated before timing
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
     for xb in xs:
         olayer.moe_layer(xb, Wr, bias, cfg.k, raws.__getitem__, sh)
     dt = time.perf_counter() - t0
-    return {"value": sample_steps * cfg.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(sample_steps * cfg.T / dt, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"first {sample_steps} of the {cfg.steps} seeded decode steps, numpy fp64 "
                       f"(dequantise + matmul per selected expert), {dt:.1f}s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--replicas", type=int, default=32)
-    ap.add_argument("--cpu-steps", type=int, default=40)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="enqueue steps one by one (no HIP graph)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
-              "(no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import moe_synth as ms
-    import sparse_moe_decode_router_amd as moe
-    from oracle import layer as olayer
-
-    torch.cuda.set_device(0)
-    cfg = ms.scaled(ms.CONFIGS["decode80b"], n_slots=512)
-    K, W, R = args.steps, args.warmup, args.replicas
+def run_decode(c, name, K, W, R, cpu_steps, eager=False):
+    torch, ms, moe = c.torch, c.ms, c.moe
+    cfg = ms.scaled(ms.CONFIGS[name], n_slots=ms.CONFIGS[name].E)
     nsteps = K + W
-    log(f"workload decode80b all-resident, R={R} replicas, steps={K} warmup={W}")
-    layers = build_layers(cfg, R, torch, moe, ms)
-
-    xall = torch.from_numpy(np.stack([ms.x_bits(cfg, s % cfg.steps) for s in range(nsteps)])
-                            .view(np.int16)).cuda().view(torch.bfloat16)       # [n, 1, d]
+    log(f"{name}: all-resident, R={R} replicas, steps={K} warmup={W}")
+    layers = build_layers(c, cfg, R)
+    xall = x_steps(c, cfg, nsteps)
     ws = torch.zeros(layers[0].workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
     y = torch.empty((nsteps, 1, cfg.d), dtype=torch.float32, device="cuda")
     idx = torch.empty((nsteps, 1, cfg.k), dtype=torch.int32, device="cuda")
@@ -125,103 +159,240 @@ def main():
         moe.moe_layer_forward(layers[i % R], xall[i], path=moe.MOE_PATH_DECODE, workspace=ws,
                               out=(y[i], idx[i], w[i], s[i]))
 
-    # eager pass over every step: reference results for the graph replay
-    for i in range(nsteps):
+    for i in range(nsteps):                 # eager reference for the graph replays
         step(i)
     torch.cuda.synchronize()
-    y_eager = y.clone()
-    idx_eager = idx.clone()
-
+    y_eager, idx_eager = y.clone(), idx.clone()
     stream = torch.cuda.Stream()
-    if args.eager:
-        run = lambda lo, hi: [step(i) for i in range(lo, hi)]  # noqa: E731
-    else:
-        gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    if eager:
         with torch.cuda.stream(stream):
-            with torch.cuda.graph(gw, stream=stream):
-                for i in range(W):
-                    step(i)
-            with torch.cuda.graph(gt, stream=stream):
-                for i in range(W, nsteps):
-                    step(i)
-        run = None
-
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        if run is None:
-            gw.replay()
-        else:
-            run(0, W)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        if run is None:
-            gt.replay()
-        else:
-            run(W, nsteps)
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / K
+            for i in range(W):
+                step(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(W, nsteps):
+                step(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / K
+    else:
+        graph_time(c, step, 0, W, stream)
+        ms_step = graph_time(c, step, W, nsteps, stream)
     assert torch.equal(y, y_eager) and torch.equal(idx, idx_eager), "graph replay differs from eager"
 
-    # dominant kernels: the expert FFN of each step (gate/up + down, two
-    # launches), replayed alone from a graph over the same steps with the
-    # routing the layer produced; HIP events on the launch stream
+    # dominant kernels: the expert FFN (gate/up + down launches) of every
+    # timed step, replayed alone from a graph with the routing the layer
+    # produced; HIP events on the launch stream
     wsf = torch.zeros(moe.moe_ffn_workspace_bytes(cfg.d, cfg.I, cfg.I_shared, 1, cfg.k, cfg.E,
                                                   moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
-    yf = torch.empty((nsteps, 1, cfg.d), dtype=torch.float32, device="cuda")
+    yf = torch.empty_like(y)
 
     def ffn(i):
         L = layers[i % R]
         moe.moe_expert_ffn_int4(L.pool, L.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
                                 workspace=wsf, out=yf[i])
 
-    gf = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(gf, stream=stream):
-            for i in range(W, nsteps):
-                ffn(i)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        f0 = torch.cuda.Event(enable_timing=True)
-        f1 = torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        gf.replay()
-        f1.record(stream)
-        torch.cuda.synchronize()
-    ffn_ms = f0.elapsed_time(f1) / K
+    ffn_ms = graph_time(c, ffn, W, nsteps, stream)
     assert torch.equal(yf[W:], y[W:]), "FFN-only replay differs from the layer"
     expert_bytes = (cfg.k + 1) * moe.moe_blob_bytes(cfg.d, cfg.I)
+    router_bytes = (cfg.E + 1) * cfg.d * 4
     achieved = expert_bytes / (ffn_ms * 1e-3) / 1e9
     layer_gbs = expert_bytes / (ms_step * 1e-3) / 1e9
-
     out = {
-        "metric": "routed-MoE layer tokens/s + achieved HBM GB/s on int4 experts (80B shape)",
-        "value": round(1000.0 / ms_step, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": round(1000.0 / ms_step, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights, bf16 x, fp32 accumulate",
-        "data": "synthetic (seeded int4 codes U{0..15}, fp16 scales U[0.002,0.02], bias -8*scale, "
-                "x ~ N(0,1) bf16, router N(0,0.02) fp32, Zipf(1.1) logit offset alpha=0.15)",
-        "config": {"workload": "80B-shape batch-1 decode MoE layer, all 512 experts resident",
+        "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
+        "config": {"workload": f"{'80B' if cfg.E == 512 else '35B'}-shape batch-1 decode MoE layer, "
+                               f"all {cfg.E} experts resident",
                    "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "I_shared": cfg.I_shared,
-                   "group": 64, "replicas": R, "graph": run is None},
+                   "group": 64, "replicas": R, "hip_graph": not eager},
         "expert_bytes_per_step": expert_bytes,
+        "all_bytes_per_step": expert_bytes + router_bytes,
         "layer_expert_GBps": round(layer_gbs, 1),
         "layer_expert_frac_of_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "expert FFN (gate_up_kernel + down_decode_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "expert FFN: gate_up_kernel + down_decode_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_ms": round(ffn_ms, 5)},
+                     "avg_us": round(ffn_ms * 1e3, 3)},
     }
-    if not args.no_cpu:
+    if cpu_steps > 0:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps, ms, olayer)
-    print(json.dumps(out), flush=True)
+        out["cpu_baseline"] = cpu_baseline(c, cfg, cpu_steps)
+    return out
+
+
+def run_refill(c, K, W):
+    """256-slot pool over 512 experts, refilled between router and experts by
+    LFU + recency from pinned host memory; outputs checked bit-identical to an
+    all-resident twin."""
+    torch, ms, moe = c.torch, c.ms, c.moe
+    cfg = ms.CONFIGS["decode80b"]
+    nsteps = K + W
+    log(f"refill80b: {cfg.n_slots} slots over {cfg.E} experts, steps={nsteps}")
+    host = packed_experts(c, cfg, pinned=True)
+    stride = host.shape[1]
+    twin = build_layers(c, ms.scaled(cfg, n_slots=cfg.E), 1, staging=host.cuda())[0]
+    pool = moe.Pool(cfg.E, cfg.n_slots, cfg.d, cfg.I)
+    xall = x_steps(c, cfg, nsteps)
+    wsr = torch.zeros(moe.moe_router_workspace_bytes(1, cfg.d, cfg.E), dtype=torch.uint8, device="cuda")
+    wsf = torch.zeros(moe.moe_ffn_workspace_bytes(cfg.d, cfg.I, cfg.I_shared, 1, cfg.k, cfg.E,
+                                                  moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
+    y = torch.empty((nsteps, 1, cfg.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nsteps, 1, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((nsteps, 1, cfg.k), dtype=torch.float32, device="cuda")
+    s = torch.empty((nsteps, 1), dtype=torch.float32, device="cuda")
+    idx_host = torch.empty((cfg.k,), dtype=torch.int32, pin_memory=True)
+
+    def step(i):
+        moe.moe_router_topk(xall[i], twin.w_router, twin.logit_bias, cfg.k, workspace=wsr,
+                            out=(idx[i], w[i], s[i]))
+        idx_host.copy_(idx[i, 0], non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        pool.refill(idx_host.numpy(), host, stride)
+        moe.moe_expert_ffn_int4(pool, twin.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
+                                workspace=wsf, out=y[i])
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    st0 = pool.stats()
+    t0 = time.perf_counter()
+    for i in range(W, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st1 = pool.stats()
+    assert pool.check_error() == moe.MOE_OK
+    # all-resident twin over the same steps: bit-identical outputs
+    wst = torch.zeros(twin.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
+    yt = torch.empty_like(y)
+    it = torch.empty_like(idx)
+    for i in range(nsteps):
+        moe.moe_layer_forward(twin, xall[i], path=moe.MOE_PATH_DECODE, workspace=wst,
+                              out=(yt[i], it[i], torch.empty_like(w[i]), torch.empty_like(s[i])))
+    torch.cuda.synchronize()
+    identical = bool(torch.equal(yt, y) and torch.equal(it, idx))
+    hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
+    ms_step = dt * 1e3 / K
+    return {"metric": METRIC, "value": round(K / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+            "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
+            "config": {"workload": "80B-shape batch-1 decode, 256-slot HBM pool refilled by LFU+recency "
+                                   "from pinned host memory (wall clock incl. PCIe and host policy)",
+                       "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "slots": cfg.n_slots},
+            "hit_rate": round(hits / max(1, hits + misses), 4),
+            "hit_rate_all_steps": round(st1["hits"] / max(1, st1["hits"] + st1["misses"]), 4),
+            "pcie_bytes_per_step": round((st1["bytes_loaded"] - st0["bytes_loaded"]) / K),
+            "bit_identical_to_all_resident": identical}
+
+
+def run_batched(c, K, W, R):
+    torch, ms, moe = c.torch, c.ms, c.moe
+    cfg = ms.CONFIGS["batch80b"]
+    T = cfg.T
+    nsteps = K + W
+    log(f"batch80b: T={T}, R={R}, steps={K}")
+    layers = build_layers(c, cfg, R)
+    xall = x_steps(c, cfg, nsteps)
+    ws = torch.zeros(layers[0].workspace_bytes(T, moe.MOE_PATH_BATCHED), dtype=torch.uint8, device="cuda")
+    y = torch.empty((nsteps, T, cfg.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nsteps, T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((nsteps, T, cfg.k), dtype=torch.float32, device="cuda")
+    s = torch.empty((nsteps, T), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        moe.moe_layer_forward(layers[i % R], xall[i], path=moe.MOE_PATH_BATCHED, workspace=ws,
+                              out=(y[i], idx[i], w[i], s[i]))
+
+    stream = torch.cuda.Stream()
+    graph_time(c, step, 0, W, stream)
+    ms_step = graph_time(c, step, W, nsteps, stream)
+    ids = idx.cpu().numpy()
+    distinct = float(np.mean([len(np.unique(ids[i])) for i in range(W, nsteps)]))
+    expert_bytes = (distinct + 1) * moe.moe_blob_bytes(cfg.d, cfg.I)
+    gbs = expert_bytes / (ms_step * 1e-3) / 1e9
+    return {"metric": METRIC, "value": round(T * 1000.0 / ms_step, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate",
+            "data": DATA,
+            "config": {"workload": "80B-shape batched decode, T=64 independent tokens, all experts resident",
+                       "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "replicas": R},
+            "distinct_experts_per_step": round(distinct, 1),
+            "layer_expert_GBps": round(gbs, 1), "layer_expert_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def run_prefill(c, name, reps):
+    torch, ms, moe = c.torch, c.ms, c.moe
+    cfg = ms.CONFIGS[name]
+    T = cfg.T
+    log(f"{name}: T={T}, reps={reps}")
+    L = build_layers(c, ms.scaled(cfg, n_slots=cfg.E), 1)[0]
+    x = x_steps(c, cfg, 1, T)[0]
+    ws = torch.zeros(L.workspace_bytes(T, moe.MOE_PATH_PREFILL), dtype=torch.uint8, device="cuda")
+    out = (torch.empty((T, cfg.d), dtype=torch.float32, device="cuda"),
+           torch.empty((T, cfg.k), dtype=torch.int32, device="cuda"),
+           torch.empty((T, cfg.k), dtype=torch.float32, device="cuda"),
+           torch.empty((T,), dtype=torch.float32, device="cuda"))
+
+    def step(i):
+        moe.moe_layer_forward(L, x, path=moe.MOE_PATH_PREFILL, workspace=ws, out=out)
+
+    stream = torch.cuda.Stream()
+    graph_time(c, step, 0, 2, stream)
+    ms_call = graph_time(c, step, 0, reps, stream)
+    assert L.pool.check_error() == moe.MOE_OK
+    counts = np.bincount(out[1].cpu().numpy().ravel(), minlength=cfg.E)
+    flops = 6.0 * cfg.d * (T * cfg.k * cfg.I + T * cfg.I_shared)
+    router_flops = 2.0 * T * cfg.d * (cfg.E + 1)
+    tf = flops / (ms_call * 1e-3) / 1e12
+    return {"metric": METRIC, "value": round(T * 1000.0 / ms_call, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": reps, "warmup": 2, "ms_per_step": round(ms_call, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None,
+            "dtype": "int4 weights -> fp16 MFMA, fp32 accumulate; fp32 router", "data": DATA,
+            "config": {"workload": f"80B-shape prefill layer, T={T}, "
+                                   f"{'Zipf-skewed' if cfg.alpha else 'unbiased'} router",
+                       "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I},
+            "expert_gflop": round(flops / 1e9, 1), "router_gflop": round(router_flops / 1e9, 2),
+            "layer_expert_TFLOPs": round(tf, 1), "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "max_bucket": int(counts.max())}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--replicas", type=int, default=32)
+    ap.add_argument("--cpu-steps", type=int, default=40)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="enqueue decode steps one by one (no HIP graph)")
+    ap.add_argument("--workload", default="decode80b",
+                    choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
+                             "prefill80b_zipf", "all"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
+              "(no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    c = Ctx()
+    c.torch.cuda.set_device(0)
+    cpu = 0 if args.no_cpu else args.cpu_steps
+    todo = ["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b", "prefill80b_zipf"] \
+        if args.workload == "all" else [args.workload]
+    for wl in todo:
+        if wl in ("decode80b", "decode35b"):
+            res = run_decode(c, wl, args.steps, args.warmup, args.replicas,
+                             cpu if wl == "decode80b" else 0, args.eager)
+        elif wl == "refill80b":
+            res = run_refill(c, min(args.steps, 300), min(args.warmup, 50))
+        elif wl == "batch80b":
+            res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4))
+        else:
+            res = run_prefill(c, wl, 10)
+        print(json.dumps(res), flush=True)
+        c.torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
