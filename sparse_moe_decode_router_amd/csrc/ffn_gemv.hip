@@ -105,6 +105,33 @@ __device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, 
 
 constexpr int kGMax = 4;        // groups of 64 inputs per lane (d <= 8192)
 
+// h of 8 consecutive intermediate rows (one 8-block m = rb) as bf16 (hi, lo)
+// pairs (h[8m+i], h[8m+i+4]) plus the sum of hi + lo, for the down pass.
+__device__ __forceinline__ void write_h8(const float* h, uint32_t* hq, float* hs8, int Imax, int hrow, int rb) {
+  uint32_t hi[4], lo[4];
+  float s8 = 0.f;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const uint32_t a0 = f32_to_bf16(h[ii]), a1 = f32_to_bf16(h[ii + 4]);
+    const float r0 = h[ii] - __uint_as_float(a0 << 16);
+    const float r1 = h[ii + 4] - __uint_as_float(a1 << 16);
+    const uint32_t b0 = f32_to_bf16(r0), b1 = f32_to_bf16(r1);
+    hi[ii] = a0 | (a1 << 16);
+    lo[ii] = b0 | (b1 << 16);
+  }
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const int p = ii & 3;
+    const float hv = ii < 4 ? __uint_as_float(hi[p] << 16) + __uint_as_float(lo[p] << 16)
+                            : __uint_as_float(hi[p] & 0xFFFF0000u) + __uint_as_float(lo[p] & 0xFFFF0000u);
+    s8 += hv;
+  }
+  uint32_t* dst = hq + (size_t)hrow * Imax;
+  *reinterpret_cast<uint4*>(dst + 4 * rb) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *reinterpret_cast<uint4*>(dst + Imax / 2 + 4 * rb) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  hs8[(size_t)hrow * (Imax / 8) + rb] = s8;
+}
+
 // Decode blocks of routed instances select their expert in-kernel: the
 // token's logits (+ bias) and the slot table are staged in LDS, wave 0 runs
 // the top-k, and the block of (rank 0, rows 0..7) publishes the token's
@@ -267,28 +294,122 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
         const float g = gu[0][tt][rr], u = gu[1][tt][rr];
         h[rr] = missing ? 0.0f : g / (1.0f + expf(-g)) * u;
       }
-      uint32_t hi[4], lo[4];
-      float s8 = 0.f;
+      write_h8(h, a.hq, a.hs8, a.Imax, hrow[tt], rb);
+    }
+    if (missing && tid == 0) atomicOr(a.pool.err, 1);
+    __syncthreads();
+  }
+}
+
+// Batched gate/up: item = (bucket chunk of <= kTC tokens, 64 rows).  The
+// chunk's activations are staged in LDS once per item; each wave computes
+// whole rows on its own (8 rows x 8 group lanes, GPL groups per lane), two
+// 8-row sub-blocks per wave, so rows meet by DPP without block barriers.
+template <int GPL>
+__global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
+  extern __shared__ uint32_t xlds[];            // [kTC][G][kXPad] | xs [kTC][G] | hbuf [4][kTC][8]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane >> 3, gl = lane & 7;
+  const int G = a.d / 64;
+  float* xsl = reinterpret_cast<float*>(xlds + kTC * G * kXPad);
+  float* hbuf = xsl + kTC * G + wave * kTC * 8;
+  const int nbR = a.I / 64, nbS = a.Ish / 64;
+  const int nR = *a.n_routed;
+  const int items = nR * nbR + a.n_shared_inst * nbS;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const bool routed = item < nR * nbR;
+    const int rel = routed ? item : item - nR * nbR;
+    const int nb = routed ? nbR : nbS;
+    const int i = rel / nb, ob = rel % nb;
+    const uint8_t* blob;
+    int Iinst, tok[kTC], hrow[kTC];
+    bool missing;
+    const int ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
+    const BlobLayout L = blob_layout(a.d, Iinst);
+    for (int q = tid; q < ntok * (a.d / 8); q += 256) {
+      const int tt = q / (a.d / 8), c4 = q % (a.d / 8);
+      const uint4 v = reinterpret_cast<const uint4*>(a.xq + (size_t)tok[tt] * (a.d / 2))[c4];
+      *reinterpret_cast<uint4*>(&xlds[(tt * G + (c4 >> 3)) * kXPad + 4 * (c4 & 7)]) = v;
+    }
+    for (int q = tid; q < ntok * G; q += 256) xsl[q] = a.xs[(size_t)tok[q / G] * G + q % G];
+    __syncthreads();
+#pragma unroll 1
+    for (int sbk = wave; sbk < 8; sbk += 4) {
+      const int rb = ob * 8 + sbk;              // 8-row block index within the expert
+      const uint64_t o = (uint64_t)(rb * 8 + r);
+      uint4 cg[GPL][2], cu[GPL][2];
+      uint32_t sbg[GPL], sbu[GPL];
+      if (!missing) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const uint32_t a0 = f32_to_bf16(h[ii]), a1 = f32_to_bf16(h[ii + 4]);
-        const float r0 = h[ii] - __uint_as_float(a0 << 16);
-        const float r1 = h[ii + 4] - __uint_as_float(a1 << 16);
-        const uint32_t b0 = f32_to_bf16(r0), b1 = f32_to_bf16(r1);
-        hi[ii] = a0 | (a1 << 16);
-        lo[ii] = b0 | (b1 << 16);
+        for (int gi = 0; gi < GPL; ++gi) {
+          const int g = gl + 8 * gi;
+          if (g < G) {
+            const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
+            const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
+            cg[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c0);
+            cg[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c1);
+            cu[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c0);
+            cu[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c1);
+            sbg[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[0].sb + ((uint64_t)g * Iinst + o) * 4);
+            sbu[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[1].sb + ((uint64_t)g * Iinst + o) * 4);
+          }
+        }
+      }
+      float vg[kTC], vu[kTC];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt) { vg[tt] = 0.f; vu[tt] = 0.f; }
+      if (!missing) {
+#pragma unroll
+        for (int gi = 0; gi < GPL; ++gi) {
+          const int g = gl + 8 * gi;
+          if (g >= G) continue;
+          const uint32_t gw[8] = {cg[gi][0].x, cg[gi][0].y, cg[gi][0].z, cg[gi][0].w,
+                                  cg[gi][1].x, cg[gi][1].y, cg[gi][1].z, cg[gi][1].w};
+          const uint32_t uw[8] = {cu[gi][0].x, cu[gi][0].y, cu[gi][0].z, cu[gi][0].w,
+                                  cu[gi][1].x, cu[gi][1].y, cu[gi][1].z, cu[gi][1].w};
+          const float sg = f16_to_f32(sbg[gi]), bg = f16_to_f32(sbg[gi] >> 16);
+          const float su = f16_to_f32(sbu[gi]), bu = f16_to_f32(sbu[gi] >> 16);
+#pragma unroll
+          for (int tt = 0; tt < kTC; ++tt) {
+            if (tt < ntok) {
+              const uint32_t* xp = &xlds[(tt * G + g) * kXPad];
+              float ag0 = 0.f, au0 = 0.f, ag1 = 0.f, au1 = 0.f;
+#pragma unroll
+              for (int w = 0; w < 8; ++w) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * w);
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int ii = 0; ii < 4; ii += 2) {
+                  ag0 = dot2_bf16(nib_pair(gw[w], ii), xw[ii], ag0);
+                  au0 = dot2_bf16(nib_pair(uw[w], ii), xw[ii], au0);
+                  ag1 = dot2_bf16(nib_pair(gw[w], ii + 1), xw[ii + 1], ag1);
+                  au1 = dot2_bf16(nib_pair(uw[w], ii + 1), xw[ii + 1], au1);
+                }
+              }
+              const float sx = xsl[tt * G + g];
+              vg[tt] += sg * (ag0 + ag1) + (bg - 128.0f * sg) * sx;
+              vu[tt] += su * (au0 + au1) + (bu - 128.0f * su) * sx;
+            }
+          }
+        }
       }
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int p = ii & 3;
-        const float hv = ii < 4 ? __uint_as_float(hi[p] << 16) + __uint_as_float(lo[p] << 16)
-                                : __uint_as_float(hi[p] & 0xFFFF0000u) + __uint_as_float(lo[p] & 0xFFFF0000u);
-        s8 += hv;
+      for (int tt = 0; tt < kTC; ++tt) {
+        const float gg = sum8_dpp(vg[tt]), uu = sum8_dpp(vu[tt]);
+        if (gl == 0) hbuf[tt * 8 + r] = missing ? 0.f : gg / (1.0f + expf(-gg)) * uu;
       }
-      uint32_t* dst = a.hq + (size_t)hrow[tt] * a.Imax;
-      *reinterpret_cast<uint4*>(dst + 4 * rb) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(dst + a.Imax / 2 + 4 * rb) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      a.hs8[(size_t)hrow[tt] * (a.Imax / 8) + rb] = s8;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane < ntok) {
+        float h[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) h[rr] = hbuf[lane * 8 + rr];
+        write_h8(h, a.hq, a.hs8, a.Imax, hrow[lane], rb);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (missing && tid == 0) atomicOr(a.pool.err, 1);
     __syncthreads();
@@ -436,15 +557,19 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   }
 }
 
-// Batched: item = (instance, 32 rows); wave = 8 rows x 8 group lanes.
+// Batched down: item = (bucket chunk, 256 output rows).  The chunk's h
+// records are staged in LDS once; each wave takes 8-row sub-blocks (8 rows x
+// 8 group lanes), loads the codes once and applies them to every token.
 __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
+  extern __shared__ uint32_t hst[];            // [kTC][Imax + Imax/8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 7, gl = lane >> 3;
-  const int rbs = a.d / 32;
+  const int r = lane >> 3, gl = lane & 7;
+  const int nrb = (a.d + 255) / 256;            // d is a multiple of 64: last block may be partial
   const int nR = *a.n_routed;
-  const int items = (nR + a.n_shared_inst) * rbs;
+  const int items = (nR + a.n_shared_inst) * nrb;
+  const int rec = a.Imax + a.Imax / 8;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int ii = item / rbs, rb = item % rbs;
+    const int ii = item / nrb, j0 = (item % nrb) * 256;
     const bool routed = ii < nR;
     const Inst in = a.inst[ii];
     const uint8_t* blob;
@@ -460,24 +585,53 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
       blob = a.shared_blob;
       Iinst = a.Ish;
     }
+    int hrow[kTC];
+#pragma unroll
+    for (int tt = 0; tt < kTC; ++tt)
+      hrow[tt] = tt < in.n ? (routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt) : 0;
+    for (int q4 = tid; q4 < in.n * (rec / 4); q4 += 256) {
+      const int tt = q4 / (rec / 4), c = q4 % (rec / 4);
+      const int hr = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
+      uint4 v;
+      if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)hr * a.Imax)[c];
+      else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)hr * (a.Imax / 8))[c - a.Imax / 4];
+      *reinterpret_cast<uint4*>(hst + tt * rec + 4 * c) = v;
+    }
+    __syncthreads();
     const BlobLayout L = blob_layout(a.d, Iinst);
-    const int j = rb * 32 + wave * 8 + r;
-    for (int tt = 0; tt < in.n; ++tt) {
-      const int hrow = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
-      const uint32_t* hrec = a.hq + (size_t)hrow * a.Imax;
-      const float* hs = a.hs8 + (size_t)hrow * (a.Imax / 8);
-      float acc = 0.f;
-      if (!missing)
-        for (int g = gl; g < Iinst / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
-      acc += __shfl_xor(acc, 8, 64);
-      acc += __shfl_xor(acc, 16, 64);
-      acc += __shfl_xor(acc, 32, 64);
-      if (lane < 8) {
-        if (routed) a.partial[(size_t)hrow * a.d + j] = acc;
-        else a.shared_out[(size_t)(in.start + tt) * a.d + j] = acc;
+#pragma unroll 1
+    for (int sbk = wave; sbk < 32; sbk += 4) {
+      const int j = j0 + sbk * 8 + r;
+      const bool jv = j < a.d;
+      float acc[kTC];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt) acc[tt] = 0.f;
+      if (!missing && jv) {
+        for (int g = gl; g < Iinst / 64; g += 8) {
+          const uint64_t c0 = ((uint64_t)(2 * g) * a.d + j) * 16;
+          const uint4 q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
+          const uint4 q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
+          const uint32_t sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * a.d + j) * 4);
+#pragma unroll
+          for (int tt = 0; tt < kTC; ++tt) {
+            if (tt < in.n) {
+              const uint32_t* hrec = hst + tt * rec;
+              acc[tt] += down_group_regs(q0, q1, sb, g, hrec, a.Imax, reinterpret_cast<const float*>(hrec + a.Imax));
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt) {
+        const float v = sum8_dpp(acc[tt]);
+        if (gl == 0 && tt < in.n && jv) {
+          if (routed) a.partial[(size_t)hrow[tt] * a.d + j] = v;
+          else a.shared_out[(size_t)(in.start + tt) * a.d + j] = v;
+        }
       }
     }
     if (missing && tid == 0) atomicOr(a.pool.err, 1);
+    __syncthreads();
   }
 }
 
@@ -619,17 +773,19 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   MOE_HIP(hipGetLastError());
   g.batched = 1;
   g.inst = w.inst; g.n_routed = w.n_routed; g.n_shared_inst = nsh; g.pair_ids = f.pair_ids;
-  const long upper = ((long)f.T * f.k + nsh) * (Imax / 8);
-  const size_t lds = (size_t)kTC * G * kXPad * 4;
+  const long upper = ((long)f.T * f.k + nsh) * (Imax / 64);
+  const size_t lds = ((size_t)kTC * G * kXPad + kTC * G + 4 * kTC * 8) * 4;
+  void* gfn = G <= 8 ? (void*)gate_up_batched_kernel<1> : G <= 16 ? (void*)gate_up_batched_kernel<2>
+            : G <= 32 ? (void*)gate_up_batched_kernel<4> : G <= 64 ? (void*)gate_up_batched_kernel<8>
+            : (void*)gate_up_batched_kernel<16>;
   void* args[] = {&g};
-  MOE_HIP(hipLaunchKernel((void*)gate_up_kernel<kTC, 1>, dim3(grid_for((int)(upper < 65536 ? upper : 65536))),
-                          dim3(256), args, lds, s));
+  MOE_HIP(hipLaunchKernel(gfn, dim3(grid_for((int)(upper < 65536 ? upper : 65536))), dim3(256), args, lds, s));
   dn.inst = w.inst; dn.n_routed = w.n_routed; dn.n_shared_inst = nsh; dn.pair_ids = f.pair_ids;
   dn.partial = f.partial; dn.shared_out = f.shared_out;
-  const long dupper = ((long)f.T * f.k + nsh) * (f.d / 32);
+  const long dupper = ((long)f.T * f.k + nsh) * ((f.d + 255) / 256);
   void* dargs[] = {&dn};
   MOE_HIP(hipLaunchKernel((void*)down_batched_kernel, dim3(grid_for((int)(dupper < 65536 ? dupper : 65536))),
-                          dim3(256), dargs, 0, s));
+                          dim3(256), dargs, (size_t)kTC * (Imax + Imax / 8) * 4, s));
   return MOE_OK;
 }
 

@@ -79,8 +79,9 @@ struct Carver {
 // -------------------------------------------------------- internal entry
 // Router pieces used by the layer driver (router.hip).
 struct RouterWs {
-  float* logits;      // [T][E+1]
-  uint32_t* ticket;   // one counter, zero between calls
+  float* logits;      // [S][T][E+1] (S split-K partials, S = 1 for T <= 8)
+  uint32_t* ticket;   // unused, kept zero
+  uint16_t* wsplit;   // [3][E+1][d] bf16 parts of the router weights (T > 8)
   uint32_t* xq;       // [T][d/2]  bf16 pairs (x[8m+i], x[8m+i+4])
   float* xs;          // [T][d/64] group sums of x
 };
@@ -92,7 +93,7 @@ int router_launch(const uint16_t* x, int T, int d, const float* W, const float* 
 // logits [T][E+1] (+ xq/xs) only; the decode FFN selects in-kernel
 int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
                          const RouterWs& ws, hipStream_t s);
-int topk_launch(const float* logits, const float* bias, int T, int E, int k, int32_t* idx,
+int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx,
                 float* w, float* sgate, uint32_t* usage, hipStream_t s);
 
 int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts,

@@ -100,71 +100,101 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   if (tid < T) a.logits[(size_t)tid * (E + 1) + row] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
 }
 
-// ---------------------------------------------------------- batched router
-// logits[t][e] for T > 8: 64x64 output tiles, K tiles of 32 staged in LDS.
-// Each K tile is summed on its own (depth 32) before joining the running
-// total (depth d/32): depth 32 + d/32, plus one for the bias.
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int d,
-                                                          const float* __restrict__ W, int R,
-                                                          float* __restrict__ logits) {
-  __shared__ float As[32][64 + 4];
-  __shared__ float Bs[32][64 + 4];
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    {  // x tile: 64 tokens x 32 cols, 8 bf16 per thread
-      const int m = tid >> 2, c8 = (tid & 3) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + m < T) v = *reinterpret_cast<const uint4*>(x + (size_t)(m0 + m) * d + k0 + c8);
-      As[c8 + 0][m] = bf16_lo(v.x); As[c8 + 1][m] = bf16_hi(v.x);
-      As[c8 + 2][m] = bf16_lo(v.y); As[c8 + 3][m] = bf16_hi(v.y);
-      As[c8 + 4][m] = bf16_lo(v.z); As[c8 + 5][m] = bf16_hi(v.z);
-      As[c8 + 6][m] = bf16_lo(v.w); As[c8 + 7][m] = bf16_hi(v.w);
-    }
+// ------------------------------------------------------ MFMA router (T > 8)
+// fp32 router rows split into three bf16 parts (hi, mid, lo: hi + mid + lo
+// carries the fp32 significand); x is exactly bf16, so every product on the
+// matrix cores is exact in fp32.  Each 32-wide K step starts fresh
+// accumulators (<= 32 additions) that are folded into a running fp32 sum
+// (d/(32 S) additions), so the summation depth stays near a plain tiled GEMM:
+// 32 + 2 + d/(32 S) per split, plus S-1 for the fixed-order sum of the S
+// split-K partials in the top-k kernel, plus one for the bias.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W, long n,
+                                                           uint16_t* __restrict__ Wsplit) {
+  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= n) return;
+  const float w = W[id];
+  const uint32_t hi = f32_to_bf16(w);
+  const float r1 = w - __uint_as_float(hi << 16);
+  const uint32_t mid = f32_to_bf16(r1);
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  const uint32_t lo = f32_to_bf16(r2);
+  Wsplit[id] = (uint16_t)hi;
+  Wsplit[n + id] = (uint16_t)mid;
+  Wsplit[2 * n + id] = (uint16_t)lo;
+}
+
+constexpr int kRtM = 128, kRtN = 64, kRtLds = 40;   // block tile, LDS row (bf16)
+
+__global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __restrict__ x, int T, int d,
+                                                          const uint16_t* __restrict__ Wsplit, int R,
+                                                          int S, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kRtM * kRtLds];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[3][kRtN * kRtLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * kRtM, n0 = blockIdx.x * kRtN, sp = blockIdx.z;
+  const int kspan = d / S, kbeg = sp * kspan;
+  const long nW = (long)R * d;
+  const int wm = 32 * (wave & 3), wn = 32 * (wave >> 2);
+  float run[16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // W tile: 64 rows x 32 cols
-      const int idx = tid + 256 * h;
-      const int n = idx >> 3, c4 = (idx & 7) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (n0 + n < R) v = *reinterpret_cast<const float4*>(W + (size_t)(n0 + n) * d + k0 + c4);
-      Bs[c4 + 0][n] = v.x; Bs[c4 + 1][n] = v.y; Bs[c4 + 2][n] = v.z; Bs[c4 + 3][n] = v.w;
+  for (int i = 0; i < 16; ++i) run[i] = 0.f;
+  for (int k0 = kbeg; k0 < kbeg + kspan; k0 += 32) {
+    {  // x tile: 128 tokens x 32, one uint4 (8 bf16) per thread
+      const int row = tid >> 2, q = tid & 3;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m0 + row < T) v = *reinterpret_cast<const uint4*>(x + (size_t)(m0 + row) * d + k0 + 8 * q);
+      *reinterpret_cast<uint4*>(&xs[row * kRtLds + 8 * q]) = v;
+    }
+    for (int qq = tid; qq < 3 * kRtN * 4; qq += 512) {   // W parts: 3 x 64 rows x 32
+      const int j = qq / (kRtN * 4), rem = qq % (kRtN * 4), row = rem >> 2, q = rem & 3;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n0 + row < R) v = *reinterpret_cast<const uint4*>(Wsplit + j * nW + (size_t)(n0 + row) * d + k0 + 8 * q);
+      *reinterpret_cast<uint4*>(&ws[j][row * kRtLds + 8 * q]) = v;
     }
     __syncthreads();
-    float part[4][4] = {};
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float av[4], bv[4];
+    f32x16_t acc[3];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+    for (int j = 0; j < 3; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bv[i] = Bs[kk][tx * 4 + i];
+      for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xs[(wm + (lane & 31)) * kRtLds + 16 * kh + 8 * (lane >> 5)]);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) part[i][jj] += av[i] * bv[jj];
+      for (int j = 0; j < 3; ++j) {
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&ws[j][(wn + (lane & 31)) * kRtLds + 16 * kh + 8 * (lane >> 5)]);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[j], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[i][jj] += part[i][jj];
+    for (int i = 0; i < 16; ++i) run[i] += (acc[0][i] + acc[1][i]) + acc[2][i];
     __syncthreads();
   }
+  float* out = part + (size_t)sp * T * R;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
-    if (m >= T) continue;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int n = n0 + tx * 4 + jj;
-      if (n < R) logits[(size_t)m * R + n] = acc[i][jj];
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+    const int n = n0 + wn + (lane & 31);
+    if (m < T && n < R) out[(size_t)m * R + n] = run[i];
   }
 }
 
+// split-K count for T > 8: enough blocks for small T; every split spans a
+// multiple of 32 columns (d is a multiple of 64)
+int router_splits(int T, int d) {
+  int S = T <= 128 ? 8 : T <= 1024 ? 2 : 1;
+  while (S > 1 && (d / 32) % S != 0) S /= 2;
+  return S;
+}
+
+// One wave per token.  With S > 1 the logits arrive as S split-K partials
+// [S][T][E+1], summed here in split order before the selection.
 template <int NK>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int S,
+                                                   const float* __restrict__ bias,
                                                    int T, int E, int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ sgate,
                                                    uint32_t* __restrict__ usage) {
@@ -173,13 +203,25 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int k4 = (k + 3) & ~3;
-  uint32_t* base = dyn_lds + wave * (2 * k4 + topk_scratch_words(E));
+  const int stride = 2 * k4 + topk_scratch_words(E) + ((E + 1 + 3) & ~3);
+  uint32_t* base = dyn_lds + wave * stride;
   float* sel_l = reinterpret_cast<float*>(base);
   int32_t* sel_e = reinterpret_cast<int32_t*>(base + k4);
-  const float* lrow = logits + (size_t)t * (E + 1);
-  topk_select<NK>(lrow, bias, E, k, sel_l, sel_e, base + 2 * k4);
+  uint32_t* scr = base + 2 * k4;
+  float* lsum = reinterpret_cast<float*>(scr + topk_scratch_words(E));
+  const size_t TR = (size_t)T * (E + 1);
+  for (int e = lane; e <= E; e += 64) {
+    const float* p = logits + (size_t)t * (E + 1) + e;
+    float v = p[0];
+    for (int q = 1; q < S; ++q) v += p[q * TR];
+    lsum[e] = v;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  topk_select<NK>(lsum, bias, E, k, sel_l, sel_e, scr);
   topk_finish(sel_l, sel_e, k, idx + (size_t)t * k, w + (size_t)t * k, usage);
-  if (lane == 0 && sgate) sgate[t] = sigmoidf_(lrow[E]);
+  if (lane == 0 && sgate) sgate[t] = sigmoidf_(lsum[E]);
 }
 
 }  // namespace
@@ -201,7 +243,8 @@ size_t router_ws_bytes(int T, int d, int E) {
 
 bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws) {
   ws->ticket = c.take<uint32_t>(64);
-  ws->logits = c.take<float>((size_t)T * (E + 1));
+  ws->logits = c.take<float>((size_t)(T <= 8 ? 1 : router_splits(T, d)) * T * (E + 1));
+  ws->wsplit = T <= 8 ? nullptr : c.take<uint16_t>((size_t)3 * (E + 1) * d);
   ws->xq = c.take<uint32_t>((size_t)T * d / 2);
   ws->xs = c.take<float>((size_t)T * d / 64);
   return c.ok();
@@ -219,22 +262,28 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
     return MOE_OK;
   }
   MOE_TRY(xprep_launch(x, T, d, ws.xq, ws.xs, s));
-  router_gemm_kernel<<<dim3((E + 1 + 63) / 64, (T + 63) / 64), 256, 0, s>>>(x, T, d, W, E + 1, ws.logits);
+  const int R = E + 1, S = router_splits(T, d);
+  const long nW = (long)R * d;
+  router_split_kernel<<<(unsigned)((nW + 255) / 256), 256, 0, s>>>(W, nW, ws.wsplit);
+  MOE_HIP(hipGetLastError());
+  router_mfma_kernel<<<dim3((R + kRtN - 1) / kRtN, (T + kRtM - 1) / kRtM, S), 512, 0, s>>>(
+      x, T, d, ws.wsplit, R, S, ws.logits);
   MOE_HIP(hipGetLastError());
   return MOE_OK;
 }
 
-int topk_launch(const float* logits, const float* bias, int T, int E, int k, int32_t* idx, float* w,
+int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx, float* w,
                 float* sgate, uint32_t* usage, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  const size_t lds = (size_t)4 * (2 * ((k + 3) & ~3) + topk_scratch_words(E)) * 4;
+  const int S = T <= 8 ? 1 : router_splits(T, d);
+  const size_t lds = (size_t)4 * (2 * ((k + 3) & ~3) + topk_scratch_words(E) + ((E + 1 + 3) & ~3)) * 4;
   const dim3 tg((T + 3) / 4);
   switch (nk_for(E)) {
-    case 1: topk_kernel<1><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
-    case 2: topk_kernel<2><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
-    case 4: topk_kernel<4><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
-    case 8: topk_kernel<8><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
-    default: topk_kernel<16><<<tg, 256, lds, s>>>(logits, bias, T, E, k, idx, w, sgate, usage); break;
+    case 1: topk_kernel<1><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
+    case 2: topk_kernel<2><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
+    case 4: topk_kernel<4><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
+    case 8: topk_kernel<8><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
+    default: topk_kernel<16><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
   }
   MOE_HIP(hipGetLastError());
   return MOE_OK;
@@ -244,7 +293,7 @@ int router_launch(const uint16_t* x, int T, int d, const float* W, const float* 
                   int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
                   const RouterWs& ws, hipStream_t s) {
   MOE_TRY(router_logits_launch(x, T, d, W, E, ws, s));
-  return topk_launch(ws.logits, bias, T, E, k, idx, w, sgate, usage, s);
+  return topk_launch(ws.logits, bias, T, d, E, k, idx, w, sgate, usage, s);
 }
 
 }  // namespace moe
@@ -258,7 +307,9 @@ extern "C" size_t moe_router_workspace_bytes(int32_t T, int32_t d, int32_t E) {
 
 extern "C" int32_t moe_router_sum_depth(int32_t T, int32_t d) {
   if (d <= 0) return -1;
-  return T <= 8 ? d / 256 + 9 : 32 + d / 32 + 1;
+  if (T <= 8) return d / 256 + 9;
+  const int S = router_splits(T, d);
+  return 32 + 2 + d / (32 * S) + (S - 1) + 1;
 }
 
 extern "C" int moe_router_topk(const uint16_t* x, int32_t T, int32_t d, const float* W,

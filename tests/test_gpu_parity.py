@@ -313,3 +313,10 @@ def test_prefill_matches_batched_path():
     torch.cuda.synchronize()
     assert np.array_equal(_np(ip), _np(ib))
     assert_close_y(_np(yp), _np(yb).astype(np.float64))
+
+
+def test_batched_small_d_partial_row_block():
+    """d = 192 (not a multiple of the 256-row down tile) on the batched path."""
+    cfg = ms.scaled(TINY, d=192, I=64, I_shared=64, T=12, E=16, k=3)
+    L = DeviceLayer(cfg)
+    _check_layer_step(L, 2, path=moe.MOE_PATH_BATCHED, T=12)

@@ -144,6 +144,8 @@ def test_validation_without_device_work():
     h = C.c_void_p()
     assert lib.moe_pool_create(16, 4, C.byref(moe.shape(100, 64)), C.byref(h)) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_router_sum_depth(1, 2048) == 17
+    assert lib.moe_router_sum_depth(64, 2048) == 32 + 2 + 8 + 7 + 1
+    assert lib.moe_router_sum_depth(4096, 2048) == 32 + 2 + 64 + 0 + 1
     assert lib.moe_router_workspace_bytes(1, 2048, 512) > 0
 
 
