@@ -27,7 +27,6 @@ namespace moe {
 namespace {
 
 constexpr int kPM = 128;        // tokens per bucket chunk (m-tile)
-constexpr int kLdsRow = 40;     // fp16 per LDS row: 32 + 8 pad (80 B)
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -82,23 +81,159 @@ __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool rou
   }
 }
 
-__global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kPM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kPM * kLdsRow];   // 64 gate + 64 up rows
+// Pipeline of both GEMMs (one block = 4 waves, a chunk of <= 128 tokens x
+// 128 weight rows, k in steps of 64 = one quantisation group): every wave
+// owns 32 weight rows and all 128 tokens (four 32x32 MFMA tiles).  Its int4
+// codes (one 16-byte load per lane per step: lanes 0-31 take the first 32 k
+// of the step, lanes 32-63 the second) are prefetched kPD steps ahead in
+// registers and dequantised straight into the MFMA B operand, so each weight
+// is dequantised once and nothing of B goes through LDS.  The activation
+// tile (128 x 64 fp16) goes through a double-buffered LDS tile shared by the
+// four waves, loaded three steps ahead: one barrier per step.  The k order
+// inside a step is (lane half, code word, nibble order) on both operands.
+constexpr int kPD = 4;          // k steps of B prefetched ahead
+constexpr int kKS = 64;         // k per step
+constexpr int kAR = 72;         // fp16 per LDS row: 64 + 8 pad (144 B)
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+struct BStage {
+  uint4 c;                      // this lane's 16 code bytes of the step
+  uint32_t sb;                  // (scale, bias) of the step's group
+};
+
+struct AStage {
+  uint4 v[4];                   // 16 bytes of rows (tid/8) + 32i
+};
+
+// Grouped-GEMM main loop: C steps of 64 along k.
+//   rA / a_vo[i]: activation rows (byte offset of row (tid/8)+32i, plus the
+//                 thread's 16-byte column); rows past the chunk point at row
+//                 0: MFMA row r of C depends on row r of A only, and those
+//                 output rows are never stored.
+//   rB: the expert blob; codes_off / sb_off: the matrix's sections in it;
+//   rows: the matrix's output rows; row: this lane's weight row.
+// Loads past the last step are clamped to it so every step issues the same
+// loads and the waits stay exact.
+// MT: live 32-token tiles of the chunk (a template so the inner loop has no
+// branches and the compiler can overlap LDS reads with MFMAs).
+template <int MT>
+__device__ __forceinline__ void gemm_loop(_Float16 (*As)[kPM * kAR], rsrc_t rA, const uint32_t* a_vo, rsrc_t rB,
+                                          uint32_t codes_off, uint32_t sb_off, uint32_t rows, uint32_t row, int C,
+                                          float16_t* acc) {
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const uint32_t b_vo = (h * rows + row) * 16, s_vo = row * 4;
+  const int a_lds = (tid >> 3) * kAR + 8 * (tid & 7);
+  auto load_b = [&](int c) {
+    BStage b;
+    b.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, b_vo, codes_off + 2u * c * rows * 16, 0));
+    b.sb = __builtin_amdgcn_raw_buffer_load_b32(rB, s_vo, sb_off + (uint32_t)c * rows * 4, 0);
+    return b;
+  };
+  auto load_a = [&](int c) {
+    AStage r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo[i], (uint32_t)c * kKS * 2, 0));
+    return r;
+  };
+  auto store_a = [&](int buf, const AStage& r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[buf][a_lds + 32 * i * kAR]) = r.v[i];
+  };
+  auto clamp = [&](int c) { return c < C ? c : C - 1; };
+
+  BStage ring[kPD];
+#pragma unroll
+  for (int q = 0; q < kPD; ++q) ring[q] = load_b(clamp(q));
+  AStage ra[2];
+  ra[0] = load_a(0);
+  store_a(0, ra[0]);
+  ra[1] = load_a(clamp(1));
+  ra[0] = load_a(clamp(2));
+  __syncthreads();
+  // k steps in groups of kPD so that ring slots and buffers are static
+  for (int c0 = 0; c0 < C; c0 += kPD) {
+#pragma unroll
+    for (int q = 0; q < kPD; ++q) {
+      const int c = c0 + q;
+      if (c >= C) break;
+      const int buf = q & 1;
+      // LDS buffer buf holds step c; A(c+1) sits in ra[buf^1], A(c+2) in ra[buf]
+      store_a(buf ^ 1, ra[buf ^ 1]);
+      ra[buf ^ 1] = load_a(clamp(c + 3));
+      const BStage bs = ring[q];
+      ring[q] = load_b(clamp(c + kPD));
+      const half2_t s2 = __builtin_bit_cast(half2_t, (bs.sb & 0xFFFFu) * 0x10001u);
+      const half2_t b2 = __builtin_bit_cast(half2_t, (bs.sb >> 16) * 0x10001u);
+      half8_t bv[4];
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(bs.c.x, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(bs.c.y, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(bs.c.z, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(bs.c.w, s2, b2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        half8_t av[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          av[mt] = *reinterpret_cast<const half8_t*>(&As[buf][(32 * mt + (lane & 31)) * kAR + 32 * h + 8 * j]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[j], acc[mt], 0, 0, 0);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ void gemm_tiles(int n_tok, _Float16 (*As)[kPM * kAR], rsrc_t rA, const uint32_t* a_vo,
+                                           rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
+                                           uint32_t row, int C, float16_t* acc) {
+  switch ((n_tok + 31) >> 5) {
+    case 1: gemm_loop<1>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 2: gemm_loop<2>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 3: gemm_loop<3>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    default: gemm_loop<4>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+  }
+}
+
+// Work item L -> (chunk, tile).  Workgroups are handed to the 8 XCDs in
+// turn, so workgroups L, L+8, L+16, ... run on one XCD and share its L2; they
+// take the tiles of one chunk one after another, so the chunk's activation
+// rows come from HBM once instead of once per XCD.  Grids are multiples of 8.
+constexpr int kXcd = 8;
+__device__ __forceinline__ bool xcd_item(long L, int nch, int nt, int* chunk, int* tile) {
+  const long j = L / kXcd;
+  *tile = (int)(j % nt);
+  *chunk = (int)(kXcd * (j / nt) + L % kXcd);
+  return *chunk < nch;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gate_up_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kPM * kAR];
+  __shared__ __attribute__((aligned(16))) float xch[2][16][64];   // up tiles handed to gate waves, per mt
   __shared__ int tok_s[kPM], hrow_s[kPM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = *a.n_routed;
   const int ntR = a.I / 64, ntS = a.Ish / 64;
-  const int items = nR * ntR + a.n_shared_inst * ntS;
-  const int C = a.d / 32;                       // k steps (blob chunks)
-  const int lrow = tid >> 1, lhalf = tid & 1;   // loader: row, 16-column half
+  const int nt = ntR > ntS ? ntR : ntS;
+  const int nch = nR + a.n_shared_inst;
+  const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
+  const int C = a.d / kKS;
+  const rsrc_t rX = make_rsrc(a.xh, (uint32_t)a.T * a.d * 2);
+  const int mat = wave >> 1;                    // waves 0,1: gate rows; 2,3: up rows
+  const int colb = 32 * (wave & 1);
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const bool routed = item < nR * ntR;
-    const int rel = routed ? item : item - nR * ntR;
-    const int nt = routed ? ntR : ntS;
-    const int ii = routed ? rel / nt : nR + rel / nt;
-    const int o0 = (rel % nt) * 64;
+  for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
+    int ii, tile;
+    if (!xcd_item(wi, nch, nt, &ii, &tile)) continue;
+    const bool routed = ii < nR;
+    if (tile >= (routed ? ntR : ntS)) continue;
+    const int o0 = tile * 64;
     const uint8_t* blob;
     int Iinst;
     bool missing;
@@ -121,112 +256,67 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
     }
     __syncthreads();
     const BlobLayout L = blob_layout(a.d, Iinst);
-    // loader roles: A row lrow (token), B row lrow (0..63 gate, 64..127 up)
-    const int my_tok = tok_s[lrow];
-    const int mat = lrow >> 6;
-    const uint64_t brow = (uint64_t)(o0 + (lrow & 63));
-    const uint8_t* bcodes = blob + L.m[mat].codes;
-    const uint8_t* bsb = blob + L.m[mat].sb;
-
-    uint4 ra0, ra1;
-    uint2 rb;
-    uint32_t rsb;
-    auto gload = [&](int c) {
-      if (my_tok >= 0) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.xh + (size_t)my_tok * a.d + 32 * c + 16 * lhalf);
-        ra0 = src[0];
-        ra1 = src[1];
-      } else {
-        ra0 = make_uint4(0, 0, 0, 0);
-        ra1 = ra0;
-      }
-      if (!missing) {
-        rb = *reinterpret_cast<const uint2*>(bcodes + ((uint64_t)c * Iinst + brow) * 16 + 8 * lhalf);
-        rsb = *reinterpret_cast<const uint32_t*>(bsb + ((uint64_t)(c >> 1) * Iinst + brow) * 4);
-      } else {
-        rb = make_uint2(0x88888888u, 0x88888888u);
-        rsb = 0;
-      }
-    };
-    auto lstore = [&](int buf) {
-      _Float16* ad = &As[buf][lrow * kLdsRow + 16 * lhalf];
-      *reinterpret_cast<uint4*>(ad) = ra0;
-      *reinterpret_cast<uint4*>(ad + 8) = ra1;
-      const half2_t s2 = __builtin_bit_cast(half2_t, (rsb & 0xFFFFu) * 0x10001u);
-      const half2_t b2 = __builtin_bit_cast(half2_t, (rsb >> 16) * 0x10001u);
-      _Float16* bd = &Bs[buf][lrow * kLdsRow + 16 * lhalf];
-      *reinterpret_cast<uint4*>(bd) = dequant8(rb.x, s2, b2);
-      *reinterpret_cast<uint4*>(bd + 8) = dequant8(rb.y, s2, b2);
-    };
-
+    uint32_t a_vo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok_s[(tid >> 3) + 32 * i];
+      a_vo[i] = ((uint32_t)(t >= 0 ? t : 0) * a.d + 8 * (tid & 7)) * 2;
+    }
     float16_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-    const bool active = 32 * wave < in.n;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int c = 0; c < C; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < C) gload(c + 1);
-      if (active) {
+    const uint32_t mc = (uint32_t)(mat ? L.m[1].codes : L.m[0].codes);
+    const uint32_t ms = (uint32_t)(mat ? L.m[1].sb : L.m[0].sb);
+    gemm_tiles(in.n, As, rX, a_vo, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
+               (uint32_t)(o0 + colb + (lane & 31)), C, acc);
+    // epilogue: up waves hand their tiles to the gate waves, one m-tile at a time
+    const int mt_live = (in.n + 31) >> 5;
+    bool ovf = false;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const half8_t av = *reinterpret_cast<const half8_t*>(
-              &As[buf][(32 * wave + (lane & 31)) * kLdsRow + 16 * kh + 8 * (lane >> 5)]);
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= mt_live) break;
+      if (mat == 1) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const half8_t bv = *reinterpret_cast<const half8_t*>(
-                &Bs[buf][(32 * t + (lane & 31)) * kLdsRow + 16 * kh + 8 * (lane >> 5)]);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[t], 0, 0, 0);
-          }
-        }
+        for (int i = 0; i < 16; ++i) xch[wave & 1][i][lane] = acc[mt][i];
       }
-      if (c + 1 < C) lstore(buf ^ 1);
       __syncthreads();
-    }
-    // epilogue: h = silu(g) * u (tiles 0/2 and 1/3 pair up), fp16, permuted
-    if (active) {
-      bool ovf = false;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int col = 32 * half + (lane & 31);
-        const int o = o0 + col;
+      if (mat == 0) {
+        const int o = o0 + colb + (lane & 31);
         const int po = (o & ~7) | (2 * (o & 3) + ((o >> 2) & 1));
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = 32 * wave + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+          const int r = 32 * mt + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
           if (r < in.n) {
-            const float g = acc[half][i], u = acc[2 + half][i];
+            const float g = acc[mt][i], u = xch[wave & 1][i][lane];
             const float h = missing ? 0.f : g / (1.0f + expf(-g)) * u;
             ovf |= !(fabsf(h) <= 65504.0f);
             a.hh[(size_t)hrow_s[r] * a.Imax + po] = __builtin_bit_cast(uint16_t, (_Float16)h);
           }
         }
       }
-      if (ovf) atomicOr(a.pool.err, 2);
+      __syncthreads();
     }
+    if (ovf) atomicOr(a.pool.err, 2);
     if (missing && tid == 0) atomicOr(a.pool.err, 1);
-    __syncthreads();
   }
 }
 
 __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kPM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kPM * kLdsRow];   // 128 output rows
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kPM * kAR];
   __shared__ int hrow_s[kPM], tok_s[kPM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = *a.n_routed;
   const int nt = a.d / 128;
-  const int items = (nR + a.n_shared_inst) * nt;
-  const int lrow = tid >> 1, lhalf = tid & 1;
+  const int nch = nR + a.n_shared_inst;
+  const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
+  const rsrc_t rH = make_rsrc(a.hh, (uint32_t)(a.T * a.k + a.T) * a.Imax * 2);
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int ii = item / nt;
-    const int n0 = (item % nt) * 128;
+  for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
+    int ii, tile;
+    if (!xcd_item(wi, nch, nt, &ii, &tile)) continue;
+    const int n0 = tile * 128;
     const bool routed = ii < nR;
     const uint8_t* blob;
     int Iinst;
@@ -248,84 +338,29 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
     }
     __syncthreads();
     const BlobLayout L = blob_layout(a.d, Iinst);
-    const int C = Iinst / 32;
-    const int my_h = hrow_s[lrow];
-    const uint64_t brow = (uint64_t)(n0 + lrow);
-    const uint8_t* bcodes = blob + L.m[2].codes;
-    const uint8_t* bsb = blob + L.m[2].sb;
-
-    uint4 ra0, ra1;
-    uint2 rb;
-    uint32_t rsb;
-    auto gload = [&](int c) {
-      if (my_h >= 0) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.hh + (size_t)my_h * a.Imax + 32 * c + 16 * lhalf);
-        ra0 = src[0];
-        ra1 = src[1];
-      } else {
-        ra0 = make_uint4(0, 0, 0, 0);
-        ra1 = ra0;
-      }
-      if (!missing) {
-        rb = *reinterpret_cast<const uint2*>(bcodes + ((uint64_t)c * a.d + brow) * 16 + 8 * lhalf);
-        rsb = *reinterpret_cast<const uint32_t*>(bsb + ((uint64_t)(c >> 1) * a.d + brow) * 4);
-      } else {
-        rb = make_uint2(0x88888888u, 0x88888888u);
-        rsb = 0;
-      }
-    };
-    auto lstore = [&](int buf) {
-      _Float16* ad = &As[buf][lrow * kLdsRow + 16 * lhalf];
-      *reinterpret_cast<uint4*>(ad) = ra0;
-      *reinterpret_cast<uint4*>(ad + 8) = ra1;
-      const half2_t s2 = __builtin_bit_cast(half2_t, (rsb & 0xFFFFu) * 0x10001u);
-      const half2_t b2 = __builtin_bit_cast(half2_t, (rsb >> 16) * 0x10001u);
-      _Float16* bd = &Bs[buf][lrow * kLdsRow + 16 * lhalf];
-      *reinterpret_cast<uint4*>(bd) = dequant8(rb.x, s2, b2);
-      *reinterpret_cast<uint4*>(bd + 8) = dequant8(rb.y, s2, b2);
-    };
-
+    uint32_t a_vo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hr = hrow_s[(tid >> 3) + 32 * i];
+      a_vo[i] = ((uint32_t)(hr >= 0 ? hr : 0) * a.Imax + 8 * (tid & 7)) * 2;
+    }
     float16_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-    const bool active = 32 * wave < in.n;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int c = 0; c < C; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < C) gload(c + 1);
-      if (active) {
+    gemm_tiles(in.n, As, rH, a_vo, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
+               (uint32_t)L.m[2].sb, (uint32_t)a.d, (uint32_t)(n0 + 32 * wave + (lane & 31)), Iinst / kKS, acc);
+    const int n = n0 + 32 * wave + (lane & 31);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const half8_t av = *reinterpret_cast<const half8_t*>(
-              &As[buf][(32 * wave + (lane & 31)) * kLdsRow + 16 * kh + 8 * (lane >> 5)]);
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const half8_t bv = *reinterpret_cast<const half8_t*>(
-                &Bs[buf][(32 * t + (lane & 31)) * kLdsRow + 16 * kh + 8 * (lane >> 5)]);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[t], 0, 0, 0);
-          }
-        }
-      }
-      if (c + 1 < C) lstore(buf ^ 1);
-      __syncthreads();
-    }
-    if (active) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = n0 + 32 * t + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * wave + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-          if (r < in.n) {
-            const float v = missing ? 0.f : acc[t][i];
-            if (routed) a.partial[(size_t)hrow_s[r] * a.d + n] = v;
-            else a.shared_out[(size_t)tok_s[r] * a.d + n] = v;
-          }
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mt + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (r < in.n) {
+          const float v = missing ? 0.f : acc[mt][i];
+          if (routed) a.partial[(size_t)hrow_s[r] * a.d + n] = v;
+          else a.shared_out[(size_t)tok_s[r] * a.d + n] = v;
         }
       }
     }
@@ -441,9 +476,11 @@ int prefill_launch(const FfnArgs& f, void* ws, size_t ws_bytes, hipStream_t s) {
   a.pair_ids = f.pair_ids;
   a.hh = w.hh; a.partial = f.partial; a.shared_out = f.shared_out;
   // upper bounds on the work items; kernels stride over the device count
-  const long chunks = ((long)f.T * f.k + kPM - 1) / kPM + f.pool.E + a.n_shared_inst;
+  long chunks = ((long)f.T * f.k + kPM - 1) / kPM + f.pool.E + a.n_shared_inst;
+  chunks = (chunks + kXcd - 1) / kXcd * kXcd;   // grids stay multiples of 8
   const long gu_items = chunks * (Imax / 64);
   const long dn_items = chunks * (f.d / 128);
+  if (f.d % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const int gu_grid = (int)(gu_items < 4096 ? gu_items : 4096);
   const int dn_grid = (int)(dn_items < 4096 ? dn_items : 4096);
   void* args[] = {&a};
