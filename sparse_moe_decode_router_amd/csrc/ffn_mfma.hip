@@ -67,11 +67,13 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t b2) {
 
 __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool routed, const uint8_t** blob,
                                           int* Iinst, bool* missing) {
-  const PInst in = a.inst[ii];
+  PInst in = a.inst[ii];
+  in.expert = __builtin_amdgcn_readfirstlane(in.expert);
   *missing = false;
   if (routed) {
     const int e = in.expert;
-    const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
+    // uniform across the block: keeps the blob descriptor in scalar registers
+    const int slot = __builtin_amdgcn_readfirstlane((e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1);
     *missing = slot < 0;
     *blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
     *Iinst = a.I;
@@ -83,121 +85,147 @@ __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool rou
 
 // Pipeline of both GEMMs (one block = 4 waves, a chunk of <= 128 tokens x
 // 128 weight rows, k in steps of 64 = one quantisation group): every wave
-// owns 32 weight rows and all 128 tokens (four 32x32 MFMA tiles).  Its int4
-// codes (one 16-byte load per lane per step: lanes 0-31 take the first 32 k
-// of the step, lanes 32-63 the second) are prefetched kPD steps ahead in
-// registers and dequantised straight into the MFMA B operand, so each weight
-// is dequantised once and nothing of B goes through LDS.  The activation
-// tile (128 x 64 fp16) goes through a double-buffered LDS tile shared by the
-// four waves, loaded three steps ahead: one barrier per step.  The k order
-// inside a step is (lane half, code word, nibble order) on both operands.
-constexpr int kPD = 4;          // k steps of B prefetched ahead
-constexpr int kKS = 64;         // k per step
-constexpr int kAR = 72;         // fp16 per LDS row: 64 + 8 pad (144 B)
+// owns 32 weight rows and all 128 tokens (up to four 32x32 MFMA tiles).
+// Each step's operands go global -> LDS by the buffer unit itself (LDS DMA,
+// no registers), three stages in flight: the activation tile (128 rows x
+// 128 B), every wave's int4 codes (one 16-byte piece per lane: lanes 0-31
+// hold the first 32 k of the step for their row, lanes 32-63 the second) and
+// its (scale, bias) words.  A wave dequantises its own codes straight into
+// the MFMA B operand, so each weight is dequantised once.  The k order inside
+// a step is (lane half, code word, nibble order) on both operands.
+//
+// Synchronisation is explicit: every step issues the same six DMAs per wave,
+// waits until at most the next stage's six are in flight (s_waitcnt vmcnt),
+// then meets the other waves at a bare s_barrier.  The DMA destinations are
+// passed as opaque LDS addresses, so the compiler adds no waits of its own
+// (a __syncthreads fence, or its alias tracking, would wait for every DMA in
+// flight and serialise the pipeline); empty asm statements with a memory
+// clobber keep it from moving LDS accesses across the wait and barrier.
+constexpr int kKS = 64;                         // k per step
+constexpr int kStA = kPM * 128;                 // activation tile bytes
+constexpr int kStB = 4 * 1024;                  // codes, 1 KB per wave
+constexpr int kStS = 4 * 256;                   // (scale, bias), 256 B per wave
+constexpr int kStage = kStA + kStB + kStS;
+constexpr int kDmaPerStage = 6;                 // DMA instructions per wave per stage
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-struct BStage {
-  uint4 c;                      // this lane's 16 code bytes of the step
-  uint32_t sb;                  // (scale, bias) of the step's group
-};
+// Block-uniform LDS address of p, opaque to the compiler's alias tracking.
+__device__ __forceinline__ lds_void* lds_opaque(const uint8_t* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_void*)p;
+  return (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(a);
+}
 
-struct AStage {
-  uint4 v[4];                   // 16 bytes of rows (tid/8) + 32i
-};
+// s_waitcnt vmcnt <= N, lgkmcnt == 0, then s_barrier; no code motion of
+// memory accesses across it.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS position of the 16-byte piece `cc` (0..7) of activation row r: pieces
+// are XOR-swizzled by r mod 8 so the MFMA reads (32 rows, one piece) hit 32
+// distinct banks.
+__device__ __forceinline__ int a_pos(int r, int cc) { return r * 128 + 16 * (cc ^ (r & 7)); }
 
 // Grouped-GEMM main loop: C steps of 64 along k.
-//   rA / a_vo[i]: activation rows (byte offset of row (tid/8)+32i, plus the
-//                 thread's 16-byte column); rows past the chunk point at row
-//                 0: MFMA row r of C depends on row r of A only, and those
+//   S0, S1, S2: the stages, kStage bytes each (distinct arrays, used in a
+//                 fixed rotation).
+//   rA / a_vo[i]: activation rows; a_vo[i] = byte offset of the row this
+//                 lane fetches for DMA i (row 8*(4*wave+i) + lane/8), plus
+//                 16 * the swizzled piece.  Rows past the chunk fetch row 0:
+//                 MFMA row r of C depends on row r of A only, and those
 //                 output rows are never stored.
 //   rB: the expert blob; codes_off / sb_off: the matrix's sections in it;
 //   rows: the matrix's output rows; row: this lane's weight row.
-// Loads past the last step are clamped to it so every step issues the same
-// loads and the waits stay exact.
 // MT: live 32-token tiles of the chunk (a template so the inner loop has no
-// branches and the compiler can overlap LDS reads with MFMAs).
+// branches and LDS reads overlap the MFMAs).
 template <int MT>
-__device__ __forceinline__ void gemm_loop(_Float16 (*As)[kPM * kAR], rsrc_t rA, const uint32_t* a_vo, rsrc_t rB,
-                                          uint32_t codes_off, uint32_t sb_off, uint32_t rows, uint32_t row, int C,
-                                          float16_t* acc) {
+__device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2, rsrc_t rA, const uint32_t* a_vo,
+                                          rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
+                                          uint32_t row, int C, float16_t* acc) {
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t b_vo = (h * rows + row) * 16, s_vo = row * 4;
-  const int a_lds = (tid >> 3) * kAR + 8 * (tid & 7);
-  auto load_b = [&](int c) {
-    BStage b;
-    b.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, b_vo, codes_off + 2u * c * rows * 16, 0));
-    b.sb = __builtin_amdgcn_raw_buffer_load_b32(rB, s_vo, sb_off + (uint32_t)c * rows * 4, 0);
-    return b;
-  };
-  auto load_a = [&](int c) {
-    AStage r;
+  // Stages past the end read through a zero-size descriptor: no memory
+  // traffic, zeros land in a stage nobody reads, and the count stays six.
+  const rsrc_t rN = make_rsrc(nullptr, 0);
+  auto issue = [&](int s, uint8_t* st) {
+    const bool live = s < C;
+    const rsrc_t ra = live ? rA : rN, rb = live ? rB : rN;
+    const uint32_t ao = __builtin_amdgcn_readfirstlane(s * 128);
+    const uint32_t co = __builtin_amdgcn_readfirstlane(codes_off + 2u * s * rows * 16);
+    const uint32_t so = __builtin_amdgcn_readfirstlane(sb_off + (uint32_t)s * rows * 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      r.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo[i], (uint32_t)c * kKS * 2, 0));
-    return r;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_opaque(st + (4 * wave + i) * 1024), 16, a_vo[i], ao, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + wave * 1024), 16, b_vo, co, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + kStB + wave * 256), 4, s_vo, so, 0, 0);
   };
-  auto store_a = [&](int buf, const AStage& r) {
+  // One step on stage `st` while stage s+2 refills `nx` (the stage read in
+  // the previous step).
+  auto step = [&](int s, const uint8_t* st, uint8_t* nx) {
+    // stage s landed for this wave (stage s+1 may be in flight) and this
+    // wave's reads of the previous stage are done; then the block meets
+    stage_barrier<kDmaPerStage>();
+    issue(s + 2, nx);
+    const uint4 cw = *reinterpret_cast<const uint4*>(st + kStA + wave * 1024 + 16 * lane);
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kStA + kStB + wave * 256 + 4 * (lane & 31));
+    const half2_t s2 = __builtin_bit_cast(half2_t, (sb & 0xFFFFu) * 0x10001u);
+    const half2_t b2 = __builtin_bit_cast(half2_t, (sb >> 16) * 0x10001u);
+    half8_t bv[4];
+    bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
+    bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
+    bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
+    bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[buf][a_lds + 32 * i * kAR]) = r.v[i];
-  };
-  auto clamp = [&](int c) { return c < C ? c : C - 1; };
-
-  BStage ring[kPD];
+    for (int j = 0; j < 4; ++j) {
+      half8_t av[MT];
 #pragma unroll
-  for (int q = 0; q < kPD; ++q) ring[q] = load_b(clamp(q));
-  AStage ra[2];
-  ra[0] = load_a(0);
-  store_a(0, ra[0]);
-  ra[1] = load_a(clamp(1));
-  ra[0] = load_a(clamp(2));
-  __syncthreads();
-  // k steps in groups of kPD so that ring slots and buffers are static
-  for (int c0 = 0; c0 < C; c0 += kPD) {
+      for (int mt = 0; mt < MT; ++mt)
+        av[mt] = *reinterpret_cast<const half8_t*>(st + a_pos(32 * mt + (lane & 31), 4 * h + j));
 #pragma unroll
-    for (int q = 0; q < kPD; ++q) {
-      const int c = c0 + q;
-      if (c >= C) break;
-      const int buf = q & 1;
-      // LDS buffer buf holds step c; A(c+1) sits in ra[buf^1], A(c+2) in ra[buf]
-      store_a(buf ^ 1, ra[buf ^ 1]);
-      ra[buf ^ 1] = load_a(clamp(c + 3));
-      const BStage bs = ring[q];
-      ring[q] = load_b(clamp(c + kPD));
-      const half2_t s2 = __builtin_bit_cast(half2_t, (bs.sb & 0xFFFFu) * 0x10001u);
-      const half2_t b2 = __builtin_bit_cast(half2_t, (bs.sb >> 16) * 0x10001u);
-      half8_t bv[4];
-      bv[0] = __builtin_bit_cast(half8_t, dequant8(bs.c.x, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8(bs.c.y, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8(bs.c.z, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8(bs.c.w, s2, b2));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half8_t av[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          av[mt] = *reinterpret_cast<const half8_t*>(&As[buf][(32 * mt + (lane & 31)) * kAR + 32 * h + 8 * j]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[j], acc[mt], 0, 0, 0);
-      }
-      __syncthreads();
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[j], acc[mt], 0, 0, 0);
     }
+  };
+  // earlier stores / DMAs of this block are done and every wave is past its
+  // last reads of the stages before they refill
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  issue(0, S0);
+  issue(1, S1);
+  for (int s = 0; s < C; s += 3) {
+    step(s, S0, S2);
+    if (s + 1 >= C) break;
+    step(s + 1, S1, S0);
+    if (s + 2 >= C) break;
+    step(s + 2, S2, S1);
   }
+  // the (empty) DMAs still in flight land before anyone reuses the stages
+  stage_barrier<0>();
 }
 
-__device__ __forceinline__ void gemm_tiles(int n_tok, _Float16 (*As)[kPM * kAR], rsrc_t rA, const uint32_t* a_vo,
+__device__ __forceinline__ void gemm_tiles(int n_tok, uint8_t* S0, uint8_t* S1, uint8_t* S2, rsrc_t rA,
+                                           const uint32_t* a_vo,
                                            rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
                                            uint32_t row, int C, float16_t* acc) {
   switch ((n_tok + 31) >> 5) {
-    case 1: gemm_loop<1>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
-    case 2: gemm_loop<2>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
-    case 3: gemm_loop<3>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
-    default: gemm_loop<4>(As, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 1: gemm_loop<1>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 2: gemm_loop<2>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 3: gemm_loop<3>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    default: gemm_loop<4>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
   }
 }
 
@@ -214,11 +242,11 @@ __device__ __forceinline__ bool xcd_item(long L, int nch, int nt, int* chunk, in
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gate_up_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kPM * kAR];
+  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage], S1[kStage], S2[kStage];
   __shared__ __attribute__((aligned(16))) float xch[2][16][64];   // up tiles handed to gate waves, per mt
   __shared__ int tok_s[kPM], hrow_s[kPM];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nR = *a.n_routed;
+  const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
   const int ntR = a.I / 64, ntS = a.Ish / 64;
   const int nt = ntR > ntS ? ntR : ntS;
   const int nch = nR + a.n_shared_inst;
@@ -238,7 +266,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int Iinst;
     bool missing;
     resolve_p(a, ii, routed, &blob, &Iinst, &missing);
-    const PInst in = a.inst[ii];
+    PInst in = a.inst[ii];
+    in.start = __builtin_amdgcn_readfirstlane(in.start);
+    in.n = __builtin_amdgcn_readfirstlane(in.n);
     if (tid < kPM) {
       int t = -1, h = -1;
       if (tid < in.n) {
@@ -259,8 +289,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint32_t a_vo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = tok_s[(tid >> 3) + 32 * i];
-      a_vo[i] = ((uint32_t)(t >= 0 ? t : 0) * a.d + 8 * (tid & 7)) * 2;
+      const int r = 8 * (4 * wave + i) + (lane >> 3);
+      const int t = tok_s[r];
+      a_vo[i] = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ (r & 7));
     }
     float16_t acc[4];
 #pragma unroll
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
     const uint32_t mc = (uint32_t)(mat ? L.m[1].codes : L.m[0].codes);
     const uint32_t ms = (uint32_t)(mat ? L.m[1].sb : L.m[0].sb);
-    gemm_tiles(in.n, As, rX, a_vo, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
+    gemm_tiles(in.n, S0, S1, S2, rX, a_vo, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
                (uint32_t)(o0 + colb + (lane & 31)), C, acc);
     // epilogue: up waves hand their tiles to the gate waves, one m-tile at a time
     const int mt_live = (in.n + 31) >> 5;
@@ -303,11 +334,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-__global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kPM * kAR];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_down_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage], S1[kStage], S2[kStage];
   __shared__ int hrow_s[kPM], tok_s[kPM];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nR = *a.n_routed;
+  const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
   const int nt = a.d / 128;
   const int nch = nR + a.n_shared_inst;
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
@@ -322,7 +353,9 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
     int Iinst;
     bool missing;
     resolve_p(a, ii, routed, &blob, &Iinst, &missing);
-    const PInst in = a.inst[ii];
+    PInst in = a.inst[ii];
+    in.start = __builtin_amdgcn_readfirstlane(in.start);
+    in.n = __builtin_amdgcn_readfirstlane(in.n);
     if (tid < kPM) {
       int h = -1, t = -1;
       if (tid < in.n) {
@@ -341,15 +374,16 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
     uint32_t a_vo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hr = hrow_s[(tid >> 3) + 32 * i];
-      a_vo[i] = ((uint32_t)(hr >= 0 ? hr : 0) * a.Imax + 8 * (tid & 7)) * 2;
+      const int r = 8 * (4 * wave + i) + (lane >> 3);
+      const int hr = hrow_s[r];
+      a_vo[i] = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ (r & 7));
     }
     float16_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-    gemm_tiles(in.n, As, rH, a_vo, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
+    gemm_tiles(in.n, S0, S1, S2, rH, a_vo, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
                (uint32_t)L.m[2].sb, (uint32_t)a.d, (uint32_t)(n0 + 32 * wave + (lane & 31)), Iinst / kKS, acc);
     const int n = n0 + 32 * wave + (lane & 31);
 #pragma unroll
