@@ -359,6 +359,20 @@ def run_prefill(c, name, reps):
             "max_bucket": int(counts.max())}
 
 
+def copy_probe(mb):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +382,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="enqueue decode steps one by one (no HIP graph)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only copy an MB-sized device buffer 5 times (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="decode80b",
                     choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
                              "prefill80b_zipf", "all"])
@@ -376,6 +392,9 @@ def main():
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
               "(no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe)
+        return
     c = Ctx()
     c.torch.cuda.set_device(0)
     cpu = 0 if args.no_cpu else args.cpu_steps

@@ -37,6 +37,15 @@ struct Inst {                   // batched instance
   int32_t n;                    // tokens (1..kTC)
 };
 
+// Workgroups go to the 8 XCDs in turn (b, b+8, ... share one XCD and its
+// L2).  With a grid that is a multiple of 8, workgroup b takes work index
+// (b % 8) * (G / 8) + b / 8: each XCD walks a contiguous range, so rows that
+// share a cache line (e.g. the (scale, bias) words of 32 consecutive rows)
+// are fetched into one L2 once instead of once per XCD.
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+  return (G & 7) ? b : (b & 7) * (G >> 3) + (b >> 3);
+}
+
 struct GateUpArgs {
   PoolView pool;
   const uint8_t* shared_blob;
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   float* sel_l = reinterpret_cast<float*>(rslot + E);            // [k]
   int32_t* sel_e = reinterpret_cast<int32_t*>(sel_l + a.k);      // [k]
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+  for (int item = xcd_remap(blockIdx.x, gridDim.x); item < items; item += gridDim.x) {
     const bool routed = item < nR * rbR;
     const int rel = routed ? item : item - nR * rbR;
     const int rb_per = routed ? rbR : rbS;
@@ -487,7 +496,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   extern __shared__ float dyn[];                // oi[nI][8] | hst[kDnRound][Imax + Imax/8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 3, gl = lane & 7;       // group lanes of a row are consecutive
-  const int j = blockIdx.x * 8 + r;
+  const int jb = xcd_remap(blockIdx.x, gridDim.x);   // this block's 8 output rows
+  const int j = jb * 8 + r;
   const int nR = a.T * a.k, nI = nR + a.T;
   const int rec = a.Imax + a.Imax / 8;          // dwords per staged record
   float* oi = dyn;
@@ -553,7 +563,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
     float y = 0.f;
     for (int q2 = 0; q2 < a.k; ++q2) y += a.w[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
     y += a.sgate[t] * oi[(nR + t) * 8 + rr];
-    a.y[(size_t)t * a.d + blockIdx.x * 8 + rr] = y;
+    a.y[(size_t)t * a.d + jb * 8 + rr] = y;
   }
 }
 
@@ -759,7 +769,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
       default: fn = (void*)gate_up_kernel<1, 16>; break;
     }
     void* args[] = {&g};
-    MOE_HIP(hipLaunchKernel(fn, dim3(items), dim3(256), args, lds, s));
+    MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));   // multiple of 8: xcd_remap
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 8 + 3) & ~3) + kDnRound * (Imax + Imax / 8)) * 4;

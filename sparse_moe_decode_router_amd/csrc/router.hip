@@ -210,18 +210,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   uint32_t* scr = base + 2 * k4;
   float* lsum = reinterpret_cast<float*>(scr + topk_scratch_words(E));
   const size_t TR = (size_t)T * (E + 1);
-  for (int e = lane; e <= E; e += 64) {
-    const float* p = logits + (size_t)t * (E + 1) + e;
-    float v = p[0];
-    for (int q = 1; q < S; ++q) v += p[q * TR];
-    lsum[e] = v;
+  const float* row = logits + (size_t)t * (E + 1);
+  if (S > 1) {
+    for (int e = lane; e <= E; e += 64) {
+      const float* p = row + e;
+      float v = p[0];
+      for (int q = 1; q < S; ++q) v += p[q * TR];
+      lsum[e] = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    row = lsum;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  topk_select<NK>(lsum, bias, E, k, sel_l, sel_e, scr);
+  // one partial: the selection reads the logits where they are (its loads
+  // are all issued before any use)
+  topk_select<NK>(row, bias, E, k, sel_l, sel_e, scr);
   topk_finish(sel_l, sel_e, k, idx + (size_t)t * k, w + (size_t)t * k, usage);
-  if (lane == 0 && sgate) sgate[t] = sigmoidf_(lsum[E]);
+  if (lane == 0 && sgate) sgate[t] = sigmoidf_(row[E]);
 }
 
 }  // namespace
