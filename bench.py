@@ -142,6 +142,32 @@ def cpu_baseline(c, cfg, sample_steps):
                       f"(dequantise + matmul per selected expert), {dt:.1f}s"}
 
 
+def ffn_traffic(name):
+    """HBM bytes per expert-FFN launch pair from the committed rocprofv3 counter
+    record (profiles/decode80b_ffn_traffic.md), scaled by its copy calibration;
+    None when there is no record for this workload or the kernels' sources
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{name}_ffn_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-record:"):
+            rec = json.loads(line.split(":", 1)[1])
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    fs = rec["copy_probe_bytes"] / 1024 / rec["copy_fetch_kib"]
+    wsc = rec["copy_probe_bytes"] / 1024 / rec["copy_write_kib"]
+    return int(sum(rec["fetch_kib_per_dispatch"].values()) * 1024 * fs
+               + sum(rec["write_kib_per_dispatch"].values()) * 1024 * wsc)
+
+
 def run_decode(c, name, K, W, R, cpu_steps, eager=False):
     torch, ms, moe = c.torch, c.ms, c.moe
     cfg = ms.scaled(ms.CONFIGS[name], n_slots=ms.CONFIGS[name].E)
@@ -214,7 +240,7 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
         "layer_expert_frac_of_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "expert FFN: gate_up_kernel + down_decode_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": ffn_traffic(name),
                      "avg_us": round(ffn_ms * 1e3, 3)},
     }
     if cpu_steps > 0:
