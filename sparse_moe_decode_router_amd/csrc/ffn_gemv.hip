@@ -426,15 +426,30 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
 }
 
 // One group (64 inputs) of one down row: s*sum((128+q)h) + (b-128s)*sum(h),
-// h given as bf16 (hi, lo) pairs and per-8 sums (hrec: hi pairs at [0, Imax/2),
-// lo pairs at [Imax/2, Imax); hs: per-8 sums).
+// LDS image of one h record (bf16 hi pairs, bf16 lo pairs, per-8 sums): the
+// 32 dwords of each 64-row group are padded to kHG = 36, so the 8 group lanes
+// of a wave (groups g = 0..7 read together) hit distinct banks; the per-8
+// sums follow.  hrec_pos maps a dword of the record as stored in HBM (hi
+// pairs [0, Imax/2), lo pairs [Imax/2, Imax), sums [Imax, Imax + Imax/8)).
+constexpr int kHG = 36;
+__host__ __device__ inline int hrec_words(int Imax) { return 2 * (Imax / 64) * kHG + Imax / 8; }
+__device__ __forceinline__ int hrec_pos(int j, int Imax) {
+  if (j >= Imax) return 2 * (Imax / 64) * kHG + (j - Imax);
+  const int part = j >= Imax / 2, jj = part ? j - Imax / 2 : j;
+  return (part * (Imax / 64) + (jj >> 5)) * kHG + (jj & 31);
+}
+__device__ __forceinline__ const float* hrec_sums(const uint32_t* hrec, int Imax) {
+  return reinterpret_cast<const float*>(hrec + 2 * (Imax / 64) * kHG);
+}
+
+// h given as the LDS record above (hs: its per-8 sums).
 __device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint32_t sb, int g,
                                                  const uint32_t* hrec, int Imax, const float* hs) {
   const float s = f16_to_f32(sb);
   const float b = f16_to_f32(sb >> 16);
   const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-  const uint4* hh = reinterpret_cast<const uint4*>(hrec + 32 * g);
-  const uint4* hl = reinterpret_cast<const uint4*>(hrec + Imax / 2 + 32 * g);
+  const uint4* hh = reinterpret_cast<const uint4*>(hrec + g * kHG);
+  const uint4* hl = reinterpret_cast<const uint4*>(hrec + (Imax / 64 + g) * kHG);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;      // four independent chains
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
@@ -499,7 +514,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   const int jb = xcd_remap(blockIdx.x, gridDim.x);   // this block's 8 output rows
   const int j = jb * 8 + r;
   const int nR = a.T * a.k, nI = nR + a.T;
-  const int rec = a.Imax + a.Imax / 8;          // dwords per staged record
+  const int rec = hrec_words(a.Imax);           // dwords per staged record
   float* oi = dyn;
   uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 8 + 3) & ~3));
   for (int base = 0; base < nI; base += kDnRound) {
@@ -532,19 +547,20 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
       }
     }
     // 2. stage the round's h records (pairs + per-8 sums) in LDS
-    for (int q4 = tid; q4 < nr * (rec / 4); q4 += 64 * kDnWaves) {
-      const int u = q4 / (rec / 4), c = q4 % (rec / 4);
+    const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
+    for (int q4 = tid; q4 < nr * src4; q4 += 64 * kDnWaves) {
+      const int u = q4 / src4, c = q4 % src4;
       const int ii = base + u;
       uint4 v;
       if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)ii * a.Imax)[c];
       else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)ii * (a.Imax / 8))[c - a.Imax / 4];
-      *reinterpret_cast<uint4*>(hst + u * rec + 4 * c) = v;
+      *reinterpret_cast<uint4*>(hst + u * rec + hrec_pos(4 * c, a.Imax)) = v;
     }
     __syncthreads();
     // 3. compute
     if (active) {
       const uint32_t* hrec = hst + wave * rec;
-      const float* hs = reinterpret_cast<const float*>(hrec + a.Imax);
+      const float* hs = hrec_sums(hrec, a.Imax);
       float acc = 0.f;
       if (!miss) {
         if (gl < Iinst / 64) acc = down_group_regs(q0, q1, sb, gl, hrec, a.Imax, hs);
@@ -577,7 +593,7 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
   const int nrb = (a.d + 255) / 256;            // d is a multiple of 64: last block may be partial
   const int nR = *a.n_routed;
   const int items = (nR + a.n_shared_inst) * nrb;
-  const int rec = a.Imax + a.Imax / 8;
+  const int rec = hrec_words(a.Imax);
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int ii = item / nrb, j0 = (item % nrb) * 256;
     const bool routed = ii < nR;
@@ -599,13 +615,14 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
 #pragma unroll
     for (int tt = 0; tt < kTC; ++tt)
       hrow[tt] = tt < in.n ? (routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt) : 0;
-    for (int q4 = tid; q4 < in.n * (rec / 4); q4 += 256) {
-      const int tt = q4 / (rec / 4), c = q4 % (rec / 4);
+    const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
+    for (int q4 = tid; q4 < in.n * src4; q4 += 256) {
+      const int tt = q4 / src4, c = q4 % src4;
       const int hr = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
       uint4 v;
       if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)hr * a.Imax)[c];
       else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)hr * (a.Imax / 8))[c - a.Imax / 4];
-      *reinterpret_cast<uint4*>(hst + tt * rec + 4 * c) = v;
+      *reinterpret_cast<uint4*>(hst + tt * rec + hrec_pos(4 * c, a.Imax)) = v;
     }
     __syncthreads();
     const BlobLayout L = blob_layout(a.d, Iinst);
@@ -626,7 +643,7 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
           for (int tt = 0; tt < kTC; ++tt) {
             if (tt < in.n) {
               const uint32_t* hrec = hst + tt * rec;
-              acc[tt] += down_group_regs(q0, q1, sb, g, hrec, a.Imax, reinterpret_cast<const float*>(hrec + a.Imax));
+              acc[tt] += down_group_regs(q0, q1, sb, g, hrec, a.Imax, hrec_sums(hrec, a.Imax));
             }
           }
         }
@@ -772,7 +789,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));   // multiple of 8: xcd_remap
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
-    const size_t dlds = (size_t)(((nI * 8 + 3) & ~3) + kDnRound * (Imax + Imax / 8)) * 4;
+    const size_t dlds = (size_t)(((nI * 8 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
     MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
     return MOE_OK;
   }
@@ -795,7 +812,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   const long dupper = ((long)f.T * f.k + nsh) * ((f.d + 255) / 256);
   void* dargs[] = {&dn};
   MOE_HIP(hipLaunchKernel((void*)down_batched_kernel, dim3(grid_for((int)(dupper < 65536 ? dupper : 65536))),
-                          dim3(256), dargs, (size_t)kTC * (Imax + Imax / 8) * 4, s));
+                          dim3(256), dargs, (size_t)kTC * hrec_words(Imax) * 4, s));
   return MOE_OK;
 }
 
