@@ -310,10 +310,10 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   }
 }
 
-// Batched gate/up: item = (bucket chunk of <= kTC tokens, 64 rows).  The
-// chunk's activations are staged in LDS once per item; each wave computes
-// whole rows on its own (8 rows x 8 group lanes, GPL groups per lane), two
-// 8-row sub-blocks per wave, so rows meet by DPP without block barriers.
+// Batched gate/up: item = (bucket chunk of <= kTC tokens, 32 rows).  Each
+// wave computes one 8-row sub-block on its own (8 rows x 8 group lanes, GPL
+// groups per lane; rows meet by DPP without block barriers); its codes are
+// all in flight before the chunk's activations are staged in LDS.
 template <int GPL>
 __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
   extern __shared__ uint32_t xlds[];            // [kTC][G][kXPad] | xs [kTC][G] | hbuf [4][kTC][8]
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
   const int G = a.d / 64;
   float* xsl = reinterpret_cast<float*>(xlds + kTC * G * kXPad);
   float* hbuf = xsl + kTC * G + wave * kTC * 8;
-  const int nbR = a.I / 64, nbS = a.Ish / 64;
+  const int nbR = a.I / 32, nbS = a.Ish / 32;   // items of 32 rows
   const int nR = *a.n_routed;
   const int items = nR * nbR + a.n_shared_inst * nbS;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -335,6 +335,32 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
     bool missing;
     const int ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
     const BlobLayout L = blob_layout(a.d, Iinst);
+    // 1. the codes of both of this wave's 8-row sub-blocks, all in flight
+    //    before the activations are staged
+    constexpr int kSub = 1;                     // sub-blocks per wave (4 per item / 4 waves)
+    uint4 cg[kSub][GPL][2], cu[kSub][GPL][2];
+    uint32_t sbg[kSub][GPL], sbu[kSub][GPL];
+    if (!missing) {
+#pragma unroll
+      for (int it = 0; it < kSub; ++it) {
+        const uint64_t o = (uint64_t)((ob * 4 + wave + 4 * it) * 8 + r);
+#pragma unroll
+        for (int gi = 0; gi < GPL; ++gi) {
+          const int g = gl + 8 * gi;
+          if (g < G) {
+            const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
+            const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
+            cg[it][gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c0);
+            cg[it][gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c1);
+            cu[it][gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c0);
+            cu[it][gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c1);
+            sbg[it][gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[0].sb + ((uint64_t)g * Iinst + o) * 4);
+            sbu[it][gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[1].sb + ((uint64_t)g * Iinst + o) * 4);
+          }
+        }
+      }
+    }
+    // 2. activations (bf16 pairs) and group sums of the chunk's tokens
     for (int q = tid; q < ntok * (a.d / 8); q += 256) {
       const int tt = q / (a.d / 8), c4 = q % (a.d / 8);
       const uint4 v = reinterpret_cast<const uint4*>(a.xq + (size_t)tok[tt] * (a.d / 2))[c4];
@@ -342,28 +368,10 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
     }
     for (int q = tid; q < ntok * G; q += 256) xsl[q] = a.xs[(size_t)tok[q / G] * G + q % G];
     __syncthreads();
-#pragma unroll 1
-    for (int sbk = wave; sbk < 8; sbk += 4) {
-      const int rb = ob * 8 + sbk;              // 8-row block index within the expert
-      const uint64_t o = (uint64_t)(rb * 8 + r);
-      uint4 cg[GPL][2], cu[GPL][2];
-      uint32_t sbg[GPL], sbu[GPL];
-      if (!missing) {
+    // 3. compute, SwiGLU and store per sub-block
 #pragma unroll
-        for (int gi = 0; gi < GPL; ++gi) {
-          const int g = gl + 8 * gi;
-          if (g < G) {
-            const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
-            const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
-            cg[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c0);
-            cg[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c1);
-            cu[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c0);
-            cu[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c1);
-            sbg[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[0].sb + ((uint64_t)g * Iinst + o) * 4);
-            sbu[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[1].sb + ((uint64_t)g * Iinst + o) * 4);
-          }
-        }
-      }
+    for (int it = 0; it < kSub; ++it) {
+      const int rb = ob * 4 + wave + 4 * it;    // 8-row block index within the expert
       float vg[kTC], vu[kTC];
 #pragma unroll
       for (int tt = 0; tt < kTC; ++tt) { vg[tt] = 0.f; vu[tt] = 0.f; }
@@ -372,32 +380,46 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
         for (int gi = 0; gi < GPL; ++gi) {
           const int g = gl + 8 * gi;
           if (g >= G) continue;
-          const uint32_t gw[8] = {cg[gi][0].x, cg[gi][0].y, cg[gi][0].z, cg[gi][0].w,
-                                  cg[gi][1].x, cg[gi][1].y, cg[gi][1].z, cg[gi][1].w};
-          const uint32_t uw[8] = {cu[gi][0].x, cu[gi][0].y, cu[gi][0].z, cu[gi][0].w,
-                                  cu[gi][1].x, cu[gi][1].y, cu[gi][1].z, cu[gi][1].w};
-          const float sg = f16_to_f32(sbg[gi]), bg = f16_to_f32(sbg[gi] >> 16);
-          const float su = f16_to_f32(sbu[gi]), bu = f16_to_f32(sbu[gi] >> 16);
+          const uint32_t gw[8] = {cg[it][gi][0].x, cg[it][gi][0].y, cg[it][gi][0].z, cg[it][gi][0].w,
+                                  cg[it][gi][1].x, cg[it][gi][1].y, cg[it][gi][1].z, cg[it][gi][1].w};
+          const uint32_t uw[8] = {cu[it][gi][0].x, cu[it][gi][0].y, cu[it][gi][0].z, cu[it][gi][0].w,
+                                  cu[it][gi][1].x, cu[it][gi][1].y, cu[it][gi][1].z, cu[it][gi][1].w};
+          const float sg = f16_to_f32(sbg[it][gi]), bg = f16_to_f32(sbg[it][gi] >> 16);
+          const float su = f16_to_f32(sbu[it][gi]), bu = f16_to_f32(sbu[it][gi] >> 16);
+          // tokens innermost: each nibble pair is formed once and applied to
+          // every token of the chunk (per-token chains as in the decode GEMV)
+          float ag0[kTC], au0[kTC], ag1[kTC], au1[kTC];
+#pragma unroll
+          for (int tt = 0; tt < kTC; ++tt) { ag0[tt] = au0[tt] = ag1[tt] = au1[tt] = 0.f; }
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            uint4 xv[kTC];
+#pragma unroll
+            for (int tt = 0; tt < kTC; ++tt)
+              xv[tt] = tt < ntok ? *reinterpret_cast<const uint4*>(&xlds[(tt * G + g) * kXPad + 4 * w])
+                                 : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int ii = 0; ii < 4; ii += 2) {
+              const uint32_t qg0 = nib_pair(gw[w], ii), qu0 = nib_pair(uw[w], ii);
+              const uint32_t qg1 = nib_pair(gw[w], ii + 1), qu1 = nib_pair(uw[w], ii + 1);
+#pragma unroll
+              for (int tt = 0; tt < kTC; ++tt) {
+                if (tt < ntok) {
+                  const uint32_t xw[4] = {xv[tt].x, xv[tt].y, xv[tt].z, xv[tt].w};
+                  ag0[tt] = dot2_bf16(qg0, xw[ii], ag0[tt]);
+                  au0[tt] = dot2_bf16(qu0, xw[ii], au0[tt]);
+                  ag1[tt] = dot2_bf16(qg1, xw[ii + 1], ag1[tt]);
+                  au1[tt] = dot2_bf16(qu1, xw[ii + 1], au1[tt]);
+                }
+              }
+            }
+          }
 #pragma unroll
           for (int tt = 0; tt < kTC; ++tt) {
             if (tt < ntok) {
-              const uint32_t* xp = &xlds[(tt * G + g) * kXPad];
-              float ag0 = 0.f, au0 = 0.f, ag1 = 0.f, au1 = 0.f;
-#pragma unroll
-              for (int w = 0; w < 8; ++w) {
-                const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * w);
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int ii = 0; ii < 4; ii += 2) {
-                  ag0 = dot2_bf16(nib_pair(gw[w], ii), xw[ii], ag0);
-                  au0 = dot2_bf16(nib_pair(uw[w], ii), xw[ii], au0);
-                  ag1 = dot2_bf16(nib_pair(gw[w], ii + 1), xw[ii + 1], ag1);
-                  au1 = dot2_bf16(nib_pair(uw[w], ii + 1), xw[ii + 1], au1);
-                }
-              }
               const float sx = xsl[tt * G + g];
-              vg[tt] += sg * (ag0 + ag1) + (bg - 128.0f * sg) * sx;
-              vu[tt] += su * (au0 + au1) + (bu - 128.0f * su) * sx;
+              vg[tt] += sg * (ag0[tt] + ag1[tt]) + (bg - 128.0f * sg) * sx;
+              vu[tt] += su * (au0[tt] + au1[tt]) + (bu - 128.0f * su) * sx;
             }
           }
         }
@@ -615,6 +637,26 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
 #pragma unroll
     for (int tt = 0; tt < kTC; ++tt)
       hrow[tt] = tt < in.n ? (routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt) : 0;
+    const BlobLayout L = blob_layout(a.d, Iinst);
+    // 1. every code this wave needs (its 8 sub-blocks of 8 rows, group gl):
+    //    all loads in flight at once, ahead of the h staging
+    constexpr int kSub = 8;                     // sub-blocks per wave (32 per item / 4 waves)
+    uint4 q0[kSub], q1[kSub];
+    uint32_t sbv[kSub];
+    const bool gok = gl < Iinst / 64;
+#pragma unroll
+    for (int it = 0; it < kSub; ++it) {
+      const int j = j0 + (wave + 4 * it) * 8 + r;
+      q0[it] = q1[it] = make_uint4(0, 0, 0, 0);
+      sbv[it] = 0;
+      if (!missing && gok && j < a.d) {
+        const uint64_t c0 = ((uint64_t)(2 * gl) * a.d + j) * 16;
+        q0[it] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
+        q1[it] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
+        sbv[it] = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
+      }
+    }
+    // 2. the chunk's h records
     const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
     for (int q4 = tid; q4 < in.n * src4; q4 += 256) {
       const int tt = q4 / src4, c = q4 % src4;
@@ -625,25 +667,32 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
       *reinterpret_cast<uint4*>(hst + tt * rec + hrec_pos(4 * c, a.Imax)) = v;
     }
     __syncthreads();
-    const BlobLayout L = blob_layout(a.d, Iinst);
-#pragma unroll 1
-    for (int sbk = wave; sbk < 32; sbk += 4) {
-      const int j = j0 + sbk * 8 + r;
+    // 3. compute and store, sub-block by sub-block
+#pragma unroll
+    for (int it = 0; it < kSub; ++it) {
+      const int j = j0 + (wave + 4 * it) * 8 + r;
       const bool jv = j < a.d;
       float acc[kTC];
 #pragma unroll
       for (int tt = 0; tt < kTC; ++tt) acc[tt] = 0.f;
       if (!missing && jv) {
-        for (int g = gl; g < Iinst / 64; g += 8) {
-          const uint64_t c0 = ((uint64_t)(2 * g) * a.d + j) * 16;
-          const uint4 q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
-          const uint4 q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
-          const uint32_t sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * a.d + j) * 4);
+        if (gok) {
 #pragma unroll
           for (int tt = 0; tt < kTC; ++tt) {
             if (tt < in.n) {
               const uint32_t* hrec = hst + tt * rec;
-              acc[tt] += down_group_regs(q0, q1, sb, g, hrec, a.Imax, hrec_sums(hrec, a.Imax));
+              acc[tt] += down_group_regs(q0[it], q1[it], sbv[it], gl, hrec, a.Imax, hrec_sums(hrec, a.Imax));
+            }
+          }
+        }
+        if (Iinst > 512) {                      // intermediates wider than 512: further groups
+          for (int g = gl + 8; g < Iinst / 64; g += 8) {
+            for (int tt = 0; tt < in.n; ++tt) {
+              const uint32_t* hrec = hst + tt * rec;
+              const float v = down_group(blob, L, a.d, j, g, hrec, a.Imax, hrec_sums(hrec, a.Imax));
+#pragma unroll
+              for (int u = 0; u < kTC; ++u)
+                if (u == tt) acc[u] += v;
             }
           }
         }
@@ -800,7 +849,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   MOE_HIP(hipGetLastError());
   g.batched = 1;
   g.inst = w.inst; g.n_routed = w.n_routed; g.n_shared_inst = nsh; g.pair_ids = f.pair_ids;
-  const long upper = ((long)f.T * f.k + nsh) * (Imax / 64);
+  const long upper = ((long)f.T * f.k + nsh) * (Imax / 32);
   const size_t lds = ((size_t)kTC * G * kXPad + kTC * G + 4 * kTC * 8) * 4;
   void* gfn = G <= 8 ? (void*)gate_up_batched_kernel<1> : G <= 16 ? (void*)gate_up_batched_kernel<2>
             : G <= 32 ? (void*)gate_up_batched_kernel<4> : G <= 64 ? (void*)gate_up_batched_kernel<8>

@@ -212,11 +212,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const size_t TR = (size_t)T * (E + 1);
   const float* row = logits + (size_t)t * (E + 1);
   if (S > 1) {
-    for (int e = lane; e <= E; e += 64) {
-      const float* p = row + e;
-      float v = p[0];
-      for (int q = 1; q < S; ++q) v += p[q * TR];
-      lsum[e] = v;
+    // every partial of this lane's logits in flight at once (S <= 8), then
+    // summed in split order
+    constexpr int kMaxS = 8;
+    float pv[NK + 1][kMaxS];
+#pragma unroll
+    for (int j = 0; j <= NK; ++j) {
+      const int ec = min(lane + 64 * j, E);
+#pragma unroll
+      for (int q = 0; q < kMaxS; ++q) pv[j][q] = row[ec + (size_t)min(q, S - 1) * TR];
+    }
+#pragma unroll
+    for (int j = 0; j <= NK; ++j) {
+      float v = pv[j][0];
+#pragma unroll
+      for (int q = 1; q < kMaxS; ++q)
+        if (q < S) v += pv[j][q];
+      if (lane + 64 * j <= E) lsum[lane + 64 * j] = v;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
