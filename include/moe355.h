@@ -196,9 +196,10 @@ int moe_pool_reset_usage(moe_pool* pool, hipStream_t stream);
  * 1 <= k <= E <= 1024, d a multiple of 64 and <= 8192.
  * Each logit is an fp32 sum of the d products (plus the bias) in a fixed
  * tree, so the result is deterministic; moe_router_sum_depth gives the
- * largest number of additions on any path of that tree for (T, d), which
- * bounds the rounding error (gamma_n * sum|x_j W_ej|). */
-int32_t moe_router_sum_depth(int32_t T, int32_t d);
+ * largest number of additions on any path of that tree for (T, d, E) (the
+ * tree's split of the d products depends on all three), which bounds the
+ * rounding error (gamma_n * sum|x_j W_ej|); -1 for invalid sizes. */
+int32_t moe_router_sum_depth(int32_t T, int32_t d, int32_t E);
 size_t moe_router_workspace_bytes(int32_t T, int32_t d, int32_t E);
 int moe_router_topk(const uint16_t* x_dev, int32_t T, int32_t d,
                     const float* w_router_dev, const float* logit_bias_dev,

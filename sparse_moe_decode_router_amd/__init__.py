@@ -90,7 +90,7 @@ _SIGS = {
     "moe_pool_check_error": (C.c_int, [_P, _P, _P]),
     "moe_pool_reset_usage": (C.c_int, [_P, _P]),
     "moe_pool_read_state": (C.c_int, [_P, _P, _P, _P]),
-    "moe_router_sum_depth": (_I, [_I, _I]),
+    "moe_router_sum_depth": (_I, [_I, _I, _I]),
     "moe_router_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_router_topk": (C.c_int, [_P, _I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _S, _P]),
     "moe_bucket_workspace_bytes": (_S, [_I, _I, _I]),
@@ -313,8 +313,8 @@ def _ws(nbytes: int):
 
 
 # ------------------------------------------------------------------- router
-def moe_router_sum_depth(T: int, d: int) -> int:
-    return int(_lib.moe_router_sum_depth(T, d))
+def moe_router_sum_depth(T: int, d: int, E: int) -> int:
+    return int(_lib.moe_router_sum_depth(T, d, E))
 
 
 def moe_router_workspace_bytes(T: int, d: int, E: int) -> int:

@@ -182,10 +182,14 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
   }
 }
 
-// split-K count for T > 8: enough blocks for small T; every split spans a
-// multiple of 32 columns (d is a multiple of 64)
-int router_splits(int T, int d) {
-  int S = T <= 128 ? 8 : T <= 1024 ? 2 : 1;
+// split-K count for T > 8: the smallest power of two (<= 8) that gives the
+// launch about 1024 blocks of 128 tokens x 64 rows (at E = 512: 8 below 128
+// tokens, 4 at 4096 tokens); every split spans a multiple of 32 columns (d is
+// a multiple of 64)
+int router_splits(int T, int d, int E) {
+  const long tiles = (long)((E + 1 + kRtN - 1) / kRtN) * ((T + kRtM - 1) / kRtM);
+  int S = 1;
+  while (S < 8 && tiles * S < 1024) S *= 2;
   while (S > 1 && (d / 32) % S != 0) S /= 2;
   return S;
 }
@@ -261,7 +265,7 @@ size_t router_ws_bytes(int T, int d, int E) {
 
 bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws) {
   ws->ticket = c.take<uint32_t>(64);
-  ws->logits = c.take<float>((size_t)(T <= 8 ? 1 : router_splits(T, d)) * T * (E + 1));
+  ws->logits = c.take<float>((size_t)(T <= 8 ? 1 : router_splits(T, d, E)) * T * (E + 1));
   ws->wsplit = T <= 8 ? nullptr : c.take<uint16_t>((size_t)3 * (E + 1) * d);
   ws->xq = c.take<uint32_t>((size_t)T * d / 2);
   ws->xs = c.take<float>((size_t)T * d / 64);
@@ -280,7 +284,7 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
     return MOE_OK;
   }
   MOE_TRY(xprep_launch(x, T, d, ws.xq, ws.xs, s));
-  const int R = E + 1, S = router_splits(T, d);
+  const int R = E + 1, S = router_splits(T, d, E);
   const long nW = (long)R * d;
   router_split_kernel<<<(unsigned)((nW + 255) / 256), 256, 0, s>>>(W, nW, ws.wsplit);
   MOE_HIP(hipGetLastError());
@@ -293,7 +297,7 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
 int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx, float* w,
                 float* sgate, uint32_t* usage, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  const int S = T <= 8 ? 1 : router_splits(T, d);
+  const int S = T <= 8 ? 1 : router_splits(T, d, E);
   const size_t lds = (size_t)4 * (2 * ((k + 3) & ~3) + topk_scratch_words(E) + ((E + 1 + 3) & ~3)) * 4;
   const dim3 tg((T + 3) / 4);
   switch (nk_for(E)) {
@@ -323,10 +327,10 @@ extern "C" size_t moe_router_workspace_bytes(int32_t T, int32_t d, int32_t E) {
   return router_ws_bytes(T, d, E);
 }
 
-extern "C" int32_t moe_router_sum_depth(int32_t T, int32_t d) {
-  if (d <= 0) return -1;
+extern "C" int32_t moe_router_sum_depth(int32_t T, int32_t d, int32_t E) {
+  if (d <= 0 || T < 0 || E < 1) return -1;
   if (T <= 8) return d / 256 + 9;
-  const int S = router_splits(T, d);
+  const int S = router_splits(T, d, E);
   return 32 + 2 + d / (32 * S) + (S - 1) + 1;
 }
 

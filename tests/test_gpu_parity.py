@@ -47,7 +47,7 @@ def _check_layer_step(L, step, path=moe.MOE_PATH_AUTO, T=None):
     y, idx, w, s = moe.moe_layer_forward(L.layer, x, path=path)
     torch.cuda.synchronize()
     idx_np = _np(idx)
-    depth = moe.moe_router_sum_depth(xb.shape[0], L.cfg.d)
+    depth = moe.moe_router_sum_depth(xb.shape[0], L.cfg.d, L.cfg.E)
     namb, amb = certify_routing(xb, L.Wr_np, L.bias_np, L.cfg.k, idx_np, depth)
     ref = L.oracle(xb, idx=idx_np if namb else None)
     assert np.array_equal(idx_np, ref["idx"])
@@ -75,7 +75,7 @@ def test_router_parity(name, T):
         idx, w, s = moe.moe_router_topk(x, Wd, bd, cfg.k, usage_ptr=usage.data_ptr())
         torch.cuda.synchronize()
         idx = _np(idx)
-        namb, amb = certify_routing(xb, Wr, bias, cfg.k, idx, moe.moe_router_sum_depth(T, cfg.d))
+        namb, amb = certify_routing(xb, Wr, bias, cfg.k, idx, moe.moe_router_sum_depth(T, cfg.d, cfg.E))
         namb_all += namb
         ref_idx, ref_w, ref_s, _ = olayer.route(xb, Wr, bias, cfg.k)
         l, _ = olayer.router_logits(olayer.bf16_to_f64(xb), Wr, bias)
@@ -113,7 +113,7 @@ def test_router_k_extremes(k):
     x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
     idx, w, _ = moe.moe_router_topk(x, torch.from_numpy(Wr).cuda(), None, k)
     idx, w = _np(idx), _np(w)
-    certify_routing(xb, Wr, None, k, idx, moe.moe_router_sum_depth(cfg.T, cfg.d))
+    certify_routing(xb, Wr, None, k, idx, moe.moe_router_sum_depth(cfg.T, cfg.d, cfg.E))
     if k == 1:
         assert (w == 1.0).all()
     else:                                    # k = E: the full softmax
@@ -181,7 +181,7 @@ def test_token_independence(l80):
     # the two paths sum logits in different orders: tokens inside the
     # certified near-tie bound of either may legitimately route differently
     _, amb = certify_routing(xb, l80.Wr_np, l80.bias_np, l80.cfg.k, _np(ib),
-                             moe.moe_router_sum_depth(64, l80.cfg.d))
+                             moe.moe_router_sum_depth(64, l80.cfg.d, l80.cfg.E))
     for t in [t for t in range(64) if not amb[t]][:6]:
         y1, i1, _, _ = moe.moe_layer_forward(l80.layer, x[t:t + 1].contiguous(), path=moe.MOE_PATH_DECODE)
         torch.cuda.synchronize()
@@ -272,7 +272,7 @@ def _prefill_check(L, step, T, sample=None):
     assert L.pool.check_error() == moe.MOE_OK
     idx_np, y_np = _np(idx), _np(y)
     rows = np.arange(T) if sample is None else sample
-    depth = moe.moe_router_sum_depth(T, L.cfg.d)
+    depth = moe.moe_router_sum_depth(T, L.cfg.d, L.cfg.E)
     namb, _ = certify_routing(xb[rows], L.Wr_np, L.bias_np, L.cfg.k, idx_np[rows], depth)
     ref = L.oracle(xb[rows], idx=idx_np[rows])
     assert np.allclose(_np(w)[rows], ref["w"], rtol=0, atol=2e-5)

@@ -143,9 +143,13 @@ def test_validation_without_device_work():
     # pool creation with an invalid shape never reaches hipMalloc
     h = C.c_void_p()
     assert lib.moe_pool_create(16, 4, C.byref(moe.shape(100, 64)), C.byref(h)) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_router_sum_depth(1, 2048) == 17
-    assert lib.moe_router_sum_depth(64, 2048) == 32 + 2 + 8 + 7 + 1
-    assert lib.moe_router_sum_depth(4096, 2048) == 32 + 2 + 64 + 0 + 1
+    # depth of the device's summation tree: T <= 8 one row per block (d/256
+    # per thread, 6 butterfly, 2 tree, 1 bias); T > 8 split-K MFMA with S
+    # splits (S = 8 for 64 tokens, 4 for 4096 tokens at E = 512)
+    assert lib.moe_router_sum_depth(1, 2048, 512) == 17
+    assert lib.moe_router_sum_depth(64, 2048, 512) == 32 + 2 + 8 + 7 + 1
+    assert lib.moe_router_sum_depth(4096, 2048, 512) == 32 + 2 + 16 + 3 + 1
+    assert lib.moe_router_sum_depth(8, 2048, 0) == -1
     assert lib.moe_router_workspace_bytes(1, 2048, 512) > 0
 
 
