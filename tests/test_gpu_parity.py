@@ -189,6 +189,36 @@ def test_token_independence(l80):
         assert_close_y(_np(y1)[0], _np(yb)[t].astype(np.float64))
 
 
+# ------------------------------------------------------- shape envelope
+# The edges of what the kernels accept: intermediates wider than 512 (the
+# down GEMVs' extra-group loops), the largest expert count (E = 1024, k = 16:
+# the widest top-k), the largest hidden size (d = 8192) and k = E (every
+# expert selected).  Each on the decode, batched and prefill paths.
+ENVELOPE = {
+    "wide_I": dict(d=512, E=32, k=4, I=1024, I_shared=1024, n_slots=32),
+    "max_E": dict(d=512, E=1024, k=16, I=128, I_shared=128, n_slots=1024),
+    "max_d": dict(d=8192, E=16, k=2, I=128, I_shared=128, n_slots=16),
+    "k_eq_E": dict(d=256, E=16, k=16, I=64, I_shared=64, n_slots=16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ENVELOPE))
+def test_envelope_decode_and_batched(name):
+    L = DeviceLayer(ms.scaled(ms.CONFIGS["decode80b"], alpha=0.0, **ENVELOPE[name]))
+    _check_layer_step(L, 0, path=moe.MOE_PATH_DECODE, T=1)
+    _check_layer_step(L, 1, path=moe.MOE_PATH_DECODE, T=4)
+    _check_layer_step(L, 2, path=moe.MOE_PATH_BATCHED, T=24)
+    assert L.pool.check_error() == moe.MOE_OK
+
+
+@pytest.mark.parametrize("name", sorted(ENVELOPE))
+def test_envelope_prefill(name):
+    cfg = ms.scaled(ms.CONFIGS["prefill80b"], T=160, **ENVELOPE[name])
+    L = DeviceLayer(cfg)
+    rel, namb, _ = _prefill_check(L, 0, cfg.T)
+    print(f"prefill {name}: rel err {rel:.2e}, near-ties {namb}")
+
+
 # ------------------------------------------------------ placement invariance
 def test_placement_invariance_bit_identical():
     """Two pools holding the same experts at different slots, and a smaller
