@@ -530,7 +530,7 @@ struct DownArgs {
 constexpr int kDnWaves = 16;
 constexpr int kDnRound = kDnWaves;
 __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) {
-  extern __shared__ float dyn[];                // oi[nI][8] | hst[kDnRound][Imax + Imax/8]
+  extern __shared__ float dyn[];                // oi[nI][8] | wk[nI] | hst[kDnRound][hrec_words]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 3, gl = lane & 7;       // group lanes of a row are consecutive
   const int jb = xcd_remap(blockIdx.x, gridDim.x);   // this block's 8 output rows
@@ -538,7 +538,11 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   const int nR = a.T * a.k, nI = nR + a.T;
   const int rec = hrec_words(a.Imax);           // dwords per staged record
   float* oi = dyn;
-  uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 8 + 3) & ~3));
+  float* wk = dyn + nI * 8;                     // combine weights: w[T*k] then sgate[T]
+  uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 9 + 3) & ~3));
+  // the combine weights are read now, not after the GEMV (their latency
+  // would land at the very end of the kernel)
+  for (int q = tid; q < nI; q += 64 * kDnWaves) wk[q] = q < nR ? a.w[q] : a.sgate[q - nR];
   for (int base = 0; base < nI; base += kDnRound) {
     const int nr = min(kDnRound, nI - base);
     const int i = base + wave;
@@ -599,8 +603,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   if (tid < 8 * a.T) {
     const int t = tid / 8, rr = tid % 8;
     float y = 0.f;
-    for (int q2 = 0; q2 < a.k; ++q2) y += a.w[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
-    y += a.sgate[t] * oi[(nR + t) * 8 + rr];
+    for (int q2 = 0; q2 < a.k; ++q2) y += wk[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
+    y += wk[nR + t] * oi[(nR + t) * 8 + rr];
     a.y[(size_t)t * a.d + jb * 8 + rr] = y;
   }
 }
@@ -838,7 +842,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));   // multiple of 8: xcd_remap
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
-    const size_t dlds = (size_t)(((nI * 8 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
+    const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
     MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
     return MOE_OK;
   }
