@@ -17,7 +17,8 @@ the CPU oracle timed on a bounded sample of the same steps (cpu_baseline).
 --workload selects another configuration (decode35b, refill80b: 256-slot
 pool refilled by LFU + recency from pinned host memory, batch80b: T=64,
 prefill80b / prefill80b_zipf: T=4096 on the matrix cores); --workload all
-prints one line per workload, the headline first.
+prints one line per workload, the headline first; --workload refill_sweep
+prints the refill run for pool sizes 64..512 (hit rate vs tokens/s).
 """
 from __future__ import annotations
 
@@ -249,15 +250,18 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
     return out
 
 
-def run_refill(c, K, W):
-    """256-slot pool over 512 experts, refilled between router and experts by
-    LFU + recency from pinned host memory; outputs checked bit-identical to an
-    all-resident twin."""
+def run_refill(c, K, W, n_slots=None, host=None):
+    """A pool of n_slots (default 256) over 512 experts, refilled between
+    router and experts by LFU + recency from pinned host memory; outputs
+    checked bit-identical to an all-resident twin."""
     torch, ms, moe = c.torch, c.ms, c.moe
     cfg = ms.CONFIGS["decode80b"]
+    if n_slots is not None:
+        cfg = ms.scaled(cfg, n_slots=n_slots)
     nsteps = K + W
     log(f"refill80b: {cfg.n_slots} slots over {cfg.E} experts, steps={nsteps}")
-    host = packed_experts(c, cfg, pinned=True)
+    if host is None:
+        host = packed_experts(c, cfg, pinned=True)
     stride = host.shape[1]
     twin = build_layers(c, ms.scaled(cfg, n_slots=cfg.E), 1, staging=host.cuda())[0]
     pool = moe.Pool(cfg.E, cfg.n_slots, cfg.d, cfg.I)
@@ -305,8 +309,8 @@ def run_refill(c, K, W):
     return {"metric": METRIC, "value": round(K / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
             "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
-            "config": {"workload": "80B-shape batch-1 decode, 256-slot HBM pool refilled by LFU+recency "
-                                   "from pinned host memory (wall clock incl. PCIe and host policy)",
+            "config": {"workload": f"80B-shape batch-1 decode, {cfg.n_slots}-slot HBM pool refilled by "
+                                   "LFU+recency from pinned host memory (wall clock incl. PCIe and host policy)",
                        "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "slots": cfg.n_slots},
             "hit_rate": round(hits / max(1, hits + misses), 4),
             "hit_rate_all_steps": round(st1["hits"] / max(1, st1["hits"] + st1["misses"]), 4),
@@ -412,7 +416,7 @@ def main():
                     help="only copy an MB-sized device buffer 5 times (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="decode80b",
                     choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
-                             "prefill80b_zipf", "all"])
+                             "prefill80b_zipf", "all", "refill_sweep"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
@@ -432,6 +436,15 @@ def main():
                              cpu if wl == "decode80b" else 0, args.eager)
         elif wl == "refill80b":
             res = run_refill(c, min(args.steps, 300), min(args.warmup, 50))
+        elif wl == "refill_sweep":
+            # hit rate and tokens/s against the pool size (the pages report that
+            # pool size barely changes speed on their SSD-backed machine)
+            host = packed_experts(c, c.ms.CONFIGS["decode80b"], pinned=True)
+            for slots in (64, 128, 192, 256, 384, 512):
+                res = run_refill(c, min(args.steps, 200), min(args.warmup, 50), slots, host)
+                print(json.dumps(res), flush=True)
+                c.torch.cuda.empty_cache()
+            continue
         elif wl == "batch80b":
             res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4))
         else:
