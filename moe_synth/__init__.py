@@ -12,7 +12,10 @@ the 35B model; the router and the shared expert stay resident; routed experts
 are 4-bit MLX affine group-quantised weights).  Value distributions are the
 synthetic recipe of the workload table (x ~ N(0,1) rounded to bf16, router
 weights ~ N(0, 0.02) in fp32, codes uniform on 0..15, scales ~ U[0.002, 0.02]
-rounded to fp16, bias = -8 * scale).
+rounded to fp16, bias = -8 * scale).  8-bit experts (the pages' kernels also
+cover MLX affine int8) draw codes uniform on 0..255, scales U[0.002, 0.02]/16
+rounded to fp16 and bias = -128 * scale, so their weights span the same range
+as the 4-bit ones.
 
 Every array comes from its own counter-keyed numpy PCG64 stream
 (``default_rng([seed, component, index])``) so that any expert or any decode
@@ -52,6 +55,7 @@ class LayerConfig:
     alpha: float      # Zipf logit-offset scale (0 = unbiased router)
     seed: int
     permute_slots: bool = True
+    bits: int = 4     # code width of routed and shared experts (4 or 8)
 
     @property
     def group(self) -> int:
@@ -83,6 +87,19 @@ CONFIGS: Dict[str, LayerConfig] = {
     "prefill80b_zipf": LayerConfig("prefill80b_zipf", T=4096, d=2048, E=512,
                                    k=10, I=512, I_shared=512, n_slots=512,
                                    steps=1, alpha=ZIPF_ALPHA, seed=1005),
+    # the same layers with 8-bit experts
+    "tiny_int8": LayerConfig("tiny_int8", T=4, d=256, E=16, k=2, I=64, I_shared=64,
+                             n_slots=16, steps=8, alpha=0.0, seed=1100,
+                             permute_slots=False, bits=8),
+    "decode80b_int8": LayerConfig("decode80b_int8", T=1, d=2048, E=512, k=10, I=512,
+                                  I_shared=512, n_slots=512, steps=1000,
+                                  alpha=ZIPF_ALPHA, seed=1102, bits=8),
+    "batch80b_int8": LayerConfig("batch80b_int8", T=64, d=2048, E=512, k=10, I=512,
+                                 I_shared=512, n_slots=512, steps=100,
+                                 alpha=ZIPF_ALPHA, seed=1103, bits=8),
+    "prefill80b_int8": LayerConfig("prefill80b_int8", T=4096, d=2048, E=512, k=10,
+                                   I=512, I_shared=512, n_slots=512, steps=1,
+                                   alpha=0.0, seed=1104, bits=8),
 }
 
 
@@ -131,24 +148,32 @@ def logit_bias(cfg: LayerConfig, alpha: Optional[float] = None) -> Optional[np.n
     return (-a * 1.1 * np.log(r)).astype(np.float32)
 
 
-def _matrix(g: np.random.Generator, out: int, inp: int):
-    codes = g.integers(0, 16, size=(out, inp), dtype=np.uint8)
-    sc = g.uniform(0.002, 0.02, size=(out, inp // GROUP)).astype(np.float16)
-    bi = (np.float16(-8.0) * sc).astype(np.float16)   # exact in fp16
+def _matrix(g: np.random.Generator, out: int, inp: int, bits: int = 4):
+    if bits == 4:
+        codes = g.integers(0, 16, size=(out, inp), dtype=np.uint8)
+        sc = g.uniform(0.002, 0.02, size=(out, inp // GROUP)).astype(np.float16)
+        bi = (np.float16(-8.0) * sc).astype(np.float16)   # exact in fp16
+    elif bits == 8:
+        codes = g.integers(0, 256, size=(out, inp), dtype=np.uint8)
+        sc = (g.uniform(0.002, 0.02, size=(out, inp // GROUP)) / 16).astype(np.float16)
+        bi = (np.float16(-128.0) * sc).astype(np.float16)  # exact in fp16
+    else:
+        raise ValueError(f"bits must be 4 or 8, not {bits}")
     return {"codes": codes, "scales": sc, "biases": bi}
 
 
 def expert_raw(cfg: LayerConfig, e: int, I: Optional[int] = None,
                component: int = _C_EXPERT) -> Dict[str, Dict[str, np.ndarray]]:
-    """Raw int4 weights of one expert, MLX orientation [out][in] / [out][in/64].
+    """Raw int4 / int8 (cfg.bits) weights of one expert, MLX orientation
+    [out][in] / [out][in/64].
 
     gate, up: out = I, in = d.  down: out = d, in = I.
     """
     I = cfg.I if I is None else I
     g = rng(cfg.seed, component, e)
-    return {"gate": _matrix(g, I, cfg.d),
-            "up": _matrix(g, I, cfg.d),
-            "down": _matrix(g, cfg.d, I)}
+    return {"gate": _matrix(g, I, cfg.d, cfg.bits),
+            "up": _matrix(g, I, cfg.d, cfg.bits),
+            "down": _matrix(g, cfg.d, I, cfg.bits)}
 
 
 def shared_raw(cfg: LayerConfig):

@@ -9,7 +9,7 @@ generators in ``moe_synth``).
 What it computes, and on what authority (Swiftlet pages):
   * routing of every token to k of E experts (10 of 512 / 8 of 256 —
     "How it works"), router and shared expert resident;
-  * routed experts as 4-bit MLX affine group-quantised weights
+  * routed experts as 4-bit (or 8-bit) MLX affine group-quantised weights
     (relationship-to-TurboFieldfare section: MLX affine int4/int8 group
     quantisation with byte-addressed kernels and 64-bit offsets);
   * each expert repacked as one fixed-stride blob so one fetch is one read,

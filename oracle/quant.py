@@ -1,10 +1,11 @@
-"""Oracle: int4 affine group dequantisation and the fixed-stride blob layout.
+"""Oracle: int4 / int8 affine group dequantisation and the fixed-stride blob layout.
 
-Dequantisation (MLX affine group quantisation, named on the Swiftlet pages in
-the relationship-to-TurboFieldfare section): for an [out, in] matrix with
-group size 64 along the input dimension,
+Dequantisation (MLX affine int4/int8 group quantisation, named on the
+Swiftlet pages in the relationship-to-TurboFieldfare section): for an
+[out, in] matrix with group size 64 along the input dimension,
 
-    W[o, j] = scale[o, j // 64] * q[o, j] + bias[o, j // 64],   q in 0..15.
+    W[o, j] = scale[o, j // 64] * q[o, j] + bias[o, j // 64],
+    q in 0..15 (4-bit) or 0..255 (8-bit).
 
 Blob layout (the pages fix only that each routed expert is repacked as one
 fixed-stride blob so that fetching it is one read — "How it works"; the byte
@@ -20,14 +21,23 @@ layout below is this library's reading, chosen for wide coalesced loads):
   sections in the order gate codes, gate sb, up codes, up sb, down codes,
   down sb; blob bytes = 27/16 * d * I; stride = bytes rounded up to 4096,
   zero padded.
+
+8-bit blobs (same sections and order, same sb): codes_m is [in/16][out][16]
+bytes, one code per byte; inside every 8 consecutive inputs the bytes hold
+inputs (0, 1, 4, 5, 2, 3, 6, 7) of the block, so byte pairs (0, 2) and
+(1, 3) of each 32-bit word are the input pairs (i, i+4) the 4-bit layout
+forms from nibbles i and i+4.  blob bytes = 51/16 * d * I.
 """
 from __future__ import annotations
 
 import numpy as np
 
 GROUP = 64
-CHUNK = 32
+CHUNK = 32                   # inputs per 16-byte piece, 4-bit
+CHUNK8 = 16                  # inputs per 16-byte piece, 8-bit
 MATS = ("gate", "up", "down")
+BITS = (4, 8)
+PERM8 = np.array([0, 1, 4, 5, 2, 3, 6, 7])   # byte j of an 8-input block holds input PERM8[j]
 
 
 def dequant(m) -> np.ndarray:
@@ -42,20 +52,21 @@ def mat_dims(d: int, I: int):
     return {"gate": (I, d), "up": (I, d), "down": (d, I)}
 
 
-def section_bytes(out: int, inp: int):
-    return out * inp // 2, (inp // GROUP) * out * 4
+def section_bytes(out: int, inp: int, bits: int = 4):
+    assert bits in BITS
+    return out * inp * bits // 8, (inp // GROUP) * out * 4
 
 
-def blob_bytes(d: int, I: int) -> int:
+def blob_bytes(d: int, I: int, bits: int = 4) -> int:
     tot = 0
     for o, i in mat_dims(d, I).values():
-        c, s = section_bytes(o, i)
+        c, s = section_bytes(o, i, bits)
         tot += c + s
     return tot
 
 
-def blob_stride(d: int, I: int) -> int:
-    b = blob_bytes(d, I)
+def blob_stride(d: int, I: int, bits: int = 4) -> int:
+    b = blob_bytes(d, I, bits)
     return (b + 4095) // 4096 * 4096
 
 
@@ -74,6 +85,19 @@ def _unpack_codes(buf: np.ndarray, out: int, inp: int) -> np.ndarray:
     return q
 
 
+def _pack_codes8(codes: np.ndarray) -> np.ndarray:
+    out, inp = codes.shape
+    c = np.asarray(codes, dtype=np.uint8).reshape(out, inp // 8, 8)[:, :, PERM8]
+    return c.reshape(out, inp // CHUNK8, 16).transpose(1, 0, 2).ravel()
+
+
+def _unpack_codes8(buf: np.ndarray, out: int, inp: int) -> np.ndarray:
+    b = buf.reshape(inp // CHUNK8, out, 16).transpose(1, 0, 2).reshape(out, inp // 8, 8)
+    q = np.empty_like(b)
+    q[:, :, PERM8] = b
+    return q.reshape(out, inp)
+
+
 def _pack_sb(scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
     sb = np.stack([np.asarray(scales, np.float16), np.asarray(biases, np.float16)], axis=-1)
     return np.ascontiguousarray(sb.transpose(1, 0, 2)).view(np.uint8).ravel()
@@ -84,27 +108,29 @@ def _unpack_sb(buf: np.ndarray, out: int, inp: int):
     return (np.ascontiguousarray(sb[:, :, 0].T), np.ascontiguousarray(sb[:, :, 1].T))
 
 
-def pack_expert(raw, d: int, I: int) -> np.ndarray:
+def pack_expert(raw, d: int, I: int, bits: int = 4) -> np.ndarray:
     """Blob bytes (length = stride) of one expert from its raw matrices."""
     parts = []
     for name in MATS:
         m = raw[name]
-        parts.append(_pack_codes(m["codes"]))
+        assert int(np.max(m["codes"])) < (1 << bits)
+        parts.append(_pack_codes(m["codes"]) if bits == 4 else _pack_codes8(m["codes"]))
         parts.append(_pack_sb(m["scales"], m["biases"]))
     body = np.concatenate(parts)
-    assert body.size == blob_bytes(d, I)
-    blob = np.zeros(blob_stride(d, I), dtype=np.uint8)
+    assert body.size == blob_bytes(d, I, bits)
+    blob = np.zeros(blob_stride(d, I, bits), dtype=np.uint8)
     blob[:body.size] = body
     return blob
 
 
-def unpack_expert(blob: np.ndarray, d: int, I: int):
+def unpack_expert(blob: np.ndarray, d: int, I: int, bits: int = 4):
     blob = np.asarray(blob, dtype=np.uint8)
     off = 0
     raw = {}
     for name, (o, i) in mat_dims(d, I).items():
-        cb, sbb = section_bytes(o, i)
-        codes = _unpack_codes(blob[off:off + cb], o, i)
+        cb, sbb = section_bytes(o, i, bits)
+        unpack = _unpack_codes if bits == 4 else _unpack_codes8
+        codes = unpack(blob[off:off + cb], o, i)
         off += cb
         sc, bi = _unpack_sb(blob[off:off + sbb], o, i)
         off += sbb

@@ -36,18 +36,19 @@ def lfu_traces():
 
 
 def blob_layout():
-    """[(d, I, bytes, stride, codes[(mat,row,col,val,off,byte)], sbs[(mat,row,g,soff,boff)])]."""
+    """[(d, I, bits, bytes, stride, codes[(mat,row,col,val,off,byte)], sbs[(mat,row,g,soff,boff)])]."""
     out = []
     cur = None
     for line in _lines("blob_layout.txt"):
         t = line.split()
         if t[0] == "shape":
             kv = dict(a.split("=") for a in t[1:])
-            cur = (int(kv["d"]), int(kv["I"]), int(kv["bytes"]), int(kv["stride"]), [], [])
+            cur = (int(kv["d"]), int(kv["I"]), int(kv.get("bits", 4)), int(kv["bytes"]),
+                   int(kv["stride"]), [], [])
         elif t[0] == "end":
             out.append(cur)
         elif t[0] == "code":
-            cur[4].append((t[1], int(t[2]), int(t[3]), int(t[4]), int(t[6]), int(t[7], 16)))
+            cur[5].append((t[1], int(t[2]), int(t[3]), int(t[4]), int(t[6]), int(t[7], 16)))
         elif t[0] == "sb":
-            cur[5].append((t[1], int(t[2]), int(t[3]), int(t[5]), int(t[6])))
+            cur[6].append((t[1], int(t[2]), int(t[3]), int(t[5]), int(t[6])))
     return out

@@ -110,8 +110,9 @@ def test_shared_gate_closed_form():
 
 
 # ---- P5: whole tiny layer vs 50-digit brute force ---------------------------
-def test_layer_vs_mpmath_bruteforce():
-    cfg = TINY
+@pytest.mark.parametrize("name", ["tiny", "tiny_int8"])
+def test_layer_vs_mpmath_bruteforce(name):
+    cfg = ms.CONFIGS[name]
     Wr = ms.router_weight(cfg)
     xb = ms.x_bits(cfg, 0)
     ex = _tiny_experts(cfg)
@@ -212,47 +213,96 @@ def test_dequant_exact_in_fp32():
 
 
 # ---- P7: blob layout ---------------------------------------------------------
-@pytest.mark.parametrize("case", range(2))
+@pytest.mark.parametrize("case", range(4))
 def test_blob_layout_golden(case):
-    d, I, nbytes, stride, codes, sbs = golden_io.blob_layout()[case]
-    assert oquant.blob_bytes(d, I) == nbytes == 27 * d * I // 16
-    assert oquant.blob_stride(d, I) == stride
+    d, I, bits, nbytes, stride, codes, sbs = golden_io.blob_layout()[case]
+    per16 = 27 if bits == 4 else 51
+    assert oquant.blob_bytes(d, I, bits) == nbytes == per16 * d * I // 16
+    assert oquant.blob_stride(d, I, bits) == stride
     dims = oquant.mat_dims(d, I)
+
+    def zero():
+        return {m: {"codes": np.zeros(dims[m], np.uint8),
+                    "scales": np.zeros((dims[m][0], dims[m][1] // 64), np.float16),
+                    "biases": np.zeros((dims[m][0], dims[m][1] // 64), np.float16)}
+                for m in oquant.MATS}
     for mat, row, col, val, off, byte in codes:
-        raw = {m: {"codes": np.zeros(dims[m], np.uint8),
-                   "scales": np.zeros((dims[m][0], dims[m][1] // 64), np.float16),
-                   "biases": np.zeros((dims[m][0], dims[m][1] // 64), np.float16)}
-               for m in oquant.MATS}
+        raw = zero()
         raw[mat]["codes"][row, col] = val
-        blob = oquant.pack_expert(raw, d, I)
+        blob = oquant.pack_expert(raw, d, I, bits)
         assert blob.size == stride
         nz = np.nonzero(blob)[0]
         assert nz.tolist() == [off] and blob[off] == byte
     for mat, row, g, soff, boff in sbs:
-        raw = {m: {"codes": np.zeros(dims[m], np.uint8),
-                   "scales": np.zeros((dims[m][0], dims[m][1] // 64), np.float16),
-                   "biases": np.zeros((dims[m][0], dims[m][1] // 64), np.float16)}
-               for m in oquant.MATS}
+        raw = zero()
         raw[mat]["scales"][row, g] = np.float16(0.5)      # 0x3800
         raw[mat]["biases"][row, g] = np.float16(-2.0)     # 0xC000
-        blob = oquant.pack_expert(raw, d, I)
+        blob = oquant.pack_expert(raw, d, I, bits)
         assert blob[soff:soff + 2].tobytes() == b"\x00\x38"
         assert blob[boff:boff + 2].tobytes() == b"\x00\xc0"
         assert np.count_nonzero(blob) == 2
 
 
-def test_pack_roundtrip():
-    for cfg in (TINY, ms.CONFIGS["decode80b"]):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_pack_roundtrip(bits):
+    small = TINY if bits == 4 else ms.CONFIGS["tiny_int8"]
+    big = ms.scaled(ms.CONFIGS["decode80b"], bits=bits)
+    for cfg in (small, big):
         raw = ms.expert_raw(cfg, 9)
-        blob = oquant.pack_expert(raw, cfg.d, cfg.I)
-        assert blob.size == oquant.blob_stride(cfg.d, cfg.I)
-        assert not blob[oquant.blob_bytes(cfg.d, cfg.I):].any()
-        back = oquant.unpack_expert(blob, cfg.d, cfg.I)
+        blob = oquant.pack_expert(raw, cfg.d, cfg.I, bits)
+        assert blob.size == oquant.blob_stride(cfg.d, cfg.I, bits)
+        assert not blob[oquant.blob_bytes(cfg.d, cfg.I, bits):].any()
+        back = oquant.unpack_expert(blob, cfg.d, cfg.I, bits)
         for m in oquant.MATS:
             for f in ("codes", "scales", "biases"):
                 assert np.array_equal(back[m][f], raw[m][f])
-        assert np.array_equal(oquant.pack_expert(back, cfg.d, cfg.I), blob)
+        assert np.array_equal(oquant.pack_expert(back, cfg.d, cfg.I, bits), blob)
+    # 80B shape: 27/16 and 51/16 bytes per weight, already multiples of 4096
     assert oquant.blob_bytes(2048, 512) == 1769472 == oquant.blob_stride(2048, 512)
+    assert oquant.blob_bytes(2048, 512, 8) == 3342336 == oquant.blob_stride(2048, 512, 8)
+
+
+def test_int8_codes_are_bytes():
+    """Every 8-bit code is one byte of the blob, each byte of the codes
+    sections holds one code (a permutation of the codes, nothing lost or
+    merged), and the (scale, bias) sections are the 4-bit ones."""
+    cfg = ms.CONFIGS["tiny_int8"]
+    raw = ms.expert_raw(cfg, 2)
+    blob = oquant.pack_expert(raw, cfg.d, cfg.I, 8)
+    off = 0
+    for m in oquant.MATS:
+        o, i = oquant.mat_dims(cfg.d, cfg.I)[m]
+        sec = blob[off:off + o * i]
+        assert np.array_equal(np.sort(sec), np.sort(raw[m]["codes"].ravel()))
+        off += o * i
+        sb = blob[off:off + (i // 64) * o * 4].view(np.float16).reshape(i // 64, o, 2)
+        assert np.array_equal(sb[:, :, 0].T, raw[m]["scales"])
+        assert np.array_equal(sb[:, :, 1].T, raw[m]["biases"])
+        off += (i // 64) * o * 4
+    assert off == oquant.blob_bytes(cfg.d, cfg.I, 8)
+
+
+def test_int8_with_4bit_codes_is_the_int4_expert():
+    """An 8-bit expert whose codes all lie in 0..15 is the same function as
+    the 4-bit expert with those codes, scales and biases (MLX affine
+    dequantisation does not depend on the code width)."""
+    raw4 = ms.expert_raw(TINY, 4)
+    x = ms.bf16_bits_to_f32(ms.x_bits(TINY, 1)).astype(np.float64)
+    y4 = olayer.expert_ffn(raw4, x)
+    blob8 = oquant.pack_expert(raw4, TINY.d, TINY.I, 8)
+    raw8 = oquant.unpack_expert(blob8, TINY.d, TINY.I, 8)
+    assert np.array_equal(olayer.expert_ffn(raw8, x), y4)
+
+
+def test_int8_dequant_exact_in_fp32():
+    """s*q + b with fp16 s, b = -128 s and q in 0..255 is s*(q-128): at most
+    11 + 8 significant bits, exactly representable in fp32."""
+    raw = ms.expert_raw(ms.CONFIGS["decode80b_int8"], 5)
+    for m in raw.values():
+        W = oquant.dequant(m)
+        assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
+        assert np.array_equal(W, m["scales"].astype(np.float64).repeat(64, 1)
+                              * (m["codes"].astype(np.float64) - 128))
 
 
 # ---- P8: placement invariance (oracle reading blobs through a slot table) ---
