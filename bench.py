@@ -16,9 +16,11 @@ the CPU oracle timed on a bounded sample of the same steps (cpu_baseline).
 
 --workload selects another configuration (decode35b, refill80b: 256-slot
 pool refilled by LFU + recency from pinned host memory, batch80b: T=64,
-prefill80b / prefill80b_zipf: T=4096 on the matrix cores); --workload all
-prints one line per workload, the headline first; --workload refill_sweep
-prints the refill run for pool sizes 64..512 (hit rate vs tokens/s).
+prefill80b / prefill80b_zipf: T=4096 on the matrix cores; decode80b_int8,
+batch80b_int8, prefill80b_int8: the same layers with 8-bit experts);
+--workload all prints one line per workload, the headline first;
+--workload refill_sweep prints the refill run for pool sizes 64..512 (hit
+rate vs tokens/s).
 """
 from __future__ import annotations
 
@@ -36,8 +38,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "routed-MoE layer tokens/s + achieved HBM GB/s on int4 experts (80B shape)"
+METRIC8 = "routed-MoE layer tokens/s + achieved HBM GB/s on int8 experts (80B shape)"
 DATA = ("synthetic (seeded int4 codes U{0..15}, fp16 scales U[0.002,0.02], bias -8*scale, "
         "x ~ N(0,1) bf16, router N(0,0.02) fp32, Zipf(1.1) logit offset alpha=0.15 where skewed)")
+DATA8 = ("synthetic (seeded int8 codes U{0..255}, fp16 scales U[0.002,0.02]/16, bias -128*scale, "
+         "x ~ N(0,1) bf16, router N(0,0.02) fp32, Zipf(1.1) logit offset alpha=0.15 where skewed)")
+
+
+def labels(cfg):
+    """(metric, data, weight dtype) of a workload by its code width."""
+    if cfg.bits == 8:
+        return METRIC8, DATA8, "int8"
+    return METRIC, DATA, "int4"
 
 
 def log(msg):
@@ -56,14 +68,14 @@ class Ctx:
 def packed_experts(c, cfg, pinned=False):
     """All E blobs packed by the library's packer: [E, stride] uint8."""
     torch, ms, moe = c.torch, c.ms, c.moe
-    stride = moe.moe_blob_stride(cfg.d, cfg.I)
+    stride = moe.moe_blob_stride(cfg.d, cfg.I, cfg.bits)
     t0 = time.time()
     if pinned:
         out = torch.empty((cfg.E, stride), dtype=torch.uint8, pin_memory=True)
     else:
         out = torch.empty((cfg.E, stride), dtype=torch.uint8, device="cuda")
     for e in range(cfg.E):
-        out[e].copy_(torch.from_numpy(moe.moe_pack_expert_int4(ms.expert_raw(cfg, e), cfg.d, cfg.I)))
+        out[e].copy_(torch.from_numpy(moe.moe_pack_expert(ms.expert_raw(cfg, e), cfg.d, cfg.I, cfg.bits)))
         if e % 128 == 127:
             log(f"packed {e + 1}/{cfg.E} experts ({time.time() - t0:.1f}s)")
     return out
@@ -78,10 +90,10 @@ def build_layers(c, cfg, R, staging=None):
     Wr = torch.from_numpy(ms.router_weight(cfg)).cuda()
     b = ms.logit_bias(cfg)
     bias = None if b is None else torch.from_numpy(b).cuda()
-    shared = torch.from_numpy(moe.moe_pack_expert_int4(ms.shared_raw(cfg), d, cfg.I_shared)).cuda()
+    shared = torch.from_numpy(moe.moe_pack_expert(ms.shared_raw(cfg), d, cfg.I_shared, cfg.bits)).cuda()
     layers = []
     for r in range(R):
-        pool = moe.Pool(E, E, d, I)
+        pool = moe.Pool(E, E, d, I, cfg.bits)
         for e in range(E):
             pool.load(e, int(perm[e]), staging[e])
         pool.set_slot_table(perm)
@@ -212,29 +224,30 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
     # timed step, replayed alone from a graph with the routing the layer
     # produced; HIP events on the launch stream
     wsf = torch.zeros(moe.moe_ffn_workspace_bytes(cfg.d, cfg.I, cfg.I_shared, 1, cfg.k, cfg.E,
-                                                  moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
+                                                  moe.MOE_PATH_DECODE, cfg.bits), dtype=torch.uint8, device="cuda")
     yf = torch.empty_like(y)
 
     def ffn(i):
         L = layers[i % R]
-        moe.moe_expert_ffn_int4(L.pool, L.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
-                                workspace=wsf, out=yf[i])
+        moe.moe_expert_ffn(L.pool, L.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
+                           workspace=wsf, out=yf[i])
 
     ffn_ms = graph_time(c, ffn, W, nsteps, stream)
     assert torch.equal(yf[W:], y[W:]), "FFN-only replay differs from the layer"
-    expert_bytes = (cfg.k + 1) * moe.moe_blob_bytes(cfg.d, cfg.I)
+    expert_bytes = (cfg.k + 1) * moe.moe_blob_bytes(cfg.d, cfg.I, cfg.bits)
     router_bytes = (cfg.E + 1) * cfg.d * 4
     achieved = expert_bytes / (ffn_ms * 1e-3) / 1e9
     layer_gbs = expert_bytes / (ms_step * 1e-3) / 1e9
+    metric, data, wdt = labels(cfg)
     out = {
-        "metric": METRIC, "value": round(1000.0 / ms_step, 1), "unit": "tokens/s",
+        "metric": metric, "value": round(1000.0 / ms_step, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
+        "dtype": f"{wdt} weights, bf16 activations, fp32 accumulate", "data": data,
         "config": {"workload": f"{'80B' if cfg.E == 512 else '35B'}-shape batch-1 decode MoE layer, "
-                               f"all {cfg.E} experts resident",
+                               f"{wdt} experts, all {cfg.E} experts resident",
                    "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "I_shared": cfg.I_shared,
-                   "group": 64, "replicas": R, "hip_graph": not eager},
+                   "group": 64, "bits": cfg.bits, "replicas": R, "hip_graph": not eager},
         "expert_bytes_per_step": expert_bytes,
         "all_bytes_per_step": expert_bytes + router_bytes,
         "layer_expert_GBps": round(layer_gbs, 1),
@@ -318,12 +331,12 @@ def run_refill(c, K, W, n_slots=None, host=None):
             "bit_identical_to_all_resident": identical}
 
 
-def run_batched(c, K, W, R):
+def run_batched(c, K, W, R, name="batch80b"):
     torch, ms, moe = c.torch, c.ms, c.moe
-    cfg = ms.CONFIGS["batch80b"]
+    cfg = ms.CONFIGS[name]
     T = cfg.T
     nsteps = K + W
-    log(f"batch80b: T={T}, R={R}, steps={K}")
+    log(f"{name}: T={T}, R={R}, steps={K}")
     layers = build_layers(c, cfg, R)
     xall = x_steps(c, cfg, nsteps)
     ws = torch.zeros(layers[0].workspace_bytes(T, moe.MOE_PATH_BATCHED), dtype=torch.uint8, device="cuda")
@@ -341,14 +354,16 @@ def run_batched(c, K, W, R):
     ms_step = graph_time(c, step, W, nsteps, stream)
     ids = idx.cpu().numpy()
     distinct = float(np.mean([len(np.unique(ids[i])) for i in range(W, nsteps)]))
-    expert_bytes = (distinct + 1) * moe.moe_blob_bytes(cfg.d, cfg.I)
+    expert_bytes = (distinct + 1) * moe.moe_blob_bytes(cfg.d, cfg.I, cfg.bits)
     gbs = expert_bytes / (ms_step * 1e-3) / 1e9
-    return {"metric": METRIC, "value": round(T * 1000.0 / ms_step, 1), "unit": "tokens/s", "n_gpus": 1,
+    metric, data, wdt = labels(cfg)
+    return {"metric": metric, "value": round(T * 1000.0 / ms_step, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate",
-            "data": DATA,
-            "config": {"workload": "80B-shape batched decode, T=64 independent tokens, all experts resident",
-                       "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "replicas": R},
+            "scaling": "weak", "vs_baseline": None, "dtype": f"{wdt} weights, bf16 activations, fp32 accumulate",
+            "data": data,
+            "config": {"workload": f"80B-shape batched decode, T=64 independent tokens, {wdt} experts, "
+                                   "all experts resident",
+                       "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "bits": cfg.bits, "replicas": R},
             "distinct_experts_per_step": round(distinct, 1),
             "layer_expert_GBps": round(gbs, 1), "layer_expert_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
@@ -377,13 +392,14 @@ def run_prefill(c, name, reps):
     flops = 6.0 * cfg.d * (T * cfg.k * cfg.I + T * cfg.I_shared)
     router_flops = 2.0 * T * cfg.d * (cfg.E + 1)
     tf = flops / (ms_call * 1e-3) / 1e12
-    return {"metric": METRIC, "value": round(T * 1000.0 / ms_call, 1), "unit": "tokens/s", "n_gpus": 1,
+    metric, data, wdt = labels(cfg)
+    return {"metric": metric, "value": round(T * 1000.0 / ms_call, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": reps, "warmup": 2, "ms_per_step": round(ms_call, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,
-            "dtype": "int4 weights -> fp16 MFMA, fp32 accumulate; fp32 router", "data": DATA,
-            "config": {"workload": f"80B-shape prefill layer, T={T}, "
+            "dtype": f"{wdt} weights -> fp16 MFMA, fp32 accumulate; fp32 router", "data": data,
+            "config": {"workload": f"80B-shape prefill layer, T={T}, {wdt} experts, "
                                    f"{'Zipf-skewed' if cfg.alpha else 'unbiased'} router",
-                       "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I},
+                       "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "bits": cfg.bits},
             "expert_gflop": round(flops / 1e9, 1), "router_gflop": round(router_flops / 1e9, 2),
             "layer_expert_TFLOPs": round(tf, 1), "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
             "max_bucket": int(counts.max())}
@@ -416,7 +432,8 @@ def main():
                     help="only copy an MB-sized device buffer 5 times (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="decode80b",
                     choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
-                             "prefill80b_zipf", "all", "refill_sweep"])
+                             "prefill80b_zipf", "decode80b_int8", "batch80b_int8", "prefill80b_int8",
+                             "all", "refill_sweep"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
@@ -428,10 +445,11 @@ def main():
     c = Ctx()
     c.torch.cuda.set_device(0)
     cpu = 0 if args.no_cpu else args.cpu_steps
-    todo = ["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b", "prefill80b_zipf"] \
+    todo = ["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b", "prefill80b_zipf",
+            "decode80b_int8", "batch80b_int8", "prefill80b_int8"] \
         if args.workload == "all" else [args.workload]
     for wl in todo:
-        if wl in ("decode80b", "decode35b"):
+        if wl in ("decode80b", "decode35b", "decode80b_int8"):
             res = run_decode(c, wl, args.steps, args.warmup, args.replicas,
                              cpu if wl == "decode80b" else 0, args.eager)
         elif wl == "refill80b":
@@ -445,8 +463,8 @@ def main():
                 print(json.dumps(res), flush=True)
                 c.torch.cuda.empty_cache()
             continue
-        elif wl == "batch80b":
-            res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4))
+        elif wl in ("batch80b", "batch80b_int8"):
+            res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4), wl)
         else:
             res = run_prefill(c, wl, 10)
         print(json.dumps(res), flush=True)

@@ -15,7 +15,9 @@
  *            w = softmax over the k chosen logits; shared gate
  *            s_t = sigmoid(x_t . W_r[E]).
  *   expert   SwiGLU: h = silu(W_gate x) * (W_up x), o = W_down h,
- *            W = scale * q + bias per group of 64 inputs, q in 0..15.
+ *            W = scale * q + bias per group of 64 inputs, q in 0..15
+ *            (4-bit) or 0..255 (8-bit; the pages' kernels cover MLX affine
+ *            int4 and int8, relationship-to-TurboFieldfare section).
  *   layer    y_t = sum_{r<k} w[t,r] o_{e_r}(x_t) + s_t o_shared(x_t), summed in
  *            that order, in fp32.
  *
@@ -58,7 +60,7 @@ enum {
   MOE_ERR_HIP = -5             /* HIP runtime error; see moe_last_hip_error   */
 };
 
-/* Flags for moe_expert_ffn_int4 / moe_layer_forward. */
+/* Flags for moe_expert_ffn / moe_layer_forward. */
 enum {
   MOE_PATH_AUTO = 0,       /* choose by tokens per expert                     */
   MOE_PATH_DECODE = 1,     /* per-(token, rank) GEMV, fused combine (T <= 8)  */
@@ -71,6 +73,7 @@ typedef struct moe_ffn_shape {
   int32_t d;      /* hidden size (input of gate/up, output of down)          */
   int32_t I;      /* intermediate size                                       */
   int32_t group;  /* quantisation group along the input dimension (64)       */
+  int32_t bits;   /* code width: 4 or 8 (0 is read as 4)                     */
 } moe_ffn_shape;
 
 /* ---------------------------------------------------------------- errors */
@@ -88,21 +91,32 @@ const char* moe_version(void);
  *   sb_m    [in/64][out][2] fp16: (scale, bias) of group g of row o
  * in the order gate codes, gate sb, up codes, up sb, down codes, down sb.
  * bytes = 27/16 * d * I; stride = bytes rounded up to 4096, zero padded.
+ * 8-bit blobs: the same sections, codes_m [in/16][out][16 B] with one code
+ * per byte; inside each 8 inputs the bytes hold inputs (0,1,4,5,2,3,6,7) of
+ * the block; bytes = 51/16 * d * I.
  * Offsets are 64-bit (multi-GB pools; MLX affine kernels with 64-bit offsets
  * in the relationship-to-TurboFieldfare section). */
 size_t moe_blob_bytes(const moe_ffn_shape* sh);   /* 0 if sh is invalid */
 size_t moe_blob_stride(const moe_ffn_shape* sh);  /* 0 if sh is invalid */
 
-/* Pack one expert (host).  codes[m]: [out][in] bytes, one code (0..15) each,
- * MLX orientation; scales[m], biases[m]: [out][in/64] fp16 bit patterns;
- * m = 0 gate, 1 up, 2 down.  blob_out: moe_blob_stride bytes, written whole
- * (padding zeroed).  Codes above 15: MOE_ERR_INVALID_ARG. */
+/* Pack one expert (host) in the layout of sh->bits.  codes[m]: [out][in]
+ * bytes, one code each (0..15 for 4 bits, 0..255 for 8), MLX orientation;
+ * scales[m], biases[m]: [out][in/64] fp16 bit patterns; m = 0 gate, 1 up,
+ * 2 down.  blob_out: moe_blob_stride bytes, written whole (padding zeroed).
+ * 4-bit codes above 15: MOE_ERR_INVALID_ARG. */
+int moe_pack_expert(const moe_ffn_shape* sh, const uint8_t* const codes[3],
+                    const uint16_t* const scales[3],
+                    const uint16_t* const biases[3], void* blob_out);
+/* Inverse of moe_pack_expert (host). */
+int moe_unpack_expert(const moe_ffn_shape* sh, const void* blob,
+                      uint8_t* const codes[3], uint16_t* const scales[3],
+                      uint16_t* const biases[3]);
+/* The same for 4-bit shapes only (MOE_ERR_INVALID_ARG for sh->bits == 8). */
 int moe_pack_expert_int4(const moe_ffn_shape* sh,
                          const uint8_t* const codes[3],
                          const uint16_t* const scales[3],
                          const uint16_t* const biases[3],
                          void* blob_out);
-/* Inverse of moe_pack_expert_int4 (host). */
 int moe_unpack_expert_int4(const moe_ffn_shape* sh, const void* blob,
                            uint8_t* const codes[3], uint16_t* const scales[3],
                            uint16_t* const biases[3]);
@@ -221,8 +235,10 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
                       size_t workspace_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------- expert FFN
- * Apply the selected int4 experts (read from `pool` through its slot table)
- * and the shared expert (shared_blob_dev, shape shared_sh with the same d).
+ * Apply the selected experts (read from `pool` through its slot table; sh
+ * must match the pool's shape, code width included) and the shared expert
+ * (shared_blob_dev, shape shared_sh with the same d; its code width may
+ * differ from the routed experts').
  *   MOE_PATH_DECODE : out_dev = y [T][d], combine fused (needs topk_w and
  *                     shared_gate).  offsets/pair_ids ignored.  T <= 8.
  *   MOE_PATH_BATCHED/PREFILL : needs offsets_dev/pair_ids_dev from
@@ -241,6 +257,17 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
 size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh,
                                const moe_ffn_shape* shared_sh, int32_t T,
                                int32_t k, int32_t E, int32_t path);
+int moe_expert_ffn(const moe_pool* pool, const moe_ffn_shape* sh,
+                   const void* shared_blob_dev, const moe_ffn_shape* shared_sh,
+                   const uint16_t* x_dev, int32_t T, int32_t k,
+                   const int32_t* topk_idx_dev, const float* topk_w_dev,
+                   const float* shared_gate_dev, const int32_t* offsets_dev,
+                   const int32_t* pair_ids_dev, float* out_dev,
+                   float* partial_dev, float* shared_out_dev, int32_t path,
+                   void* workspace_dev, size_t workspace_bytes,
+                   hipStream_t stream);
+/* moe_expert_ffn for 4-bit routed and shared experts only
+ * (MOE_ERR_INVALID_ARG if either shape has bits == 8). */
 int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh,
                         const void* shared_blob_dev,
                         const moe_ffn_shape* shared_sh,

@@ -43,7 +43,7 @@ _lib = C.CDLL(LIB_PATH)
 
 
 class moe_ffn_shape(C.Structure):
-    _fields_ = [("d", C.c_int32), ("I", C.c_int32), ("group", C.c_int32)]
+    _fields_ = [("d", C.c_int32), ("I", C.c_int32), ("group", C.c_int32), ("bits", C.c_int32)]
 
 
 class moe_pool_stats(C.Structure):
@@ -67,6 +67,8 @@ _SIGS = {
     "moe_version": (C.c_char_p, []),
     "moe_blob_bytes": (_S, [_P]),
     "moe_blob_stride": (_S, [_P]),
+    "moe_pack_expert": (C.c_int, [_P, _P, _P, _P, _P]),
+    "moe_unpack_expert": (C.c_int, [_P, _P, _P, _P, _P]),
     "moe_pack_expert_int4": (C.c_int, [_P, _P, _P, _P, _P]),
     "moe_unpack_expert_int4": (C.c_int, [_P, _P, _P, _P, _P]),
     "moe_lfu_create": (C.c_int, [_I, _I, _P]),
@@ -96,6 +98,8 @@ _SIGS = {
     "moe_bucket_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_bucket_tokens": (C.c_int, [_P, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
     "moe_ffn_workspace_bytes": (_S, [_P, _P, _I, _I, _I, _I]),
+    "moe_expert_ffn": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P,
+                                 _P, _P, _P, _I, _P, _S, _P]),
     "moe_expert_ffn_int4": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P,
                                       _P, _P, _P, _I, _P, _S, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
@@ -139,24 +143,41 @@ def version() -> str:
     return _lib.moe_version().decode()
 
 
-def shape(d: int, I: int) -> moe_ffn_shape:
-    return moe_ffn_shape(d, I, 64)
+def shape(d: int, I: int, bits: int = 4) -> moe_ffn_shape:
+    return moe_ffn_shape(d, I, 64, bits)
 
 
 # -------------------------------------------------------------- blob layout
-def moe_blob_bytes(d: int, I: int) -> int:
-    return int(_lib.moe_blob_bytes(C.byref(shape(d, I))))
+def moe_blob_bytes(d: int, I: int, bits: int = 4) -> int:
+    return int(_lib.moe_blob_bytes(C.byref(shape(d, I, bits))))
 
 
-def moe_blob_stride(d: int, I: int) -> int:
-    return int(_lib.moe_blob_stride(C.byref(shape(d, I))))
+def moe_blob_stride(d: int, I: int, bits: int = 4) -> int:
+    return int(_lib.moe_blob_stride(C.byref(shape(d, I, bits))))
 
 
 _MATS = ("gate", "up", "down")
 
 
+def moe_pack_expert(raw, d: int, I: int, bits: int = 4) -> np.ndarray:
+    """Blob bytes (uint8[stride]) of one expert (4- or 8-bit codes)."""
+    return _pack(_lib.moe_pack_expert, raw, d, I, bits)
+
+
+def moe_unpack_expert(blob: np.ndarray, d: int, I: int, bits: int = 4):
+    return _unpack(_lib.moe_unpack_expert, blob, d, I, bits)
+
+
 def moe_pack_expert_int4(raw, d: int, I: int) -> np.ndarray:
-    """Blob bytes (uint8[stride]) of one expert from raw MLX-orientation arrays."""
+    """Blob bytes (uint8[stride]) of one 4-bit expert from raw MLX-orientation arrays."""
+    return _pack(_lib.moe_pack_expert_int4, raw, d, I, 4)
+
+
+def moe_unpack_expert_int4(blob: np.ndarray, d: int, I: int):
+    return _unpack(_lib.moe_unpack_expert_int4, blob, d, I, 4)
+
+
+def _pack(fn, raw, d: int, I: int, bits: int) -> np.ndarray:
     keep = []
     cp, sp, bp = (C.c_void_p * 3)(), (C.c_void_p * 3)(), (C.c_void_p * 3)()
     for m, name in enumerate(_MATS):
@@ -165,13 +186,12 @@ def moe_pack_expert_int4(raw, d: int, I: int) -> np.ndarray:
         b = np.ascontiguousarray(np.asarray(raw[name]["biases"], np.float16)).view(np.uint16)
         keep += [c, s, b]
         cp[m], sp[m], bp[m] = c.ctypes.data, s.ctypes.data, b.ctypes.data
-    out = np.empty(moe_blob_stride(d, I), dtype=np.uint8)
-    _check(_lib.moe_pack_expert_int4(C.byref(shape(d, I)), cp, sp, bp, out.ctypes.data),
-           "moe_pack_expert_int4")
+    out = np.empty(moe_blob_stride(d, I, bits), dtype=np.uint8)
+    _check(fn(C.byref(shape(d, I, bits)), cp, sp, bp, out.ctypes.data), fn.__name__)
     return out
 
 
-def moe_unpack_expert_int4(blob: np.ndarray, d: int, I: int):
+def _unpack(fn, blob: np.ndarray, d: int, I: int, bits: int):
     dims = {"gate": (I, d), "up": (I, d), "down": (d, I)}
     raw = {}
     cp, sp, bp = (C.c_void_p * 3)(), (C.c_void_p * 3)(), (C.c_void_p * 3)()
@@ -184,8 +204,7 @@ def moe_unpack_expert_int4(blob: np.ndarray, d: int, I: int):
         sp[m] = raw[name]["scales"].ctypes.data
         bp[m] = raw[name]["biases"].ctypes.data
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
-    _check(_lib.moe_unpack_expert_int4(C.byref(shape(d, I)), blob.ctypes.data, cp, sp, bp),
-           "moe_unpack_expert_int4")
+    _check(fn(C.byref(shape(d, I, bits)), blob.ctypes.data, cp, sp, bp), fn.__name__)
     return raw
 
 
@@ -233,10 +252,10 @@ class Lfu:
 class Pool:
     """A bounded HBM slot pool of expert blobs (owns its device memory)."""
 
-    def __init__(self, E: int, n_slots: int, d: int, I: int):
-        self.E, self.n_slots, self.d, self.I = E, n_slots, d, I
+    def __init__(self, E: int, n_slots: int, d: int, I: int, bits: int = 4):
+        self.E, self.n_slots, self.d, self.I, self.bits = E, n_slots, d, I, bits
         h = C.c_void_p()
-        _check(_lib.moe_pool_create(E, n_slots, C.byref(shape(d, I)), C.byref(h)), "moe_pool_create")
+        _check(_lib.moe_pool_create(E, n_slots, C.byref(shape(d, I, bits)), C.byref(h)), "moe_pool_create")
         self.handle = h
         self.stride = int(_lib.moe_pool_stride(h))
 
@@ -357,31 +376,47 @@ def moe_bucket_tokens(topk_idx, E: int, workspace=None, stream=None):
 
 
 # --------------------------------------------------------------- expert FFN
-def moe_ffn_workspace_bytes(d, I, Ish, T, k, E, path) -> int:
-    return int(_lib.moe_ffn_workspace_bytes(C.byref(shape(d, I)), C.byref(shape(d, Ish)), T, k, E, path))
+def moe_ffn_workspace_bytes(d, I, Ish, T, k, E, path, bits: int = 4) -> int:
+    return int(_lib.moe_ffn_workspace_bytes(C.byref(shape(d, I, bits)), C.byref(shape(d, Ish, bits)),
+                                            T, k, E, path))
 
 
 def moe_expert_ffn_int4(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, shared_gate,
                         path: int = MOE_PATH_DECODE, offsets=None, pair_ids=None,
                         workspace=None, out=None, stream=None):
-    """DECODE: returns y [T, d].  BATCHED/PREFILL: returns (partial [T*k, d], shared_out [T, d])."""
+    """moe_expert_ffn through the 4-bit-only entry point."""
+    return _expert_ffn(_lib.moe_expert_ffn_int4, pool, shared_blob, Ish, x, topk_idx, topk_w, shared_gate,
+                       path, offsets, pair_ids, workspace, out, stream, 4)
+
+
+def moe_expert_ffn(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, shared_gate,
+                   path: int = MOE_PATH_DECODE, offsets=None, pair_ids=None,
+                   workspace=None, out=None, stream=None, shared_bits: Optional[int] = None):
+    """DECODE: returns y [T, d].  BATCHED/PREFILL: returns (partial [T*k, d], shared_out [T, d]).
+    The routed experts' code width is the pool's; the shared expert's is shared_bits (default: the same)."""
+    return _expert_ffn(_lib.moe_expert_ffn, pool, shared_blob, Ish, x, topk_idx, topk_w, shared_gate,
+                       path, offsets, pair_ids, workspace, out, stream,
+                       pool.bits if shared_bits is None else shared_bits)
+
+
+def _expert_ffn(fn, pool, shared_blob, Ish, x, topk_idx, topk_w, shared_gate, path, offsets, pair_ids,
+                workspace, out, stream, shared_bits):
     import torch
     T, d = x.shape
     k = topk_idx.shape[1]
     if workspace is None:
-        workspace = _ws(moe_ffn_workspace_bytes(d, pool.I, Ish, T, k, pool.E, path))
+        workspace = _ws(moe_ffn_workspace_bytes(d, pool.I, Ish, T, k, pool.E, path, pool.bits))
     y = partial = shared_out = None
     if path == MOE_PATH_DECODE:
         y = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
     else:
         partial = torch.empty((T * k, d), dtype=torch.float32, device=x.device)
         shared_out = torch.empty((T, d), dtype=torch.float32, device=x.device)
-    st = _lib.moe_expert_ffn_int4(pool.handle, C.byref(shape(d, pool.I)), _ptr(shared_blob),
-                                  C.byref(shape(d, Ish)), _ptr(x), T, k, _ptr(topk_idx), _ptr(topk_w),
-                                  _ptr(shared_gate), _ptr(offsets), _ptr(pair_ids), _ptr(y), _ptr(partial),
-                                  _ptr(shared_out), path, _ptr(workspace), workspace.numel(),
-                                  _stream(stream))
-    _check(st, "moe_expert_ffn_int4")
+    st = fn(pool.handle, C.byref(shape(d, pool.I, pool.bits)), _ptr(shared_blob),
+            C.byref(shape(d, Ish, shared_bits)), _ptr(x), T, k, _ptr(topk_idx), _ptr(topk_w),
+            _ptr(shared_gate), _ptr(offsets), _ptr(pair_ids), _ptr(y), _ptr(partial),
+            _ptr(shared_out), path, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, fn.__name__)
     return y if path == MOE_PATH_DECODE else (partial, shared_out)
 
 
@@ -401,10 +436,12 @@ class Layer:
     """Descriptor of one MoE layer (router, pool of routed experts, shared expert)."""
 
     def __init__(self, w_router, logit_bias, pool: Pool, shared_blob, Ish: int, k: int,
-                 usage: bool = True):
+                 usage: bool = True, shared_bits: Optional[int] = None):
         self.w_router, self.logit_bias, self.pool, self.shared_blob = w_router, logit_bias, pool, shared_blob
         self.k, self.Ish = k, Ish
-        self.desc = moe_layer_desc(shape(pool.d, pool.I), shape(pool.d, Ish), pool.E, k,
+        self.shared_bits = pool.bits if shared_bits is None else shared_bits
+        self.desc = moe_layer_desc(shape(pool.d, pool.I, pool.bits), shape(pool.d, Ish, self.shared_bits),
+                                   pool.E, k,
                                    _ptr(w_router), _ptr(logit_bias), pool.handle.value,
                                    _ptr(shared_blob), pool.usage_ptr if usage else None)
 

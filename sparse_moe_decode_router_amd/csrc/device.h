@@ -15,13 +15,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
-// Nibbles i and i+4 of a code word as a packed bf16 pair (128 + q each):
-// bf16 0x4300 is 128.0 with a mantissa step of 1, so OR-ing a 4-bit code
-// into its low mantissa bits gives exactly 128 + q.
-__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int i) {
-  return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-}
-
 // fp16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits16 & 0xFFFFu));

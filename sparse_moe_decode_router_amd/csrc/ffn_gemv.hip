@@ -1,13 +1,17 @@
-// Int4 expert FFN as GEMVs (decode and batched decode).
+// Int4 / int8 expert FFN as GEMVs (decode and batched decode).
 //
-// Experts are MLX affine int4 group-quantised (relationship-to-TurboFieldfare
-// section of the Swiftlet pages), fetched from the slot pool through the slot
-// table with 64-bit offsets; the SwiGLU form and group 64 are this library's
-// readings.  With W = s*q + b per group of 64 inputs, a group's dot product
-// is  s * sum(q x) + b * sum(x).  The kernels form sum((128 + q) x) with
-// v_dot2c_f32_bf16 on bf16 pairs built by OR-ing nibbles into 0x4300 (exact
-// 128 + q), and fold the offset into the bias term:
-//     group = s * sum((128+q) x) + (b - 128 s) * sum(x).
+// Experts are MLX affine int4 or int8 group-quantised (relationship-to-
+// TurboFieldfare section of the Swiftlet pages), fetched from the slot pool
+// through the slot table with 64-bit offsets; the SwiGLU form and group 64
+// are this library's readings.  With W = s*q + b per group of 64 inputs, a
+// group's dot product is  s * sum(q x) + b * sum(x).  The kernels form
+// sum((c + q) x) with v_dot2c_f32_bf16 on bf16 pairs built by OR-ing nibbles
+// into a bf16 constant, and fold the offset c into the bias term:
+//     group = s * sum((c+q) x) + (b - c s) * sum(x).
+//   4-bit: nibble q into 0x4300 (128.0, mantissa step 1) -> 128 + q, c = 128;
+//   8-bit: low nibble into 0x4300 -> 128 + lo, high nibble into 0x4500
+//          (2048.0, mantissa step 16) -> 2048 + 16 hi; both products go to
+//          the same sums, so c = 2176 and q = lo + 16 hi.
 // Products of bf16 values are exact in fp32; accumulation is fp32.
 //
 // gate/up: one work item = (instance, 8 rows).  Lane (row r, group g) loads
@@ -112,7 +116,42 @@ __device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, 
   return in.n;
 }
 
-constexpr int kGMax = 4;        // groups of 64 inputs per lane (d <= 8192)
+// Decode gate/up: GPL groups of 64 inputs per lane (32 group lanes per row):
+// 1 for d <= 2048, 2 for d <= 4096, 4 for d <= 8192.
+
+// Code words of one 64-input group held as NP 16-byte pieces (4-bit: 2
+// pieces, word m = inputs 8m..8m+7, nibble i = input 8m+i; 8-bit: 4 pieces,
+// words 2m and 2m+1 = inputs (0,1,4,5) and (2,3,6,7) of block m, a byte
+// each).
+template <int NP>
+__device__ __forceinline__ uint32_t qword(const uint4 (&q)[NP], int i) {
+  const uint4 v = q[i >> 2];
+  return (i & 3) == 0 ? v.x : (i & 3) == 1 ? v.y : (i & 3) == 2 ? v.z : v.w;
+}
+
+// Product u of 8-input block m as a bf16 pair (c + q terms), to be taken
+// against x pair qx<BITS>(u) of the block, i.e. (x[8m+p], x[8m+p+4]).
+//   4-bit: u = 0..3, nibbles u and u+4 of word m, pair p = u.
+//   8-bit: u = 0..7, pair p = u/2: its inputs are bytes (0,2) (p even) or
+//          (1,3) (p odd) of word 2m + p/2; u even takes their low nibbles
+//          (128 + lo), u odd their high nibbles (2048 + 16 hi).
+template <int BITS, int NP>
+__device__ __forceinline__ uint32_t qpair(const uint4 (&q)[NP], int m, int u) {
+  static_assert(NP >= BITS / 2, "code pieces");
+  const uint32_t w = qword(q, (BITS / 4) * m + (u >> 2));
+  const uint32_t mag = (BITS == 8 && (u & 1)) ? 0x45004500u : 0x43004300u;
+  return ((w >> (4 * (u & 3))) & 0x000F000Fu) | mag;
+}
+template <int BITS> __device__ __forceinline__ constexpr int qx(int u) { return BITS == 4 ? u : u >> 1; }
+// The same from the group's code words: word index of product u of block m,
+// and the pair from that word.
+template <int BITS> __device__ __forceinline__ constexpr int qwi(int m, int u) { return (BITS / 4) * m + (u >> 2); }
+template <int BITS>
+__device__ __forceinline__ uint32_t qpw(uint32_t w, int u) {
+  const uint32_t mag = (BITS == 8 && (u & 1)) ? 0x45004500u : 0x43004300u;
+  return ((w >> (4 * (u & 3))) & 0x000F000Fu) | mag;
+}
+template <int BITS> __device__ __forceinline__ constexpr float qoff() { return BITS == 4 ? 128.0f : 2176.0f; }
 
 // h of 8 consecutive intermediate rows (one 8-block m = rb) as bf16 (hi, lo)
 // pairs (h[8m+i], h[8m+i+4]) plus the sum of hi + lo, for the down pass.
@@ -146,8 +185,9 @@ __device__ __forceinline__ void write_h8(const float* h, uint32_t* hq, float* hs
 // the top-k, and the block of (rank 0, rows 0..7) publishes the token's
 // indices, weights, shared gate and usage.  This trades a redundant ~1k-cycle
 // selection per block for the dependent global loads of a separate top-k.
-template <int TC, int NK>
+template <int TC, int NK, int GPL, int BITS>
 __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
+  constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ uint32_t xlds[];            // [TC][G][kXPad] | routing area
   __shared__ float red[4][2][TC][8];
   __shared__ float gu[2][TC][8];
@@ -205,15 +245,15 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
       if (!a.batched && routed && rb == 0 && tid == 0)
         a.sel_slot[i] = missing ? -1 : (int32_t)((blob - a.pool.slab) / a.pool.stride);
     }
-    const BlobLayout L = blob_layout(a.d, Iinst);
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
     const int o0 = rb * 8;
 
     // 1. weight loads first: all of this lane's codes and (scale, bias) words
-    uint4 cg[kGMax][2], cu[kGMax][2];
-    uint32_t sbg[kGMax], sbu[kGMax];
-    float sxv[kGMax][TC];                       // group sums of x, loaded up front
+    uint4 cg[GPL][kNP], cu[GPL][kNP];
+    uint32_t sbg[GPL], sbu[GPL];
+    float sxv[GPL][TC];                       // group sums of x, loaded up front
 #pragma unroll
-    for (int gi = 0; gi < kGMax; ++gi) {
+    for (int gi = 0; gi < GPL; ++gi) {
       const int g = cpl + 32 * gi;
 #pragma unroll
       for (int tt = 0; tt < TC; ++tt)
@@ -222,15 +262,16 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     if (!missing) {
       const uint64_t o = (uint64_t)(o0 + r);
 #pragma unroll
-      for (int gi = 0; gi < kGMax; ++gi) {
+      for (int gi = 0; gi < GPL; ++gi) {
         const int g = cpl + 32 * gi;
         if (g < G) {
-          const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
-          const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
-          cg[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c0);
-          cg[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c1);
-          cu[gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c0);
-          cu[gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c1);
+          const uint64_t c0 = ((uint64_t)(kNP * g) * Iinst + o) * 16;
+#pragma unroll
+          for (int p = 0; p < kNP; ++p) {
+            const uint64_t c = c0 + (uint64_t)p * Iinst * 16;
+            cg[gi][p] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c);
+            cu[gi][p] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c);
+          }
           sbg[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[0].sb + ((uint64_t)g * Iinst + o) * 4);
           sbu[gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[1].sb + ((uint64_t)g * Iinst + o) * 4);
         }
@@ -250,36 +291,33 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     for (int tt = 0; tt < TC; ++tt) { vg[tt] = 0.f; vu[tt] = 0.f; }
     if (!missing) {
 #pragma unroll
-      for (int gi = 0; gi < kGMax; ++gi) {
+      for (int gi = 0; gi < GPL; ++gi) {
         const int g = cpl + 32 * gi;
         if (g >= G) continue;
-        const uint32_t gw[8] = {cg[gi][0].x, cg[gi][0].y, cg[gi][0].z, cg[gi][0].w,
-                                cg[gi][1].x, cg[gi][1].y, cg[gi][1].z, cg[gi][1].w};
-        const uint32_t uw[8] = {cu[gi][0].x, cu[gi][0].y, cu[gi][0].z, cu[gi][0].w,
-                                cu[gi][1].x, cu[gi][1].y, cu[gi][1].z, cu[gi][1].w};
         const float sg = f16_to_f32(sbg[gi]), bg = f16_to_f32(sbg[gi] >> 16);
         const float su = f16_to_f32(sbu[gi]), bu = f16_to_f32(sbu[gi] >> 16);
 #pragma unroll
         for (int tt = 0; tt < TC; ++tt) {
           if (tt < ntok) {
             const uint32_t* xp = &xlds[(tt * G + g) * kXPad];
+            const float sx = sxv[gi][tt];
             float ag0 = 0.f, au0 = 0.f, ag1 = 0.f, au1 = 0.f;   // two chains each
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-              const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * w);
+            for (int m = 0; m < 8; ++m) {
+              const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * m);
               const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-              for (int ii = 0; ii < 4; ii += 2) {
-                ag0 = dot2_bf16(nib_pair(gw[w], ii), xw[ii], ag0);
-                au0 = dot2_bf16(nib_pair(uw[w], ii), xw[ii], au0);
-                ag1 = dot2_bf16(nib_pair(gw[w], ii + 1), xw[ii + 1], ag1);
-                au1 = dot2_bf16(nib_pair(uw[w], ii + 1), xw[ii + 1], au1);
+              for (int s2 = 0; s2 < BITS / 2; ++s2) {     // products u = 2 s2 and 2 s2 + 1
+                const int u0 = 2 * s2, u1 = 2 * s2 + 1;
+                ag0 = dot2_bf16(qpair<BITS>(cg[gi], m, u0), xw[qx<BITS>(u0)], ag0);
+                au0 = dot2_bf16(qpair<BITS>(cu[gi], m, u0), xw[qx<BITS>(u0)], au0);
+                ag1 = dot2_bf16(qpair<BITS>(cg[gi], m, u1), xw[qx<BITS>(u1)], ag1);
+                au1 = dot2_bf16(qpair<BITS>(cu[gi], m, u1), xw[qx<BITS>(u1)], au1);
               }
             }
             const float ag = ag0 + ag1, au = au0 + au1;
-            const float sx = sxv[gi][tt];
-            vg[tt] += sg * ag + (bg - 128.0f * sg) * sx;
-            vu[tt] += su * au + (bu - 128.0f * su) * sx;
+            vg[tt] += sg * ag + (bg - qoff<BITS>() * sg) * sx;
+            vu[tt] += su * au + (bu - qoff<BITS>() * su) * sx;
           }
         }
       }
@@ -314,8 +352,9 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 // wave computes one 8-row sub-block on its own (8 rows x 8 group lanes, GPL
 // groups per lane; rows meet by DPP without block barriers); its codes are
 // all in flight before the chunk's activations are staged in LDS.
-template <int GPL>
+template <int GPL, int BITS>
 __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
+  constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ uint32_t xlds[];            // [kTC][G][kXPad] | xs [kTC][G] | hbuf [4][kTC][8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 3, gl = lane & 7;
@@ -334,11 +373,11 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
     int Iinst, tok[kTC], hrow[kTC];
     bool missing;
     const int ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
-    const BlobLayout L = blob_layout(a.d, Iinst);
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
     // 1. the codes of both of this wave's 8-row sub-blocks, all in flight
     //    before the activations are staged
     constexpr int kSub = 1;                     // sub-blocks per wave (4 per item / 4 waves)
-    uint4 cg[kSub][GPL][2], cu[kSub][GPL][2];
+    uint4 cg[kSub][GPL][kNP], cu[kSub][GPL][kNP];
     uint32_t sbg[kSub][GPL], sbu[kSub][GPL];
     if (!missing) {
 #pragma unroll
@@ -348,12 +387,12 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
         for (int gi = 0; gi < GPL; ++gi) {
           const int g = gl + 8 * gi;
           if (g < G) {
-            const uint64_t c0 = ((uint64_t)(2 * g) * Iinst + o) * 16;
-            const uint64_t c1 = c0 + (uint64_t)Iinst * 16;
-            cg[it][gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c0);
-            cg[it][gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c1);
-            cu[it][gi][0] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c0);
-            cu[it][gi][1] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c1);
+#pragma unroll
+            for (int p = 0; p < kNP; ++p) {
+              const uint64_t c = ((uint64_t)(kNP * g + p) * Iinst + o) * 16;
+              cg[it][gi][p] = *reinterpret_cast<const uint4*>(blob + L.m[0].codes + c);
+              cu[it][gi][p] = *reinterpret_cast<const uint4*>(blob + L.m[1].codes + c);
+            }
             sbg[it][gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[0].sb + ((uint64_t)g * Iinst + o) * 4);
             sbu[it][gi] = *reinterpret_cast<const uint32_t*>(blob + L.m[1].sb + ((uint64_t)g * Iinst + o) * 4);
           }
@@ -380,36 +419,32 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
         for (int gi = 0; gi < GPL; ++gi) {
           const int g = gl + 8 * gi;
           if (g >= G) continue;
-          const uint32_t gw[8] = {cg[it][gi][0].x, cg[it][gi][0].y, cg[it][gi][0].z, cg[it][gi][0].w,
-                                  cg[it][gi][1].x, cg[it][gi][1].y, cg[it][gi][1].z, cg[it][gi][1].w};
-          const uint32_t uw[8] = {cu[it][gi][0].x, cu[it][gi][0].y, cu[it][gi][0].z, cu[it][gi][0].w,
-                                  cu[it][gi][1].x, cu[it][gi][1].y, cu[it][gi][1].z, cu[it][gi][1].w};
           const float sg = f16_to_f32(sbg[it][gi]), bg = f16_to_f32(sbg[it][gi] >> 16);
           const float su = f16_to_f32(sbu[it][gi]), bu = f16_to_f32(sbu[it][gi] >> 16);
-          // tokens innermost: each nibble pair is formed once and applied to
+          // tokens innermost: each code pair is formed once and applied to
           // every token of the chunk (per-token chains as in the decode GEMV)
           float ag0[kTC], au0[kTC], ag1[kTC], au1[kTC];
 #pragma unroll
           for (int tt = 0; tt < kTC; ++tt) { ag0[tt] = au0[tt] = ag1[tt] = au1[tt] = 0.f; }
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
+          for (int m = 0; m < 8; ++m) {
             uint4 xv[kTC];
 #pragma unroll
             for (int tt = 0; tt < kTC; ++tt)
-              xv[tt] = tt < ntok ? *reinterpret_cast<const uint4*>(&xlds[(tt * G + g) * kXPad + 4 * w])
+              xv[tt] = tt < ntok ? *reinterpret_cast<const uint4*>(&xlds[(tt * G + g) * kXPad + 4 * m])
                                  : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int ii = 0; ii < 4; ii += 2) {
-              const uint32_t qg0 = nib_pair(gw[w], ii), qu0 = nib_pair(uw[w], ii);
-              const uint32_t qg1 = nib_pair(gw[w], ii + 1), qu1 = nib_pair(uw[w], ii + 1);
+            for (int s2 = 0; s2 < BITS / 2; ++s2) {       // products u = 2 s2 and 2 s2 + 1
+              const uint32_t qg0 = qpair<BITS>(cg[it][gi], m, 2 * s2), qu0 = qpair<BITS>(cu[it][gi], m, 2 * s2);
+              const uint32_t qg1 = qpair<BITS>(cg[it][gi], m, 2 * s2 + 1), qu1 = qpair<BITS>(cu[it][gi], m, 2 * s2 + 1);
 #pragma unroll
               for (int tt = 0; tt < kTC; ++tt) {
                 if (tt < ntok) {
                   const uint32_t xw[4] = {xv[tt].x, xv[tt].y, xv[tt].z, xv[tt].w};
-                  ag0[tt] = dot2_bf16(qg0, xw[ii], ag0[tt]);
-                  au0[tt] = dot2_bf16(qu0, xw[ii], au0[tt]);
-                  ag1[tt] = dot2_bf16(qg1, xw[ii + 1], ag1[tt]);
-                  au1[tt] = dot2_bf16(qu1, xw[ii + 1], au1[tt]);
+                  ag0[tt] = dot2_bf16(qg0, xw[qx<BITS>(2 * s2)], ag0[tt]);
+                  au0[tt] = dot2_bf16(qu0, xw[qx<BITS>(2 * s2)], au0[tt]);
+                  ag1[tt] = dot2_bf16(qg1, xw[qx<BITS>(2 * s2 + 1)], ag1[tt]);
+                  au1[tt] = dot2_bf16(qu1, xw[qx<BITS>(2 * s2 + 1)], au1[tt]);
                 }
               }
             }
@@ -418,8 +453,8 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
           for (int tt = 0; tt < kTC; ++tt) {
             if (tt < ntok) {
               const float sx = xsl[tt * G + g];
-              vg[tt] += sg * (ag0[tt] + ag1[tt]) + (bg - 128.0f * sg) * sx;
-              vu[tt] += su * (au0[tt] + au1[tt]) + (bu - 128.0f * su) * sx;
+              vg[tt] += sg * (ag0[tt] + ag1[tt]) + (bg - qoff<BITS>() * sg) * sx;
+              vu[tt] += su * (au0[tt] + au1[tt]) + (bu - qoff<BITS>() * su) * sx;
             }
           }
         }
@@ -464,44 +499,58 @@ __device__ __forceinline__ const float* hrec_sums(const uint32_t* hrec, int Imax
   return reinterpret_cast<const float*>(hrec + 2 * (Imax / 64) * kHG);
 }
 
-// h given as the LDS record above (hs: its per-8 sums).
-__device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint32_t sb, int g,
+// h given as the LDS record above (hs: its per-8 sums); q0..q3: the
+// group's code pieces (4-bit: q0, q1; 8-bit: q0..q3), qpair layout.
+template <int BITS>
+__device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint4 q2, uint4 q3, uint32_t sb, int g,
                                                  const uint32_t* hrec, int Imax, const float* hs) {
   const float s = f16_to_f32(sb);
   const float b = f16_to_f32(sb >> 16);
-  const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint32_t qw[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                           q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
   const uint4* hh = reinterpret_cast<const uint4*>(hrec + g * kHG);
   const uint4* hl = reinterpret_cast<const uint4*>(hrec + (Imax / 64 + g) * kHG);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;      // four independent chains
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const uint4 vh = hh[w], vl = hl[w];
+  for (int m = 0; m < 8; ++m) {
+    const uint4 vh = hh[m], vl = hl[m];
     const uint32_t ph[4] = {vh.x, vh.y, vh.z, vh.w};
     const uint32_t pl[4] = {vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
-    for (int ii = 0; ii < 4; ii += 2) {
-      const uint32_t q0 = nib_pair(qw[w], ii), q1 = nib_pair(qw[w], ii + 1);
-      a0 = dot2_bf16(q0, ph[ii], a0);
-      a1 = dot2_bf16(q0, pl[ii], a1);
-      a2 = dot2_bf16(q1, ph[ii + 1], a2);
-      a3 = dot2_bf16(q1, pl[ii + 1], a3);
+    for (int s2 = 0; s2 < BITS / 2; ++s2) {         // products u = 2 s2 and 2 s2 + 1
+      const uint32_t c0 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2)], 2 * s2);
+      const uint32_t c1 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2 + 1)], 2 * s2 + 1);
+      a0 = dot2_bf16(c0, ph[qx<BITS>(2 * s2)], a0);
+      a1 = dot2_bf16(c0, pl[qx<BITS>(2 * s2)], a1);
+      a2 = dot2_bf16(c1, ph[qx<BITS>(2 * s2 + 1)], a2);
+      a3 = dot2_bf16(c1, pl[qx<BITS>(2 * s2 + 1)], a3);
     }
   }
   const float acc = (a0 + a2) + (a1 + a3);
   float sh = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) sh += hs[8 * g + m];
-  return s * acc + (b - 128.0f * s) * sh;
+  return s * acc + (b - qoff<BITS>() * s) * sh;
 }
 
+// Code pieces of group g of down row j (qpair layout).
+template <int BITS>
+__device__ __forceinline__ void down_load(const uint8_t* blob, const BlobLayout& L, int d, int j, int g,
+                                          uint4 (&q)[BITS / 2], uint32_t* sb) {
+#pragma unroll
+  for (int p = 0; p < BITS / 2; ++p)
+    q[p] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + ((uint64_t)((BITS / 2) * g + p) * d + j) * 16);
+  *sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * d + j) * 4);
+}
+
+template <int BITS>
 __device__ __forceinline__ float down_group(const uint8_t* blob, const BlobLayout& L, int d, int j,
                                             int g, const uint32_t* __restrict__ hrec, int Imax,
                                             const float* __restrict__ hs) {
-  const uint64_t c0 = ((uint64_t)(2 * g) * d + j) * 16;
-  const uint4 q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
-  const uint4 q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)d * 16);
-  const uint32_t sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)g * d + j) * 4);
-  return down_group_regs(q0, q1, sb, g, hrec, Imax, hs);
+  uint4 q[BITS / 2];
+  uint32_t sb;
+  down_load<BITS>(blob, L, d, j, g, q, &sb);
+  return down_group_regs<BITS>(q[0], q[1], q[BITS / 2 > 2 ? 2 : 0], q[BITS / 2 > 3 ? 3 : 0], sb, g, hrec, Imax, hs);
 }
 
 struct DownArgs {
@@ -529,7 +578,9 @@ struct DownArgs {
 // meanwhile.
 constexpr int kDnWaves = 16;
 constexpr int kDnRound = kDnWaves;
+template <int BITS>
 __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) {
+  constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ float dyn[];                // oi[nI][8] | wk[nI] | hst[kDnRound][hrec_words]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 3, gl = lane & 7;       // group lanes of a row are consecutive
@@ -548,7 +599,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
     const int i = base + wave;
     const bool active = wave < nr;
     // 1. this wave's code loads
-    uint4 q0, q1;
+    uint4 q[kNP];
     uint32_t sb = 0;
     bool miss = true;
     int Iinst = 0;
@@ -565,10 +616,10 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
         Iinst = a.Ish;
       }
       if (!miss && gl < Iinst / 64) {
-        const BlobLayout L = blob_layout(a.d, Iinst);
-        const uint64_t c0 = ((uint64_t)(2 * gl) * a.d + j) * 16;
-        q0 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
-        q1 = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
+        const BlobLayout L = blob_layout(a.d, Iinst, BITS);
+#pragma unroll
+        for (int p = 0; p < kNP; ++p)
+          q[p] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + ((uint64_t)(kNP * gl + p) * a.d + j) * 16);
         sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
       }
     }
@@ -589,10 +640,10 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
       const float* hs = hrec_sums(hrec, a.Imax);
       float acc = 0.f;
       if (!miss) {
-        if (gl < Iinst / 64) acc = down_group_regs(q0, q1, sb, gl, hrec, a.Imax, hs);
-        if (Iinst > 512) {                      // wider intermediates: further groups
-          const BlobLayout L = blob_layout(a.d, Iinst);
-          for (int g = gl + 8; g < Iinst / 64; g += 8) acc += down_group(blob, L, a.d, j, g, hrec, a.Imax, hs);
+        if (gl < Iinst / 64) acc = down_group_regs<BITS>(q[0], q[1], q[kNP > 2 ? 2 : 0], q[kNP > 3 ? 3 : 0], sb, gl, hrec, a.Imax, hs);
+        if (Iinst > 512) {                    // wider intermediates: further groups
+          const BlobLayout L = blob_layout(a.d, Iinst, BITS);
+          for (int g = gl + 8; g < Iinst / 64; g += 8) acc += down_group<BITS>(blob, L, a.d, j, g, hrec, a.Imax, hs);
         }
       }
       acc = sum8_dpp(acc);
@@ -609,19 +660,26 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   }
 }
 
-// Batched down: item = (bucket chunk, 256 output rows).  The chunk's h
+// Sub-blocks of 8 rows per wave in the batched down GEMV: all their codes
+// are in registers at once (4-bit: 8 x 32 B, 8-bit: 4 x 64 B).
+template <int BITS> constexpr int kDnSub = BITS == 4 ? 8 : 4;
+
+// Batched down: item = (bucket chunk, 256 (4-bit) or 128 (8-bit) output rows).  The chunk's h
 // records are staged in LDS once; each wave takes 8-row sub-blocks (8 rows x
 // 8 group lanes), loads the codes once and applies them to every token.
+template <int BITS>
 __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
+  constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ uint32_t hst[];            // [kTC][Imax + Imax/8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 3, gl = lane & 7;
-  const int nrb = (a.d + 255) / 256;            // d is a multiple of 64: last block may be partial
+  constexpr int kRows = 32 * kDnSub<BITS>;     // output rows per item
+  const int nrb = (a.d + kRows - 1) / kRows;    // d is a multiple of 64: last block may be partial
   const int nR = *a.n_routed;
   const int items = (nR + a.n_shared_inst) * nrb;
   const int rec = hrec_words(a.Imax);
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int ii = item / nrb, j0 = (item % nrb) * 256;
+    const int ii = item / nrb, j0 = (item % nrb) * kRows;
     const bool routed = ii < nR;
     const Inst in = a.inst[ii];
     const uint8_t* blob;
@@ -641,22 +699,23 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
 #pragma unroll
     for (int tt = 0; tt < kTC; ++tt)
       hrow[tt] = tt < in.n ? (routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt) : 0;
-    const BlobLayout L = blob_layout(a.d, Iinst);
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
     // 1. every code this wave needs (its 8 sub-blocks of 8 rows, group gl):
     //    all loads in flight at once, ahead of the h staging
-    constexpr int kSub = 8;                     // sub-blocks per wave (32 per item / 4 waves)
-    uint4 q0[kSub], q1[kSub];
+    constexpr int kSub = kDnSub<BITS>;          // sub-blocks of 8 rows per wave
+    uint4 q[kSub][kNP];
     uint32_t sbv[kSub];
     const bool gok = gl < Iinst / 64;
 #pragma unroll
     for (int it = 0; it < kSub; ++it) {
       const int j = j0 + (wave + 4 * it) * 8 + r;
-      q0[it] = q1[it] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int p = 0; p < kNP; ++p) q[it][p] = make_uint4(0, 0, 0, 0);
       sbv[it] = 0;
       if (!missing && gok && j < a.d) {
-        const uint64_t c0 = ((uint64_t)(2 * gl) * a.d + j) * 16;
-        q0[it] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0);
-        q1[it] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + c0 + (uint64_t)a.d * 16);
+#pragma unroll
+        for (int p = 0; p < kNP; ++p)
+          q[it][p] = *reinterpret_cast<const uint4*>(blob + L.m[2].codes + ((uint64_t)(kNP * gl + p) * a.d + j) * 16);
         sbv[it] = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
       }
     }
@@ -685,15 +744,16 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
           for (int tt = 0; tt < kTC; ++tt) {
             if (tt < in.n) {
               const uint32_t* hrec = hst + tt * rec;
-              acc[tt] += down_group_regs(q0[it], q1[it], sbv[it], gl, hrec, a.Imax, hrec_sums(hrec, a.Imax));
+              acc[tt] += down_group_regs<BITS>(q[it][0], q[it][1], q[it][kNP > 2 ? 2 : 0], q[it][kNP > 3 ? 3 : 0], sbv[it],
+                                                 gl, hrec, a.Imax, hrec_sums(hrec, a.Imax));
             }
           }
         }
-        if (Iinst > 512) {                      // intermediates wider than 512: further groups
+        if (Iinst > 512) {                    // intermediates wider than 512: further groups
           for (int g = gl + 8; g < Iinst / 64; g += 8) {
             for (int tt = 0; tt < in.n; ++tt) {
               const uint32_t* hrec = hst + tt * rec;
-              const float v = down_group(blob, L, a.d, j, g, hrec, a.Imax, hrec_sums(hrec, a.Imax));
+              const float v = down_group<BITS>(blob, L, a.d, j, g, hrec, a.Imax, hrec_sums(hrec, a.Imax));
 #pragma unroll
               for (int u = 0; u < kTC; ++u)
                 if (u == tt) acc[u] += v;
@@ -779,6 +839,43 @@ int grid_for(int items_upper) {
   return items_upper < 8192 ? (items_upper > 0 ? items_upper : 1) : 8192;
 }
 
+// Kernel instances for experts of BITS-bit codes.
+template <int BITS>
+struct GemvFns {
+  template <int GPL>
+  static void* gate_up_g(int nk) {
+    switch (nk) {
+      case 1: return (void*)gate_up_kernel<1, 1, GPL, BITS>;
+      case 2: return (void*)gate_up_kernel<1, 2, GPL, BITS>;
+      case 4: return (void*)gate_up_kernel<1, 4, GPL, BITS>;
+      case 8: return (void*)gate_up_kernel<1, 8, GPL, BITS>;
+      default: return (void*)gate_up_kernel<1, 16, GPL, BITS>;
+    }
+  }
+  static void* gate_up(int nk, int G) {
+    return G <= 32 ? gate_up_g<1>(nk) : G <= 64 ? gate_up_g<2>(nk) : gate_up_g<4>(nk);
+  }
+  static void* gate_up_batched(int G) {
+    return G <= 8 ? (void*)gate_up_batched_kernel<1, BITS> : G <= 16 ? (void*)gate_up_batched_kernel<2, BITS>
+         : G <= 32 ? (void*)gate_up_batched_kernel<4, BITS> : G <= 64 ? (void*)gate_up_batched_kernel<8, BITS>
+         : (void*)gate_up_batched_kernel<16, BITS>;
+  }
+  static void* down_decode() { return (void*)down_decode_kernel<BITS>; }
+  static void* down_batched() { return (void*)down_batched_kernel<BITS>; }
+};
+
+struct GemvSet {
+  void* (*gate_up)(int, int);
+  void* (*gate_up_batched)(int);
+  void* (*down_decode)();
+  void* (*down_batched)();
+};
+template <int BITS>
+GemvSet gemv_set() {
+  return {GemvFns<BITS>::gate_up, GemvFns<BITS>::gate_up_batched, GemvFns<BITS>::down_decode,
+          GemvFns<BITS>::down_batched};
+}
+
 }  // namespace
 
 int resolve_path(int path, int T, int k, int E) {
@@ -799,6 +896,8 @@ size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
 int xprep_launch(const uint16_t* x, int T, int d, uint32_t* xq, float* xs, hipStream_t s);
 
 int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_t s) {
+  // one code width for routed and shared experts (both 4-bit or both 8-bit)
+  if (f.bits != f.bits_sh || (f.bits != 4 && f.bits != 8)) return MOE_ERR_UNSUPPORTED;
   if (path == MOE_PATH_PREFILL) return prefill_launch(f, ws, ws_bytes, s);
   const int Imax = f.I > f.Ish ? f.I : f.Ish;
   Carver c(ws, ws_bytes);
@@ -812,6 +911,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     xs = w.xs;
   }
   const int G = f.d / 64;
+  const GemvSet kf = f.bits == 8 ? gemv_set<8>() : gemv_set<4>();
   GateUpArgs g{};
   g.pool = f.pool; g.shared_blob = f.shared_blob;
   g.d = f.d; g.I = f.I; g.Ish = f.Ish; g.Imax = Imax; g.T = f.T; g.k = f.k;
@@ -830,20 +930,13 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int E = f.pool.E;
     const size_t lds = (size_t)1 * G * kXPad * 4 +
                        (f.logits ? (size_t)(topk_scratch_words(E) + 2 * E + 1 + 2 * f.k) * 4 : 0);
-    void* fn;
-    switch (nk_for(E)) {
-      case 1: fn = (void*)gate_up_kernel<1, 1>; break;
-      case 2: fn = (void*)gate_up_kernel<1, 2>; break;
-      case 4: fn = (void*)gate_up_kernel<1, 4>; break;
-      case 8: fn = (void*)gate_up_kernel<1, 8>; break;
-      default: fn = (void*)gate_up_kernel<1, 16>; break;
-    }
+    void* fn = kf.gate_up(nk_for(E), G);
     void* args[] = {&g};
     MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));   // multiple of 8: xcd_remap
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
-    MOE_HIP(hipLaunchKernel((void*)down_decode_kernel, dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
+    MOE_HIP(hipLaunchKernel(kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
     return MOE_OK;
   }
   // batched: bucketed instances of up to kTC tokens
@@ -855,16 +948,15 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   g.inst = w.inst; g.n_routed = w.n_routed; g.n_shared_inst = nsh; g.pair_ids = f.pair_ids;
   const long upper = ((long)f.T * f.k + nsh) * (Imax / 32);
   const size_t lds = ((size_t)kTC * G * kXPad + kTC * G + 4 * kTC * 8) * 4;
-  void* gfn = G <= 8 ? (void*)gate_up_batched_kernel<1> : G <= 16 ? (void*)gate_up_batched_kernel<2>
-            : G <= 32 ? (void*)gate_up_batched_kernel<4> : G <= 64 ? (void*)gate_up_batched_kernel<8>
-            : (void*)gate_up_batched_kernel<16>;
+  void* gfn = kf.gate_up_batched(G);
   void* args[] = {&g};
   MOE_HIP(hipLaunchKernel(gfn, dim3(grid_for((int)(upper < 65536 ? upper : 65536))), dim3(256), args, lds, s));
   dn.inst = w.inst; dn.n_routed = w.n_routed; dn.n_shared_inst = nsh; dn.pair_ids = f.pair_ids;
   dn.partial = f.partial; dn.shared_out = f.shared_out;
-  const long dupper = ((long)f.T * f.k + nsh) * ((f.d + 255) / 256);
+  const int drows = f.bits == 8 ? 128 : 256;   // output rows per item (32 * kDnSub)
+  const long dupper = ((long)f.T * f.k + nsh) * ((f.d + drows - 1) / drows);
   void* dargs[] = {&dn};
-  MOE_HIP(hipLaunchKernel((void*)down_batched_kernel, dim3(grid_for((int)(dupper < 65536 ? dupper : 65536))),
+  MOE_HIP(hipLaunchKernel(kf.down_batched(), dim3(grid_for((int)(dupper < 65536 ? dupper : 65536))),
                           dim3(256), dargs, (size_t)kTC * hrec_words(Imax) * 4, s));
   return MOE_OK;
 }

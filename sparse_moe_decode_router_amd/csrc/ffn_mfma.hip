@@ -1,15 +1,17 @@
-// Int4 expert FFN as grouped GEMMs on the matrix cores (prefill).
+// Int4 / int8 expert FFN as grouped GEMMs on the matrix cores (prefill).
 //
 // With ~80 tokens per expert (4096 tokens, top-10 of 512) each expert's
 // weights are a real dense contraction, so they run on MFMA
 // (v_mfma_f32_32x32x16_f16, fp32 accumulate).  Experts are MLX affine int4
-// group-quantised (relationship-to-TurboFieldfare section of the Swiftlet
-// pages); SwiGLU and group 64 are this library's readings.
+// or int8 group-quantised (relationship-to-TurboFieldfare section of the
+// Swiftlet pages); SwiGLU and group 64 are this library's readings.
 //
-// Dequantisation: a code word's nibbles i and i+4 become the fp16 pair
-// (1024+q_i, 1024+q_{i+4}) by OR-ing them into 0x6400 (fp16 1024.0 has a
-// mantissa step of 1), a packed subtract gives q exactly, and one packed fma
-// gives s*q + b rounded once to fp16 (11-bit significand: |rel err| <= 2^-11).
+// Dequantisation: a 4-bit code word's nibbles i and i+4 (an 8-bit word
+// pair's bytes (0,2) and (1,3), which hold inputs i and i+4 of the block)
+// become the fp16 pair (1024+q_i, 1024+q_{i+4}) by OR-ing them into 0x6400
+// (fp16 1024.0 has a mantissa step of 1, exact for q < 1024), a packed
+// subtract gives q exactly, and one packed fma gives s*q + b rounded once to
+// fp16 (11-bit significand: |rel err| <= 2^-11).
 // bf16 (8-bit significand) rounding of the weights would spend most of the
 // 2e-3 output tolerance; fp16 keeps it small.  Activations enter as fp16.
 // The k order inside every 8-column block is (0,4,1,5,2,6,3,7) in both
@@ -65,6 +67,21 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t b2) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// 8-bit codes of one 8-input block (words wa = inputs (0,1,4,5), wb =
+// inputs (2,3,6,7), a byte each) -> 8 fp16 weights in (0,4,1,5,2,6,3,7) order.
+__device__ __forceinline__ uint4 dequant8_b(uint32_t wa, uint32_t wb, half2_t s2, half2_t b2) {
+  const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const uint32_t w[2] = {wa, wb};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p = ((w[i >> 1] >> (8 * (i & 1))) & 0x00FF00FFu) | 0x64006400u;
+    const half2_t q = __builtin_bit_cast(half2_t, p) + m1024;
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool routed, const uint8_t** blob,
                                           int* Iinst, bool* missing) {
   PInst in = a.inst[ii];
@@ -88,14 +105,16 @@ __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool rou
 // owns 32 weight rows and all 128 tokens (up to four 32x32 MFMA tiles).
 // Each step's operands go global -> LDS by the buffer unit itself (LDS DMA,
 // no registers), three stages in flight: the activation tile (128 rows x
-// 128 B), every wave's int4 codes (one 16-byte piece per lane: lanes 0-31
-// hold the first 32 k of the step for their row, lanes 32-63 the second) and
-// its (scale, bias) words.  A wave dequantises its own codes straight into
-// the MFMA B operand, so each weight is dequantised once.  The k order inside
-// a step is (lane half, code word, nibble order) on both operands.
+// 128 B), every wave's codes (lanes 0-31 hold the first 32 k of the step for
+// their row, lanes 32-63 the second: one 16-byte piece per lane for 4-bit
+// codes, two for 8-bit) and its (scale, bias) words.  A wave dequantises its
+// own codes straight into the MFMA B operand, so each weight is dequantised
+// once.  The k order inside a step is (lane half, 8-input block, the
+// (0,4,1,5,2,6,3,7) order) on both operands.
 //
-// Synchronisation is explicit: every step issues the same six DMAs per wave,
-// waits until at most the next stage's six are in flight (s_waitcnt vmcnt),
+// Synchronisation is explicit: every step issues the same DMAs per wave (six
+// for 4-bit codes, seven for 8-bit), waits until at most the next stage's
+// are in flight (s_waitcnt vmcnt),
 // then meets the other waves at a bare s_barrier.  The DMA destinations are
 // passed as opaque LDS addresses, so the compiler adds no waits of its own
 // (a __syncthreads fence, or its alias tracking, would wait for every DMA in
@@ -103,10 +122,13 @@ __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool rou
 // clobber keep it from moving LDS accesses across the wait and barrier.
 constexpr int kKS = 64;                         // k per step
 constexpr int kStA = kPM * 128;                 // activation tile bytes
-constexpr int kStB = 4 * 1024;                  // codes, 1 KB per wave
 constexpr int kStS = 4 * 256;                   // (scale, bias), 256 B per wave
-constexpr int kStage = kStA + kStB + kStS;
-constexpr int kDmaPerStage = 6;                 // DMA instructions per wave per stage
+// per code width: 16-byte code DMAs per lane, codes bytes (1 KB per wave per
+// DMA), stage bytes and DMA instructions per wave per stage
+template <int BITS> constexpr int kCodeDma = BITS / 4;
+template <int BITS> constexpr int kStB = 4 * 1024 * kCodeDma<BITS>;
+template <int BITS> constexpr int kStage = kStA + kStB<BITS> + kStS;
+template <int BITS> constexpr int kDmaPerStage = 5 + kCodeDma<BITS>;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -149,13 +171,18 @@ __device__ __forceinline__ int a_pos(int r, int cc) { return r * 128 + 16 * (cc 
 //   rows: the matrix's output rows; row: this lane's weight row.
 // MT: live 32-token tiles of the chunk (a template so the inner loop has no
 // branches and LDS reads overlap the MFMAs).
-template <int MT>
+template <int MT, int BITS>
 __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2, rsrc_t rA, const uint32_t* a_vo,
                                           rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
                                           uint32_t row, int C, float16_t* acc) {
+  constexpr int ND = kCodeDma<BITS>;            // 16-byte code pieces per lane per step
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t b_vo = (h * rows + row) * 16, s_vo = row * 4;
+  // piece (ND h + j) of the step's 2 ND pieces of this lane's row
+  uint32_t b_vo[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) b_vo[j] = ((ND * h + j) * rows + row) * 16;
+  const uint32_t s_vo = row * 4;
   // Stages past the end read through a zero-size descriptor: no memory
   // traffic, zeros land in a stage nobody reads, and the count stays six.
   const rsrc_t rN = make_rsrc(nullptr, 0);
@@ -163,30 +190,42 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
     const bool live = s < C;
     const rsrc_t ra = live ? rA : rN, rb = live ? rB : rN;
     const uint32_t ao = __builtin_amdgcn_readfirstlane(s * 128);
-    const uint32_t co = __builtin_amdgcn_readfirstlane(codes_off + 2u * s * rows * 16);
+    const uint32_t co = __builtin_amdgcn_readfirstlane(codes_off + (uint32_t)(2 * ND) * s * rows * 16);
     const uint32_t so = __builtin_amdgcn_readfirstlane(sb_off + (uint32_t)s * rows * 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_opaque(st + (4 * wave + i) * 1024), 16, a_vo[i], ao, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + wave * 1024), 16, b_vo, co, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + kStB + wave * 256), 4, s_vo, so, 0, 0);
+#pragma unroll
+    for (int j = 0; j < ND; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + (ND * wave + j) * 1024), 16, b_vo[j], co,
+                                               0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + kStB<BITS> + wave * 256), 4, s_vo, so, 0, 0);
   };
   // One step on stage `st` while stage s+2 refills `nx` (the stage read in
   // the previous step).
   auto step = [&](int s, const uint8_t* st, uint8_t* nx) {
     // stage s landed for this wave (stage s+1 may be in flight) and this
     // wave's reads of the previous stage are done; then the block meets
-    stage_barrier<kDmaPerStage>();
+    stage_barrier<kDmaPerStage<BITS>>();
     issue(s + 2, nx);
-    const uint4 cw = *reinterpret_cast<const uint4*>(st + kStA + wave * 1024 + 16 * lane);
-    const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kStA + kStB + wave * 256 + 4 * (lane & 31));
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kStA + kStB<BITS> + wave * 256 + 4 * (lane & 31));
     const half2_t s2 = __builtin_bit_cast(half2_t, (sb & 0xFFFFu) * 0x10001u);
     const half2_t b2 = __builtin_bit_cast(half2_t, (sb >> 16) * 0x10001u);
     half8_t bv[4];
-    bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
-    bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
-    bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
-    bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+    if constexpr (BITS == 4) {
+      const uint4 cw = *reinterpret_cast<const uint4*>(st + kStA + wave * 1024 + 16 * lane);
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+    } else {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(st + kStA + (2 * wave) * 1024 + 16 * lane);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(st + kStA + (2 * wave + 1) * 1024 + 16 * lane);
+      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2));
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half8_t av[MT];
@@ -217,15 +256,16 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
   stage_barrier<0>();
 }
 
+template <int BITS>
 __device__ __forceinline__ void gemm_tiles(int n_tok, uint8_t* S0, uint8_t* S1, uint8_t* S2, rsrc_t rA,
                                            const uint32_t* a_vo,
                                            rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
                                            uint32_t row, int C, float16_t* acc) {
   switch ((n_tok + 31) >> 5) {
-    case 1: gemm_loop<1>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
-    case 2: gemm_loop<2>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
-    case 3: gemm_loop<3>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
-    default: gemm_loop<4>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 1: gemm_loop<1, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 2: gemm_loop<2, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 3: gemm_loop<3, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    default: gemm_loop<4, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
   }
 }
 
@@ -241,10 +281,15 @@ __device__ __forceinline__ bool xcd_item(long L, int nch, int nt, int* chunk, in
   return *chunk < nch;
 }
 
+template <int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gate_up_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage], S1[kStage], S2[kStage];
-  __shared__ __attribute__((aligned(16))) float xch[2][16][64];   // up tiles handed to gate waves, per mt
+  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage<BITS>], S1[kStage<BITS>], S2[kStage<BITS>];
   __shared__ int tok_s[kPM], hrow_s[kPM];
+  // up tiles handed to the gate waves after the GEMM, one m-tile at a time;
+  // they reuse stage 0 (no DMA is in flight and no wave reads the stages
+  // once the GEMM has ended)
+  static_assert(sizeof(float) * 2 * 16 * 64 <= kStage<BITS>, "exchange fits a stage");
+  float (*xch)[16][64] = reinterpret_cast<float (*)[16][64]>(S0);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
   const int ntR = a.I / 64, ntS = a.Ish / 64;
@@ -285,7 +330,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       hrow_s[tid] = h;
     }
     __syncthreads();
-    const BlobLayout L = blob_layout(a.d, Iinst);
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
     uint32_t a_vo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -300,8 +345,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
     const uint32_t mc = (uint32_t)(mat ? L.m[1].codes : L.m[0].codes);
     const uint32_t ms = (uint32_t)(mat ? L.m[1].sb : L.m[0].sb);
-    gemm_tiles(in.n, S0, S1, S2, rX, a_vo, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
-               (uint32_t)(o0 + colb + (lane & 31)), C, acc);
+    gemm_tiles<BITS>(in.n, S0, S1, S2, rX, a_vo, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
+                     (uint32_t)(o0 + colb + (lane & 31)), C, acc);
     // epilogue: up waves hand their tiles to the gate waves, one m-tile at a time
     const int mt_live = (in.n + 31) >> 5;
     bool ovf = false;
@@ -334,8 +379,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+template <int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_down_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage], S1[kStage], S2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage<BITS>], S1[kStage<BITS>], S2[kStage<BITS>];
   __shared__ int hrow_s[kPM], tok_s[kPM];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
@@ -370,7 +416,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       tok_s[tid] = t;
     }
     __syncthreads();
-    const BlobLayout L = blob_layout(a.d, Iinst);
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
     uint32_t a_vo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -383,8 +429,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-    gemm_tiles(in.n, S0, S1, S2, rH, a_vo, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
-               (uint32_t)L.m[2].sb, (uint32_t)a.d, (uint32_t)(n0 + 32 * wave + (lane & 31)), Iinst / kKS, acc);
+    gemm_tiles<BITS>(in.n, S0, S1, S2, rH, a_vo, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
+                     (uint32_t)L.m[2].sb, (uint32_t)a.d, (uint32_t)(n0 + 32 * wave + (lane & 31)), Iinst / kKS, acc);
     const int n = n0 + 32 * wave + (lane & 31);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -518,8 +564,10 @@ int prefill_launch(const FfnArgs& f, void* ws, size_t ws_bytes, hipStream_t s) {
   const int gu_grid = (int)(gu_items < 4096 ? gu_items : 4096);
   const int dn_grid = (int)(dn_items < 4096 ? dn_items : 4096);
   void* args[] = {&a};
-  MOE_HIP(hipLaunchKernel((void*)prefill_gate_up_kernel, dim3(gu_grid), dim3(256), args, 0, s));
-  MOE_HIP(hipLaunchKernel((void*)prefill_down_kernel, dim3(dn_grid), dim3(256), args, 0, s));
+  void* gu = f.bits == 8 ? (void*)prefill_gate_up_kernel<8> : (void*)prefill_gate_up_kernel<4>;
+  void* dn = f.bits == 8 ? (void*)prefill_down_kernel<8> : (void*)prefill_down_kernel<4>;
+  MOE_HIP(hipLaunchKernel(gu, dim3(gu_grid), dim3(256), args, 0, s));
+  MOE_HIP(hipLaunchKernel(dn, dim3(dn_grid), dim3(256), args, 0, s));
   return MOE_OK;
 }
 

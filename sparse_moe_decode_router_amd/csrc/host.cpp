@@ -24,7 +24,7 @@ int hip_fail(hipError_t e) {
 
 bool shape_ok(const moe_ffn_shape* sh) {
   return sh && sh->group == 64 && sh->d >= 64 && sh->I >= 64 && sh->d % 64 == 0 && sh->I % 64 == 0 &&
-         sh->d <= 16384 && sh->I <= 16384;
+         sh->d <= 16384 && sh->I <= 16384 && (sh->bits == 0 || sh->bits == 4 || sh->bits == 8);
 }
 
 int table_edit_launch(int32_t* table, const int32_t* experts, const int32_t* slots, int n,
@@ -52,36 +52,52 @@ extern "C" const char* moe_version(void) { return "libmoe355 0.1 gfx950"; }
 
 // ------------------------------------------------------------------ blobs
 extern "C" size_t moe_blob_bytes(const moe_ffn_shape* sh) {
-  return shape_ok(sh) ? blob_layout(sh->d, sh->I).bytes : 0;
+  return shape_ok(sh) ? blob_layout(sh->d, sh->I, shape_bits(sh)).bytes : 0;
 }
 extern "C" size_t moe_blob_stride(const moe_ffn_shape* sh) {
-  return shape_ok(sh) ? blob_layout(sh->d, sh->I).stride : 0;
+  return shape_ok(sh) ? blob_layout(sh->d, sh->I, shape_bits(sh)).stride : 0;
 }
 
-extern "C" int moe_pack_expert_int4(const moe_ffn_shape* sh, const uint8_t* const codes[3],
-                                    const uint16_t* const scales[3], const uint16_t* const biases[3],
-                                    void* out) {
+// Inside each 8 inputs, 8-bit codes are stored in the byte order
+// (0, 1, 4, 5, 2, 3, 6, 7): byte j of the block holds input kPerm8[j] (the
+// permutation is its own inverse).
+static const int kPerm8[8] = {0, 1, 4, 5, 2, 3, 6, 7};
+
+extern "C" int moe_pack_expert(const moe_ffn_shape* sh, const uint8_t* const codes[3],
+                               const uint16_t* const scales[3], const uint16_t* const biases[3],
+                               void* out) {
   if (!shape_ok(sh) || !codes || !scales || !biases || !out) return MOE_ERR_INVALID_ARG;
-  const BlobLayout L = blob_layout(sh->d, sh->I);
+  const int bits = shape_bits(sh);
+  const BlobLayout L = blob_layout(sh->d, sh->I, bits);
   const int outs[3] = {sh->I, sh->I, sh->d};
   const int ins[3] = {sh->d, sh->d, sh->I};
   uint8_t* blob = static_cast<uint8_t*>(out);
   for (int m = 0; m < 3; ++m) {
     if (!codes[m] || !scales[m] || !biases[m]) return MOE_ERR_INVALID_ARG;
     const size_t n = (size_t)outs[m] * ins[m];
-    for (size_t q = 0; q < n; ++q)
-      if (codes[m][q] > 15) return MOE_ERR_INVALID_ARG;
+    if (bits == 4)
+      for (size_t q = 0; q < n; ++q)
+        if (codes[m][q] > 15) return MOE_ERR_INVALID_ARG;
   }
   std::memset(blob, 0, L.stride);
   for (int m = 0; m < 3; ++m) {
     const int O = outs[m], N = ins[m];
     uint8_t* cd = blob + L.m[m].codes;
-    for (int c = 0; c < N / 32; ++c)
-      for (int o = 0; o < O; ++o) {
-        const uint8_t* src = codes[m] + (size_t)o * N + 32 * c;
-        uint8_t* dst = cd + ((size_t)c * O + o) * 16;
-        for (int b = 0; b < 16; ++b) dst[b] = (uint8_t)(src[2 * b] | (src[2 * b + 1] << 4));
-      }
+    if (bits == 4) {
+      for (int c = 0; c < N / 32; ++c)
+        for (int o = 0; o < O; ++o) {
+          const uint8_t* src = codes[m] + (size_t)o * N + 32 * c;
+          uint8_t* dst = cd + ((size_t)c * O + o) * 16;
+          for (int b = 0; b < 16; ++b) dst[b] = (uint8_t)(src[2 * b] | (src[2 * b + 1] << 4));
+        }
+    } else {
+      for (int c = 0; c < N / 16; ++c)
+        for (int o = 0; o < O; ++o) {
+          const uint8_t* src = codes[m] + (size_t)o * N + 16 * c;
+          uint8_t* dst = cd + ((size_t)c * O + o) * 16;
+          for (int b = 0; b < 16; ++b) dst[b] = src[(b & 8) + kPerm8[b & 7]];
+        }
+    }
     uint16_t* sb = reinterpret_cast<uint16_t*>(blob + L.m[m].sb);
     for (int g = 0; g < N / 64; ++g)
       for (int o = 0; o < O; ++o) {
@@ -92,10 +108,11 @@ extern "C" int moe_pack_expert_int4(const moe_ffn_shape* sh, const uint8_t* cons
   return MOE_OK;
 }
 
-extern "C" int moe_unpack_expert_int4(const moe_ffn_shape* sh, const void* in, uint8_t* const codes[3],
-                                      uint16_t* const scales[3], uint16_t* const biases[3]) {
+extern "C" int moe_unpack_expert(const moe_ffn_shape* sh, const void* in, uint8_t* const codes[3],
+                                 uint16_t* const scales[3], uint16_t* const biases[3]) {
   if (!shape_ok(sh) || !in || !codes || !scales || !biases) return MOE_ERR_INVALID_ARG;
-  const BlobLayout L = blob_layout(sh->d, sh->I);
+  const int bits = shape_bits(sh);
+  const BlobLayout L = blob_layout(sh->d, sh->I, bits);
   const int outs[3] = {sh->I, sh->I, sh->d};
   const int ins[3] = {sh->d, sh->d, sh->I};
   const uint8_t* blob = static_cast<const uint8_t*>(in);
@@ -103,15 +120,24 @@ extern "C" int moe_unpack_expert_int4(const moe_ffn_shape* sh, const void* in, u
     if (!codes[m] || !scales[m] || !biases[m]) return MOE_ERR_INVALID_ARG;
     const int O = outs[m], N = ins[m];
     const uint8_t* cd = blob + L.m[m].codes;
-    for (int c = 0; c < N / 32; ++c)
-      for (int o = 0; o < O; ++o) {
-        const uint8_t* src = cd + ((size_t)c * O + o) * 16;
-        uint8_t* dst = codes[m] + (size_t)o * N + 32 * c;
-        for (int b = 0; b < 16; ++b) {
-          dst[2 * b] = src[b] & 0xF;
-          dst[2 * b + 1] = src[b] >> 4;
+    if (bits == 4) {
+      for (int c = 0; c < N / 32; ++c)
+        for (int o = 0; o < O; ++o) {
+          const uint8_t* src = cd + ((size_t)c * O + o) * 16;
+          uint8_t* dst = codes[m] + (size_t)o * N + 32 * c;
+          for (int b = 0; b < 16; ++b) {
+            dst[2 * b] = src[b] & 0xF;
+            dst[2 * b + 1] = src[b] >> 4;
+          }
         }
-      }
+    } else {
+      for (int c = 0; c < N / 16; ++c)
+        for (int o = 0; o < O; ++o) {
+          const uint8_t* src = cd + ((size_t)c * O + o) * 16;
+          uint8_t* dst = codes[m] + (size_t)o * N + 16 * c;
+          for (int b = 0; b < 16; ++b) dst[(b & 8) + kPerm8[b & 7]] = src[b];
+        }
+    }
     const uint16_t* sb = reinterpret_cast<const uint16_t*>(blob + L.m[m].sb);
     for (int g = 0; g < N / 64; ++g)
       for (int o = 0; o < O; ++o) {
@@ -120,6 +146,19 @@ extern "C" int moe_unpack_expert_int4(const moe_ffn_shape* sh, const void* in, u
       }
   }
   return MOE_OK;
+}
+
+extern "C" int moe_pack_expert_int4(const moe_ffn_shape* sh, const uint8_t* const codes[3],
+                                    const uint16_t* const scales[3], const uint16_t* const biases[3],
+                                    void* out) {
+  if (!shape_ok(sh) || shape_bits(sh) != 4) return MOE_ERR_INVALID_ARG;
+  return moe_pack_expert(sh, codes, scales, biases, out);
+}
+
+extern "C" int moe_unpack_expert_int4(const moe_ffn_shape* sh, const void* in, uint8_t* const codes[3],
+                                      uint16_t* const scales[3], uint16_t* const biases[3]) {
+  if (!shape_ok(sh) || shape_bits(sh) != 4) return MOE_ERR_INVALID_ARG;
+  return moe_unpack_expert(sh, in, codes, scales, biases);
 }
 
 // -------------------------------------------------------- LFU + recency
@@ -248,7 +287,7 @@ extern "C" int moe_pool_create(int32_t E, int32_t n_slots, const moe_ffn_shape* 
   p->E = E;
   p->n_slots = n_slots;
   p->sh = *sh;
-  p->stride = blob_layout(sh->d, sh->I).stride;
+  p->stride = blob_layout(sh->d, sh->I, shape_bits(sh)).stride;
   p->lfu.E = E;
   p->lfu.n_slots = n_slots;
   p->lfu.count.assign(E, 0);
@@ -419,18 +458,19 @@ extern "C" size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh, const moe_ffn
 static int check_ffn(const moe_pool* pool, const moe_ffn_shape* sh, const moe_ffn_shape* ssh,
                      const void* shared_blob, int T, int k) {
   if (!pool || !shape_ok(sh) || !shape_ok(ssh) || sh->d != ssh->d) return MOE_ERR_INVALID_ARG;
-  if (pool->sh.d != sh->d || pool->sh.I != sh->I) return MOE_ERR_INVALID_ARG;
+  if (pool->sh.d != sh->d || pool->sh.I != sh->I || shape_bits(&pool->sh) != shape_bits(sh))
+    return MOE_ERR_INVALID_ARG;
   if (T < 0 || k < 1 || k > pool->E || !shared_blob || !aligned(shared_blob, 16)) return MOE_ERR_INVALID_ARG;
   if (sh->d > 8192) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-extern "C" int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh, const void* shared_blob,
-                                   const moe_ffn_shape* ssh, const uint16_t* x, int32_t T, int32_t k,
-                                   const int32_t* idx, const float* w, const float* sgate,
-                                   const int32_t* offsets, const int32_t* pair_ids, float* out,
-                                   float* partial, float* shared_out, int32_t path, void* ws,
-                                   size_t ws_bytes, hipStream_t s) {
+extern "C" int moe_expert_ffn(const moe_pool* pool, const moe_ffn_shape* sh, const void* shared_blob,
+                              const moe_ffn_shape* ssh, const uint16_t* x, int32_t T, int32_t k,
+                              const int32_t* idx, const float* w, const float* sgate,
+                              const int32_t* offsets, const int32_t* pair_ids, float* out,
+                              float* partial, float* shared_out, int32_t path, void* ws,
+                              size_t ws_bytes, hipStream_t s) {
   MOE_TRY(check_ffn(pool, sh, ssh, shared_blob, T, k));
   if (T == 0) return MOE_OK;
   path = resolve_path(path, T, k, pool->E);
@@ -438,6 +478,7 @@ extern "C" int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh
   FfnArgs a{};
   pool_view(pool, &a.pool);
   a.d = sh->d; a.I = sh->I; a.Ish = ssh->I;
+  a.bits = shape_bits(sh); a.bits_sh = shape_bits(ssh);
   a.shared_blob = static_cast<const uint8_t*>(shared_blob);
   a.x = x; a.xq = nullptr; a.xs = nullptr;
   a.T = T; a.k = k; a.idx = const_cast<int32_t*>(idx); a.w = const_cast<float*>(w);
@@ -453,6 +494,18 @@ extern "C" int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh
     return MOE_ERR_INVALID_ARG;
   }
   return ffn_launch(a, path, ws, ws_bytes, s);
+}
+
+extern "C" int moe_expert_ffn_int4(const moe_pool* pool, const moe_ffn_shape* sh, const void* shared_blob,
+                                   const moe_ffn_shape* ssh, const uint16_t* x, int32_t T, int32_t k,
+                                   const int32_t* idx, const float* w, const float* sgate,
+                                   const int32_t* offsets, const int32_t* pair_ids, float* out,
+                                   float* partial, float* shared_out, int32_t path, void* ws,
+                                   size_t ws_bytes, hipStream_t s) {
+  if (!shape_ok(sh) || !shape_ok(ssh) || shape_bits(sh) != 4 || shape_bits(ssh) != 4)
+    return MOE_ERR_INVALID_ARG;
+  return moe_expert_ffn(pool, sh, shared_blob, ssh, x, T, k, idx, w, sgate, offsets, pair_ids, out,
+                        partial, shared_out, path, ws, ws_bytes, s);
 }
 
 // ------------------------------------------------------------- whole layer
@@ -489,7 +542,8 @@ static int check_layer(const moe_layer_desc* L) {
   if (!L || !L->pool || !L->w_router_dev || !L->shared_blob_dev) return MOE_ERR_INVALID_ARG;
   if (!shape_ok(&L->sh) || !shape_ok(&L->shared_sh) || L->sh.d != L->shared_sh.d) return MOE_ERR_INVALID_ARG;
   if (L->E != L->pool->E || L->k < 1 || L->k > L->E) return MOE_ERR_INVALID_ARG;
-  if (L->pool->sh.d != L->sh.d || L->pool->sh.I != L->sh.I) return MOE_ERR_INVALID_ARG;
+  if (L->pool->sh.d != L->sh.d || L->pool->sh.I != L->sh.I || shape_bits(&L->pool->sh) != shape_bits(&L->sh))
+    return MOE_ERR_INVALID_ARG;
   if (L->sh.d > 8192) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -527,6 +581,7 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   FfnArgs a{};
   pool_view(L->pool, &a.pool);
   a.d = d; a.I = L->sh.I; a.Ish = L->shared_sh.I;
+  a.bits = shape_bits(&L->sh); a.bits_sh = shape_bits(&L->shared_sh);
   a.shared_blob = static_cast<const uint8_t*>(L->shared_blob_dev);
   a.x = x; a.xq = lw.r.xq; a.xs = lw.r.xs;
   a.T = T; a.k = L->k; a.idx = idx; a.w = w; a.sgate = sgate;

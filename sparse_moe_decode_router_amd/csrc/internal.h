@@ -26,7 +26,7 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // -------------------------------------------------------------- layout
 // Byte offsets of the six sections of an expert blob (see moe355.h).
 struct MatLayout {
-  uint64_t codes;   // [in/32][out][16]
+  uint64_t codes;   // [in/32][out][16] (4-bit) or [in/16][out][16] (8-bit)
   uint64_t sb;      // [in/64][out][2] fp16 (scale, bias)
 };
 struct BlobLayout {
@@ -34,14 +34,14 @@ struct BlobLayout {
   uint64_t bytes, stride;
 };
 
-__host__ __device__ inline BlobLayout blob_layout(int d, int I) {
+__host__ __device__ inline BlobLayout blob_layout(int d, int I, int bits) {
   BlobLayout L;
   uint64_t off = 0;
   const int outs[3] = {I, I, d};
   const int ins[3] = {d, d, I};
   for (int m = 0; m < 3; ++m) {
     L.m[m].codes = off;
-    off += (uint64_t)outs[m] * (uint64_t)ins[m] / 2;
+    off += (uint64_t)outs[m] * (uint64_t)ins[m] * (uint64_t)bits / 8;
     L.m[m].sb = off;
     off += (uint64_t)(ins[m] / 64) * (uint64_t)outs[m] * 4;
   }
@@ -51,6 +51,8 @@ __host__ __device__ inline BlobLayout blob_layout(int d, int I) {
 }
 
 bool shape_ok(const moe_ffn_shape* sh);
+// Code width of a valid shape (bits 0 reads as 4).
+inline int shape_bits(const moe_ffn_shape* sh) { return sh->bits == 8 ? 8 : 4; }
 
 // Device view of a pool, passed to kernels by value.
 struct PoolView {
@@ -108,6 +110,7 @@ int combine_launch(const float* partial, const float* shared_out, const float* w
 struct FfnArgs {
   PoolView pool;
   int d, I, Ish;
+  int bits, bits_sh;        // code width of the routed / shared experts (4 or 8)
   const uint8_t* shared_blob;
   const uint16_t* x;        // bf16 [T][d]
   const uint32_t* xq;       // [T][d/2]

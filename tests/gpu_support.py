@@ -24,9 +24,9 @@ class DeviceLayer:
         self.bias = None if self.bias_np is None else torch.from_numpy(self.bias_np).cuda()
         self.shared_raw = ms.shared_raw(cfg)
         self.shared_blob = torch.from_numpy(
-            moe.moe_pack_expert_int4(self.shared_raw, cfg.d, cfg.I_shared)).cuda()
+            moe.moe_pack_expert(self.shared_raw, cfg.d, cfg.I_shared, cfg.bits)).cuda()
         n_slots = cfg.E if n_slots is None else n_slots
-        self.pool = moe.Pool(cfg.E, n_slots, cfg.d, cfg.I)
+        self.pool = moe.Pool(cfg.E, n_slots, cfg.d, cfg.I, cfg.bits)
         if table is None:
             table = ms.slot_permutation(cfg) if n_slots == cfg.E else None
         self._raw = {}
@@ -50,7 +50,7 @@ class DeviceLayer:
         return self._raw[e]
 
     def blob(self, e: int) -> np.ndarray:
-        return self.moe.moe_pack_expert_int4(self.raw(e), self.cfg.d, self.cfg.I)
+        return self.moe.moe_pack_expert(self.raw(e), self.cfg.d, self.cfg.I, self.cfg.bits)
 
     def x(self, step: int, T=None):
         import torch

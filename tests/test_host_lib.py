@@ -60,9 +60,7 @@ def test_c_pack_matches_oracle_pack(name):
 
 def test_c_pack_golden_layout():
     for d, I, bits, nbytes, stride, codes, sbs in golden_io.blob_layout():
-        if bits != 4:
-            continue
-        assert moe.moe_blob_bytes(d, I) == nbytes and moe.moe_blob_stride(d, I) == stride
+        assert moe.moe_blob_bytes(d, I, bits) == nbytes and moe.moe_blob_stride(d, I, bits) == stride
         dims = oquant.mat_dims(d, I)
         for mat, row, col, val, off, byte in codes:
             raw = {m: {"codes": np.zeros(dims[m], np.uint8),
@@ -70,8 +68,50 @@ def test_c_pack_golden_layout():
                        "biases": np.zeros((dims[m][0], dims[m][1] // 64), np.float16)}
                    for m in oquant.MATS}
             raw[mat]["codes"][row, col] = val
-            blob = moe.moe_pack_expert_int4(raw, d, I)
+            blob = moe.moe_pack_expert(raw, d, I, bits)
             assert np.nonzero(blob)[0].tolist() == [off] and blob[off] == byte
+            back = moe.moe_unpack_expert(blob, d, I, bits)
+            assert back[mat]["codes"][row, col] == val and np.count_nonzero(back[mat]["codes"]) == 1
+
+
+@pytest.mark.parametrize("name", ["tiny_int8", "decode80b_int8"])
+def test_c_pack_int8_matches_oracle_pack(name):
+    cfg = ms.CONFIGS[name]
+    for e in (0, 5):
+        raw = ms.expert_raw(cfg, e)
+        a = moe.moe_pack_expert(raw, cfg.d, cfg.I, 8)
+        b = oquant.pack_expert(raw, cfg.d, cfg.I, 8)
+        assert a.size == oquant.blob_stride(cfg.d, cfg.I, 8) and np.array_equal(a, b)
+        back = moe.moe_unpack_expert(a, cfg.d, cfg.I, 8)
+        for m in oquant.MATS:
+            for f in ("codes", "scales", "biases"):
+                assert np.array_equal(back[m][f], raw[m][f])
+    assert moe.moe_blob_bytes(2048, 512, 8) == 3342336
+
+
+def test_c_pack_width_checks():
+    """Code width must be 4 or 8 (0 reads as 4); the int4-only entry points
+    refuse 8-bit shapes; the generic packer takes 4-bit raws at bits=4."""
+    assert moe.moe_blob_bytes(2048, 512, 0) == moe.moe_blob_bytes(2048, 512, 4) == 1769472
+    assert moe.moe_blob_bytes(2048, 512, 5) == 0 and moe.moe_blob_stride(2048, 512, 16) == 0
+    cfg = ms.CONFIGS["tiny_int8"]
+    raw = ms.expert_raw(cfg, 1)
+    out = np.empty(moe.moe_blob_stride(cfg.d, cfg.I, 8), np.uint8)
+    cp, sp, bp = (C.c_void_p * 3)(), (C.c_void_p * 3)(), (C.c_void_p * 3)()
+    keep = []
+    for m, name in enumerate(oquant.MATS):
+        c = np.ascontiguousarray(raw[name]["codes"])
+        s = np.ascontiguousarray(raw[name]["scales"]).view(np.uint16)
+        b = np.ascontiguousarray(raw[name]["biases"]).view(np.uint16)
+        keep += [c, s, b]
+        cp[m], sp[m], bp[m] = c.ctypes.data, s.ctypes.data, b.ctypes.data
+    st = moe._lib.moe_pack_expert_int4(C.byref(moe.shape(cfg.d, cfg.I, 8)), cp, sp, bp, out.ctypes.data)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    # 8-bit codes above 15 cannot go into a 4-bit blob
+    with pytest.raises(moe.MoeError):
+        moe.moe_pack_expert(raw, cfg.d, cfg.I, 4)
+    raw4 = ms.expert_raw(ms.CONFIGS["tiny"], 1)
+    assert np.array_equal(moe.moe_pack_expert(raw4, 256, 64, 4), moe.moe_pack_expert_int4(raw4, 256, 64))
 
 
 def test_c_pack_rejects_bad_codes_and_shapes():
