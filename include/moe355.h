@@ -62,10 +62,10 @@ enum {
 
 /* Flags for moe_expert_ffn / moe_layer_forward. */
 enum {
-  MOE_PATH_AUTO = 0,       /* choose by tokens per expert                     */
+  MOE_PATH_AUTO = 0,       /* choose by token count (see moe_expert_ffn)      */
   MOE_PATH_DECODE = 1,     /* per-(token, rank) GEMV, fused combine (T <= 8)  */
   MOE_PATH_BATCHED = 2,    /* bucketed GEMV, partials + combine               */
-  MOE_PATH_PREFILL = 3     /* bucketed bf16 MFMA grouped GEMM + combine       */
+  MOE_PATH_PREFILL = 3     /* bucketed fp16 MFMA grouped GEMM + combine       */
 };
 
 /* Expert FFN shape.  group must be 64; d and I multiples of 64. */
@@ -250,8 +250,10 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
  *                     SwiGLU intermediate in fp16 (|v| <= 65504, else the
  *                     pool error word reports MOE_ERR_UNSUPPORTED), fp32
  *                     accumulate.
- *   MOE_PATH_AUTO   : DECODE for T <= 4, BATCHED for T*k/E < 16, else PREFILL
- *                     (the caller must then supply every buffer).
+ *   MOE_PATH_AUTO   : DECODE for T <= 8 (and T*(k+1) <= 2048), else PREFILL,
+ *                     or BATCHED if d is not a multiple of 128 (the caller
+ *                     must then supply every buffer).  PREFILL's fp16
+ *                     range applies to AUTO calls above 8 tokens.
  * A selected expert with slot_table[e] < 0 sets the pool's error word and
  * contributes zero. */
 size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh,

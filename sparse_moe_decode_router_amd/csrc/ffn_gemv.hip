@@ -878,11 +878,15 @@ GemvSet gemv_set() {
 
 }  // namespace
 
-int resolve_path(int path, int T, int k, int E) {
+// AUTO: the per-token decode GEMVs up to 8 tokens; beyond that the grouped
+// GEMMs on the matrix cores, which measured faster than the bucketed GEMVs
+// from 2 tokens up (80B shape, 4- and 8-bit experts) even with a handful of
+// tokens per bucket; the bucketed GEMVs where the GEMM tiles do not fit
+// (d not a multiple of 128).
+int resolve_path(int path, int T, int d, int k, int E) {
   if (path != MOE_PATH_AUTO) return path;
-  if (T <= 4) return MOE_PATH_DECODE;
-  if ((long)T * k < 16L * E) return MOE_PATH_BATCHED;   // < 16 tokens per expert
-  return MOE_PATH_PREFILL;
+  if (T <= 8 && (long)T * (k + 1) <= 2048) return MOE_PATH_DECODE;
+  return d % 128 == 0 ? MOE_PATH_PREFILL : MOE_PATH_BATCHED;
 }
 
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {

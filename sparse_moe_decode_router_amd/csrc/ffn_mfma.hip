@@ -186,9 +186,12 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
   // Stages past the end read through a zero-size descriptor: no memory
   // traffic, zeros land in a stage nobody reads, and the count stays six.
   const rsrc_t rN = make_rsrc(nullptr, 0);
+  // Wave w fetches activation rows 32w..32w+31 (tile w): the waves past the
+  // live tiles fetch through the zero-size descriptor as well.
+  const bool a_live = wave < MT;
   auto issue = [&](int s, uint8_t* st) {
     const bool live = s < C;
-    const rsrc_t ra = live ? rA : rN, rb = live ? rB : rN;
+    const rsrc_t ra = (live && a_live) ? rA : rN, rb = live ? rB : rN;
     const uint32_t ao = __builtin_amdgcn_readfirstlane(s * 128);
     const uint32_t co = __builtin_amdgcn_readfirstlane(codes_off + (uint32_t)(2 * ND) * s * rows * 16);
     const uint32_t so = __builtin_amdgcn_readfirstlane(sb_off + (uint32_t)s * rows * 4);

@@ -451,7 +451,7 @@ extern "C" int moe_pool_reset_usage(moe_pool* p, hipStream_t s) {
 extern "C" size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh, const moe_ffn_shape* ssh, int32_t T,
                                           int32_t k, int32_t E, int32_t path) {
   if (!shape_ok(sh) || !shape_ok(ssh) || sh->d != ssh->d || T < 0 || k < 1 || E < 1) return 0;
-  path = resolve_path(path, T, k, E);
+  path = resolve_path(path, T, sh->d, k, E);
   return ffn_ws_bytes(sh->d, sh->I, ssh->I, T, k, E, path);
 }
 
@@ -473,7 +473,7 @@ extern "C" int moe_expert_ffn(const moe_pool* pool, const moe_ffn_shape* sh, con
                               size_t ws_bytes, hipStream_t s) {
   MOE_TRY(check_ffn(pool, sh, ssh, shared_blob, T, k));
   if (T == 0) return MOE_OK;
-  path = resolve_path(path, T, k, pool->E);
+  path = resolve_path(path, T, sh->d, k, pool->E);
   MOE_CHECK(x && idx && ws && aligned(x, 16) && aligned(ws, 256));
   FfnArgs a{};
   pool_view(pool, &a.pool);
@@ -550,7 +550,7 @@ static int check_layer(const moe_layer_desc* L) {
 
 extern "C" size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int32_t T, int32_t path) {
   if (check_layer(L) != MOE_OK || T < 0) return 0;
-  path = resolve_path(path, T, L->k, L->E);
+  path = resolve_path(path, T, L->sh.d, L->k, L->E);
   Carver c(nullptr, (size_t)-1);
   LayerWs w;
   carve_layer(c, L, T, path, &w);
@@ -565,7 +565,7 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   if (T == 0) return MOE_OK;
   MOE_CHECK(x && y && idx && w && sgate && ws);
   MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
-  path = resolve_path(path, T, L->k, L->E);
+  path = resolve_path(path, T, L->sh.d, L->k, L->E);
   if (path == MOE_PATH_DECODE) MOE_CHECK(T <= 8 && (long)T * (L->k + 1) <= 2048);
   Carver c(ws, ws_bytes);
   LayerWs lw;

@@ -132,6 +132,6 @@ size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
 size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E);
 int prefill_launch(const FfnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 int ffn_launch(const FfnArgs& a, int path, void* ws, size_t ws_bytes, hipStream_t s);
-int resolve_path(int path, int T, int k, int E);
+int resolve_path(int path, int T, int d, int k, int E);
 
 }  // namespace moe

@@ -350,3 +350,22 @@ def test_batched_small_d_partial_row_block():
     cfg = ms.scaled(TINY, d=192, I=64, I_shared=64, T=12, E=16, k=3)
     L = DeviceLayer(cfg)
     _check_layer_step(L, 2, path=moe.MOE_PATH_BATCHED, T=12)
+
+
+def test_auto_path_choice(l80):
+    """MOE_PATH_AUTO: the decode GEMVs up to 8 tokens, the grouped GEMMs
+    beyond (bit-identical to the explicit paths), the bucketed GEMVs when d
+    is not a multiple of 128."""
+    for T, path in ((8, moe.MOE_PATH_DECODE), (9, moe.MOE_PATH_PREFILL), (64, moe.MOE_PATH_PREFILL)):
+        _, x = l80.x(30 + T, T)
+        ya, ia, _, _ = moe.moe_layer_forward(l80.layer, x)
+        ye, ie, _, _ = moe.moe_layer_forward(l80.layer, x, path=path)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(ia), _np(ie)) and np.array_equal(_np(ya), _np(ye)), T
+    cfg = ms.scaled(TINY, d=192, I=64, I_shared=64, T=12, E=16, k=3)
+    L = DeviceLayer(cfg)
+    _, x = L.x(1, 12)
+    ya, _, _, _ = moe.moe_layer_forward(L.layer, x)
+    ye, _, _, _ = moe.moe_layer_forward(L.layer, x, path=moe.MOE_PATH_BATCHED)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(ya), _np(ye))
