@@ -49,7 +49,8 @@ __device__ void scatter_block(int key, bool valid, int i, int E, uint8_t* wc, Ba
 __global__ __launch_bounds__(kB) void bucket_single_kernel(const int32_t* __restrict__ idx, int n, int E,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ pair_ids) {
+                                                           int32_t* __restrict__ pair_ids,
+                                                           uint32_t* __restrict__ usage) {
   extern __shared__ int lds[];          // cnt[E] | scan[1024] | wc[kW][E] bytes
   int* cnt = lds;
   int* scan = lds + E;
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(kB) void bucket_single_kernel(const int32_t* __rest
     counts[tid] = c;
     offsets[tid] = scan[tid] - c;
     cnt[tid] = scan[tid] - c;           // reuse as base
+    if (usage && c > 0) atomicAdd(&usage[tid], (uint32_t)c);
   }
   if (tid == 0) offsets[E] = scan[kB - 1];
   __syncthreads();
@@ -99,16 +101,27 @@ __global__ __launch_bounds__(kB) void bucket_hist_kernel(const int32_t* __restri
 }
 
 // Exclusive scan of bc in (expert, block) order -> base; counts, offsets.
+// Each thread owns a contiguous run of bc, read kU entries at a time with
+// all loads of a batch in flight (one memory latency per batch, not per
+// entry).  usage (optional): usage[e] += counts[e], one atomic per expert.
+constexpr int kU = 16;
 __global__ __launch_bounds__(kB) void bucket_scan_kernel(int32_t* __restrict__ bc, int E, int nb,
                                                          int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets) {
+                                                         int32_t* __restrict__ offsets,
+                                                         uint32_t* __restrict__ usage) {
   __shared__ int part[kB];
   const int tid = threadIdx.x;
   const long N = (long)E * nb;
   const long per = (N + kB - 1) / kB;
   const long lo = tid * per, hi = lo + per < N ? lo + per : N;
   int s = 0;
-  for (long q = lo; q < hi; ++q) s += bc[q];
+  for (long q0 = lo; q0 < hi; q0 += kU) {
+    int v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = q0 + u < hi ? bc[q0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) s += v[u];
+  }
   part[tid] = s;
   __syncthreads();
   for (int off = 1; off < kB; off <<= 1) {
@@ -118,10 +131,15 @@ __global__ __launch_bounds__(kB) void bucket_scan_kernel(int32_t* __restrict__ b
     __syncthreads();
   }
   int run = part[tid] - s;
-  for (long q = lo; q < hi; ++q) {
-    const int v = bc[q];
-    bc[q] = run;
-    run += v;
+  for (long q0 = lo; q0 < hi; q0 += kU) {
+    int v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = q0 + u < hi ? bc[q0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (q0 + u < hi) bc[q0 + u] = run;
+      run += v[u];
+    }
   }
   __syncthreads();
   // counts/offsets per expert
@@ -130,6 +148,7 @@ __global__ __launch_bounds__(kB) void bucket_scan_kernel(int32_t* __restrict__ b
     const int next = (e + 1 < E) ? bc[(size_t)(e + 1) * nb] : part[kB - 1];
     offsets[e] = first;
     counts[e] = next - first;
+    if (usage && next > first) atomicAdd(&usage[e], (uint32_t)(next - first));
   }
   if (tid == 0) offsets[E] = part[kB - 1];
 }
@@ -154,11 +173,11 @@ size_t bucket_ws_bytes(int T, int k, int E) {
 }
 
 int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
-                  int32_t* pair_ids, void* ws, size_t ws_bytes, hipStream_t s) {
+                  int32_t* pair_ids, void* ws, size_t ws_bytes, hipStream_t s, uint32_t* usage) {
   const long n = (long)T * k;
   if (n <= kB) {
     const size_t lds = ((size_t)E + kB) * 4 + (size_t)kW * E;
-    bucket_single_kernel<<<1, kB, lds, s>>>(idx, (int)n, E, counts, offsets, pair_ids);
+    bucket_single_kernel<<<1, kB, lds, s>>>(idx, (int)n, E, counts, offsets, pair_ids, usage);
     MOE_HIP(hipGetLastError());
     return MOE_OK;
   }
@@ -167,7 +186,7 @@ int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts, int3
   int32_t* bc = (int32_t*)ws;
   bucket_hist_kernel<<<nb, kB, (size_t)E * 4, s>>>(idx, (int)n, E, nb, bc);
   MOE_HIP(hipGetLastError());
-  bucket_scan_kernel<<<1, kB, 0, s>>>(bc, E, nb, counts, offsets);
+  bucket_scan_kernel<<<1, kB, 0, s>>>(bc, E, nb, counts, offsets, usage);
   MOE_HIP(hipGetLastError());
   bucket_scatter_kernel<<<nb, kB, (size_t)kW * E, s>>>(idx, (int)n, E, nb, bc, pair_ids);
   MOE_HIP(hipGetLastError());
@@ -195,5 +214,5 @@ extern "C" int moe_bucket_tokens(const int32_t* idx, int32_t T, int32_t k, int32
     MOE_HIP(hipMemsetAsync(offsets, 0, (size_t)(E + 1) * 4, s));
     return MOE_OK;
   }
-  return bucket_launch(idx, T, k, E, counts, offsets, pair_ids, ws, ws_bytes, s);
+  return bucket_launch(idx, T, k, E, counts, offsets, pair_ids, ws, ws_bytes, s, nullptr);
 }

@@ -19,7 +19,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (id >= (long)T * d4) return;
   const int t = (int)(id / d4), c = (int)(id % d4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = 0; r < k; ++r) {
+  // up to kMaxK ranks: every load in flight before the (rank-order) sum
+  constexpr int kMaxK = 16;
+  float4 pv[kMaxK];
+  float wv[kMaxK];
+#pragma unroll
+  for (int r = 0; r < kMaxK; ++r) {
+    if (r < k) {
+      wv[r] = w[(size_t)t * k + r];
+      pv[r] = reinterpret_cast<const float4*>(partial + ((size_t)t * k + r) * d)[c];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxK; ++r) {
+    if (r < k) {
+      acc.x += wv[r] * pv[r].x; acc.y += wv[r] * pv[r].y; acc.z += wv[r] * pv[r].z; acc.w += wv[r] * pv[r].w;
+    }
+  }
+  for (int r = kMaxK; r < k; ++r) {
     const float wr = w[(size_t)t * k + r];
     const float4 p = reinterpret_cast<const float4*>(partial + ((size_t)t * k + r) * d)[c];
     acc.x += wr * p.x; acc.y += wr * p.y; acc.z += wr * p.z; acc.w += wr * p.w;

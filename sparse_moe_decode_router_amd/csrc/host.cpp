@@ -573,10 +573,12 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   const int d = L->sh.d;
   if (path == MOE_PATH_DECODE) {
     // logits here; the decode FFN selects the experts in-kernel
-    MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s));
+    MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s, true));
   } else {
+    // usage is counted from the buckets below (one atomic per expert); the
+    // bf16 activation pairs are prepared only for the bucketed GEMVs
     MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, L->k, idx, w, sgate,
-                          L->usage_dev, lw.r, s));
+                          nullptr, lw.r, s, path == MOE_PATH_BATCHED));
   }
   FfnArgs a{};
   pool_view(L->pool, &a.pool);
@@ -593,7 +595,7 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
     return ffn_launch(a, path, lw.ffn_ws, lw.ffn_bytes, s);
   }
   MOE_TRY(bucket_launch(idx, T, L->k, L->E, lw.counts, lw.offsets, lw.pair_ids, lw.bucket_ws,
-                        lw.bucket_bytes, s));
+                        lw.bucket_bytes, s, L->usage_dev));
   a.offsets = lw.offsets; a.pair_ids = lw.pair_ids;
   a.partial = lw.partial; a.shared_out = lw.shared_out;
   MOE_TRY(ffn_launch(a, path, lw.ffn_ws, lw.ffn_bytes, s));

@@ -89,18 +89,20 @@ struct RouterWs {
 };
 size_t router_ws_bytes(int T, int d, int E);
 bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws);
+// prep_x: also fill ws.xq / ws.xs for T > 8 (T <= 8 always does, in-kernel)
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias,
                   int E, int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
-                  const RouterWs& ws, hipStream_t s);
+                  const RouterWs& ws, hipStream_t s, bool prep_x);
 // logits [T][E+1] (+ xq/xs) only; the decode FFN selects in-kernel
 int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
-                         const RouterWs& ws, hipStream_t s);
+                         const RouterWs& ws, hipStream_t s, bool prep_x);
 int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx,
                 float* w, float* sgate, uint32_t* usage, hipStream_t s);
 
+// usage (optional): usage[e] += the pairs bucketed to e (one atomic per expert)
 int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts,
                   int32_t* offsets, int32_t* pair_ids, void* ws, size_t ws_bytes,
-                  hipStream_t s);
+                  hipStream_t s, uint32_t* usage);
 size_t bucket_ws_bytes(int T, int k, int E);
 
 int combine_launch(const float* partial, const float* shared_out, const float* w,

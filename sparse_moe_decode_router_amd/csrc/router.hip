@@ -273,7 +273,7 @@ bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws) {
 }
 
 int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E, const RouterWs& ws,
-                         hipStream_t s) {
+                         hipStream_t s, bool prep_x) {
   if (T == 0) return MOE_OK;
   if (T <= 8) {
     DecodeArgs a{x, T, d, W, E, ws.logits, ws.xq, ws.xs};
@@ -283,7 +283,7 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
     MOE_HIP(hipLaunchKernel(fn, dim3(E + 1), dim3(kRouterThreads), args, 0, s));
     return MOE_OK;
   }
-  MOE_TRY(xprep_launch(x, T, d, ws.xq, ws.xs, s));
+  if (prep_x) MOE_TRY(xprep_launch(x, T, d, ws.xq, ws.xs, s));
   const int R = E + 1, S = router_splits(T, d, E);
   const long nW = (long)R * d;
   router_split_kernel<<<(unsigned)((nW + 255) / 256), 256, 0, s>>>(W, nW, ws.wsplit);
@@ -313,8 +313,8 @@ int topk_launch(const float* logits, const float* bias, int T, int d, int E, int
 
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias, int E,
                   int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
-                  const RouterWs& ws, hipStream_t s) {
-  MOE_TRY(router_logits_launch(x, T, d, W, E, ws, s));
+                  const RouterWs& ws, hipStream_t s, bool prep_x) {
+  MOE_TRY(router_logits_launch(x, T, d, W, E, ws, s, prep_x));
   return topk_launch(ws.logits, bias, T, d, E, k, idx, w, sgate, usage, s);
 }
 
@@ -346,5 +346,5 @@ extern "C" int moe_router_topk(const uint16_t* x, int32_t T, int32_t d, const fl
   Carver c(ws, ws_bytes);
   RouterWs rw;
   if (!router_ws_carve(c, T, d, E, &rw)) return MOE_ERR_INVALID_ARG;
-  return router_launch(x, T, d, W, bias, E, k, idx, w, sgate, usage, rw, s);
+  return router_launch(x, T, d, W, bias, E, k, idx, w, sgate, usage, rw, s, false);
 }

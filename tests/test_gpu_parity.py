@@ -369,3 +369,19 @@ def test_auto_path_choice(l80):
     ye, _, _, _ = moe.moe_layer_forward(L.layer, x, path=moe.MOE_PATH_BATCHED)
     torch.cuda.synchronize()
     assert np.array_equal(_np(ya), _np(ye))
+
+
+@pytest.mark.parametrize("path", ["batched", "prefill"])
+def test_usage_counters_bucketed_paths(l80, path):
+    """On the bucketed paths the usage counters are added from the bucket
+    counts: the same totals as one count per selection."""
+    p = moe.MOE_PATH_BATCHED if path == "batched" else moe.MOE_PATH_PREFILL
+    l80.pool.reset_usage()
+    tot = np.zeros(l80.cfg.E, np.int64)
+    for step, T in ((40, 64), (41, 9), (42, 200)):
+        _, x = l80.x(step, T)
+        _, idx, _, _ = moe.moe_layer_forward(l80.layer, x, path=p)
+        torch.cuda.synchronize()
+        tot += np.bincount(_np(idx).ravel(), minlength=l80.cfg.E)
+    _, usage = l80.pool.read_state()
+    assert np.array_equal(usage.astype(np.int64), tot)
