@@ -15,7 +15,8 @@ weights ~ N(0, 0.02) in fp32, codes uniform on 0..15, scales ~ U[0.002, 0.02]
 rounded to fp16, bias = -8 * scale).  8-bit experts (the pages' kernels also
 cover MLX affine int8) draw codes uniform on 0..255, scales U[0.002, 0.02]/16
 rounded to fp16 and bias = -128 * scale, so their weights span the same range
-as the 4-bit ones.
+as the 4-bit ones.  f32 experts (unquantised) draw weights ~ N(0, 0.05) in
+fp32, about the spread of the 4-bit weights.
 
 Every array comes from its own counter-keyed numpy PCG64 stream
 (``default_rng([seed, component, index])``) so that any expert or any decode
@@ -55,7 +56,7 @@ class LayerConfig:
     alpha: float      # Zipf logit-offset scale (0 = unbiased router)
     seed: int
     permute_slots: bool = True
-    bits: int = 4     # code width of routed and shared experts (4 or 8)
+    bits: int = 4     # code width of routed and shared experts (4, 8; 32 = fp32 weights)
 
     @property
     def group(self) -> int:
@@ -100,6 +101,16 @@ CONFIGS: Dict[str, LayerConfig] = {
     "prefill80b_int8": LayerConfig("prefill80b_int8", T=4096, d=2048, E=512, k=10,
                                    I=512, I_shared=512, n_slots=512, steps=1,
                                    alpha=0.0, seed=1104, bits=8),
+    # and with unquantised fp32 experts
+    "tiny_f32": LayerConfig("tiny_f32", T=4, d=256, E=16, k=2, I=64, I_shared=64,
+                            n_slots=16, steps=8, alpha=0.0, seed=1200,
+                            permute_slots=False, bits=32),
+    "decode80b_f32": LayerConfig("decode80b_f32", T=1, d=2048, E=512, k=10, I=512,
+                                 I_shared=512, n_slots=512, steps=1000,
+                                 alpha=ZIPF_ALPHA, seed=1202, bits=32),
+    "batch80b_f32": LayerConfig("batch80b_f32", T=64, d=2048, E=512, k=10, I=512,
+                                I_shared=512, n_slots=512, steps=100,
+                                alpha=ZIPF_ALPHA, seed=1203, bits=32),
 }
 
 
@@ -157,6 +168,8 @@ def _matrix(g: np.random.Generator, out: int, inp: int, bits: int = 4):
         codes = g.integers(0, 256, size=(out, inp), dtype=np.uint8)
         sc = (g.uniform(0.002, 0.02, size=(out, inp // GROUP)) / 16).astype(np.float16)
         bi = (np.float16(-128.0) * sc).astype(np.float16)  # exact in fp16
+    elif bits == 32:
+        return {"weights": (g.standard_normal((out, inp), dtype=np.float32) * np.float32(0.05)).astype(np.float32)}
     else:
         raise ValueError(f"bits must be 4 or 8, not {bits}")
     return {"codes": codes, "scales": sc, "biases": bi}
@@ -165,7 +178,7 @@ def _matrix(g: np.random.Generator, out: int, inp: int, bits: int = 4):
 def expert_raw(cfg: LayerConfig, e: int, I: Optional[int] = None,
                component: int = _C_EXPERT) -> Dict[str, Dict[str, np.ndarray]]:
     """Raw int4 / int8 (cfg.bits) weights of one expert, MLX orientation
-    [out][in] / [out][in/64].
+    [out][in] / [out][in/64] (fp32 [out][in] for cfg.bits == 32).
 
     gate, up: out = I, in = d.  down: out = d, in = I.
     """

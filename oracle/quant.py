@@ -27,6 +27,11 @@ bytes, one code per byte; inside every 8 consecutive inputs the bytes hold
 inputs (0, 1, 4, 5, 2, 3, 6, 7) of the block, so byte pairs (0, 2) and
 (1, 3) of each 32-bit word are the input pairs (i, i+4) the 4-bit layout
 forms from nibbles i and i+4.  blob bytes = 51/16 * d * I.
+
+f32 experts (unquantised; the pages validate every layer in f32 as well as
+int4 form, correctness section): a raw matrix is {"weights": fp32 [out, in]}
+and the blob holds gate, up, down as row-major fp32 [out][in] one after the
+other (no scale/bias sections); blob bytes = 12 * d * I.
 """
 from __future__ import annotations
 
@@ -36,12 +41,15 @@ GROUP = 64
 CHUNK = 32                   # inputs per 16-byte piece, 4-bit
 CHUNK8 = 16                  # inputs per 16-byte piece, 8-bit
 MATS = ("gate", "up", "down")
-BITS = (4, 8)
+BITS = (4, 8, 32)            # 32: unquantised fp32 weights
 PERM8 = np.array([0, 1, 4, 5, 2, 3, 6, 7])   # byte j of an 8-input block holds input PERM8[j]
 
 
 def dequant(m) -> np.ndarray:
-    """fp64 [out, in] from a raw matrix dict {codes, scales, biases}."""
+    """fp64 [out, in] from a raw matrix dict {codes, scales, biases} (or the
+    weights themselves for an f32 matrix {weights})."""
+    if "weights" in m:
+        return np.asarray(m["weights"], dtype=np.float32).astype(np.float64)
     q = np.asarray(m["codes"], dtype=np.float64)
     s = np.repeat(np.asarray(m["scales"], dtype=np.float64), GROUP, axis=1)
     b = np.repeat(np.asarray(m["biases"], dtype=np.float64), GROUP, axis=1)
@@ -53,7 +61,10 @@ def mat_dims(d: int, I: int):
 
 
 def section_bytes(out: int, inp: int, bits: int = 4):
+    """(codes or weights bytes, scale/bias bytes) of one matrix."""
     assert bits in BITS
+    if bits == 32:
+        return out * inp * 4, 0
     return out * inp * bits // 8, (inp // GROUP) * out * 4
 
 
@@ -113,6 +124,9 @@ def pack_expert(raw, d: int, I: int, bits: int = 4) -> np.ndarray:
     parts = []
     for name in MATS:
         m = raw[name]
+        if bits == 32:
+            parts.append(np.ascontiguousarray(m["weights"], dtype=np.float32).view(np.uint8).ravel())
+            continue
         assert int(np.max(m["codes"])) < (1 << bits)
         parts.append(_pack_codes(m["codes"]) if bits == 4 else _pack_codes8(m["codes"]))
         parts.append(_pack_sb(m["scales"], m["biases"]))
@@ -129,6 +143,11 @@ def unpack_expert(blob: np.ndarray, d: int, I: int, bits: int = 4):
     raw = {}
     for name, (o, i) in mat_dims(d, I).items():
         cb, sbb = section_bytes(o, i, bits)
+        if bits == 32:
+            w = np.ascontiguousarray(blob[off:off + cb]).view(np.float32).reshape(o, i).copy()
+            off += cb
+            raw[name] = {"weights": w}
+            continue
         unpack = _unpack_codes if bits == 4 else _unpack_codes8
         codes = unpack(blob[off:off + cb], o, i)
         off += cb

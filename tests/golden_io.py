@@ -36,7 +36,8 @@ def lfu_traces():
 
 
 def blob_layout():
-    """[(d, I, bits, bytes, stride, codes[(mat,row,col,val,off,byte)], sbs[(mat,row,g,soff,boff)])]."""
+    """[(d, I, bits, bytes, stride, codes[(mat,row,col,val,off,byte)], sbs[(mat,row,g,soff,boff)],
+    weights[(mat,row,col,value,off,u32)])]."""
     out = []
     cur = None
     for line in _lines("blob_layout.txt"):
@@ -44,11 +45,13 @@ def blob_layout():
         if t[0] == "shape":
             kv = dict(a.split("=") for a in t[1:])
             cur = (int(kv["d"]), int(kv["I"]), int(kv.get("bits", 4)), int(kv["bytes"]),
-                   int(kv["stride"]), [], [])
+                   int(kv["stride"]), [], [], [])
         elif t[0] == "end":
             out.append(cur)
         elif t[0] == "code":
             cur[5].append((t[1], int(t[2]), int(t[3]), int(t[4]), int(t[6]), int(t[7], 16)))
         elif t[0] == "sb":
             cur[6].append((t[1], int(t[2]), int(t[3]), int(t[5]), int(t[6])))
+        elif t[0] == "weight":
+            cur[7].append((t[1], int(t[2]), int(t[3]), float(t[4]), int(t[6]), int(t[7], 16)))
     return out

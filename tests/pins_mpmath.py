@@ -22,13 +22,15 @@ def _bf16(bits):
 
 
 def _w(m, o, j):
+    if "weights" in m:
+        return mp.mpf(float(m["weights"][o, j]))
     s = mp.mpf(float(m["scales"][o, j // 64]))
     b = mp.mpf(float(m["biases"][o, j // 64]))
     return s * int(m["codes"][o, j]) + b
 
 
 def _matvec(m, v):
-    out, inp = m["codes"].shape
+    out, inp = (m["weights"] if "weights" in m else m["codes"]).shape
     return [mp.fsum(_w(m, o, j) * v[j] for j in range(inp)) for o in range(out)]
 
 

@@ -59,7 +59,9 @@ def test_c_pack_matches_oracle_pack(name):
 
 
 def test_c_pack_golden_layout():
-    for d, I, bits, nbytes, stride, codes, sbs in golden_io.blob_layout():
+    for d, I, bits, nbytes, stride, codes, sbs, weights in golden_io.blob_layout():
+        if bits == 32:
+            continue
         assert moe.moe_blob_bytes(d, I, bits) == nbytes and moe.moe_blob_stride(d, I, bits) == stride
         dims = oquant.mat_dims(d, I)
         for mat, row, col, val, off, byte in codes:

@@ -110,7 +110,7 @@ def test_shared_gate_closed_form():
 
 
 # ---- P5: whole tiny layer vs 50-digit brute force ---------------------------
-@pytest.mark.parametrize("name", ["tiny", "tiny_int8"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_int8", "tiny_f32"])
 def test_layer_vs_mpmath_bruteforce(name):
     cfg = ms.CONFIGS[name]
     Wr = ms.router_weight(cfg)
@@ -213,10 +213,10 @@ def test_dequant_exact_in_fp32():
 
 
 # ---- P7: blob layout ---------------------------------------------------------
-@pytest.mark.parametrize("case", range(4))
+@pytest.mark.parametrize("case", range(6))
 def test_blob_layout_golden(case):
-    d, I, bits, nbytes, stride, codes, sbs = golden_io.blob_layout()[case]
-    per16 = 27 if bits == 4 else 51
+    d, I, bits, nbytes, stride, codes, sbs, weights = golden_io.blob_layout()[case]
+    per16 = {4: 27, 8: 51, 32: 192}[bits]
     assert oquant.blob_bytes(d, I, bits) == nbytes == per16 * d * I // 16
     assert oquant.blob_stride(d, I, bits) == stride
     dims = oquant.mat_dims(d, I)
@@ -241,11 +241,18 @@ def test_blob_layout_golden(case):
         assert blob[soff:soff + 2].tobytes() == b"\x00\x38"
         assert blob[boff:boff + 2].tobytes() == b"\x00\xc0"
         assert np.count_nonzero(blob) == 2
+    for mat, row, col, val, off, bits32 in weights:
+        raw = {m: {"weights": np.zeros(dims[m], np.float32)} for m in oquant.MATS}
+        raw[mat]["weights"][row, col] = val
+        blob = oquant.pack_expert(raw, d, I, bits)
+        assert blob.size == stride
+        assert blob[off:off + 4].tobytes() == int(bits32).to_bytes(4, "little")
+        assert np.count_nonzero(blob) == np.count_nonzero(blob[off:off + 4])
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 8, 32])
 def test_pack_roundtrip(bits):
-    small = TINY if bits == 4 else ms.CONFIGS["tiny_int8"]
+    small = {4: TINY, 8: ms.CONFIGS["tiny_int8"], 32: ms.CONFIGS["tiny_f32"]}[bits]
     big = ms.scaled(ms.CONFIGS["decode80b"], bits=bits)
     for cfg in (small, big):
         raw = ms.expert_raw(cfg, 9)
@@ -254,12 +261,13 @@ def test_pack_roundtrip(bits):
         assert not blob[oquant.blob_bytes(cfg.d, cfg.I, bits):].any()
         back = oquant.unpack_expert(blob, cfg.d, cfg.I, bits)
         for m in oquant.MATS:
-            for f in ("codes", "scales", "biases"):
+            for f in raw[m]:
                 assert np.array_equal(back[m][f], raw[m][f])
         assert np.array_equal(oquant.pack_expert(back, cfg.d, cfg.I, bits), blob)
     # 80B shape: 27/16 and 51/16 bytes per weight, already multiples of 4096
     assert oquant.blob_bytes(2048, 512) == 1769472 == oquant.blob_stride(2048, 512)
     assert oquant.blob_bytes(2048, 512, 8) == 3342336 == oquant.blob_stride(2048, 512, 8)
+    assert oquant.blob_bytes(2048, 512, 32) == 12582912 == oquant.blob_stride(2048, 512, 32)
 
 
 def test_int8_codes_are_bytes():
@@ -292,6 +300,18 @@ def test_int8_with_4bit_codes_is_the_int4_expert():
     blob8 = oquant.pack_expert(raw4, TINY.d, TINY.I, 8)
     raw8 = oquant.unpack_expert(blob8, TINY.d, TINY.I, 8)
     assert np.array_equal(olayer.expert_ffn(raw8, x), y4)
+
+
+def test_f32_expert_is_its_weights():
+    """An f32 expert whose weights are the dequantised weights of a 4-bit
+    expert is the same function as that expert (both compute
+    W_d (silu(W_g x) * W_u x) on the same matrices)."""
+    raw4 = ms.expert_raw(TINY, 6)
+    raw32 = {m: {"weights": oquant.dequant(raw4[m]).astype(np.float32)} for m in oquant.MATS}
+    for m in oquant.MATS:    # the 4-bit weights are exact in fp32 (pinned above)
+        assert np.array_equal(oquant.dequant(raw32[m]), oquant.dequant(raw4[m]))
+    x = ms.bf16_bits_to_f32(ms.x_bits(TINY, 2)).astype(np.float64)
+    assert np.array_equal(olayer.expert_ffn(raw32, x), olayer.expert_ffn(raw4, x))
 
 
 def test_int8_dequant_exact_in_fp32():
