@@ -17,7 +17,8 @@ the CPU oracle timed on a bounded sample of the same steps (cpu_baseline).
 --workload selects another configuration (decode35b, refill80b: 256-slot
 pool refilled by LFU + recency from pinned host memory, batch80b: T=64,
 prefill80b / prefill80b_zipf: T=4096 on the matrix cores; decode80b_int8,
-batch80b_int8, prefill80b_int8: the same layers with 8-bit experts);
+batch80b_int8, prefill80b_int8: the same layers with 8-bit experts;
+decode80b_f32, batch80b_f32: with unquantised fp32 experts);
 --workload all prints one line per workload, the headline first;
 --workload refill_sweep prints the refill run for pool sizes 64..512 (hit
 rate vs tokens/s).
@@ -43,12 +44,17 @@ DATA = ("synthetic (seeded int4 codes U{0..15}, fp16 scales U[0.002,0.02], bias 
         "x ~ N(0,1) bf16, router N(0,0.02) fp32, Zipf(1.1) logit offset alpha=0.15 where skewed)")
 DATA8 = ("synthetic (seeded int8 codes U{0..255}, fp16 scales U[0.002,0.02]/16, bias -128*scale, "
          "x ~ N(0,1) bf16, router N(0,0.02) fp32, Zipf(1.1) logit offset alpha=0.15 where skewed)")
+METRIC32 = "routed-MoE layer tokens/s + achieved HBM GB/s on f32 experts (80B shape)"
+DATA32 = ("synthetic (seeded fp32 expert weights N(0,0.05), x ~ N(0,1) bf16, router N(0,0.02) fp32, "
+          "Zipf(1.1) logit offset alpha=0.15)")
 
 
 def labels(cfg):
     """(metric, data, weight dtype) of a workload by its code width."""
     if cfg.bits == 8:
         return METRIC8, DATA8, "int8"
+    if cfg.bits == 32:
+        return METRIC32, DATA32, "f32"
     return METRIC, DATA, "int4"
 
 
@@ -252,7 +258,9 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
         "all_bytes_per_step": expert_bytes + router_bytes,
         "layer_expert_GBps": round(layer_gbs, 1),
         "layer_expert_frac_of_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "expert FFN: gate_up_kernel + down_decode_kernel",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("expert FFN: gate_up_kernel + down_decode_kernel" if cfg.bits != 32
+                                else "expert FFN: gate_up_f32_kernel + down_decode_f32_kernel"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": ffn_traffic(name),
                      "avg_us": round(ffn_ms * 1e3, 3)},
@@ -366,11 +374,13 @@ def run_batched(c, K, W, R, name="batch80b"):
     return {"metric": metric, "value": round(T * 1000.0 / ms_step, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,
-            "dtype": f"{wdt} weights -> fp16 MFMA, fp32 accumulate; fp32 router", "data": data,
+            "dtype": (f"{wdt} weights -> fp16 MFMA, fp32 accumulate; fp32 router" if cfg.bits != 32
+                      else "f32 weights, bf16 activations, fp32 accumulate"), "data": data,
             "config": {"workload": f"80B-shape batched decode, T=64 independent tokens, {wdt} experts, "
                                    "all experts resident",
                        "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "bits": cfg.bits, "replicas": R,
-                       "path": "auto: bucketing + grouped GEMMs on the matrix cores"},
+                       "path": ("auto: bucketing + grouped GEMMs on the matrix cores" if cfg.bits != 32
+                                else "auto: bucketing + bucketed f32 GEMVs")},
             "distinct_experts_per_step": round(distinct, 1),
             "layer_expert_GBps": round(gbs, 1), "layer_expert_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "gemv_path_ms_per_step": round(times[moe.MOE_PATH_BATCHED], 5)}
@@ -441,7 +451,7 @@ def main():
     ap.add_argument("--workload", default="decode80b",
                     choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
                              "prefill80b_zipf", "decode80b_int8", "batch80b_int8", "prefill80b_int8",
-                             "all", "refill_sweep"])
+                             "decode80b_f32", "batch80b_f32", "all", "refill_sweep"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
@@ -454,11 +464,14 @@ def main():
     c.torch.cuda.set_device(0)
     cpu = 0 if args.no_cpu else args.cpu_steps
     todo = ["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b", "prefill80b_zipf",
-            "decode80b_int8", "batch80b_int8", "prefill80b_int8"] \
+            "decode80b_int8", "batch80b_int8", "prefill80b_int8", "decode80b_f32", "batch80b_f32"] \
         if args.workload == "all" else [args.workload]
     for wl in todo:
-        if wl in ("decode80b", "decode35b", "decode80b_int8"):
-            res = run_decode(c, wl, args.steps, args.warmup, args.replicas,
+        if wl in ("decode80b", "decode35b", "decode80b_int8", "decode80b_f32"):
+            # f32 blobs are 12.6 MB: 4 replicas already keep a step's 138 MB
+            # out of the 256 MB last-level cache until its next use
+            reps = min(args.replicas, 4) if wl.endswith("f32") else args.replicas
+            res = run_decode(c, wl, args.steps, args.warmup, reps,
                              cpu if wl == "decode80b" else 0, args.eager)
         elif wl == "refill80b":
             res = run_refill(c, min(args.steps, 300), min(args.warmup, 50))
@@ -471,7 +484,7 @@ def main():
                 print(json.dumps(res), flush=True)
                 c.torch.cuda.empty_cache()
             continue
-        elif wl in ("batch80b", "batch80b_int8"):
+        elif wl in ("batch80b", "batch80b_int8", "batch80b_f32"):
             res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4), wl)
         else:
             res = run_prefill(c, wl, 10)

@@ -73,7 +73,8 @@ typedef struct moe_ffn_shape {
   int32_t d;      /* hidden size (input of gate/up, output of down)          */
   int32_t I;      /* intermediate size                                       */
   int32_t group;  /* quantisation group along the input dimension (64)       */
-  int32_t bits;   /* code width: 4 or 8 (0 is read as 4)                     */
+  int32_t bits;   /* code width: 4 or 8 (0 is read as 4); 32 = unquantised  */
+                  /* fp32 weights                                           */
 } moe_ffn_shape;
 
 /* ---------------------------------------------------------------- errors */
@@ -94,6 +95,10 @@ const char* moe_version(void);
  * 8-bit blobs: the same sections, codes_m [in/16][out][16 B] with one code
  * per byte; inside each 8 inputs the bytes hold inputs (0,1,4,5,2,3,6,7) of
  * the block; bytes = 51/16 * d * I.
+ * f32 blobs (bits == 32, unquantised; the pages validate every layer in f32
+ * as well as int4 form, correctness section): gate, up, down as row-major
+ * fp32 [out][in], one after the other, no scale/bias sections;
+ * bytes = 12 * d * I.
  * Offsets are 64-bit (multi-GB pools; MLX affine kernels with 64-bit offsets
  * in the relationship-to-TurboFieldfare section). */
 size_t moe_blob_bytes(const moe_ffn_shape* sh);   /* 0 if sh is invalid */
@@ -111,6 +116,14 @@ int moe_pack_expert(const moe_ffn_shape* sh, const uint8_t* const codes[3],
 int moe_unpack_expert(const moe_ffn_shape* sh, const void* blob,
                       uint8_t* const codes[3], uint16_t* const scales[3],
                       uint16_t* const biases[3]);
+/* f32 experts (sh->bits == 32): w[m] = fp32 [out][in] row-major, m = 0
+ * gate, 1 up, 2 down; blob_out: moe_blob_stride bytes, written whole.
+ * moe_pack_expert / moe_unpack_expert refuse bits == 32 (and these refuse
+ * any other width) with MOE_ERR_INVALID_ARG. */
+int moe_pack_expert_f32(const moe_ffn_shape* sh, const float* const w[3],
+                        void* blob_out);
+int moe_unpack_expert_f32(const moe_ffn_shape* sh, const void* blob,
+                          float* const w[3]);
 /* The same for 4-bit shapes only (MOE_ERR_INVALID_ARG for sh->bits == 8). */
 int moe_pack_expert_int4(const moe_ffn_shape* sh,
                          const uint8_t* const codes[3],
@@ -251,9 +264,12 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
  *                     pool error word reports MOE_ERR_UNSUPPORTED), fp32
  *                     accumulate.
  *   MOE_PATH_AUTO   : DECODE for T <= 8 (and T*(k+1) <= 2048), else PREFILL,
- *                     or BATCHED if d is not a multiple of 128 (the caller
- *                     must then supply every buffer).  PREFILL's fp16
- *                     range applies to AUTO calls above 8 tokens.
+ *                     or BATCHED if d is not a multiple of 128 or the
+ *                     experts are f32 (the caller must then supply every
+ *                     buffer).  PREFILL's fp16 range applies to AUTO calls
+ *                     above 8 tokens.
+ * f32 experts (bits == 32): DECODE and BATCHED only (PREFILL:
+ * MOE_ERR_UNSUPPORTED); products and sums in fp32.
  * A selected expert with slot_table[e] < 0 sets the pool's error word and
  * contributes zero. */
 size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh,

@@ -69,6 +69,8 @@ _SIGS = {
     "moe_blob_stride": (_S, [_P]),
     "moe_pack_expert": (C.c_int, [_P, _P, _P, _P, _P]),
     "moe_unpack_expert": (C.c_int, [_P, _P, _P, _P, _P]),
+    "moe_pack_expert_f32": (C.c_int, [_P, _P, _P]),
+    "moe_unpack_expert_f32": (C.c_int, [_P, _P, _P]),
     "moe_pack_expert_int4": (C.c_int, [_P, _P, _P, _P, _P]),
     "moe_unpack_expert_int4": (C.c_int, [_P, _P, _P, _P, _P]),
     "moe_lfu_create": (C.c_int, [_I, _I, _P]),
@@ -160,11 +162,26 @@ _MATS = ("gate", "up", "down")
 
 
 def moe_pack_expert(raw, d: int, I: int, bits: int = 4) -> np.ndarray:
-    """Blob bytes (uint8[stride]) of one expert (4- or 8-bit codes)."""
+    """Blob bytes (uint8[stride]) of one expert (4- or 8-bit codes, or bits=32:
+    raw[m]["weights"] fp32 [out][in])."""
+    if bits == 32:
+        keep = [np.ascontiguousarray(raw[name]["weights"], dtype=np.float32) for name in _MATS]
+        wp = (C.c_void_p * 3)(*[k.ctypes.data for k in keep])
+        out = np.empty(moe_blob_stride(d, I, 32), dtype=np.uint8)
+        _check(_lib.moe_pack_expert_f32(C.byref(shape(d, I, 32)), wp, out.ctypes.data), "moe_pack_expert_f32")
+        return out
     return _pack(_lib.moe_pack_expert, raw, d, I, bits)
 
 
 def moe_unpack_expert(blob: np.ndarray, d: int, I: int, bits: int = 4):
+    if bits == 32:
+        dims = {"gate": (I, d), "up": (I, d), "down": (d, I)}
+        raw = {name: {"weights": np.empty(dims[name], np.float32)} for name in _MATS}
+        wp = (C.c_void_p * 3)(*[raw[name]["weights"].ctypes.data for name in _MATS])
+        blob = np.ascontiguousarray(blob, dtype=np.uint8)
+        _check(_lib.moe_unpack_expert_f32(C.byref(shape(d, I, 32)), blob.ctypes.data, wp),
+               "moe_unpack_expert_f32")
+        return raw
     return _unpack(_lib.moe_unpack_expert, blob, d, I, bits)
 
 

@@ -63,6 +63,7 @@ struct GateUpArgs {
   int32_t* sel_slot;            // decode: [T*k] slot of each selection, for the down pass
   const uint32_t* xq;           // [T][d/2]
   const float* xs;              // [T][d/64]
+  const uint16_t* x;            // [T][d] bf16 (the f32-expert kernels read it as is)
   const Inst* inst;             // batched: instances
   const int32_t* n_routed;      // batched: device count of routed instances
   int n_shared_inst;            // batched
@@ -812,6 +813,272 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
+
+// ------------------------------------------------------------- f32 experts
+// Unquantised fp32 experts (row-major [out][in] matrices, gate | up | down).
+// gate/up: one wave per weight row, its 64 lanes striding over d in float4
+// pieces (a row is one contiguous read), both matrices, every token of the
+// instance; x is staged in LDS as bf16 and widened on use.  down: 8 lanes
+// per output row (as in the quantised kernels), h staged in LDS.  Products
+// and sums in fp32; h kept in fp32.
+constexpr int kF32Pass = 2048;                  // inputs of a gate/up row per register pass
+
+__device__ __forceinline__ float4 bf16x4_to_f32(uint2 v) {
+  return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
+  acc = fmaf(a.x, b.x, acc);
+  acc = fmaf(a.y, b.y, acc);
+  acc = fmaf(a.z, b.z, acc);
+  return fmaf(a.w, b.w, acc);
+}
+
+// item = (instance, 4 rows): wave w takes row 4 rb + w of gate and up.
+template <int TC>
+__global__ __launch_bounds__(256) void gate_up_f32_kernel(GateUpArgs a) {
+  extern __shared__ uint16_t xb[];              // [TC][d] bf16
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rbR = a.I / 4, rbS = a.Ish / 4;
+  const int nR = a.batched ? *a.n_routed : a.T * a.k;
+  const int nS = a.batched ? a.n_shared_inst : a.T;
+  const int items = nR * rbR + nS * rbS;
+  const int d4 = a.d / 4;
+  constexpr int NV = kF32Pass / 256;            // float4 per lane per matrix per pass
+  for (int item = xcd_remap(blockIdx.x, gridDim.x); item < items; item += gridDim.x) {
+    const bool routed = item < nR * rbR;
+    const int rel = routed ? item : item - nR * rbR;
+    const int rb_per = routed ? rbR : rbS;
+    const int i = rel / rb_per, rb = rel % rb_per;
+    const uint8_t* blob;
+    int Iinst, tok[TC], hrow[TC];
+    bool missing;
+    const int ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
+    if (!a.batched && routed && rb == 0 && tid == 0)
+      a.sel_slot[i] = missing ? -1 : (int32_t)((blob - a.pool.slab) / a.pool.stride);
+    const BlobLayout L = blob_layout(a.d, Iinst, 32);
+    const int o = rb * 4 + wave;
+    const float4* wg = reinterpret_cast<const float4*>(blob + L.m[0].codes) + (size_t)o * d4;
+    const float4* wu = reinterpret_cast<const float4*>(blob + L.m[1].codes) + (size_t)o * d4;
+    float g[TC], u[TC];
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) { g[tt] = 0.f; u[tt] = 0.f; }
+    for (int p0 = 0; p0 < d4; p0 += kF32Pass / 4) {
+      // this pass's weights first, then (first pass) the activations
+      float4 gv[NV], uv[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int f = p0 + 64 * v + lane;
+        const bool ok = !missing && f < d4 && 64 * v < kF32Pass / 4;
+        gv[v] = ok ? wg[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        uv[v] = ok ? wu[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (p0 == 0) {
+        for (int q = tid; q < ntok * (a.d / 8); q += 256) {
+          const int tt = q / (a.d / 8), c8 = q % (a.d / 8);
+          reinterpret_cast<uint4*>(xb + (size_t)tt * a.d)[c8] =
+              reinterpret_cast<const uint4*>(a.x + (size_t)tok[tt] * a.d)[c8];
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int tt = 0; tt < TC; ++tt) {
+        if (tt < ntok) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            const int f = p0 + 64 * v + lane;
+            if (f < d4) {
+              const float4 xv = bf16x4_to_f32(reinterpret_cast<const uint2*>(xb + (size_t)tt * a.d)[f]);
+              g[tt] = dot4(gv[v], xv, g[tt]);
+              u[tt] = dot4(uv[v], xv, u[tt]);
+            }
+          }
+        }
+      }
+    }
+    float hv = 0.f;
+    int hr = 0;
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) {
+      const float gg = wave_sum(g[tt]), uu = wave_sum(u[tt]);
+      if (lane == tt) {
+        hv = missing ? 0.f : gg / (1.0f + expf(-gg)) * uu;
+        hr = hrow[tt];
+      }
+    }
+    if (lane < ntok) reinterpret_cast<float*>(a.hq)[(size_t)hr * a.Imax + o] = hv;
+    if (missing && tid == 0) atomicOr(a.pool.err, 1);
+    __syncthreads();
+  }
+}
+
+// down row j of an f32 expert against an fp32 h held in LDS: lane gl of the
+// row's 8 takes float4 pieces gl, gl+8, ...; returns this lane's part.
+template <int NW>
+__device__ __forceinline__ float down_f32_part(const float4 (&wv)[NW], const float* hl, int gl, int I4) {
+  float acc = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int f = gl + 8 * v;
+    if (f < I4) acc = dot4(wv[v], reinterpret_cast<const float4*>(hl)[f], acc);
+  }
+  return acc;
+}
+
+constexpr int kF32DnW = 16;                     // float4 per lane per register pass (I <= 512)
+
+// Decode: block = 8 output rows, all T*(k+1) instances in rounds of 16 (one
+// per wave), fused rank-order combine (as down_decode_kernel).
+__global__ __launch_bounds__(64 * kDnWaves) void down_decode_f32_kernel(DownArgs a) {
+  extern __shared__ float dyn[];                // oi[nI][8] | wk[nI] | hst[kDnRound][Imax]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane >> 3, gl = lane & 7;
+  const int jb = xcd_remap(blockIdx.x, gridDim.x);
+  const int j = jb * 8 + r;
+  const int nR = a.T * a.k, nI = nR + a.T;
+  float* oi = dyn;
+  float* wk = dyn + nI * 8;
+  float* hst = dyn + ((nI * 9 + 3) & ~3);
+  for (int q = tid; q < nI; q += 64 * kDnWaves) wk[q] = q < nR ? a.w[q] : a.sgate[q - nR];
+  for (int base = 0; base < nI; base += kDnRound) {
+    const int nr = min(kDnRound, nI - base);
+    const int i = base + wave;
+    const bool active = wave < nr;
+    bool miss = true;
+    int Iinst = 0;
+    const uint8_t* blob = nullptr;
+    float4 wv[kF32DnW];
+    if (active) {
+      if (i < nR) {
+        const int slot = a.sel_slot[i];
+        miss = slot < 0;
+        blob = a.pool.slab + (uint64_t)(miss ? 0 : slot) * a.pool.stride;
+        Iinst = a.I;
+      } else {
+        miss = false;
+        blob = a.shared_blob;
+        Iinst = a.Ish;
+      }
+    }
+    const int I4 = Iinst / 4;
+    const float4* wd = nullptr;
+    if (active && !miss) {
+      const BlobLayout L = blob_layout(a.d, Iinst, 32);
+      wd = reinterpret_cast<const float4*>(blob + L.m[2].codes) + (size_t)j * I4;
+    }
+#pragma unroll
+    for (int v = 0; v < kF32DnW; ++v) {
+      const int f = gl + 8 * v;
+      wv[v] = (wd && f < I4) ? wd[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // the round's h records
+    const int im4 = a.Imax / 4;
+    for (int q4 = tid; q4 < nr * im4; q4 += 64 * kDnWaves) {
+      const int u = q4 / im4, c = q4 % im4;
+      reinterpret_cast<float4*>(hst + (size_t)u * a.Imax)[c] =
+          reinterpret_cast<const float4*>(a.hq + (size_t)(base + u) * a.Imax)[c];
+    }
+    __syncthreads();
+    if (active) {
+      const float* hl = hst + (size_t)wave * a.Imax;
+      float acc = 0.f;
+      if (wd) {
+        acc = down_f32_part<kF32DnW>(wv, hl, gl, I4);
+        for (int p0 = 8 * kF32DnW; p0 < I4; p0 += 8 * kF32DnW) {   // intermediates wider than 512
+#pragma unroll
+          for (int v = 0; v < kF32DnW; ++v) {
+            const int f = p0 + gl + 8 * v;
+            if (f < I4) acc = dot4(wd[f], reinterpret_cast<const float4*>(hl)[f], acc);
+          }
+        }
+      }
+      acc = sum8_dpp(acc);
+      if (gl == 0) oi[i * 8 + r] = acc;
+    }
+    __syncthreads();
+  }
+  if (tid < 8 * a.T) {
+    const int t = tid / 8, rr = tid % 8;
+    float y = 0.f;
+    for (int q2 = 0; q2 < a.k; ++q2) y += wk[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
+    y += wk[nR + t] * oi[(nR + t) * 8 + rr];
+    a.y[(size_t)t * a.d + jb * 8 + rr] = y;
+  }
+}
+
+// Batched: item = (bucket chunk, 32 output rows): wave w takes rows
+// j0 + 8 w .. + 7 (8 lanes each), the chunk's h records staged in LDS.
+__global__ __launch_bounds__(256) void down_batched_f32_kernel(DownArgs a) {
+  extern __shared__ float hsf[];                // [kTC][Imax]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane >> 3, gl = lane & 7;
+  const int nrb = (a.d + 31) / 32;
+  const int nR = *a.n_routed;
+  const int items = (nR + a.n_shared_inst) * nrb;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int ii = item / nrb, j0 = (item % nrb) * 32;
+    const bool routed = ii < nR;
+    const Inst in = a.inst[ii];
+    const uint8_t* blob;
+    int Iinst;
+    bool missing = false;
+    if (routed) {
+      const int e = in.expert;
+      const int slot = (e >= 0 && e < a.pool.E) ? a.pool.slot_table[e] : -1;
+      missing = slot < 0;
+      blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
+      Iinst = a.I;
+    } else {
+      blob = a.shared_blob;
+      Iinst = a.Ish;
+    }
+    const int I4 = Iinst / 4;
+    const int j = j0 + 8 * wave + r;
+    const bool jv = j < a.d;
+    const BlobLayout L = blob_layout(a.d, Iinst, 32);
+    const float4* wd = reinterpret_cast<const float4*>(blob + L.m[2].codes) + (size_t)(jv ? j : 0) * I4;
+    float4 wv[kF32DnW];
+#pragma unroll
+    for (int v = 0; v < kF32DnW; ++v) {
+      const int f = gl + 8 * v;
+      wv[v] = (!missing && jv && f < I4) ? wd[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int im4 = a.Imax / 4;
+    for (int q4 = tid; q4 < in.n * im4; q4 += 256) {
+      const int tt = q4 / im4, c = q4 % im4;
+      const int hr = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
+      reinterpret_cast<float4*>(hsf + (size_t)tt * a.Imax)[c] =
+          reinterpret_cast<const float4*>(a.hq + (size_t)hr * a.Imax)[c];
+    }
+    __syncthreads();
+    float acc[kTC];
+#pragma unroll
+    for (int tt = 0; tt < kTC; ++tt) {
+      acc[tt] = 0.f;
+      if (tt < in.n && !missing && jv) {
+        const float* hl = hsf + (size_t)tt * a.Imax;
+        acc[tt] = down_f32_part<kF32DnW>(wv, hl, gl, I4);
+        for (int p0 = 8 * kF32DnW; p0 < I4; p0 += 8 * kF32DnW) {
+          for (int v = 0; v < kF32DnW; ++v) {
+            const int f = p0 + gl + 8 * v;
+            if (f < I4) acc[tt] = dot4(wd[f], reinterpret_cast<const float4*>(hl)[f], acc[tt]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTC; ++tt) {
+      const float v = sum8_dpp(acc[tt]);
+      if (gl == 0 && tt < in.n && jv) {
+        const int hr = routed ? a.pair_ids[in.start + tt] : 0;
+        if (routed) a.partial[(size_t)hr * a.d + j] = v;
+        else a.shared_out[(size_t)(in.start + tt) * a.d + j] = v;
+      }
+    }
+    if (missing && tid == 0) atomicOr(a.pool.err, 1);
+    __syncthreads();
+  }
+}
+
 struct FfnWs {
   uint32_t* xq; float* xs;
   uint32_t* hq; float* hs8;
@@ -882,11 +1149,11 @@ GemvSet gemv_set() {
 // GEMMs on the matrix cores, which measured faster than the bucketed GEMVs
 // from 2 tokens up (80B shape, 4- and 8-bit experts) even with a handful of
 // tokens per bucket; the bucketed GEMVs where the GEMM tiles do not fit
-// (d not a multiple of 128).
-int resolve_path(int path, int T, int d, int k, int E) {
+// (d not a multiple of 128) and for unquantised f32 experts.
+int resolve_path(int path, int T, int d, int k, int E, int bits) {
   if (path != MOE_PATH_AUTO) return path;
   if (T <= 8 && (long)T * (k + 1) <= 2048) return MOE_PATH_DECODE;
-  return d % 128 == 0 ? MOE_PATH_PREFILL : MOE_PATH_BATCHED;
+  return (d % 128 == 0 && bits != 32) ? MOE_PATH_PREFILL : MOE_PATH_BATCHED;
 }
 
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
@@ -899,17 +1166,58 @@ size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
 
 int xprep_launch(const uint16_t* x, int T, int d, uint32_t* xq, float* xs, hipStream_t s);
 
+namespace {
+// f32 experts: decode (routing given: no in-kernel selection) or bucketed.
+int f32_launch(const FfnArgs& f, int path, GateUpArgs& g, DownArgs& dn, const FfnWs& w, int Imax,
+               hipStream_t s) {
+  if (path == MOE_PATH_DECODE) {
+    if (f.logits) return MOE_ERR_UNSUPPORTED;
+    g.batched = 0;
+    g.logits = nullptr;
+    const int items = f.T * f.k * (f.I / 4) + f.T * (f.Ish / 4);
+    void* args[] = {&g};
+    MOE_HIP(hipLaunchKernel((void*)gate_up_f32_kernel<1>, dim3((items + 7) & ~7), dim3(256), args,
+                            (size_t)f.d * 2, s));
+    const int nI = f.T * (f.k + 1);
+    void* dargs[] = {&dn};
+    const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * Imax) * 4;
+    MOE_HIP(hipLaunchKernel((void*)down_decode_f32_kernel, dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
+    return MOE_OK;
+  }
+  if (!f.offsets || !f.pair_ids || !f.partial || !f.shared_out) return MOE_ERR_INVALID_ARG;
+  const int nsh = (f.T + kTC - 1) / kTC;
+  plan_kernel<<<1, 1024, 0, s>>>(f.offsets, f.pool.E, f.T, w.inst, w.n_routed);
+  MOE_HIP(hipGetLastError());
+  g.batched = 1;
+  g.inst = w.inst; g.n_routed = w.n_routed; g.n_shared_inst = nsh; g.pair_ids = f.pair_ids;
+  const long upper = ((long)f.T * f.k + nsh) * (Imax / 4);
+  void* args[] = {&g};
+  MOE_HIP(hipLaunchKernel((void*)gate_up_f32_kernel<kTC>, dim3(grid_for((int)(upper < 65536 ? upper : 65536))),
+                          dim3(256), args, (size_t)kTC * f.d * 2, s));
+  dn.inst = w.inst; dn.n_routed = w.n_routed; dn.n_shared_inst = nsh; dn.pair_ids = f.pair_ids;
+  dn.partial = f.partial; dn.shared_out = f.shared_out;
+  const long dupper = ((long)f.T * f.k + nsh) * ((f.d + 31) / 32);
+  void* dargs[] = {&dn};
+  MOE_HIP(hipLaunchKernel((void*)down_batched_f32_kernel, dim3(grid_for((int)(dupper < 65536 ? dupper : 65536))),
+                          dim3(256), dargs, (size_t)kTC * Imax * 4, s));
+  return MOE_OK;
+}
+}  // namespace
+
 int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_t s) {
-  // one code width for routed and shared experts (both 4-bit or both 8-bit)
-  if (f.bits != f.bits_sh || (f.bits != 4 && f.bits != 8)) return MOE_ERR_UNSUPPORTED;
-  if (path == MOE_PATH_PREFILL) return prefill_launch(f, ws, ws_bytes, s);
+  // one code width for routed and shared experts (4-bit, 8-bit or f32)
+  if (f.bits != f.bits_sh || (f.bits != 4 && f.bits != 8 && f.bits != 32)) return MOE_ERR_UNSUPPORTED;
+  if (path == MOE_PATH_PREFILL) {
+    if (f.bits == 32) return MOE_ERR_UNSUPPORTED;   // f32 experts: decode and bucketed GEMVs
+    return prefill_launch(f, ws, ws_bytes, s);
+  }
   const int Imax = f.I > f.Ish ? f.I : f.Ish;
   Carver c(ws, ws_bytes);
   FfnWs w;
   if (!carve_ffn(c, f.d, Imax, f.T, f.k, path, &w)) return MOE_ERR_INVALID_ARG;
   const uint32_t* xq = f.xq;
   const float* xs = f.xs;
-  if (!xq) {
+  if (!xq && f.bits != 32) {
     MOE_TRY(xprep_launch(f.x, f.T, f.d, w.xq, w.xs, s));
     xq = w.xq;
     xs = w.xs;
@@ -921,13 +1229,14 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   g.d = f.d; g.I = f.I; g.Ish = f.Ish; g.Imax = Imax; g.T = f.T; g.k = f.k;
   g.idx = f.idx; g.w = f.w; g.sgate = f.sgate; g.logits = f.logits; g.bias = f.bias; g.usage = f.usage;
   g.sel_slot = w.sel_slot;
-  g.xq = xq; g.xs = xs;
+  g.xq = xq; g.xs = xs; g.x = f.x;
   g.hq = w.hq; g.hs8 = w.hs8;
   DownArgs dn{};
   dn.pool = f.pool; dn.shared_blob = f.shared_blob;
   dn.d = f.d; dn.I = f.I; dn.Ish = f.Ish; dn.Imax = Imax; dn.T = f.T; dn.k = f.k;
   dn.sel_slot = w.sel_slot; dn.w = f.w; dn.sgate = f.sgate; dn.hq = w.hq; dn.hs8 = w.hs8; dn.y = f.y;
 
+  if (f.bits == 32) return f32_launch(f, path, g, dn, w, Imax, s);
   if (path == MOE_PATH_DECODE) {
     g.batched = 0;
     const int items = f.T * f.k * (f.I / 8) + f.T * (f.Ish / 8);

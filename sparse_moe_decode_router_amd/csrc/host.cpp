@@ -24,7 +24,8 @@ int hip_fail(hipError_t e) {
 
 bool shape_ok(const moe_ffn_shape* sh) {
   return sh && sh->group == 64 && sh->d >= 64 && sh->I >= 64 && sh->d % 64 == 0 && sh->I % 64 == 0 &&
-         sh->d <= 16384 && sh->I <= 16384 && (sh->bits == 0 || sh->bits == 4 || sh->bits == 8);
+         sh->d <= 16384 && sh->I <= 16384 &&
+         (sh->bits == 0 || sh->bits == 4 || sh->bits == 8 || sh->bits == 32);
 }
 
 int table_edit_launch(int32_t* table, const int32_t* experts, const int32_t* slots, int n,
@@ -68,6 +69,7 @@ extern "C" int moe_pack_expert(const moe_ffn_shape* sh, const uint8_t* const cod
                                void* out) {
   if (!shape_ok(sh) || !codes || !scales || !biases || !out) return MOE_ERR_INVALID_ARG;
   const int bits = shape_bits(sh);
+  if (bits == 32) return MOE_ERR_INVALID_ARG;     // f32 experts: moe_pack_expert_f32
   const BlobLayout L = blob_layout(sh->d, sh->I, bits);
   const int outs[3] = {sh->I, sh->I, sh->d};
   const int ins[3] = {sh->d, sh->d, sh->I};
@@ -112,6 +114,7 @@ extern "C" int moe_unpack_expert(const moe_ffn_shape* sh, const void* in, uint8_
                                  uint16_t* const scales[3], uint16_t* const biases[3]) {
   if (!shape_ok(sh) || !in || !codes || !scales || !biases) return MOE_ERR_INVALID_ARG;
   const int bits = shape_bits(sh);
+  if (bits == 32) return MOE_ERR_INVALID_ARG;     // f32 experts: moe_unpack_expert_f32
   const BlobLayout L = blob_layout(sh->d, sh->I, bits);
   const int outs[3] = {sh->I, sh->I, sh->d};
   const int ins[3] = {sh->d, sh->d, sh->I};
@@ -144,6 +147,30 @@ extern "C" int moe_unpack_expert(const moe_ffn_shape* sh, const void* in, uint8_
         scales[m][(size_t)o * (N / 64) + g] = sb[((size_t)g * O + o) * 2 + 0];
         biases[m][(size_t)o * (N / 64) + g] = sb[((size_t)g * O + o) * 2 + 1];
       }
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_pack_expert_f32(const moe_ffn_shape* sh, const float* const w[3], void* out) {
+  if (!shape_ok(sh) || shape_bits(sh) != 32 || !w || !out) return MOE_ERR_INVALID_ARG;
+  const BlobLayout L = blob_layout(sh->d, sh->I, 32);
+  const size_t n[3] = {(size_t)sh->I * sh->d, (size_t)sh->I * sh->d, (size_t)sh->d * sh->I};
+  for (int m = 0; m < 3; ++m)
+    if (!w[m]) return MOE_ERR_INVALID_ARG;
+  uint8_t* blob = static_cast<uint8_t*>(out);
+  std::memset(blob, 0, L.stride);
+  for (int m = 0; m < 3; ++m) std::memcpy(blob + L.m[m].codes, w[m], n[m] * sizeof(float));
+  return MOE_OK;
+}
+
+extern "C" int moe_unpack_expert_f32(const moe_ffn_shape* sh, const void* in, float* const w[3]) {
+  if (!shape_ok(sh) || shape_bits(sh) != 32 || !w || !in) return MOE_ERR_INVALID_ARG;
+  const BlobLayout L = blob_layout(sh->d, sh->I, 32);
+  const size_t n[3] = {(size_t)sh->I * sh->d, (size_t)sh->I * sh->d, (size_t)sh->d * sh->I};
+  const uint8_t* blob = static_cast<const uint8_t*>(in);
+  for (int m = 0; m < 3; ++m) {
+    if (!w[m]) return MOE_ERR_INVALID_ARG;
+    std::memcpy(w[m], blob + L.m[m].codes, n[m] * sizeof(float));
   }
   return MOE_OK;
 }
@@ -451,7 +478,7 @@ extern "C" int moe_pool_reset_usage(moe_pool* p, hipStream_t s) {
 extern "C" size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh, const moe_ffn_shape* ssh, int32_t T,
                                           int32_t k, int32_t E, int32_t path) {
   if (!shape_ok(sh) || !shape_ok(ssh) || sh->d != ssh->d || T < 0 || k < 1 || E < 1) return 0;
-  path = resolve_path(path, T, sh->d, k, E);
+  path = resolve_path(path, T, sh->d, k, E, shape_bits(sh));
   return ffn_ws_bytes(sh->d, sh->I, ssh->I, T, k, E, path);
 }
 
@@ -473,7 +500,7 @@ extern "C" int moe_expert_ffn(const moe_pool* pool, const moe_ffn_shape* sh, con
                               size_t ws_bytes, hipStream_t s) {
   MOE_TRY(check_ffn(pool, sh, ssh, shared_blob, T, k));
   if (T == 0) return MOE_OK;
-  path = resolve_path(path, T, sh->d, k, pool->E);
+  path = resolve_path(path, T, sh->d, k, pool->E, shape_bits(sh));
   MOE_CHECK(x && idx && ws && aligned(x, 16) && aligned(ws, 256));
   FfnArgs a{};
   pool_view(pool, &a.pool);
@@ -550,7 +577,7 @@ static int check_layer(const moe_layer_desc* L) {
 
 extern "C" size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int32_t T, int32_t path) {
   if (check_layer(L) != MOE_OK || T < 0) return 0;
-  path = resolve_path(path, T, L->sh.d, L->k, L->E);
+  path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh));
   Carver c(nullptr, (size_t)-1);
   LayerWs w;
   carve_layer(c, L, T, path, &w);
@@ -565,15 +592,20 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   if (T == 0) return MOE_OK;
   MOE_CHECK(x && y && idx && w && sgate && ws);
   MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
-  path = resolve_path(path, T, L->sh.d, L->k, L->E);
+  path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh));
   if (path == MOE_PATH_DECODE) MOE_CHECK(T <= 8 && (long)T * (L->k + 1) <= 2048);
   Carver c(ws, ws_bytes);
   LayerWs lw;
   if (!carve_layer(c, L, T, path, &lw)) return MOE_ERR_INVALID_ARG;
   const int d = L->sh.d;
-  if (path == MOE_PATH_DECODE) {
+  const bool f32 = shape_bits(&L->sh) == 32;
+  if (path == MOE_PATH_DECODE && !f32) {
     // logits here; the decode FFN selects the experts in-kernel
     MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s, true));
+  } else if (path == MOE_PATH_DECODE) {
+    // f32 experts: top-k here, then the FFN with the routing given
+    MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, L->k, idx, w, sgate,
+                          L->usage_dev, lw.r, s, false));
   } else {
     // usage is counted from the buckets below (one atomic per expert); the
     // bf16 activation pairs are prepared only for the bucketed GEMVs
@@ -589,9 +621,11 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   a.T = T; a.k = L->k; a.idx = idx; a.w = w; a.sgate = sgate;
   if (path == MOE_PATH_DECODE) {
     a.y = y;
-    a.logits = lw.r.logits;
-    a.bias = L->logit_bias_dev;
-    a.usage = L->usage_dev;
+    if (!f32) {
+      a.logits = lw.r.logits;
+      a.bias = L->logit_bias_dev;
+      a.usage = L->usage_dev;
+    }
     return ffn_launch(a, path, lw.ffn_ws, lw.ffn_bytes, s);
   }
   MOE_TRY(bucket_launch(idx, T, L->k, L->E, lw.counts, lw.offsets, lw.pair_ids, lw.bucket_ws,

@@ -26,7 +26,7 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // -------------------------------------------------------------- layout
 // Byte offsets of the six sections of an expert blob (see moe355.h).
 struct MatLayout {
-  uint64_t codes;   // [in/32][out][16] (4-bit) or [in/16][out][16] (8-bit)
+  uint64_t codes;   // [in/32][out][16] (4-bit), [in/16][out][16] (8-bit) or fp32 [out][in]
   uint64_t sb;      // [in/64][out][2] fp16 (scale, bias)
 };
 struct BlobLayout {
@@ -43,7 +43,7 @@ __host__ __device__ inline BlobLayout blob_layout(int d, int I, int bits) {
     L.m[m].codes = off;
     off += (uint64_t)outs[m] * (uint64_t)ins[m] * (uint64_t)bits / 8;
     L.m[m].sb = off;
-    off += (uint64_t)(ins[m] / 64) * (uint64_t)outs[m] * 4;
+    if (bits != 32) off += (uint64_t)(ins[m] / 64) * (uint64_t)outs[m] * 4;   // f32: no scale/bias
   }
   L.bytes = off;
   L.stride = (off + 4095) & ~(uint64_t)4095;
@@ -51,8 +51,8 @@ __host__ __device__ inline BlobLayout blob_layout(int d, int I, int bits) {
 }
 
 bool shape_ok(const moe_ffn_shape* sh);
-// Code width of a valid shape (bits 0 reads as 4).
-inline int shape_bits(const moe_ffn_shape* sh) { return sh->bits == 8 ? 8 : 4; }
+// Code width of a valid shape (bits 0 reads as 4; 32 = unquantised fp32).
+inline int shape_bits(const moe_ffn_shape* sh) { return sh->bits == 8 || sh->bits == 32 ? sh->bits : 4; }
 
 // Device view of a pool, passed to kernels by value.
 struct PoolView {
@@ -134,6 +134,6 @@ size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
 size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E);
 int prefill_launch(const FfnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 int ffn_launch(const FfnArgs& a, int path, void* ws, size_t ws_bytes, hipStream_t s);
-int resolve_path(int path, int T, int d, int k, int E);
+int resolve_path(int path, int T, int d, int k, int E, int bits);
 
 }  // namespace moe

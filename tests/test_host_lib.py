@@ -60,8 +60,12 @@ def test_c_pack_matches_oracle_pack(name):
 
 def test_c_pack_golden_layout():
     for d, I, bits, nbytes, stride, codes, sbs, weights in golden_io.blob_layout():
-        if bits == 32:
-            continue
+        for mat, row, col, val, off, bits32 in weights:
+            raw = {m: {"weights": np.zeros(oquant.mat_dims(d, I)[m], np.float32)} for m in oquant.MATS}
+            raw[mat]["weights"][row, col] = val
+            blob = moe.moe_pack_expert(raw, d, I, 32)
+            assert blob.size == stride and blob[off:off + 4].tobytes() == int(bits32).to_bytes(4, "little")
+            assert np.count_nonzero(blob) == np.count_nonzero(blob[off:off + 4])
         assert moe.moe_blob_bytes(d, I, bits) == nbytes and moe.moe_blob_stride(d, I, bits) == stride
         dims = oquant.mat_dims(d, I)
         for mat, row, col, val, off, byte in codes:
@@ -76,17 +80,17 @@ def test_c_pack_golden_layout():
             assert back[mat]["codes"][row, col] == val and np.count_nonzero(back[mat]["codes"]) == 1
 
 
-@pytest.mark.parametrize("name", ["tiny_int8", "decode80b_int8"])
-def test_c_pack_int8_matches_oracle_pack(name):
+@pytest.mark.parametrize("name", ["tiny_int8", "decode80b_int8", "tiny_f32", "decode80b_f32"])
+def test_c_pack_int8_f32_matches_oracle_pack(name):
     cfg = ms.CONFIGS[name]
     for e in (0, 5):
         raw = ms.expert_raw(cfg, e)
-        a = moe.moe_pack_expert(raw, cfg.d, cfg.I, 8)
-        b = oquant.pack_expert(raw, cfg.d, cfg.I, 8)
-        assert a.size == oquant.blob_stride(cfg.d, cfg.I, 8) and np.array_equal(a, b)
-        back = moe.moe_unpack_expert(a, cfg.d, cfg.I, 8)
+        a = moe.moe_pack_expert(raw, cfg.d, cfg.I, cfg.bits)
+        b = oquant.pack_expert(raw, cfg.d, cfg.I, cfg.bits)
+        assert a.size == oquant.blob_stride(cfg.d, cfg.I, cfg.bits) and np.array_equal(a, b)
+        back = moe.moe_unpack_expert(a, cfg.d, cfg.I, cfg.bits)
         for m in oquant.MATS:
-            for f in ("codes", "scales", "biases"):
+            for f in raw[m]:
                 assert np.array_equal(back[m][f], raw[m][f])
     assert moe.moe_blob_bytes(2048, 512, 8) == 3342336
 
@@ -96,6 +100,7 @@ def test_c_pack_width_checks():
     refuse 8-bit shapes; the generic packer takes 4-bit raws at bits=4."""
     assert moe.moe_blob_bytes(2048, 512, 0) == moe.moe_blob_bytes(2048, 512, 4) == 1769472
     assert moe.moe_blob_bytes(2048, 512, 5) == 0 and moe.moe_blob_stride(2048, 512, 16) == 0
+    assert moe.moe_blob_bytes(2048, 512, 32) == 12582912
     cfg = ms.CONFIGS["tiny_int8"]
     raw = ms.expert_raw(cfg, 1)
     out = np.empty(moe.moe_blob_stride(cfg.d, cfg.I, 8), np.uint8)
@@ -114,6 +119,12 @@ def test_c_pack_width_checks():
         moe.moe_pack_expert(raw, cfg.d, cfg.I, 4)
     raw4 = ms.expert_raw(ms.CONFIGS["tiny"], 1)
     assert np.array_equal(moe.moe_pack_expert(raw4, 256, 64, 4), moe.moe_pack_expert_int4(raw4, 256, 64))
+    # the code-width entry points refuse the other widths
+    st = moe._lib.moe_pack_expert(C.byref(moe.shape(256, 64, 32)), cp, sp, bp, out.ctypes.data)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    wp = (C.c_void_p * 3)(cp[0], cp[1], cp[2])
+    st = moe._lib.moe_pack_expert_f32(C.byref(moe.shape(256, 64, 8)), wp, out.ctypes.data)
+    assert st == moe.MOE_ERR_INVALID_ARG
 
 
 def test_c_pack_rejects_bad_codes_and_shapes():
