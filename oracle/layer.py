@@ -15,6 +15,16 @@ are combined.  Readings where the pages are silent:
     silu(z) = z / (1 + exp(-z));
   * y_t = sum_r w[t,r] o_{e_r}(x_t) + s_t o_shared(x_t).
 
+A chain of L such layers (several MoE layers per token, the next item after
+one layer; the pages' models stack dozens of them) follows the pre-norm
+residual form of the decoder these layers sit in, read without the
+attention half and without a learned norm weight:
+
+  u_l = bf16(x_l / sqrt(mean(x_l^2) + eps)),  x_{l+1} = bf16(fp32(x_l + MoE_l(u_l))),
+
+the residual stream and the MoE input carried in bf16 (the layer's input
+type), eps = 1e-6.
+
 Everything is float64 on exactly decoded inputs; the only library primitives
 are numpy's matmul and sort.
 """
@@ -129,3 +139,35 @@ def logit_error_bound(x_bits: np.ndarray, w_router, bias, depth: int) -> np.ndar
         b = np.abs(np.asarray(bias, np.float64))
         r = r + 2 * u * (a.max(axis=1) + b.max())
     return r
+
+
+# ----------------------------------------------------------------- chains
+def bf16_round(v) -> np.ndarray:
+    """bf16 bits of fp32 values, round to nearest, ties to even (written out
+    on the fp32 bit pattern; finite inputs)."""
+    u = np.ascontiguousarray(np.asarray(v, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    keep = u >> 16
+    rest = u & 0xFFFF
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & 1) == 1))
+    return (keep + up).astype(np.uint16)
+
+
+def rms_norm_bf16(x_bits: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """u = x / sqrt(mean(x^2) + eps) per row, exact in fp64, rounded to bf16."""
+    x = bf16_to_f64(x_bits)
+    u = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return bf16_round(u.astype(np.float32))
+
+
+def residual_bf16(x_bits: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """bf16(fp32(x + y)): the residual add in fp32, rounded to bf16."""
+    s = bf16_to_f64(x_bits).astype(np.float32) + np.asarray(y, dtype=np.float64).astype(np.float32)
+    return bf16_round(s)
+
+
+def chain_layer(x_bits: np.ndarray, layer: dict, eps: float = 1e-6, idx=None):
+    """One residual MoE block.  layer: dict(w_router, bias, k, expert, shared).
+    Returns (x_next_bits, u_bits, layer result dict)."""
+    u = rms_norm_bf16(x_bits, eps)
+    res = moe_layer(u, layer["w_router"], layer["bias"], layer["k"], layer["expert"], layer["shared"], idx=idx)
+    return residual_bf16(x_bits, res["y"]), u, res

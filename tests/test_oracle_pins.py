@@ -410,3 +410,45 @@ def test_logit_error_bound_holds_for_fp32_sums():
     seq = (seq + b).astype(np.float32)
     r = olayer.logit_error_bound(xb, Wr, b, depth=cfg.d)
     assert np.max(np.abs(seq - exact[0])) <= r[0]
+
+
+# ---- chains of MoE layers: norm, residual, bf16 rounding -------------------
+def test_bf16_round_hand_values_and_generator_agree():
+    """Round-to-nearest-even onto bf16 at hand-checked points (ties go to the
+    even mantissa), and agreement with the input generator's independent
+    rounding on random values."""
+    v = np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.5, 1 + 2 ** -7 + 2 ** -9, 0.0, -0.0])
+    assert olayer.bf16_round(v).tolist() == [0x3F80, 0x3F82, 0xC020, 0x3F81, 0x0000, 0x8000]
+    r = np.random.default_rng(3).standard_normal(100000).astype(np.float32) * 37
+    assert np.array_equal(olayer.bf16_round(r), ms.f32_to_bf16_bits(r))
+
+
+def test_rms_norm_closed_forms():
+    # constant row: x / sqrt(x^2 + eps) rounds to 1.0 in bf16
+    x = np.full((2, 256), 0x4000, np.uint16)                    # 2.0
+    assert np.all(olayer.rms_norm_bf16(x) == 0x3F80)
+    # (3, -4): mean square 12.5, u = (0.84853, -1.13137) -> bf16 0.84765625, -1.1328125
+    x = np.array([[0x4040, 0xC080]], np.uint16)
+    assert olayer.rms_norm_bf16(x).tolist() == [[0x3F59, 0xBF91]]
+    # scale invariance up to eps: a power-of-two scale leaves u unchanged
+    xb = ms.x_bits(TINY, 3)
+    xs = ms.f32_to_bf16_bits(ms.bf16_bits_to_f32(xb) * np.float32(8.0))
+    assert np.array_equal(olayer.rms_norm_bf16(xb, 0.0), olayer.rms_norm_bf16(xs, 0.0))
+
+
+def test_residual_rounding_and_zero_layer():
+    one = np.array([0x3F80], np.uint16)
+    assert olayer.residual_bf16(one, np.array([2.0 ** -8])).tolist() == [0x3F80]       # tie -> even
+    assert olayer.residual_bf16(one, np.array([3 * 2.0 ** -8])).tolist() == [0x3F82]   # tie -> even (up)
+    # a layer whose experts all have zero down matrices adds nothing
+    cfg = TINY
+    zero_down = lambda raw: {**raw, "down": {"codes": np.zeros_like(raw["down"]["codes"]),
+                                             "scales": raw["down"]["scales"],
+                                             "biases": np.zeros_like(raw["down"]["biases"])}}
+    ex = _tiny_experts(cfg)
+    layer = dict(w_router=ms.router_weight(cfg), bias=None, k=cfg.k,
+                 expert=lambda e: zero_down(ex(e)), shared=zero_down(ms.shared_raw(cfg)))
+    xb = ms.x_bits(cfg, 2)
+    xn, u, res = olayer.chain_layer(xb, layer)
+    assert np.array_equal(xn, xb) and not res["y"].any()
+    assert np.array_equal(u, olayer.rms_norm_bf16(xb))
