@@ -18,7 +18,8 @@ the CPU oracle timed on a bounded sample of the same steps (cpu_baseline).
 pool refilled by LFU + recency from pinned host memory, batch80b: T=64,
 prefill80b / prefill80b_zipf: T=4096 on the matrix cores; decode80b_int8,
 batch80b_int8, prefill80b_int8: the same layers with 8-bit experts;
-decode80b_f32, batch80b_f32: with unquantised fp32 experts);
+decode80b_f32, batch80b_f32: with unquantised fp32 experts; chain80b: 48
+such decode layers per token, as pre-norm residual blocks);
 --workload all prints one line per workload, the headline first;
 --workload refill_sweep prints the refill run for pool sizes 64..512 (hit
 rate vs tokens/s).
@@ -423,6 +424,56 @@ def run_prefill(c, name, reps):
             "max_bucket": int(counts.max())}
 
 
+def run_chain(c, K, W, L=48):
+    """L layers of the 80B decode shape per token (the 80B model stacks 48
+    MoE layers), each layer its own router, shared expert and 512-expert pool
+    (distinct HBM, 43 GB in all), applied by moe_chain_forward as pre-norm
+    residual blocks; K tokens captured in one HIP graph."""
+    torch, ms, moe = c.torch, c.ms, c.moe
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], n_slots=512)
+    log(f"chain80b: {L} layers, steps={K} warmup={W}")
+    staging = packed_experts(c, cfg)
+    layers = []
+    for l in range(L):
+        cl = ms.scaled(cfg, seed=cfg.seed + 97 * l)
+        layers.append(build_layers(c, cl, 1, staging=staging)[0])
+        if l % 8 == 7:
+            log(f"layer {l + 1}/{L} ready")
+    del staging
+    torch.cuda.empty_cache()
+    chain = moe.Chain(layers)
+    n = K + W
+    xall = x_steps(c, cfg, n)
+    ws = torch.zeros(chain.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
+    out = torch.empty((n, 1, cfg.d), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        moe.moe_chain_forward(chain, xall[i], path=moe.MOE_PATH_DECODE, workspace=ws, out=out[i])
+
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    stream = torch.cuda.Stream()
+    graph_time(c, step, 0, W, stream)
+    ms_tok = graph_time(c, step, W, n, stream)
+    assert torch.equal(out, ref), "graph replay differs from eager"
+    for Lr in layers:
+        assert Lr.pool.check_error() == moe.MOE_OK
+    expert_bytes = L * (cfg.k + 1) * moe.moe_blob_bytes(cfg.d, cfg.I)
+    gbs = expert_bytes / (ms_tok * 1e-3) / 1e9
+    return {"metric": "MoE-stack decode tokens/s (48 routed-expert layers per token, int4, 80B shape)",
+            "value": round(1000.0 / ms_tok, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+            "ms_per_step": round(ms_tok, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
+            "config": {"workload": f"chain of {L} 80B-shape MoE layers per token (pre-norm residual blocks), "
+                                   "batch-1 decode, every layer's 512 experts resident",
+                       "layers": L, "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "hip_graph": True},
+            "us_per_layer": round(ms_tok * 1e3 / L, 2),
+            "expert_bytes_per_token": expert_bytes,
+            "layer_expert_GBps": round(gbs, 1), "layer_expert_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def copy_probe(mb):
     """A plain device-to-device copy of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -451,7 +502,7 @@ def main():
     ap.add_argument("--workload", default="decode80b",
                     choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
                              "prefill80b_zipf", "decode80b_int8", "batch80b_int8", "prefill80b_int8",
-                             "decode80b_f32", "batch80b_f32", "all", "refill_sweep"])
+                             "decode80b_f32", "batch80b_f32", "chain80b", "all", "refill_sweep"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
@@ -464,7 +515,8 @@ def main():
     c.torch.cuda.set_device(0)
     cpu = 0 if args.no_cpu else args.cpu_steps
     todo = ["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b", "prefill80b_zipf",
-            "decode80b_int8", "batch80b_int8", "prefill80b_int8", "decode80b_f32", "batch80b_f32"] \
+            "decode80b_int8", "batch80b_int8", "prefill80b_int8", "decode80b_f32", "batch80b_f32",
+            "chain80b"] \
         if args.workload == "all" else [args.workload]
     for wl in todo:
         if wl in ("decode80b", "decode35b", "decode80b_int8", "decode80b_f32"):
@@ -484,6 +536,8 @@ def main():
                 print(json.dumps(res), flush=True)
                 c.torch.cuda.empty_cache()
             continue
+        elif wl == "chain80b":
+            res = run_chain(c, min(args.steps, 50), min(args.warmup, 5))
         elif wl in ("batch80b", "batch80b_int8", "batch80b_f32"):
             res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4), wl)
         else:

@@ -329,6 +329,27 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x_dev,
                       void* workspace_dev, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* ------------------------------------------------------------ layer chain
+ * L layers applied one after the other to the same T tokens (the pages'
+ * models stack dozens of MoE layers per token).  Each is a pre-norm residual
+ * block read without the attention half and without a learned norm weight:
+ *   u_l = bf16(x_l / sqrt(mean(x_l^2) + eps)),
+ *   x_{l+1} = bf16(x_l + moe_layer_forward(layers[l], u_l)),
+ * the residual add in fp32, the sum of squares in fp32 in a fixed order.
+ * All layers share d and k.  x_dev [T][d] bf16 in, x_out_dev [T][d] bf16 out
+ * (x_L).  Optional (NULL = not wanted): trace_x_dev [L+1][T][d] (x_0..x_L),
+ * trace_u_dev [L][T][d] (u_0..u_{L-1}), topk_idx_dev [L][T][k].  path as in
+ * moe_layer_forward, for every layer.  Everything goes on `stream`, one
+ * launch for the residual/norm step plus each layer's own per layer. */
+size_t moe_chain_workspace_bytes(const moe_layer_desc* layers, int32_t L,
+                                 int32_t T, int32_t path);
+int moe_chain_forward(const moe_layer_desc* layers, int32_t L, float eps,
+                      const uint16_t* x_dev, int32_t T, uint16_t* x_out_dev,
+                      uint16_t* trace_x_dev, uint16_t* trace_u_dev,
+                      int32_t* topk_idx_dev, int32_t path,
+                      void* workspace_dev, size_t workspace_bytes,
+                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,6 +107,8 @@ _SIGS = {
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_layer_workspace_bytes": (_S, [_P, _I, _I]),
     "moe_layer_forward": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
+    "moe_chain_workspace_bytes": (_S, [_P, _I, _I, _I]),
+    "moe_chain_forward": (C.c_int, [_P, _I, C.c_float, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -484,3 +486,38 @@ def moe_layer_forward(layer: Layer, x, path: int = MOE_PATH_AUTO, workspace=None
                                 path, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "moe_layer_forward")
     return y, idx, w, s
+
+
+# -------------------------------------------------------------- layer chain
+class Chain:
+    """L layers applied one after the other (pre-norm residual blocks)."""
+
+    def __init__(self, layers: Sequence[Layer], eps: float = 1e-6):
+        self.layers = list(layers)
+        self.eps = eps
+        self.descs = (moe_layer_desc * len(self.layers))(*[L.desc for L in self.layers])
+        self.k = self.layers[0].k
+
+    def workspace_bytes(self, T: int, path: int = MOE_PATH_AUTO) -> int:
+        return int(_lib.moe_chain_workspace_bytes(self.descs, len(self.layers), T, path))
+
+
+def moe_chain_forward(chain: Chain, x, path: int = MOE_PATH_AUTO, trace: bool = False, workspace=None,
+                      out=None, stream=None, trace_u: bool = True):
+    """Returns x_L (bf16 [T, d]); with trace=True also (trace_x [L+1, T, d],
+    trace_u [L, T, d] (None if trace_u=False), topk_idx [L, T, k])."""
+    import torch
+    T, d = x.shape
+    L = len(chain.layers)
+    x_out = torch.empty_like(x) if out is None else out
+    tx = tu = ti = None
+    if trace:
+        tx = torch.empty((L + 1, T, d), dtype=x.dtype, device=x.device)
+        tu = torch.empty((L, T, d), dtype=x.dtype, device=x.device) if trace_u else None
+        ti = torch.empty((L, T, chain.k), dtype=torch.int32, device=x.device)
+    if workspace is None:
+        workspace = _ws(chain.workspace_bytes(T, path))
+    st = _lib.moe_chain_forward(chain.descs, L, C.c_float(chain.eps), _ptr(x), T, _ptr(x_out), _ptr(tx), _ptr(tu),
+                                _ptr(ti), path, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "moe_chain_forward")
+    return (x_out, tx, tu, ti) if trace else x_out

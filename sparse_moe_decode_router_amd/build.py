@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmoe355.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["router.hip", "bucket.hip", "ffn_gemv.hip", "ffn_mfma.hip", "combine.hip", "host.cpp"]
+SOURCES = ["router.hip", "bucket.hip", "ffn_gemv.hip", "ffn_mfma.hip", "combine.hip", "chain.hip", "host.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
