@@ -339,8 +339,13 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x_dev,
  * All layers share d and k.  x_dev [T][d] bf16 in, x_out_dev [T][d] bf16 out
  * (x_L).  Optional (NULL = not wanted): trace_x_dev [L+1][T][d] (x_0..x_L),
  * trace_u_dev [L][T][d] (u_0..u_{L-1}), topk_idx_dev [L][T][k].  path as in
- * moe_layer_forward, for every layer.  Everything goes on `stream`, one
- * launch for the residual/norm step plus each layer's own per layer. */
+ * moe_layer_forward, for every layer.  Everything goes on `stream`.
+ * When every layer takes the decode path with 4- or 8-bit experts and
+ * trace_u_dev is NULL, the layers hand the residual stream on themselves
+ * (each down GEMV adds its output to x_l and sums the squares of x_{l+1} in
+ * groups of 8, the next router normalises): one extra launch for the whole
+ * chain.  Otherwise one launch per layer for the residual/norm step.  Both
+ * give the same bits (same fp32 operations in the same order). */
 size_t moe_chain_workspace_bytes(const moe_layer_desc* layers, int32_t L,
                                  int32_t T, int32_t path);
 int moe_chain_forward(const moe_layer_desc* layers, int32_t L, float eps,

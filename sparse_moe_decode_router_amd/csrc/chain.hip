@@ -4,10 +4,11 @@
 // residual block read without the attention half and without a learned norm
 // weight:
 //   u_l = bf16(x_l / sqrt(mean(x_l^2) + eps)),  x_{l+1} = bf16(x_l + MoE_l(u_l)),
-// the residual add in fp32.  Per layer: one glue launch (residual add of the
-// previous layer's output, sum of squares, normalised bf16 input), then the
-// layer's own launches; the whole chain goes on one stream, so a caller can
-// capture it in a single HIP graph.
+// the residual add in fp32.  Decode layers of quantised experts hand the
+// residual stream on inside their own launches (the down kernel adds the
+// layer output and sums squares, the next router normalises); other layers
+// take one glue launch each.  The whole chain goes on one stream, so a
+// caller can capture it in a single HIP graph.
 #include "internal.h"
 #include "device.h"
 
@@ -18,8 +19,15 @@ constexpr int kGlueThreads = 256;
 
 // One block per token.  y == nullptr: x_out = x (the first layer).  u_out ==
 // nullptr: no normalisation (after the last layer).
-constexpr int kGlueMax = 8192 / kGlueThreads;   // elements per thread (d <= 8192)
+constexpr int kGlueGroups = 8192 / 8 / kGlueThreads;   // groups of 8 elements per thread (d <= 8192)
 
+// The sum of squares of a row in chain order: the row cut into groups of 8
+// consecutive elements, each group summed as sq_tree8; thread tid adds the
+// groups tid, tid + 256, ... in that order; then a wave butterfly and the
+// four waves as (w0 + w1) + (w2 + w3).  The decode down kernel produces the
+// same group sums (its 8 lanes per 8 output rows, sum8_dpp) and the decode
+// router adds them up the same way, so a chain gives the same bits with or
+// without this kernel between its layers.
 __global__ __launch_bounds__(kGlueThreads) void chain_glue_kernel(const uint16_t* __restrict__ x,
                                                                   const float* __restrict__ y, int d, float eps,
                                                                   uint16_t* __restrict__ x_out,
@@ -27,26 +35,44 @@ __global__ __launch_bounds__(kGlueThreads) void chain_glue_kernel(const uint16_t
   __shared__ float red[kGlueThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t base = (size_t)t * d;
-  // all loads first, values kept in registers for the second pass
-  float v[kGlueMax];
+  const int ng = d / 8;
+  // all loads first; x_l kept in registers for the second pass
+  float v[kGlueGroups][8];
 #pragma unroll
-  for (int j = 0; j < kGlueMax; ++j) {
-    const int c = tid + kGlueThreads * j;
-    v[j] = 0.f;
-    if (c < d) {
-      v[j] = __uint_as_float((uint32_t)x[base + c] << 16);
-      if (y) v[j] += y[base + c];
+  for (int j = 0; j < kGlueGroups; ++j) {
+    const int g = tid + kGlueThreads * j;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+    if (g < ng) {
+      const uint4 xv = reinterpret_cast<const uint4*>(x + base)[g];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[j][2 * i] = bf16_lo(xw[i]);
+        v[j][2 * i + 1] = bf16_hi(xw[i]);
+      }
+      if (y) {
+        const float4 y0 = reinterpret_cast<const float4*>(y + base)[2 * g];
+        const float4 y1 = reinterpret_cast<const float4*>(y + base)[2 * g + 1];
+        v[j][0] += y0.x; v[j][1] += y0.y; v[j][2] += y0.z; v[j][3] += y0.w;
+        v[j][4] += y1.x; v[j][5] += y1.y; v[j][6] += y1.z; v[j][7] += y1.w;
+      }
     }
   }
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kGlueMax; ++j) {
-    const int c = tid + kGlueThreads * j;
-    if (c < d) {
-      const uint32_t b = f32_to_bf16(v[j]);
-      x_out[base + c] = (uint16_t)b;
-      v[j] = __uint_as_float(b << 16);
-      ss = fmaf(v[j], v[j], ss);
+  for (int j = 0; j < kGlueGroups; ++j) {
+    const int g = tid + kGlueThreads * j;
+    if (g < ng) {
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        b[i] = f32_to_bf16(v[j][i]);
+        v[j][i] = __uint_as_float(b[i] << 16);
+      }
+      reinterpret_cast<uint4*>(x_out + base)[g] =
+          make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+      ss += sq_tree8(v[j]);
     }
   }
   if (!u_out) return;
@@ -56,9 +82,15 @@ __global__ __launch_bounds__(kGlueThreads) void chain_glue_kernel(const uint16_t
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float scale = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
-  for (int j = 0; j < kGlueMax; ++j) {
-    const int c = tid + kGlueThreads * j;
-    if (c < d) u_out[base + c] = (uint16_t)f32_to_bf16(v[j] * scale);
+  for (int j = 0; j < kGlueGroups; ++j) {
+    const int g = tid + kGlueThreads * j;
+    if (g < ng) {
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = f32_to_bf16(v[j][i] * scale);
+      reinterpret_cast<uint4*>(u_out + base)[g] =
+          make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+    }
   }
 }
 
@@ -73,6 +105,7 @@ struct ChainWs {
   uint16_t* resid[2]; // [T][d] residual stream, layers alternate (when not traced)
   uint16_t* u;        // [T][d] normalised layer input (when not traced)
   float* y;           // [T][d] layer output
+  float* ssp[2];      // [T][d/8] sums of squares handed from layer to layer
   float* w;           // [T][k]
   float* sgate;       // [T]
   int32_t* idx;       // [T][k] (when not returned)
@@ -86,6 +119,8 @@ bool carve_chain(Carver& c, const moe_layer_desc* layers, int L, int T, int path
   w->resid[1] = c.take<uint16_t>((size_t)T * d);
   w->u = c.take<uint16_t>((size_t)T * d);
   w->y = c.take<float>((size_t)T * d);
+  w->ssp[0] = c.take<float>((size_t)T * d / 8);
+  w->ssp[1] = c.take<float>((size_t)T * d / 8);
   w->w = c.take<float>((size_t)T * k);
   w->sgate = c.take<float>((size_t)T);
   w->idx = c.take<int32_t>((size_t)T * k);
@@ -138,6 +173,29 @@ extern "C" int moe_chain_forward(const moe_layer_desc* layers, int32_t L, float 
   // x_l and x_{l-1} alternate between two buffers (or the trace)
   auto resid = [&](int l) { return trace_x ? trace_x + (size_t)l * td : w.resid[l & 1]; };
   auto uin = [&](int l) { return trace_u ? trace_u + (size_t)l * td : w.u; };
+  // Decode layers of 4- and 8-bit experts hand the residual stream on
+  // themselves (ChainIO): the down kernel writes x_{l+1} and its sums of
+  // squares, the next router normalises; no glue launch between them, and
+  // the same bits as with it.  Otherwise (other paths, f32 experts, or the
+  // normalised inputs wanted as a trace) a glue launch per layer.
+  bool handover = !trace_u;
+  for (int l = 0; l < L && handover; ++l) {
+    const moe_layer_desc* D = &layers[l];
+    handover = shape_bits(&D->sh) != 32 && shape_bits(&D->shared_sh) != 32 &&
+               resolve_path(path, T, d, D->k, D->E, shape_bits(&D->sh)) == MOE_PATH_DECODE;
+  }
+  if (handover) {
+    MOE_TRY(glue_launch(x, nullptr, T, d, eps, resid(0), w.u, s));        // x_0 and u_0
+    for (int l = 0; l < L; ++l) {
+      int32_t* idx = topk_idx ? topk_idx + (size_t)l * T * k : w.idx;
+      ChainIO io{l == 0 ? nullptr : w.ssp[l & 1], eps, resid(l), l + 1 == L ? x_out : resid(l + 1),
+                 w.ssp[(l + 1) & 1]};
+      MOE_TRY(layer_forward(&layers[l], l == 0 ? w.u : resid(l), T, w.y, idx, w.w, w.sgate, path, w.layer_ws,
+                            w.layer_bytes, s, &io));
+    }
+    if (trace_x) MOE_HIP(hipMemcpyAsync(trace_x + (size_t)L * td, x_out, td * 2, hipMemcpyDeviceToDevice, s));
+    return MOE_OK;
+  }
   for (int l = 0; l < L; ++l) {
     int32_t* idx = topk_idx ? topk_idx + (size_t)l * T * k : w.idx;
     // x_l = bf16(x_{l-1} + y_{l-1}) (x_0 copied) and u_l

@@ -79,4 +79,13 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Sum of squares of 8 consecutive values in the order sum8_dpp adds them
+// across 8 lanes: ((e0+e1)+(e2+e3))+((e4+e5)+(e6+e7)), e = v*v rounded.
+__device__ __forceinline__ float sq_tree8(const float* v) {
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = __fmul_rn(v[i], v[i]);
+  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+}
+
 }  // namespace moe

@@ -571,6 +571,11 @@ struct DownArgs {
   const int32_t* pair_ids;
   float* partial;
   float* shared_out;
+  // decode, chains of layers: x_{l+1} = bf16(res_in + y) and the sums of
+  // squares of each 8 output rows
+  const uint16_t* res_in;
+  uint16_t* res_out;
+  float* ssp_out;
 };
 
 // Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order
@@ -657,7 +662,15 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
     float y = 0.f;
     for (int q2 = 0; q2 < a.k; ++q2) y += wk[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
     y += wk[nR + t] * oi[(nR + t) * 8 + rr];
-    a.y[(size_t)t * a.d + jb * 8 + rr] = y;
+    const size_t yi = (size_t)t * a.d + jb * 8 + rr;
+    a.y[yi] = y;
+    if (a.res_out) {                            // chain hand-over (all 8 lanes of a token active)
+      const uint32_t b = f32_to_bf16(__uint_as_float((uint32_t)a.res_in[yi] << 16) + y);
+      a.res_out[yi] = (uint16_t)b;
+      const float r = __uint_as_float(b << 16);
+      const float p = sum8_dpp(__fmul_rn(r, r));
+      if (rr == 0) a.ssp_out[(size_t)t * (a.d / 8) + jb] = p;
+    }
   }
 }
 
@@ -1235,6 +1248,8 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   dn.pool = f.pool; dn.shared_blob = f.shared_blob;
   dn.d = f.d; dn.I = f.I; dn.Ish = f.Ish; dn.Imax = Imax; dn.T = f.T; dn.k = f.k;
   dn.sel_slot = w.sel_slot; dn.w = f.w; dn.sgate = f.sgate; dn.hq = w.hq; dn.hs8 = w.hs8; dn.y = f.y;
+  dn.res_in = f.res_in; dn.res_out = f.res_out; dn.ssp_out = f.ssp_out;
+  if (f.res_out && (path != MOE_PATH_DECODE || f.bits == 32)) return MOE_ERR_INVALID_ARG;
 
   if (f.bits == 32) return f32_launch(f, path, g, dn, w, Imax, s);
   if (path == MOE_PATH_DECODE) {

@@ -584,9 +584,9 @@ extern "C" size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int32_t T, 
   return c.off + 256;
 }
 
-extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, float* y,
-                                 int32_t* idx, float* w, float* sgate, int32_t path, void* ws,
-                                 size_t ws_bytes, hipStream_t s) {
+namespace moe {
+int layer_forward(const moe_layer_desc* L, const uint16_t* x, int T, float* y, int32_t* idx, float* w,
+                  float* sgate, int path, void* ws, size_t ws_bytes, hipStream_t s, const ChainIO* io) {
   MOE_TRY(check_layer(L));
   MOE_CHECK(T >= 0);
   if (T == 0) return MOE_OK;
@@ -594,6 +594,8 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
   path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh));
   if (path == MOE_PATH_DECODE) MOE_CHECK(T <= 8 && (long)T * (L->k + 1) <= 2048);
+  // the chain hand-over exists on the decode path of 4- and 8-bit experts
+  if (io) MOE_CHECK(path == MOE_PATH_DECODE && shape_bits(&L->sh) != 32 && shape_bits(&L->shared_sh) != 32);
   Carver c(ws, ws_bytes);
   LayerWs lw;
   if (!carve_layer(c, L, T, path, &lw)) return MOE_ERR_INVALID_ARG;
@@ -601,7 +603,8 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   const bool f32 = shape_bits(&L->sh) == 32;
   if (path == MOE_PATH_DECODE && !f32) {
     // logits here; the decode FFN selects the experts in-kernel
-    MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s, true));
+    MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s, true, io ? io->ssp_in : nullptr,
+                                 io ? io->eps : 0.f));
   } else if (path == MOE_PATH_DECODE) {
     // f32 experts: top-k here, then the FFN with the routing given
     MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, L->k, idx, w, sgate,
@@ -626,6 +629,11 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
       a.bias = L->logit_bias_dev;
       a.usage = L->usage_dev;
     }
+    if (io) {
+      a.res_in = io->res_in;
+      a.res_out = io->res_out;
+      a.ssp_out = io->ssp_out;
+    }
     return ffn_launch(a, path, lw.ffn_ws, lw.ffn_bytes, s);
   }
   MOE_TRY(bucket_launch(idx, T, L->k, L->E, lw.counts, lw.offsets, lw.pair_ids, lw.bucket_ws,
@@ -634,4 +642,11 @@ extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int
   a.partial = lw.partial; a.shared_out = lw.shared_out;
   MOE_TRY(ffn_launch(a, path, lw.ffn_ws, lw.ffn_bytes, s));
   return combine_launch(lw.partial, lw.shared_out, w, sgate, T, L->k, d, y, s);
+}
+}  // namespace moe
+
+extern "C" int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, float* y,
+                                 int32_t* idx, float* w, float* sgate, int32_t path, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
+  return layer_forward(L, x, T, y, idx, w, sgate, path, ws, ws_bytes, s, nullptr);
 }

@@ -87,15 +87,34 @@ struct RouterWs {
   uint32_t* xq;       // [T][d/2]  bf16 pairs (x[8m+i], x[8m+i+4])
   float* xs;          // [T][d/64] group sums of x
 };
+// A chain of layers (chain.hip) hands its residual stream from layer to
+// layer without a separate launch: the decode down kernel writes
+// x_{l+1} = bf16(x_l + y_l) and, per 8 output rows, the sum of their squares
+// (sq_tree8 order); the next decode router forms
+//   u = bf16(x * 1 / sqrt(sum / d + eps))
+// from x and those partial sums (summed in chain_sum_sq order).
+struct ChainIO {
+  const float* ssp_in;      // router: [T][d/8] partial sums of squares of its input (or null)
+  float eps;
+  const uint16_t* res_in;   // down: x_l [T][d]
+  uint16_t* res_out;        // down: x_{l+1} [T][d]
+  float* ssp_out;           // down: [T][d/8]
+};
 size_t router_ws_bytes(int T, int d, int E);
 bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws);
 // prep_x: also fill ws.xq / ws.xs for T > 8 (T <= 8 always does, in-kernel)
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias,
                   int E, int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
                   const RouterWs& ws, hipStream_t s, bool prep_x);
-// logits [T][E+1] (+ xq/xs) only; the decode FFN selects in-kernel
+// moe_layer_forward with a chain's hand-over (decode path of 4- and 8-bit
+// experts only) or none (io == nullptr).
+int layer_forward(const moe_layer_desc* L, const uint16_t* x, int T, float* y, int32_t* idx, float* w,
+                  float* sgate, int path, void* ws, size_t ws_bytes, hipStream_t s, const ChainIO* io);
+// logits [T][E+1] (+ xq/xs) only; the decode FFN selects in-kernel.
+// ssp/eps (T <= 8): x is a chain's residual stream, normalised here.
 int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
-                         const RouterWs& ws, hipStream_t s, bool prep_x);
+                         const RouterWs& ws, hipStream_t s, bool prep_x,
+                         const float* ssp = nullptr, float eps = 0.f);
 int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx,
                 float* w, float* sgate, uint32_t* usage, hipStream_t s);
 
@@ -129,6 +148,9 @@ struct FfnArgs {
   float* y;                 // decode: [T][d]
   float* partial;           // batched: [T*k][d]
   float* shared_out;        // batched: [T][d]
+  const uint16_t* res_in;   // decode, chains: residual hand-over (see ChainIO)
+  uint16_t* res_out;
+  float* ssp_out;
 };
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
 size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E);

@@ -40,6 +40,37 @@ __device__ void xprep_group(const uint16_t* __restrict__ x, int d, int t, int g,
   xs[(size_t)t * (d / 64) + g] = s;
 }
 
+// The same group of u = bf16(x * scale) (a chain's normalised layer input).
+__device__ __forceinline__ uint32_t scaled_bf16(uint32_t xbits16, float scale) {
+  return f32_to_bf16(__uint_as_float(xbits16 << 16) * scale);
+}
+__device__ void xprep_group_scaled(const uint16_t* __restrict__ x, float scale, int d, int t, int g,
+                                   uint32_t* __restrict__ xq, float* __restrict__ xs) {
+  const uint16_t* src = x + (size_t)t * d + 64 * g;
+  uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)t * (d / 2) + 32 * g);
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t e[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[2 * i] = scaled_bf16(w[i] & 0xFFFFu, scale);
+      e[2 * i + 1] = scaled_bf16(w[i] >> 16, scale);
+    }
+    uint4 p;
+    p.x = e[0] | (e[4] << 16);
+    p.y = e[1] | (e[5] << 16);
+    p.z = e[2] | (e[6] << 16);
+    p.w = e[3] | (e[7] << 16);
+    dst[q] = p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += __uint_as_float(e[i] << 16);
+  }
+  xs[(size_t)t * (d / 64) + g] = s;
+}
+
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int T, int d,
                                                     uint32_t* __restrict__ xq, float* __restrict__ xs) {
   const int G = d / 64;
@@ -61,6 +92,8 @@ struct DecodeArgs {
   const uint16_t* x; int T, d;
   const float* W; int E;
   float* logits; uint32_t* xq; float* xs;
+  const float* ssp;             // chains: [T][d/8] partial sums of squares of x (or null)
+  float eps;
 };
 
 template <int TMAX>
@@ -69,10 +102,42 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   const int d = a.d, T = a.T, E = a.E;
+  const bool chain = a.ssp != nullptr;
+  float scale[TMAX];
+  if (chain) {
+    // x is a chain's residual stream: every block forms the same scale from
+    // the partial sums of squares, added up in the same order as the chain
+    // glue kernel adds its own (per-thread groups tid, tid + 256, ...; wave
+    // butterfly; (w0 + w1) + (w2 + w3))
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      float ss = 0.f;
+      if (t < T)
+        for (int g = tid; g < d / 8; g += kRouterThreads) ss += a.ssp[(size_t)t * (d / 8) + g];
+      ss = wave_sum(ss);
+      if (lane == 0) red[wave][t] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+      scale[t] = 1.0f / sqrtf(((red[0][t] + red[1][t]) + (red[2][t] + red[3][t])) / (float)d + a.eps);
+    __syncthreads();
+  }
   {
     const int G = d / 64;
     const int id = blockIdx.x * kRouterThreads + tid;
-    if (id < T * G) xprep_group(a.x, d, id / G, id % G, a.xq, a.xs);
+    if (id < T * G) {
+      const int t = id / G;
+      if (chain) {
+        float sc = 1.f;
+#pragma unroll
+        for (int q = 0; q < TMAX; ++q)
+          if (q == t) sc = scale[q];
+        xprep_group_scaled(a.x, sc, d, t, id % G, a.xq, a.xs);
+      } else {
+        xprep_group(a.x, d, t, id % G, a.xq, a.xs);
+      }
+    }
   }
   float acc[TMAX];
 #pragma unroll
@@ -83,7 +148,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(a.x + (size_t)t * d + 4 * c);
+        uint2 xv = *reinterpret_cast<const uint2*>(a.x + (size_t)t * d + 4 * c);
+        if (chain)
+          xv = make_uint2(scaled_bf16(xv.x & 0xFFFFu, scale[t]) | (scaled_bf16(xv.x >> 16, scale[t]) << 16),
+                          scaled_bf16(xv.y & 0xFFFFu, scale[t]) | (scaled_bf16(xv.y >> 16, scale[t]) << 16));
         acc[t] += wv.x * bf16_lo(xv.x);
         acc[t] += wv.y * bf16_hi(xv.x);
         acc[t] += wv.z * bf16_lo(xv.y);
@@ -273,10 +341,11 @@ bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws) {
 }
 
 int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E, const RouterWs& ws,
-                         hipStream_t s, bool prep_x) {
+                         hipStream_t s, bool prep_x, const float* ssp, float eps) {
   if (T == 0) return MOE_OK;
+  if (ssp && T > 8) return MOE_ERR_INVALID_ARG;
   if (T <= 8) {
-    DecodeArgs a{x, T, d, W, E, ws.logits, ws.xq, ws.xs};
+    DecodeArgs a{x, T, d, W, E, ws.logits, ws.xq, ws.xs, ssp, eps};
     void* fn = T == 1 ? (void*)router_decode_kernel<1> : T == 2 ? (void*)router_decode_kernel<2>
              : T <= 4 ? (void*)router_decode_kernel<4> : (void*)router_decode_kernel<8>;
     void* args[] = {&a};

@@ -96,11 +96,19 @@ def test_chain_graph_replay_matches_eager():
             assert torch.equal(outs[s], eager[s])
 
 
-@pytest.mark.parametrize("T", [1, 3, 8])
-def test_chain_traces_do_not_change_results(T):
-    """Asking for the traces (or not) gives the same bits."""
-    cfg = ms.scaled(ms.CONFIGS["decode80b"], d=512, E=32, k=4, I=128, I_shared=128, n_slots=32, alpha=0.0)
-    DL = _layers(cfg, 4)
+@pytest.mark.parametrize("T,bits,shape", [(1, 4, "small"), (3, 4, "small"), (8, 4, "small"), (2, 8, "small"),
+                                          (1, 4, "80b"), (4, 8, "80b")])
+def test_chain_traces_do_not_change_results(T, bits, shape):
+    """Asking for the traces (or not) gives the same bits.  Without trace_u
+    the decode layers hand the residual stream on inside their own kernels;
+    with it a separate residual/norm launch runs per layer, whose results the
+    oracle checks above: the two must agree bit for bit."""
+    if shape == "small":
+        cfg = ms.scaled(ms.CONFIGS["decode80b"], d=512, E=32, k=4, I=128, I_shared=128, n_slots=32, alpha=0.0,
+                        bits=bits)
+    else:
+        cfg = ms.scaled(ms.CONFIGS["decode80b"], E=64, n_slots=64, bits=bits)
+    DL = _layers(cfg, 4 if shape == "small" else 3)
     chain = moe.Chain([D.layer for D in DL])
     _, x = DL[0].x(5, T)
     xa, txa, _, tia = moe.moe_chain_forward(chain, x, path=moe.MOE_PATH_DECODE, trace=True)
