@@ -190,8 +190,8 @@ template <int TC, int NK, int GPL, int BITS>
 __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ uint32_t xlds[];            // [TC][G][kXPad] | routing area
+  static_assert(TC * 8 <= 64, "the SwiGLU rows of all tokens sit in wave 0");
   __shared__ float red[4][2][TC][8];
-  __shared__ float gu[2][TC][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // lane = (row r, group lane): the 8 lanes of one row are consecutive so the
   // row's partial sums meet by DPP within groups of 8
@@ -202,10 +202,9 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   const int nS = a.batched ? a.n_shared_inst : a.T;
   const int items = nR * rbR + nS * rbS;
   const int E = a.pool.E;
-  // routing area (decode): scratch | logits | slots | sel_l | sel_e
+  // routing area (decode): scratch | slots | sel_l | sel_e
   uint32_t* tscr = xlds + TC * G * kXPad;                          // topk scratch
-  float* rl = reinterpret_cast<float*>(tscr + topk_scratch_words(E));   // [E+1] logits
-  int32_t* rslot = reinterpret_cast<int32_t*>(rl + E + 1);       // [E] slot table
+  int32_t* rslot = reinterpret_cast<int32_t*>(tscr + topk_scratch_words(E));   // [E] slot table
   float* sel_l = reinterpret_cast<float*>(rslot + E);            // [k]
   int32_t* sel_e = reinterpret_cast<int32_t*>(sel_l + a.k);      // [k]
 
@@ -221,14 +220,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     if (!a.batched && routed && a.logits) {
       const int t = i / a.k, rank = i % a.k;
       const float* lrow = a.logits + (size_t)t * (E + 1);
-      for (int q = tid; q <= E; q += 256) rl[q] = (q < E && a.bias) ? lrow[q] + a.bias[q] : lrow[q];
       for (int q = tid; q < E; q += 256) rslot[q] = a.pool.slot_table[q];
-      __syncthreads();
       if (wave == 0) {
-        topk_select<NK>(rl, nullptr, E, a.k, sel_l, sel_e, tscr);
+        // the logits (+ bias) go from memory straight into wave 0's registers
+        topk_select<NK>(lrow, a.bias, E, a.k, sel_l, sel_e, tscr);
         if (rank == 0 && rb == 0) {
           topk_finish(sel_l, sel_e, a.k, a.idx + (size_t)t * a.k, a.w + (size_t)t * a.k, a.usage);
-          if (lane == 0) a.sgate[t] = sigmoidf_(rl[E]);
+          if (lane == 0) a.sgate[t] = sigmoidf_(lrow[E]);
         }
       }
       __syncthreads();
@@ -329,20 +327,15 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
       if ((lane & 7) == 0) { red[wave][0][tt][r] = x1; red[wave][1][tt][r] = x2; }
     }
     __syncthreads();
-    if (tid < 2 * TC * 8) {
-      const int m = tid / (TC * 8), tt = (tid / 8) % TC, rr = tid % 8;
-      gu[m][tt][rr] = ((red[0][m][tt][rr] + red[1][m][tt][rr]) + red[2][m][tt][rr]) + red[3][m][tt][rr];
-    }
-    __syncthreads();
-    if (tid < ntok) {
-      const int tt = tid;
+    if (tid < TC * 8) {                       // lanes 8 tt + rr of wave 0: one row each
+      const int tt = tid / 8, rr = tid % 8;
+      const float g = ((red[0][0][tt][rr] + red[1][0][tt][rr]) + red[2][0][tt][rr]) + red[3][0][tt][rr];
+      const float u = ((red[0][1][tt][rr] + red[1][1][tt][rr]) + red[2][1][tt][rr]) + red[3][1][tt][rr];
+      const float hv = missing ? 0.0f : g / (1.0f + expf(-g)) * u;
       float h[8];
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const float g = gu[0][tt][rr], u = gu[1][tt][rr];
-        h[rr] = missing ? 0.0f : g / (1.0f + expf(-g)) * u;
-      }
-      write_h8(h, a.hq, a.hs8, a.Imax, hrow[tt], rb);
+      for (int q = 0; q < 8; ++q) h[q] = __shfl(hv, 8 * tt + q, 64);
+      if (rr == 0 && tt < ntok) write_h8(h, a.hq, a.hs8, a.Imax, hrow[tt], rb);
     }
     if (missing && tid == 0) atomicOr(a.pool.err, 1);
     __syncthreads();
@@ -1257,7 +1250,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int items = f.T * f.k * (f.I / 8) + f.T * (f.Ish / 8);
     const int E = f.pool.E;
     const size_t lds = (size_t)1 * G * kXPad * 4 +
-                       (f.logits ? (size_t)(topk_scratch_words(E) + 2 * E + 1 + 2 * f.k) * 4 : 0);
+                       (f.logits ? (size_t)(topk_scratch_words(E) + E + 2 * f.k) * 4 : 0);
     void* fn = kf.gate_up(nk_for(E), G);
     void* args[] = {&g};
     MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));   // multiple of 8: xcd_remap
