@@ -74,8 +74,9 @@ struct GateUpArgs {
 };
 
 // Resolve instance -> (blob, I, tokens, hrows).  Returns ntok (0 = skip).
+template <int TC>
 __device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, const uint8_t** blob,
-                                       int* Iinst, int* tok, int* hrow, bool* missing) {
+                                       int* Iinst, int (&tok)[TC], int (&hrow)[TC], bool* missing) {
   *missing = false;
   if (!a.batched) {
     if (routed) {
@@ -94,6 +95,8 @@ __device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, 
     }
     return 1;
   }
+  // instances hold at most TC tokens; entries past in.n repeat the first
+  // (every index constant, so tok and hrow stay in registers)
   const Inst in = a.inst[routed ? i : *a.n_routed + i];
   if (routed) {
     const int e = in.expert;
@@ -101,20 +104,22 @@ __device__ __forceinline__ int resolve(const GateUpArgs& a, bool routed, int i, 
     *missing = slot < 0;
     *blob = a.pool.slab + (uint64_t)(slot < 0 ? 0 : slot) * a.pool.stride;
     *Iinst = a.I;
-    for (int j = 0; j < in.n; ++j) {
-      const int p = a.pair_ids[in.start + j];
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      const int p = a.pair_ids[in.start + (j < in.n ? j : 0)];
       tok[j] = p / a.k;
       hrow[j] = p;
     }
   } else {
     *blob = a.shared_blob;
     *Iinst = a.Ish;
-    for (int j = 0; j < in.n; ++j) {
-      tok[j] = in.start + j;
-      hrow[j] = a.T * a.k + in.start + j;
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      tok[j] = in.start + (j < in.n ? j : 0);
+      hrow[j] = a.T * a.k + tok[j];
     }
   }
-  return in.n;
+  return in.n < TC ? in.n : TC;
 }
 
 // Decode gate/up: GPL groups of 64 inputs per lane (32 group lanes per row):
@@ -153,6 +158,28 @@ __device__ __forceinline__ uint32_t qpw(uint32_t w, int u) {
   return ((w >> (4 * (u & 3))) & 0x000F000Fu) | mag;
 }
 template <int BITS> __device__ __forceinline__ constexpr float qoff() { return BITS == 4 ? 128.0f : 2176.0f; }
+
+// Activation pairs of ntok (<= TC) tokens into the LDS tile [TC][G][kXPad]
+// by a 256-thread block: the pieces of all TC tokens are loaded before any is
+// stored, so they are in flight together (a plain strided loop waits for
+// each load before it issues the next).  Tokens past ntok load token 0's
+// piece again and drop it (unconditional loads keep v in registers).
+template <int TC>
+__device__ __forceinline__ void stage_x(const uint32_t* __restrict__ xq, const int (&tok)[TC], int ntok, int d,
+                                        uint32_t* xlds) {
+  const int per = d / 8;
+  for (int c4 = threadIdx.x; c4 < per; c4 += 256) {
+    uint4 v[TC];
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) {
+      const int tk = tt < ntok ? tok[tt] : tok[0];
+      v[tt] = reinterpret_cast<const uint4*>(xq + (size_t)tk * (d / 2))[c4];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt)
+      if (tt < ntok) *reinterpret_cast<uint4*>(&xlds[(tt * (d / 64) + (c4 >> 3)) * kXPad + 4 * (c4 & 7)]) = v[tt];
+  }
+}
 
 // h of 8 consecutive intermediate rows (one 8-block m = rb) as bf16 (hi, lo)
 // pairs (h[8m+i], h[8m+i+4]) plus the sum of hi + lo, for the down pass.
@@ -220,7 +247,23 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     if (!a.batched && routed && a.logits) {
       const int t = i / a.k, rank = i % a.k;
       const float* lrow = a.logits + (size_t)t * (E + 1);
-      for (int q = tid; q < E; q += 256) rslot[q] = a.pool.slot_table[q];
+      if (wave != 0) {
+        // the slot table goes to LDS through waves 1-3 (E <= 1024: at most
+        // six entries per thread, all loads in flight at once) while wave 0
+        // selects
+        constexpr int kSP = (1024 + 191) / 192;
+        int32_t sv[kSP];
+#pragma unroll
+        for (int u = 0; u < kSP; ++u) {
+          const int q = tid - 64 + 192 * u;
+          sv[u] = a.pool.slot_table[q < E ? q : 0];     // clamped: loads stay unconditional
+        }
+#pragma unroll
+        for (int u = 0; u < kSP; ++u) {
+          const int q = tid - 64 + 192 * u;
+          if (q < E) rslot[q] = sv[u];
+        }
+      }
       if (wave == 0) {
         // the logits (+ bias) go from memory straight into wave 0's registers
         topk_select<NK>(lrow, a.bias, E, a.k, sel_l, sel_e, tscr);
@@ -277,12 +320,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
       }
     }
     // 2. stage activations (bf16 pairs) while the weights are in flight
-    for (int q = tid; q < ntok * (a.d / 8); q += 256) {
-      const int tt = q / (a.d / 8), c4 = q % (a.d / 8);           // c4: 4-dword piece
-      const uint4 v = reinterpret_cast<const uint4*>(a.xq + (size_t)tok[tt] * (a.d / 2))[c4];
-      const int g = c4 >> 3, w4 = c4 & 7;
-      *reinterpret_cast<uint4*>(&xlds[(tt * G + g) * kXPad + 4 * w4]) = v;
-    }
+    stage_x<TC>(a.xq, tok, ntok, a.d, xlds);
     __syncthreads();
 
     float vg[TC], vu[TC];
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 // groups per lane; rows meet by DPP without block barriers); its codes are
 // all in flight before the chunk's activations are staged in LDS.
 template <int GPL, int BITS>
-__global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
+__global__ __launch_bounds__(256, (GPL <= 4 && BITS == 4) ? 3 : 1) void gate_up_batched_kernel(GateUpArgs a) {
   constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ uint32_t xlds[];            // [kTC][G][kXPad] | xs [kTC][G] | hbuf [4][kTC][8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -394,12 +432,15 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
       }
     }
     // 2. activations (bf16 pairs) and group sums of the chunk's tokens
-    for (int q = tid; q < ntok * (a.d / 8); q += 256) {
-      const int tt = q / (a.d / 8), c4 = q % (a.d / 8);
-      const uint4 v = reinterpret_cast<const uint4*>(a.xq + (size_t)tok[tt] * (a.d / 2))[c4];
-      *reinterpret_cast<uint4*>(&xlds[(tt * G + (c4 >> 3)) * kXPad + 4 * (c4 & 7)]) = v;
+    stage_x<kTC>(a.xq, tok, ntok, a.d, xlds);
+    for (int g = tid; g < G; g += 256) {
+      float sv[kTC];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt) sv[tt] = a.xs[(size_t)(tt < ntok ? tok[tt] : tok[0]) * G + g];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt)
+        if (tt < ntok) xsl[tt * G + g] = sv[tt];
     }
-    for (int q = tid; q < ntok * G; q += 256) xsl[q] = a.xs[(size_t)tok[q / G] * G + q % G];
     __syncthreads();
     // 3. compute, SwiGLU and store per sub-block
 #pragma unroll
@@ -465,7 +506,11 @@ __global__ __launch_bounds__(256) void gate_up_batched_kernel(GateUpArgs a) {
         float h[8];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) h[rr] = hbuf[lane * 8 + rr];
-        write_h8(h, a.hq, a.hs8, a.Imax, hrow[lane], rb);
+        int hr = hrow[0];
+#pragma unroll
+        for (int tt = 1; tt < kTC; ++tt)
+          if (lane == tt) hr = hrow[tt];
+        write_h8(h, a.hq, a.hs8, a.Imax, hr, rb);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -623,14 +668,24 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
       }
     }
     // 2. stage the round's h records (pairs + per-8 sums) in LDS
+    //    (four pieces per thread in flight at once)
     const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
-    for (int q4 = tid; q4 < nr * src4; q4 += 64 * kDnWaves) {
-      const int u = q4 / src4, c = q4 % src4;
-      const int ii = base + u;
-      uint4 v;
-      if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)ii * a.Imax)[c];
-      else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)ii * (a.Imax / 8))[c - a.Imax / 4];
-      *reinterpret_cast<uint4*>(hst + u * rec + hrec_pos(4 * c, a.Imax)) = v;
+    const int n4 = nr * src4;
+    for (int q0 = tid; q0 < n4; q0 += 4 * 64 * kDnWaves) {
+      uint4 v[4];
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int q4 = q0 + 64 * kDnWaves * uu < n4 ? q0 + 64 * kDnWaves * uu : 0;   // clamped
+        const int ii = base + q4 / src4, c = q4 % src4;
+        const uint4* src = c < a.Imax / 4 ? reinterpret_cast<const uint4*>(a.hq + (size_t)ii * a.Imax) + c
+                                          : reinterpret_cast<const uint4*>(a.hs8 + (size_t)ii * (a.Imax / 8)) + (c - a.Imax / 4);
+        v[uu] = *src;
+      }
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int q4 = q0 + 64 * kDnWaves * uu;
+        if (q4 < n4) *reinterpret_cast<uint4*>(hst + (q4 / src4) * rec + hrec_pos(4 * (q4 % src4), a.Imax)) = v[uu];
+      }
     }
     __syncthreads();
     // 3. compute
@@ -727,14 +782,19 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
       }
     }
     // 2. the chunk's h records
+    //    (four pieces per thread in flight at once)
     const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
-    for (int q4 = tid; q4 < in.n * src4; q4 += 256) {
-      const int tt = q4 / src4, c = q4 % src4;
-      const int hr = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
-      uint4 v;
-      if (c < a.Imax / 4) v = reinterpret_cast<const uint4*>(a.hq + (size_t)hr * a.Imax)[c];
-      else v = reinterpret_cast<const uint4*>(a.hs8 + (size_t)hr * (a.Imax / 8))[c - a.Imax / 4];
-      *reinterpret_cast<uint4*>(hst + tt * rec + hrec_pos(4 * c, a.Imax)) = v;
+    for (int c = tid; c < src4; c += 256) {      // the kTC records' pieces in flight together
+      uint4 v[kTC];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt) {
+        const int hr = tt < in.n ? hrow[tt] : hrow[0];
+        v[tt] = c < a.Imax / 4 ? reinterpret_cast<const uint4*>(a.hq + (size_t)hr * a.Imax)[c]
+                               : reinterpret_cast<const uint4*>(a.hs8 + (size_t)hr * (a.Imax / 8))[c - a.Imax / 4];
+      }
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt)
+        if (tt < in.n) *reinterpret_cast<uint4*>(hst + tt * rec + hrec_pos(4 * c, a.Imax)) = v[tt];
     }
     __syncthreads();
     // 3. compute and store, sub-block by sub-block
@@ -841,7 +901,7 @@ __device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
 
 // item = (instance, 4 rows): wave w takes row 4 rb + w of gate and up.
 template <int TC>
-__global__ __launch_bounds__(256) void gate_up_f32_kernel(GateUpArgs a) {
+__global__ __launch_bounds__(256, 4) void gate_up_f32_kernel(GateUpArgs a) {
   extern __shared__ uint16_t xb[];              // [TC][d] bf16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rbR = a.I / 4, rbS = a.Ish / 4;
@@ -879,10 +939,14 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(GateUpArgs a) {
         uv[v] = ok ? wu[f] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       if (p0 == 0) {
-        for (int q = tid; q < ntok * (a.d / 8); q += 256) {
-          const int tt = q / (a.d / 8), c8 = q % (a.d / 8);
-          reinterpret_cast<uint4*>(xb + (size_t)tt * a.d)[c8] =
-              reinterpret_cast<const uint4*>(a.x + (size_t)tok[tt] * a.d)[c8];
+        for (int c8 = tid; c8 < a.d / 8; c8 += 256) {   // all tokens' pieces in flight together
+          uint4 v4[TC];
+#pragma unroll
+          for (int tt = 0; tt < TC; ++tt)
+            v4[tt] = reinterpret_cast<const uint4*>(a.x + (size_t)(tt < ntok ? tok[tt] : tok[0]) * a.d)[c8];
+#pragma unroll
+          for (int tt = 0; tt < TC; ++tt)
+            if (tt < ntok) reinterpret_cast<uint4*>(xb + (size_t)tt * a.d)[c8] = v4[tt];
         }
         __syncthreads();
       }
@@ -978,10 +1042,18 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_f32_kernel(DownArgs
     }
     // the round's h records
     const int im4 = a.Imax / 4;
-    for (int q4 = tid; q4 < nr * im4; q4 += 64 * kDnWaves) {
-      const int u = q4 / im4, c = q4 % im4;
-      reinterpret_cast<float4*>(hst + (size_t)u * a.Imax)[c] =
-          reinterpret_cast<const float4*>(a.hq + (size_t)(base + u) * a.Imax)[c];
+    for (int q0 = tid; q0 < nr * im4; q0 += 4 * 64 * kDnWaves) {   // four pieces per thread in flight
+      float4 v4[4];
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int q4 = q0 + 64 * kDnWaves * uu < nr * im4 ? q0 + 64 * kDnWaves * uu : 0;   // clamped
+        v4[uu] = reinterpret_cast<const float4*>(a.hq + (size_t)(base + q4 / im4) * a.Imax)[q4 % im4];
+      }
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int q4 = q0 + 64 * kDnWaves * uu;
+        if (q4 < nr * im4) reinterpret_cast<float4*>(hst + (size_t)(q4 / im4) * a.Imax)[q4 % im4] = v4[uu];
+      }
     }
     __syncthreads();
     if (active) {
@@ -1049,11 +1121,18 @@ __global__ __launch_bounds__(256) void down_batched_f32_kernel(DownArgs a) {
       wv[v] = (!missing && jv && f < I4) ? wd[f] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const int im4 = a.Imax / 4;
-    for (int q4 = tid; q4 < in.n * im4; q4 += 256) {
-      const int tt = q4 / im4, c = q4 % im4;
-      const int hr = routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt;
-      reinterpret_cast<float4*>(hsf + (size_t)tt * a.Imax)[c] =
-          reinterpret_cast<const float4*>(a.hq + (size_t)hr * a.Imax)[c];
+    int hrow[kTC];
+#pragma unroll
+    for (int tt = 0; tt < kTC; ++tt)
+      hrow[tt] = tt < in.n ? (routed ? a.pair_ids[in.start + tt] : a.T * a.k + in.start + tt) : 0;
+    for (int c = tid; c < im4; c += 256) {        // the kTC records' pieces in flight together
+      float4 v4[kTC];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt)
+        v4[tt] = reinterpret_cast<const float4*>(a.hq + (size_t)(tt < in.n ? hrow[tt] : hrow[0]) * a.Imax)[c];
+#pragma unroll
+      for (int tt = 0; tt < kTC; ++tt)
+        if (tt < in.n) reinterpret_cast<float4*>(hsf + (size_t)tt * a.Imax)[c] = v4[tt];
     }
     __syncthreads();
     float acc[kTC];

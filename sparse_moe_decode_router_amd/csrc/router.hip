@@ -112,8 +112,18 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       float ss = 0.f;
-      if (t < T)
-        for (int g = tid; g < d / 8; g += kRouterThreads) ss += a.ssp[(size_t)t * (d / 8) + g];
+      if (t < T) {
+        // d <= 8192: at most four partials per thread, all loads in flight at once
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int g = tid + u * kRouterThreads;
+          pv[u] = a.ssp[(size_t)t * (d / 8) + (g < d / 8 ? g : 0)];   // clamped: unconditional loads
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (tid + u * kRouterThreads < d / 8) ss += pv[u];
+      }
       ss = wave_sum(ss);
       if (lane == 0) red[wave][t] = ss;
     }
@@ -143,19 +153,39 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) acc[t] = 0.0f;
   const float4* Wr = reinterpret_cast<const float4*>(a.W + (size_t)row * d);
-  for (int c = tid; c < d / 4; c += kRouterThreads) {
-    const float4 wv = Wr[c];
+  // kRU pieces of 4 columns per thread: their weight and activation loads
+  // are all issued before the first product (a plain strided loop would wait
+  // for each piece's loads before issuing the next); columns are still added
+  // in the order c = tid, tid + 256, ...
+  constexpr int kRU = 2;
+  for (int c0 = tid; c0 < d / 4; c0 += kRU * kRouterThreads) {
+    float4 wv[kRU];
+    uint2 xv[kRU][TMAX];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        uint2 xv = *reinterpret_cast<const uint2*>(a.x + (size_t)t * d + 4 * c);
-        if (chain)
-          xv = make_uint2(scaled_bf16(xv.x & 0xFFFFu, scale[t]) | (scaled_bf16(xv.x >> 16, scale[t]) << 16),
-                          scaled_bf16(xv.y & 0xFFFFu, scale[t]) | (scaled_bf16(xv.y >> 16, scale[t]) << 16));
-        acc[t] += wv.x * bf16_lo(xv.x);
-        acc[t] += wv.y * bf16_hi(xv.x);
-        acc[t] += wv.z * bf16_lo(xv.y);
-        acc[t] += wv.w * bf16_hi(xv.y);
+    for (int u = 0; u < kRU; ++u) {
+      const int c = c0 + u * kRouterThreads;
+      const bool ok = c < d / 4;
+      const int cc = ok ? c : 0;                 // clamped: unconditional loads
+      wv[u] = Wr[cc];
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t)
+        xv[u][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * d + 4 * cc);
+    }
+#pragma unroll
+    for (int u = 0; u < kRU; ++u) {
+      if (c0 + u * kRouterThreads >= d / 4) continue;
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+          uint2 x2 = xv[u][t];
+          if (chain)
+            x2 = make_uint2(scaled_bf16(x2.x & 0xFFFFu, scale[t]) | (scaled_bf16(x2.x >> 16, scale[t]) << 16),
+                            scaled_bf16(x2.y & 0xFFFFu, scale[t]) | (scaled_bf16(x2.y >> 16, scale[t]) << 16));
+          acc[t] += wv[u].x * bf16_lo(x2.x);
+          acc[t] += wv[u].y * bf16_hi(x2.x);
+          acc[t] += wv[u].z * bf16_lo(x2.y);
+          acc[t] += wv[u].w * bf16_hi(x2.y);
+        }
       }
     }
   }

@@ -91,11 +91,15 @@ __device__ __forceinline__ void topk_select(const float* lrow, const float* __re
     const bool mine = lane < C;
     const uint32_t v = mine ? cv[lane] : 0u;
     const uint32_t e = mine ? ce[lane] : 0u;
+    // one 64-bit key per candidate, key(a) > key(b) iff a ranks before b:
+    // larger logit key, or the same and a lower index
+    const uint64_t key = ((uint64_t)v << 32) | (uint32_t)~e;
+    const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
     int rank = 0;
     for (int q = 0; q < C; ++q) {
-      const uint32_t v2 = (uint32_t)__builtin_amdgcn_readlane((int)v, q);
-      const uint32_t e2 = (uint32_t)__builtin_amdgcn_readlane((int)e, q);
-      rank += (v2 > v) | ((v2 == v) & (e2 < e));
+      const uint64_t k2 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, q) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)klo, q);
+      rank += k2 > key;
     }
     if (mine && rank < k) {
       sel_e[rank] = (int32_t)e;
