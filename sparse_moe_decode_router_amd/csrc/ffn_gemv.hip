@@ -177,7 +177,7 @@ __device__ __forceinline__ void stage_x(const uint32_t* __restrict__ xq, const i
     }
 #pragma unroll
     for (int tt = 0; tt < TC; ++tt)
-      if (tt < ntok) *reinterpret_cast<uint4*>(&xlds[(tt * (d / 64) + (c4 >> 3)) * kXPad + 4 * (c4 & 7)]) = v[tt];
+      *reinterpret_cast<uint4*>(&xlds[((tt < ntok ? tt : 0) * (d / 64) + (c4 >> 3)) * kXPad + 4 * (c4 & 7)]) = v[tt];
   }
 }
 
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 #pragma unroll
         for (int u = 0; u < kSP; ++u) {
           const int q = tid - 64 + 192 * u;
-          if (q < E) rslot[q] = sv[u];
+          rslot[q < E ? q : 0] = sv[u];
         }
       }
       if (wave == 0) {
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256, (GPL <= 4 && BITS == 4) ? 3 : 1) void gate_up_
       for (int tt = 0; tt < kTC; ++tt) sv[tt] = a.xs[(size_t)(tt < ntok ? tok[tt] : tok[0]) * G + g];
 #pragma unroll
       for (int tt = 0; tt < kTC; ++tt)
-        if (tt < ntok) xsl[tt * G + g] = sv[tt];
+        xsl[(tt < ntok ? tt : 0) * G + g] = sv[tt];
     }
     __syncthreads();
     // 3. compute, SwiGLU and store per sub-block
@@ -536,6 +536,53 @@ __device__ __forceinline__ int hrec_pos(int j, int Imax) {
 }
 __device__ __forceinline__ const float* hrec_sums(const uint32_t* hrec, int Imax) {
   return reinterpret_cast<const float*>(hrec + 2 * (Imax / 64) * kHG);
+}
+
+// h record rows: consecutive (decode rounds) or a short list (bucket chunks).
+struct RowsFrom {
+  int base;
+  __device__ int operator()(int r) const { return base + r; }
+};
+struct Rows4 {                                  // up to four rows, named (no array to index)
+  int v0, v1, v2, v3;
+  __device__ int operator()(int r) const { return r == 0 ? v0 : r == 1 ? v1 : r == 2 ? v2 : v3; }
+};
+
+// Stage nrec h records (rows rows(0..nrec-1) of hq / hs8) into their LDS
+// images by an NT-thread block.  Per pass every thread loads four 16-byte
+// pair pieces and one sum piece before it stores any, with branch-free
+// addressing (so the compiler neither waits per piece nor sinks the loads
+// to their stores); pieces past the end reload and rewrite piece 0 of
+// record 0 (same value, same place).
+template <int NT, class Rows>
+__device__ __forceinline__ void stage_h(const uint32_t* __restrict__ hq, const float* __restrict__ hs8, int Imax,
+                                        int nrec, Rows rows, uint32_t* hst, int rec) {
+  const int pp = Imax / 4, sp = Imax / 32;      // pair pieces and sum pieces per record
+  const int np = nrec * pp, ns = nrec * sp;
+  const int K = max((np + 4 * NT - 1) / (4 * NT), (ns + NT - 1) / NT);
+  for (int it = 0; it < K; ++it) {
+    uint4 vp[4], vs;
+    int dp[4], ds;
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      int q = it * 4 * NT + NT * uu + (int)threadIdx.x;
+      q = q < np ? q : 0;
+      const int r = q / pp, c = q % pp;
+      vp[uu] = reinterpret_cast<const uint4*>(hq + (size_t)rows(r) * Imax)[c];
+      const int j = 4 * c, part = j >= Imax / 2 ? 1 : 0, jj = j - part * (Imax / 2);
+      dp[uu] = r * rec + (part * (Imax / 64) + (jj >> 5)) * kHG + (jj & 31);
+    }
+    {
+      int q = it * NT + (int)threadIdx.x;
+      q = q < ns ? q : 0;
+      const int r = q / sp, c = q % sp;
+      vs = reinterpret_cast<const uint4*>(hs8 + (size_t)rows(r) * (Imax / 8))[c];
+      ds = r * rec + 2 * (Imax / 64) * kHG + 4 * c;
+    }
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) *reinterpret_cast<uint4*>(hst + dp[uu]) = vp[uu];
+    *reinterpret_cast<uint4*>(hst + ds) = vs;
+  }
 }
 
 // h given as the LDS record above (hs: its per-8 sums); q0..q3: the
@@ -635,14 +682,24 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   float* oi = dyn;
   float* wk = dyn + nI * 8;                     // combine weights: w[T*k] then sgate[T]
   uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 9 + 3) & ~3));
-  // the combine weights are read now, not after the GEMV (their latency
-  // would land at the very end of the kernel)
-  for (int q = tid; q < nI; q += 64 * kDnWaves) wk[q] = q < nR ? a.w[q] : a.sgate[q - nR];
   for (int base = 0; base < nI; base += kDnRound) {
     const int nr = min(kDnRound, nI - base);
     const int i = base + wave;
     const bool active = wave < nr;
-    // 1. this wave's code loads
+    // 1. the wave's selection slot (issued first: the code addresses wait
+    //    for it), in the first round the combine weights (read now, their
+    //    latency would otherwise land at the very end; nI <= 2048: two per
+    //    thread, clamped so the loads stay unconditional), then the codes
+    //    (no load of this round is conditional before the slot is used, so
+    //    the wait for it is exact; the weights are loaded every round, the
+    //    first round's are the ones stored)
+    const int slot_ld = a.sel_slot[(active && i < nR) ? i : 0];
+    float wkv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qw = tid + 64 * kDnWaves * u < nI ? tid + 64 * kDnWaves * u : 0;
+      wkv[u] = *(qw < nR ? a.w + qw : a.sgate + (qw - nR));
+    }
     uint4 q[kNP];
     uint32_t sb = 0;
     bool miss = true;
@@ -650,7 +707,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
     const uint8_t* blob = nullptr;
     if (active) {
       if (i < nR) {
-        const int slot = a.sel_slot[i];
+        const int slot = slot_ld;
         miss = slot < 0;
         blob = a.pool.slab + (uint64_t)(miss ? 0 : slot) * a.pool.stride;
         Iinst = a.I;
@@ -667,25 +724,14 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
         sb = *reinterpret_cast<const uint32_t*>(blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
       }
     }
-    // 2. stage the round's h records (pairs + per-8 sums) in LDS
-    //    (four pieces per thread in flight at once)
-    const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
-    const int n4 = nr * src4;
-    for (int q0 = tid; q0 < n4; q0 += 4 * 64 * kDnWaves) {
-      uint4 v[4];
+    // 2. stage the round's h records (pairs + per-8 sums) in LDS; the
+    //    weights go to LDS after them (a store before the h loads would wait
+    //    for the code loads issued ahead of it)
+    stage_h<64 * kDnWaves>(a.hq, a.hs8, a.Imax, nr, RowsFrom{base}, hst, rec);
+    if (base == 0) {
 #pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
-        const int q4 = q0 + 64 * kDnWaves * uu < n4 ? q0 + 64 * kDnWaves * uu : 0;   // clamped
-        const int ii = base + q4 / src4, c = q4 % src4;
-        const uint4* src = c < a.Imax / 4 ? reinterpret_cast<const uint4*>(a.hq + (size_t)ii * a.Imax) + c
-                                          : reinterpret_cast<const uint4*>(a.hs8 + (size_t)ii * (a.Imax / 8)) + (c - a.Imax / 4);
-        v[uu] = *src;
-      }
-#pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
-        const int q4 = q0 + 64 * kDnWaves * uu;
-        if (q4 < n4) *reinterpret_cast<uint4*>(hst + (q4 / src4) * rec + hrec_pos(4 * (q4 % src4), a.Imax)) = v[uu];
-      }
+      for (int u = 0; u < 2; ++u)
+        wk[tid + 64 * kDnWaves * u < nI ? tid + 64 * kDnWaves * u : 0] = wkv[u];
     }
     __syncthreads();
     // 3. compute
@@ -782,19 +828,9 @@ __global__ __launch_bounds__(256) void down_batched_kernel(DownArgs a) {
       }
     }
     // 2. the chunk's h records
-    //    (four pieces per thread in flight at once)
-    const int src4 = (a.Imax + a.Imax / 8) / 4;   // uint4s of a record in HBM
-    for (int c = tid; c < src4; c += 256) {      // the kTC records' pieces in flight together
-      uint4 v[kTC];
-#pragma unroll
-      for (int tt = 0; tt < kTC; ++tt) {
-        const int hr = tt < in.n ? hrow[tt] : hrow[0];
-        v[tt] = c < a.Imax / 4 ? reinterpret_cast<const uint4*>(a.hq + (size_t)hr * a.Imax)[c]
-                               : reinterpret_cast<const uint4*>(a.hs8 + (size_t)hr * (a.Imax / 8))[c - a.Imax / 4];
-      }
-#pragma unroll
-      for (int tt = 0; tt < kTC; ++tt)
-        if (tt < in.n) *reinterpret_cast<uint4*>(hst + tt * rec + hrec_pos(4 * c, a.Imax)) = v[tt];
+    {
+      static_assert(kTC == 4, "bucket chunks of four tokens");
+      stage_h<256>(a.hq, a.hs8, a.Imax, in.n, Rows4{hrow[0], hrow[1], hrow[2], hrow[3]}, hst, rec);
     }
     __syncthreads();
     // 3. compute and store, sub-block by sub-block
@@ -946,7 +982,7 @@ __global__ __launch_bounds__(256, 4) void gate_up_f32_kernel(GateUpArgs a) {
             v4[tt] = reinterpret_cast<const uint4*>(a.x + (size_t)(tt < ntok ? tok[tt] : tok[0]) * a.d)[c8];
 #pragma unroll
           for (int tt = 0; tt < TC; ++tt)
-            if (tt < ntok) reinterpret_cast<uint4*>(xb + (size_t)tt * a.d)[c8] = v4[tt];
+            reinterpret_cast<uint4*>(xb + (size_t)(tt < ntok ? tt : 0) * a.d)[c8] = v4[tt];
         }
         __syncthreads();
       }
@@ -1008,18 +1044,26 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_f32_kernel(DownArgs
   float* oi = dyn;
   float* wk = dyn + nI * 8;
   float* hst = dyn + ((nI * 9 + 3) & ~3);
-  for (int q = tid; q < nI; q += 64 * kDnWaves) wk[q] = q < nR ? a.w[q] : a.sgate[q - nR];
   for (int base = 0; base < nI; base += kDnRound) {
     const int nr = min(kDnRound, nI - base);
     const int i = base + wave;
     const bool active = wave < nr;
+    // the selection slot first, then the combine weights (every round,
+    // unconditional; the first round's are stored), then the weights
+    const int slot_ld = a.sel_slot[(active && i < nR) ? i : 0];
+    float wkv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qw = tid + 64 * kDnWaves * u < nI ? tid + 64 * kDnWaves * u : 0;
+      wkv[u] = *(qw < nR ? a.w + qw : a.sgate + (qw - nR));
+    }
     bool miss = true;
     int Iinst = 0;
     const uint8_t* blob = nullptr;
     float4 wv[kF32DnW];
     if (active) {
       if (i < nR) {
-        const int slot = a.sel_slot[i];
+        const int slot = slot_ld;
         miss = slot < 0;
         blob = a.pool.slab + (uint64_t)(miss ? 0 : slot) * a.pool.stride;
         Iinst = a.I;
@@ -1040,20 +1084,25 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_f32_kernel(DownArgs
       const int f = gl + 8 * v;
       wv[v] = (wd && f < I4) ? wd[f] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // the round's h records
+    // the round's h records, then the weights (see the quantised kernel)
     const int im4 = a.Imax / 4;
-    for (int q0 = tid; q0 < nr * im4; q0 += 4 * 64 * kDnWaves) {   // four pieces per thread in flight
-      float4 v4[4];
+    for (int q0 = tid; q0 < nr * im4; q0 += 2 * 64 * kDnWaves) {   // two pieces per thread in flight
+      float4 v4[2];
 #pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
+      for (int uu = 0; uu < 2; ++uu) {
         const int q4 = q0 + 64 * kDnWaves * uu < nr * im4 ? q0 + 64 * kDnWaves * uu : 0;   // clamped
         v4[uu] = reinterpret_cast<const float4*>(a.hq + (size_t)(base + q4 / im4) * a.Imax)[q4 % im4];
       }
 #pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
-        const int q4 = q0 + 64 * kDnWaves * uu;
-        if (q4 < nr * im4) reinterpret_cast<float4*>(hst + (size_t)(q4 / im4) * a.Imax)[q4 % im4] = v4[uu];
+      for (int uu = 0; uu < 2; ++uu) {
+        const int q4 = q0 + 64 * kDnWaves * uu < nr * im4 ? q0 + 64 * kDnWaves * uu : 0;
+        reinterpret_cast<float4*>(hst + (size_t)(q4 / im4) * a.Imax)[q4 % im4] = v4[uu];
       }
+    }
+    if (base == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        wk[tid + 64 * kDnWaves * u < nI ? tid + 64 * kDnWaves * u : 0] = wkv[u];
     }
     __syncthreads();
     if (active) {
@@ -1132,7 +1181,7 @@ __global__ __launch_bounds__(256) void down_batched_f32_kernel(DownArgs a) {
         v4[tt] = reinterpret_cast<const float4*>(a.hq + (size_t)(tt < in.n ? hrow[tt] : hrow[0]) * a.Imax)[c];
 #pragma unroll
       for (int tt = 0; tt < kTC; ++tt)
-        if (tt < in.n) reinterpret_cast<float4*>(hsf + (size_t)tt * a.Imax)[c] = v4[tt];
+        reinterpret_cast<float4*>(hsf + (size_t)(tt < in.n ? tt : 0) * a.Imax)[c] = v4[tt];
     }
     __syncthreads();
     float acc[kTC];
