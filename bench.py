@@ -15,14 +15,16 @@ kernels' achieved HBM bandwidth on algorithmic expert bytes (roofline), and
 the CPU oracle timed on a bounded sample of the same steps (cpu_baseline).
 
 --workload selects another configuration (decode35b, refill80b: 256-slot
-pool refilled by LFU + recency from pinned host memory, batch80b: T=64,
+pool refilled by LFU + recency from pinned host memory, stream80b: the same
+with the misses copied on a second stream while the resident experts
+compute, batch80b: T=64,
 prefill80b / prefill80b_zipf: T=4096 on the matrix cores; decode80b_int8,
 batch80b_int8, prefill80b_int8: the same layers with 8-bit experts;
 decode80b_f32, batch80b_f32: with unquantised fp32 experts; chain80b: 48
 such decode layers per token, as pre-norm residual blocks);
 --workload all prints one line per workload, the headline first;
---workload refill_sweep prints the refill run for pool sizes 64..512 (hit
-rate vs tokens/s).
+--workload refill_sweep prints the refill run, serial and streamed, for pool
+sizes 64..512 (hit rate vs tokens/s).
 """
 from __future__ import annotations
 
@@ -272,10 +274,13 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
     return out
 
 
-def run_refill(c, K, W, n_slots=None, host=None):
+def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     """A pool of n_slots (default 256) over 512 experts, refilled between
     router and experts by LFU + recency from pinned host memory; outputs
-    checked bit-identical to an all-resident twin."""
+    checked bit-identical to an all-resident twin.  streamed: one
+    moe_layer_forward_streamed call per step (the misses copy in on a second
+    stream while the resident experts compute) instead of router -> refill
+    -> experts in sequence."""
     torch, ms, moe = c.torch, c.ms, c.moe
     cfg = ms.CONFIGS["decode80b"]
     if n_slots is not None:
@@ -296,8 +301,15 @@ def run_refill(c, K, W, n_slots=None, host=None):
     w = torch.empty((nsteps, 1, cfg.k), dtype=torch.float32, device="cuda")
     s = torch.empty((nsteps, 1), dtype=torch.float32, device="cuda")
     idx_host = torch.empty((cfg.k,), dtype=torch.int32, pin_memory=True)
+    part = moe.Layer(twin.w_router, twin.logit_bias, pool, twin.shared_blob, cfg.I_shared, cfg.k)
+    wsl = torch.zeros(part.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
 
     def step(i):
+        if streamed:
+            moe.moe_layer_forward_streamed(part, xall[i], host, copy_stream=copy_stream, workspace=wsl,
+                                           out=(y[i], idx[i], w[i], s[i]))
+            return
         moe.moe_router_topk(xall[i], twin.w_router, twin.logit_bias, cfg.k, workspace=wsr,
                             out=(idx[i], w[i], s[i]))
         idx_host.copy_(idx[i, 0], non_blocking=True)
@@ -332,8 +344,10 @@ def run_refill(c, K, W, n_slots=None, host=None):
             "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
             "config": {"workload": f"80B-shape batch-1 decode, {cfg.n_slots}-slot HBM pool refilled by "
-                                   "LFU+recency from pinned host memory (wall clock incl. PCIe and host policy)",
-                       "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "slots": cfg.n_slots},
+                                   "LFU+recency from pinned host memory (wall clock incl. PCIe and host policy)"
+                                   + (", misses copied on a second stream while the resident experts compute"
+                                      if streamed else ", router -> refill -> experts in sequence"),
+                       "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "slots": cfg.n_slots, "streamed": streamed},
             "hit_rate": round(hits / max(1, hits + misses), 4),
             "hit_rate_all_steps": round(st1["hits"] / max(1, st1["hits"] + st1["misses"]), 4),
             "pcie_bytes_per_step": round((st1["bytes_loaded"] - st0["bytes_loaded"]) / K),
@@ -500,7 +514,7 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only copy an MB-sized device buffer 5 times (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="decode80b",
-                    choices=["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b",
+                    choices=["decode80b", "decode35b", "refill80b", "stream80b", "batch80b", "prefill80b",
                              "prefill80b_zipf", "decode80b_int8", "batch80b_int8", "prefill80b_int8",
                              "decode80b_f32", "batch80b_f32", "chain80b", "all", "refill_sweep"])
     args = ap.parse_args()
@@ -514,7 +528,7 @@ def main():
     c = Ctx()
     c.torch.cuda.set_device(0)
     cpu = 0 if args.no_cpu else args.cpu_steps
-    todo = ["decode80b", "decode35b", "refill80b", "batch80b", "prefill80b", "prefill80b_zipf",
+    todo = ["decode80b", "decode35b", "refill80b", "stream80b", "batch80b", "prefill80b", "prefill80b_zipf",
             "decode80b_int8", "batch80b_int8", "prefill80b_int8", "decode80b_f32", "batch80b_f32",
             "chain80b"] \
         if args.workload == "all" else [args.workload]
@@ -525,16 +539,18 @@ def main():
             reps = min(args.replicas, 4) if wl.endswith("f32") else args.replicas
             res = run_decode(c, wl, args.steps, args.warmup, reps,
                              cpu if wl == "decode80b" else 0, args.eager)
-        elif wl == "refill80b":
-            res = run_refill(c, min(args.steps, 300), min(args.warmup, 50))
+        elif wl in ("refill80b", "stream80b"):
+            res = run_refill(c, min(args.steps, 300), min(args.warmup, 50), streamed=wl == "stream80b")
         elif wl == "refill_sweep":
             # hit rate and tokens/s against the pool size (the pages report that
-            # pool size barely changes speed on their SSD-backed machine)
+            # pool size barely changes speed on their SSD-backed machine), the
+            # serial and the streamed step for each size
             host = packed_experts(c, c.ms.CONFIGS["decode80b"], pinned=True)
             for slots in (64, 128, 192, 256, 384, 512):
-                res = run_refill(c, min(args.steps, 200), min(args.warmup, 50), slots, host)
-                print(json.dumps(res), flush=True)
-                c.torch.cuda.empty_cache()
+                for streamed in (False, True):
+                    res = run_refill(c, min(args.steps, 200), min(args.warmup, 50), slots, host, streamed)
+                    print(json.dumps(res), flush=True)
+                    c.torch.cuda.empty_cache()
             continue
         elif wl == "chain80b":
             res = run_chain(c, min(args.steps, 50), min(args.warmup, 5))

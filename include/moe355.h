@@ -329,6 +329,39 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x_dev,
                       void* workspace_dev, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* ------------------------------------------------- streamed decode step
+ * One decode step (T <= 8, T*(k+1) <= 2048, 4- or 8-bit experts) on a pool
+ * that holds only some experts, with the misses copied in while the resident
+ * experts compute (the pages keep routed experts in a bounded pool refilled
+ * from storage by LFU + recency, "How it works" and the cache discussion;
+ * here the storage tier is pinned host memory).  In order:
+ *   1. router and top-k on `stream`; the selections are copied to pinned
+ *      host memory owned by the pool;
+ *   2. phase 1 on `stream`: gate/up and down of the resident selections and
+ *      the shared expert (missing selections are deferred, not errors);
+ *   3. the calling thread waits for the selections only, plans the refill
+ *      (moe_pool_plan: same policy, stats and residency map), and queues the
+ *      host_blobs + expert * host_stride -> slot copies on `copy_stream`;
+ *   4. `stream` waits for those copies, publishes the slot-table edits and
+ *      runs phase 2: the deferred selections, then the rank-order combine.
+ * Outputs as moe_layer_forward (decode path) and bit-identical to it on an
+ * all-resident pool: every expert's outputs are computed by the same code
+ * and combined in the same order.  host_blobs: pinned host memory holding all
+ * E blobs (host_stride >= the pool stride), valid until the copies pass.
+ * workspace: moe_layer_workspace_bytes(L, T, MOE_PATH_DECODE) bytes.
+ * *n_loads (may be NULL): blobs copied this step.  copy_stream may equal
+ * stream (no overlap then).  The pool's selection staging is per pool:
+ * streamed steps on one pool must not overlap.  Errors as moe_pool_plan
+ * (MOE_ERR_POOL_TOO_SMALL: nothing copied, y not written) and the decode
+ * path; a selection still missing in phase 2 sets the pool error word. */
+int moe_layer_forward_streamed(const moe_layer_desc* L,
+                               const void* host_blobs, size_t host_stride,
+                               const uint16_t* x_dev, int32_t T, float* y_dev,
+                               int32_t* topk_idx_dev, float* topk_w_dev,
+                               float* shared_gate_dev, void* workspace_dev,
+                               size_t workspace_bytes, hipStream_t stream,
+                               hipStream_t copy_stream, int32_t* n_loads);
+
 /* ------------------------------------------------------------ layer chain
  * L layers applied one after the other to the same T tokens (the pages'
  * models stack dozens of MoE layers per token).  Each is a pre-norm residual

@@ -107,6 +107,7 @@ _SIGS = {
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_layer_workspace_bytes": (_S, [_P, _I, _I]),
     "moe_layer_forward": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
+    "moe_layer_forward_streamed": (C.c_int, [_P, _P, _S, _P, _I, _P, _P, _P, _P, _P, _S, _P, _P, _P]),
     "moe_chain_workspace_bytes": (_S, [_P, _I, _I, _I]),
     "moe_chain_forward": (C.c_int, [_P, _I, C.c_float, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
 }
@@ -486,6 +487,33 @@ def moe_layer_forward(layer: Layer, x, path: int = MOE_PATH_AUTO, workspace=None
                                 path, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "moe_layer_forward")
     return y, idx, w, s
+
+
+def moe_layer_forward_streamed(layer: Layer, x, host_blobs, copy_stream=None, workspace=None, out=None,
+                               stream=None):
+    """One decode step on a partly resident pool, the misses copied in from
+    host_blobs (pinned uint8 [E, stride]) on copy_stream while the resident
+    experts compute.  Returns (y, topk_idx, topk_w, shared_gate, n_loads);
+    blocks the calling thread until the step's selections reach the host."""
+    import torch
+    T, d = x.shape
+    k = layer.k
+    if out is None:
+        out = (torch.empty((T, d), dtype=torch.float32, device=x.device),
+               torch.empty((T, k), dtype=torch.int32, device=x.device),
+               torch.empty((T, k), dtype=torch.float32, device=x.device),
+               torch.empty((T,), dtype=torch.float32, device=x.device))
+    y, idx, w, s = out
+    if workspace is None:
+        workspace = _ws(layer.workspace_bytes(T, MOE_PATH_DECODE))
+    nl = C.c_int32(0)
+    st = _lib.moe_layer_forward_streamed(C.byref(layer.desc), host_blobs.data_ptr(), host_blobs.stride(0),
+                                         _ptr(x), T, _ptr(y), _ptr(idx), _ptr(w), _ptr(s), _ptr(workspace),
+                                         workspace.numel(), _stream(stream),
+                                         _stream(copy_stream) if copy_stream is not None else _stream(stream),
+                                         C.byref(nl))
+    _check(st, "moe_layer_forward_streamed")
+    return y, idx, w, s, int(nl.value)
 
 
 # -------------------------------------------------------------- layer chain

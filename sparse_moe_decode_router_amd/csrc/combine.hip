@@ -63,7 +63,68 @@ __global__ void table_edit_kernel(int32_t* __restrict__ table, TableEdit ed) {
     for (int q = 0; q < ed.n; ++q) table[ed.expert[q]] = ed.slot[q];
 }
 
+// Blob copies host -> slot carried by value as well: blob q of the launch is
+// read from src + expert[q] * src_stride (pinned host memory, read over PCIe
+// by the CUs) and written to dst + slot[q] * dst_stride.
+struct BlobPull {
+  const uint4* src;
+  uint4* dst;
+  long src_stride16, dst_stride16, n16;     // in 16-byte pieces (n16 per blob, from off16)
+  long off16;
+  int32_t n;
+  int32_t expert[30];
+  int32_t slot[30];
+};
+
+__global__ __launch_bounds__(256) void blob_pull_kernel(BlobPull j) {
+  const long total = j.n16 * j.n;
+  const long step = (long)gridDim.x * blockDim.x;
+  // four pieces per thread in flight (clamped loads, guarded stores)
+  for (long q0 = (long)blockIdx.x * blockDim.x + threadIdx.x; q0 < total; q0 += 4 * step) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long q = q0 + u * step < total ? q0 + u * step : 0;
+      const int b = (int)(q / j.n16);
+      v[u] = j.src[j.expert[b] * j.src_stride16 + j.off16 + q % j.n16];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long q = q0 + u * step;
+      if (q < total) {
+        const int b = (int)(q / j.n16);
+        j.dst[j.slot[b] * j.dst_stride16 + j.off16 + q % j.n16] = v[u];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+int blob_pull_launch(const void* src_dev, size_t src_stride, void* dst, size_t dst_stride, size_t off,
+                     size_t bytes, const int32_t* experts, const int32_t* slots, int n, hipStream_t s) {
+  if ((uintptr_t)src_dev % 16 || (uintptr_t)dst % 16 || src_stride % 16 || dst_stride % 16 || bytes % 16 ||
+      off % 16)
+    return MOE_ERR_INVALID_ARG;
+  for (int base = 0; base < n; base += 30) {
+    BlobPull j;
+    j.src = static_cast<const uint4*>(src_dev);
+    j.dst = static_cast<uint4*>(dst);
+    j.src_stride16 = (long)(src_stride / 16);
+    j.dst_stride16 = (long)(dst_stride / 16);
+    j.n16 = (long)(bytes / 16);
+    j.off16 = (long)(off / 16);
+    j.n = (n - base) < 30 ? (n - base) : 30;
+    for (int q = 0; q < j.n; ++q) {
+      j.expert[q] = experts[base + q];
+      j.slot[q] = slots[base + q];
+    }
+    // 64 blocks already keep the PCIe link full; more would only take CUs
+    blob_pull_kernel<<<64, 256, 0, s>>>(j);
+    MOE_HIP(hipGetLastError());
+  }
+  return MOE_OK;
+}
 
 int combine_launch(const float* partial, const float* shared_out, const float* w, const float* sgate,
                    int T, int k, int d, float* y, hipStream_t s) {

@@ -71,6 +71,11 @@ struct GateUpArgs {
   uint32_t* hq;                 // [hrows][Imax]: hi pairs then lo pairs
   float* hs8;                   // [hrows][Imax/8]
   int batched;
+  // decode in two phases (expert streaming): phase 1 computes the resident
+  // selections and defers the missing ones (pend[i] = their slot then, -1 =
+  // deferred); phase 2, after the refill, computes only the deferred ones
+  int phase;                    // 0: one pass
+  int32_t* pend;                // [T*k]
 };
 
 // Resolve instance -> (blob, I, tokens, hrows).  Returns ntok (0 = skip).
@@ -240,6 +245,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     const int rel = routed ? item : item - nR * rbR;
     const int rb_per = routed ? rbR : rbS;
     const int i = rel / rb_per, rb = rel % rb_per;
+    if (a.phase == 2 && (!routed || a.pend[i] >= 0)) continue;   // done in phase 1
     const uint8_t* blob;
     int Iinst, tok[TC], hrow[TC];
     bool missing = false;
@@ -284,8 +290,12 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
       if (rb == 0 && tid == 0) a.sel_slot[i] = slot;
     } else {
       ntok = resolve(a, routed, i, &blob, &Iinst, tok, hrow, &missing);
-      if (!a.batched && routed && rb == 0 && tid == 0)
-        a.sel_slot[i] = missing ? -1 : (int32_t)((blob - a.pool.slab) / a.pool.stride);
+      if (!a.batched && routed && rb == 0 && tid == 0) {
+        const int32_t sl = missing ? -1 : (int32_t)((blob - a.pool.slab) / a.pool.stride);
+        a.sel_slot[i] = sl;
+        if (a.phase == 1) a.pend[i] = sl;
+      }
+      if (a.phase == 1 && missing) continue;    // deferred: its blob is still on the way
     }
     const BlobLayout L = blob_layout(a.d, Iinst, BITS);
     const int o0 = rb * 8;
@@ -661,6 +671,13 @@ struct DownArgs {
   const uint16_t* res_in;
   uint16_t* res_out;
   float* ssp_out;
+  // decode in two phases (expert streaming): phase 1 writes every
+  // instance's outputs for these rows to oi_buf [T*(k+1)][d] (deferred
+  // selections as 0) and stops; phase 2 computes the deferred selections
+  // (pend[i] < 0), takes the others from oi_buf and combines
+  int phase;
+  const int32_t* pend;
+  float* oi_buf;
 };
 
 // Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order
@@ -700,12 +717,19 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
       const int qw = tid + 64 * kDnWaves * u < nI ? tid + 64 * kDnWaves * u : 0;
       wkv[u] = *(qw < nR ? a.w + qw : a.sgate + (qw - nR));
     }
+    // phase 2 of a streamed step: instances done in phase 1 come from oi_buf
+    bool from_buf = false;
+    float obuf = 0.f;
+    if (a.phase == 2 && active) {
+      from_buf = i >= nR || a.pend[i] >= 0;
+      if (from_buf) obuf = a.oi_buf[(size_t)i * a.d + j];
+    }
     uint4 q[kNP];
     uint32_t sb = 0;
     bool miss = true;
     int Iinst = 0;
     const uint8_t* blob = nullptr;
-    if (active) {
+    if (active && !from_buf) {
       if (i < nR) {
         const int slot = slot_ld;
         miss = slot < 0;
@@ -747,9 +771,14 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
         }
       }
       acc = sum8_dpp(acc);
-      if (gl == 0) oi[i * 8 + r] = acc;
+      if (gl == 0) oi[i * 8 + r] = from_buf ? obuf : acc;
     }
     __syncthreads();
+  }
+  if (a.phase == 1) {                           // streamed step: hand the outputs to phase 2
+    for (int q2 = tid; q2 < nI * 8; q2 += 64 * kDnWaves)
+      a.oi_buf[(size_t)(q2 / 8) * a.d + jb * 8 + (q2 % 8)] = oi[q2];
+    return;
   }
   if (tid < 8 * a.T) {
     const int t = tid / 8, rr = tid % 8;
@@ -1217,6 +1246,7 @@ struct FfnWs {
   uint32_t* xq; float* xs;
   uint32_t* hq; float* hs8;
   int32_t* sel_slot;
+  int32_t* pend; float* oi_buf;     // decode: two-phase steps
   Inst* inst; int32_t* n_routed;
 };
 
@@ -1227,6 +1257,12 @@ bool carve_ffn(Carver& c, int d, int Imax, int T, int k, int path, FfnWs* w) {
   w->hq = c.take<uint32_t>(hrows * Imax);
   w->hs8 = c.take<float>(hrows * Imax / 8);
   w->sel_slot = c.take<int32_t>((size_t)T * k);
+  w->pend = nullptr;
+  w->oi_buf = nullptr;
+  if (path == MOE_PATH_DECODE) {
+    w->pend = c.take<int32_t>((size_t)T * k);
+    w->oi_buf = c.take<float>(hrows * d);
+  }
   w->inst = nullptr;
   w->n_routed = nullptr;
   if (path != MOE_PATH_DECODE) {
@@ -1371,6 +1407,12 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   dn.sel_slot = w.sel_slot; dn.w = f.w; dn.sgate = f.sgate; dn.hq = w.hq; dn.hs8 = w.hs8; dn.y = f.y;
   dn.res_in = f.res_in; dn.res_out = f.res_out; dn.ssp_out = f.ssp_out;
   if (f.res_out && (path != MOE_PATH_DECODE || f.bits == 32)) return MOE_ERR_INVALID_ARG;
+  // two-phase decode: routing given, quantised experts, no hand-over in phase 1
+  if (f.phase != 0 && (path != MOE_PATH_DECODE || f.bits == 32 || f.logits || f.phase < 0 || f.phase > 2 ||
+                       (f.phase == 1 && f.res_out)))
+    return MOE_ERR_INVALID_ARG;
+  g.phase = f.phase; g.pend = w.pend;
+  dn.phase = f.phase; dn.pend = w.pend; dn.oi_buf = w.oi_buf;
 
   if (f.bits == 32) return f32_launch(f, path, g, dn, w, Imax, s);
   if (path == MOE_PATH_DECODE) {
@@ -1381,10 +1423,12 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
                        (f.logits ? (size_t)(topk_scratch_words(E) + E + 2 * f.k) * 4 : 0);
     void* fn = kf.gate_up(nk_for(E), G);
     void* args[] = {&g};
-    MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));   // multiple of 8: xcd_remap
+    if (f.phase != 2 || f.pending > 0)   // multiple of 8: xcd_remap
+      MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
+    if (f.phase == 2 && f.down_wait) MOE_HIP(hipStreamWaitEvent(s, f.down_wait, 0));
     MOE_HIP(hipLaunchKernel(kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
     return MOE_OK;
   }

@@ -151,6 +151,13 @@ struct FfnArgs {
   const uint16_t* res_in;   // decode, chains: residual hand-over (see ChainIO)
   uint16_t* res_out;
   float* ssp_out;
+  // decode with routing given, in two phases around a pool refill (the same
+  // workspace for both): 1 = resident selections only (missing ones are
+  // deferred, not errors), 2 = the deferred ones, then the combine; pending =
+  // number of deferred selections (phase 2 skips the gate/up pass at 0)
+  int phase;
+  int pending;
+  hipEvent_t down_wait;     // phase 2: the stream waits for it between the gate/up and down passes
 };
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
 size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E);

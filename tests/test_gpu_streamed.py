@@ -1,0 +1,74 @@
+"""Streamed decode steps (moe_layer_forward_streamed): a pool holding only
+some experts, refilled by LFU + recency from pinned host memory on a copy
+stream while the resident experts compute.  Every output must be
+bit-identical to the same step on an all-resident pool (the decode path of
+moe_layer_forward), whatever was resident, copied or deferred."""
+import numpy as np
+import pytest
+
+import moe_synth as ms
+from gpu_support import DeviceLayer
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("sparse_moe_decode_router_amd")
+
+
+def _host_blobs(L):
+    return torch.from_numpy(np.stack([L.blob(e) for e in range(L.cfg.E)])).pin_memory()
+
+
+def _run(cfg, n_slots, T, steps, copy_stream=True):
+    twin = DeviceLayer(cfg)                                  # all resident, permuted slots
+    part = DeviceLayer(cfg, table=None, n_slots=n_slots)     # starts empty
+    host = _host_blobs(twin)
+    cs = torch.cuda.Stream() if copy_stream else None
+    ws = torch.zeros(part.layer.workspace_bytes(T, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
+    loads = []
+    for step in range(steps):
+        _, x = twin.x(step, T)
+        y, idx, w, s, nl = moe.moe_layer_forward_streamed(part.layer, x, host, copy_stream=cs, workspace=ws)
+        yt, it, wt, st = moe.moe_layer_forward(twin.layer, x, path=moe.MOE_PATH_DECODE)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, it) and torch.equal(w, wt) and torch.equal(s, st), step
+        assert torch.equal(y, yt), (step, float((y - yt).abs().max()))
+        loads.append(nl)
+    assert part.pool.check_error() == moe.MOE_OK
+    stats = part.pool.stats()
+    assert stats["misses"] > 0 and sum(loads) == stats["loads"]
+    return loads, stats
+
+
+def test_streamed_small_pool_bit_identical():
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], d=256, E=64, k=6, I=64, I_shared=64, alpha=0.0)
+    loads, st = _run(cfg, 16, 1, 24)
+    assert loads[0] == 6 and st["hits"] > 0               # cold start: every selection is a miss
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_streamed_several_tokens(T):
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], d=512, E=64, k=4, I=128, I_shared=128, alpha=0.15)
+    _run(cfg, 32, T, 12)
+
+
+def test_streamed_same_stream_and_int8():
+    cfg = ms.scaled(ms.CONFIGS["decode80b_int8"], d=256, E=32, k=4, I=64, I_shared=64)
+    _run(cfg, 12, 1, 12, copy_stream=False)
+
+
+def test_streamed_80b_shape():
+    cfg = ms.CONFIGS["decode80b"]                           # 256 slots over 512 experts
+    loads, st = _run(cfg, cfg.n_slots, 1, 6)
+    assert loads[0] == cfg.k
+
+
+def test_streamed_pool_too_small():
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], d=256, E=64, k=6, I=64, I_shared=64, alpha=0.0)
+    part = DeviceLayer(cfg, table=None, n_slots=8)
+    host = _host_blobs(part)
+    _, x = part.x(0, 4)                                     # 4 tokens x 6 picks: more than 8 experts
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_forward_streamed(part.layer, x, host)
+    assert ei.value.status == moe.MOE_ERR_POOL_TOO_SMALL
+    torch.cuda.synchronize()
