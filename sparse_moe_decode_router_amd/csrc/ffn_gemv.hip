@@ -186,6 +186,31 @@ __device__ __forceinline__ void stage_x(const uint32_t* __restrict__ xq, const i
   }
 }
 
+// The same LDS tile from bf16 x itself: piece c4 (x[8 c4 .. 8 c4 + 7]) goes
+// in as the pairs (x[i], x[i+4]) the GEMVs read, i = 0..3.
+template <int TC>
+__device__ __forceinline__ void stage_x_raw(const uint16_t* __restrict__ x, const int (&tok)[TC], int ntok, int d,
+                                            uint32_t* xlds) {
+  const int per = d / 8;
+  for (int c4 = threadIdx.x; c4 < per; c4 += 256) {
+    uint4 v[TC];
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) {
+      const int tk = tt < ntok ? tok[tt] : tok[0];
+      v[tt] = reinterpret_cast<const uint4*>(x + (size_t)tk * d)[c4];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) {
+      uint4 p;
+      p.x = (v[tt].x & 0xFFFFu) | (v[tt].z << 16);
+      p.y = (v[tt].x >> 16) | (v[tt].z & 0xFFFF0000u);
+      p.z = (v[tt].y & 0xFFFFu) | (v[tt].w << 16);
+      p.w = (v[tt].y >> 16) | (v[tt].w & 0xFFFF0000u);
+      *reinterpret_cast<uint4*>(&xlds[((tt < ntok ? tt : 0) * (d / 64) + (c4 >> 3)) * kXPad + 4 * (c4 & 7)]) = p;
+    }
+  }
+}
+
 // h of 8 consecutive intermediate rows (one 8-block m = rb) as bf16 (hi, lo)
 // pairs (h[8m+i], h[8m+i+4]) plus the sum of hi + lo, for the down pass.
 __device__ __forceinline__ void write_h8(const float* h, uint32_t* hq, float* hs8, int Imax, int hrow, int rb) {
@@ -218,7 +243,10 @@ __device__ __forceinline__ void write_h8(const float* h, uint32_t* hq, float* hs
 // the top-k, and the block of (rank 0, rows 0..7) publishes the token's
 // indices, weights, shared gate and usage.  This trades a redundant ~1k-cycle
 // selection per block for the dependent global loads of a separate top-k.
-template <int TC, int NK, int GPL, int BITS>
+// RAW (routing given, no prepared activations): the block forms the bf16
+// pairs from x and the group sums in the order the router's preparation
+// uses, so the results are the same bits; the in-kernel selection is absent.
+template <int TC, int NK, int GPL, int BITS, bool RAW>
 __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   constexpr int kNP = BITS / 2;                 // 16-byte code pieces per group
   extern __shared__ uint32_t xlds[];            // [TC][G][kXPad] | routing area
@@ -250,7 +278,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     int Iinst, tok[TC], hrow[TC];
     bool missing = false;
     int ntok;
-    if (!a.batched && routed && a.logits) {
+    if (!RAW && !a.batched && routed && a.logits) {
       const int t = i / a.k, rank = i % a.k;
       const float* lrow = a.logits + (size_t)t * (E + 1);
       if (wave != 0) {
@@ -309,7 +337,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
       const int g = cpl + 32 * gi;
 #pragma unroll
       for (int tt = 0; tt < TC; ++tt)
-        sxv[gi][tt] = (g < G && tt < ntok) ? a.xs[(size_t)tok[tt] * G + g] : 0.f;
+        sxv[gi][tt] = (!RAW && g < G && tt < ntok) ? a.xs[(size_t)tok[tt] * G + g] : 0.f;
     }
     if (!missing) {
       const uint64_t o = (uint64_t)(o0 + r);
@@ -330,7 +358,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
       }
     }
     // 2. stage activations (bf16 pairs) while the weights are in flight
-    stage_x<TC>(a.xq, tok, ntok, a.d, xlds);
+    if constexpr (RAW) stage_x_raw<TC>(a.x, tok, ntok, a.d, xlds);
+    else stage_x<TC>(a.xq, tok, ntok, a.d, xlds);
     __syncthreads();
 
     float vg[TC], vu[TC];
@@ -347,12 +376,16 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
         for (int tt = 0; tt < TC; ++tt) {
           if (tt < ntok) {
             const uint32_t* xp = &xlds[(tt * G + g) * kXPad];
-            const float sx = sxv[gi][tt];
+            float sxl = 0.f;                  // RAW: the group sum
             float ag0 = 0.f, au0 = 0.f, ag1 = 0.f, au1 = 0.f;   // two chains each
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
               const uint4 xv = *reinterpret_cast<const uint4*>(xp + 4 * m);
               const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+              if constexpr (RAW) {            // x[8m .. 8m+7] in column order
+                sxl += bf16_lo(xv.x); sxl += bf16_lo(xv.y); sxl += bf16_lo(xv.z); sxl += bf16_lo(xv.w);
+                sxl += bf16_hi(xv.x); sxl += bf16_hi(xv.y); sxl += bf16_hi(xv.z); sxl += bf16_hi(xv.w);
+              }
 #pragma unroll
               for (int s2 = 0; s2 < BITS / 2; ++s2) {     // products u = 2 s2 and 2 s2 + 1
                 const int u0 = 2 * s2, u1 = 2 * s2 + 1;
@@ -363,8 +396,12 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
               }
             }
             const float ag = ag0 + ag1, au = au0 + au1;
-            vg[tt] += sg * ag + (bg - qoff<BITS>() * sg) * sx;
-            vu[tt] += su * au + (bu - qoff<BITS>() * su) * sx;
+            const float sx = RAW ? sxl : sxv[gi][tt];
+            // explicit roundings: every instance of this kernel (with or
+            // without in-kernel selection, RAW or not) does the same arithmetic
+            const float cg = __fmaf_rn(-qoff<BITS>(), sg, bg), cu = __fmaf_rn(-qoff<BITS>(), su, bu);
+            vg[tt] = __fmaf_rn(sg, ag, __fmaf_rn(cg, sx, vg[tt]));
+            vu[tt] = __fmaf_rn(su, au, __fmaf_rn(cu, sx, vu[tt]));
           }
         }
       }
@@ -1282,14 +1319,17 @@ struct GemvFns {
   template <int GPL>
   static void* gate_up_g(int nk) {
     switch (nk) {
-      case 1: return (void*)gate_up_kernel<1, 1, GPL, BITS>;
-      case 2: return (void*)gate_up_kernel<1, 2, GPL, BITS>;
-      case 4: return (void*)gate_up_kernel<1, 4, GPL, BITS>;
-      case 8: return (void*)gate_up_kernel<1, 8, GPL, BITS>;
-      default: return (void*)gate_up_kernel<1, 16, GPL, BITS>;
+      case 1: return (void*)gate_up_kernel<1, 1, GPL, BITS, false>;
+      case 2: return (void*)gate_up_kernel<1, 2, GPL, BITS, false>;
+      case 4: return (void*)gate_up_kernel<1, 4, GPL, BITS, false>;
+      case 8: return (void*)gate_up_kernel<1, 8, GPL, BITS, false>;
+      case 0: return (void*)gate_up_kernel<1, 1, GPL, BITS, true>;   // RAW (nk unused)
+      default: return (void*)gate_up_kernel<1, 16, GPL, BITS, false>;
     }
   }
-  static void* gate_up(int nk, int G) {
+  // raw: routing given and no prepared activations (the blocks form them)
+  static void* gate_up(int nk, int G, bool raw = false) {
+    if (raw) nk = 0;
     return G <= 32 ? gate_up_g<1>(nk) : G <= 64 ? gate_up_g<2>(nk) : gate_up_g<4>(nk);
   }
   static void* gate_up_batched(int G) {
@@ -1302,7 +1342,7 @@ struct GemvFns {
 };
 
 struct GemvSet {
-  void* (*gate_up)(int, int);
+  void* (*gate_up)(int, int, bool);
   void* (*gate_up_batched)(int);
   void* (*down_decode)();
   void* (*down_batched)();
@@ -1387,7 +1427,8 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
   if (!carve_ffn(c, f.d, Imax, f.T, f.k, path, &w)) return MOE_ERR_INVALID_ARG;
   const uint32_t* xq = f.xq;
   const float* xs = f.xs;
-  if (!xq && f.bits != 32) {
+  // decode without prepared pairs: the gate/up blocks form them from x
+  if (!xq && f.bits != 32 && path != MOE_PATH_DECODE) {
     MOE_TRY(xprep_launch(f.x, f.T, f.d, w.xq, w.xs, s));
     xq = w.xq;
     xs = w.xs;
@@ -1421,7 +1462,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int E = f.pool.E;
     const size_t lds = (size_t)1 * G * kXPad * 4 +
                        (f.logits ? (size_t)(topk_scratch_words(E) + E + 2 * f.k) * 4 : 0);
-    void* fn = kf.gate_up(nk_for(E), G);
+    void* fn = kf.gate_up(nk_for(E), G, xq == nullptr);
     void* args[] = {&g};
     if (f.phase != 2 || f.pending > 0)   // multiple of 8: xcd_remap
       MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));
