@@ -498,6 +498,9 @@ def moe_layer_forward_streamed(layer: Layer, x, host_blobs, copy_stream=None, wo
     import torch
     T, d = x.shape
     k = layer.k
+    if (host_blobs.dtype != torch.uint8 or host_blobs.dim() != 2 or host_blobs.is_cuda
+            or not host_blobs.is_pinned() or not host_blobs.is_contiguous()):
+        raise ValueError("host_blobs must be a contiguous pinned uint8 host tensor [E, stride]")
     if out is None:
         out = (torch.empty((T, d), dtype=torch.float32, device=x.device),
                torch.empty((T, k), dtype=torch.int32, device=x.device),
