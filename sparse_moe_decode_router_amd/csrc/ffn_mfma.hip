@@ -259,13 +259,108 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
   stage_barrier<0>();
 }
 
+// The same GEMM for chunks of at most 32 tokens (one m-tile), with more
+// steps in flight: a stage holds only the live 32 activation rows (4 KB, one
+// 1 KB DMA per wave), the codes and the (scale, bias) words, so the LDS of
+// the three full stages takes NS of these and NS - 1 steps are in flight.
+// Used for 8-bit codes (batched 80B shape: gate/up 236 -> 219 us, down
+// 141 -> 121 us); with 4-bit codes it measured slower than the full-stage
+// loop (gate/up 131 -> 193 us at any depth from 3 to 7 stages), not yet
+// understood, so 4-bit keeps that loop.
+// a_vo_n: this lane's activation offset for row 8 * wave + lane / 8.
+template <int BITS> constexpr int kNarrowStage = 4096 + 4096 * kCodeDma<BITS> + 1024;
+template <int BITS> constexpr int kNarrowNS = (3 * kStage<BITS>) / kNarrowStage<BITS>;
+
+template <int BITS>
+__device__ __forceinline__ void gemm_loop_narrow(uint8_t* SM, rsrc_t rA, uint32_t a_vo_n, rsrc_t rB,
+                                                 uint32_t codes_off, uint32_t sb_off, uint32_t rows, uint32_t row,
+                                                 int C, float16_t* acc) {
+  constexpr int ND = kCodeDma<BITS>;
+  constexpr int kA = 4096, kB = 4096 * ND, kSt = kNarrowStage<BITS>, NS = kNarrowNS<BITS>;
+  constexpr int kPer = 2 + ND;                  // DMAs per wave per stage
+  static_assert(NS >= 3 && NS <= 7 && (NS - 2) * kPer < 64, "stages in flight");
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t b_vo[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) b_vo[j] = ((ND * h + j) * rows + row) * 16;
+  const uint32_t s_vo = row * 4;
+  const rsrc_t rN = make_rsrc(nullptr, 0);
+  auto issue = [&](int s) {
+    uint8_t* st = SM + (s % NS) * kSt;
+    const bool live = s < C;
+    const rsrc_t ra = live ? rA : rN, rb = live ? rB : rN;
+    const uint32_t ao = __builtin_amdgcn_readfirstlane(s * 128);
+    const uint32_t co = __builtin_amdgcn_readfirstlane(codes_off + (uint32_t)(2 * ND) * s * rows * 16);
+    const uint32_t so = __builtin_amdgcn_readfirstlane(sb_off + (uint32_t)s * rows * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_opaque(st + wave * 1024), 16, a_vo_n, ao, 0, 0);
+#pragma unroll
+    for (int j = 0; j < ND; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kA + (ND * wave + j) * 1024), 16, b_vo[j], co,
+                                               0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kA + kB + wave * 256), 4, s_vo, so, 0, 0);
+  };
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (q < C) issue(q);
+  for (int s = 0; s < C; ++s) {
+    // stage s landed for this wave (the stages issued after it, at most
+    // NS - 2, may still be in flight; no stage past the end is issued) and
+    // every wave is done with stage s - 1, which the next issue refills
+    const int behind = C - 1 - s < NS - 2 ? C - 1 - s : NS - 2;
+    switch (behind) {
+      case 0: stage_barrier<0>(); break;
+      case 1: stage_barrier<kPer>(); break;
+      case 2: stage_barrier<2 * kPer>(); break;
+      case 3: stage_barrier<3 * kPer>(); break;
+      case 4: stage_barrier<(NS - 2 >= 4 ? 4 : 0) * kPer>(); break;
+      default: stage_barrier<(NS - 2 >= 5 ? 5 : 0) * kPer>(); break;
+    }
+    if (s + NS - 1 < C) issue(s + NS - 1);
+    const uint8_t* st = SM + (s % NS) * kSt;
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kA + kB + wave * 256 + 4 * (lane & 31));
+    const half2_t s2 = __builtin_bit_cast(half2_t, (sb & 0xFFFFu) * 0x10001u);
+    const half2_t b2 = __builtin_bit_cast(half2_t, (sb >> 16) * 0x10001u);
+    half8_t bv[4];
+    if constexpr (BITS == 4) {
+      const uint4 cw = *reinterpret_cast<const uint4*>(st + kA + wave * 1024 + 16 * lane);
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+    } else {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(st + kA + (2 * wave) * 1024 + 16 * lane);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(st + kA + (2 * wave + 1) * 1024 + 16 * lane);
+      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half8_t av = *reinterpret_cast<const half8_t*>(st + a_pos(lane & 31, 4 * h + j));
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[0], 0, 0, 0);
+    }
+  }
+  stage_barrier<0>();
+}
+
 template <int BITS>
 __device__ __forceinline__ void gemm_tiles(int n_tok, uint8_t* S0, uint8_t* S1, uint8_t* S2, rsrc_t rA,
-                                           const uint32_t* a_vo,
+                                           const uint32_t* a_vo, uint32_t a_vo_n,
                                            rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
                                            uint32_t row, int C, float16_t* acc) {
   switch ((n_tok + 31) >> 5) {
-    case 1: gemm_loop<1, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
+    case 1:
+      // 8-bit: the narrow stages (measured faster on one-tile chunks); 4-bit
+      // stays on the full-stage loop, which measured faster there
+      if constexpr (BITS == 8) gemm_loop_narrow<BITS>(S0, rA, a_vo_n, rB, codes_off, sb_off, rows, row, C, acc);
+      else gemm_loop<1, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc);
+      break;
     case 2: gemm_loop<2, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
     case 3: gemm_loop<3, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
     default: gemm_loop<4, BITS>(S0, S1, S2, rA, a_vo, rB, codes_off, sb_off, rows, row, C, acc); break;
@@ -286,7 +381,11 @@ __device__ __forceinline__ bool xcd_item(long L, int nch, int nt, int* chunk, in
 
 template <int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gate_up_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage<BITS>], S1[kStage<BITS>], S2[kStage<BITS>];
+  // three stages, contiguous (chunks of <= 32 tokens use the space as more, smaller stages)
+  __shared__ __attribute__((aligned(16))) uint8_t SM[3 * kStage<BITS>];
+  uint8_t* S0 = SM;
+  uint8_t* S1 = SM + kStage<BITS>;
+  uint8_t* S2 = SM + 2 * kStage<BITS>;
   __shared__ int tok_s[kPM], hrow_s[kPM];
   // up tiles handed to the gate waves after the GEMM, one m-tile at a time;
   // they reuse stage 0 (no DMA is in flight and no wave reads the stages
@@ -341,6 +440,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int t = tok_s[r];
       a_vo[i] = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ (r & 7));
     }
+    uint32_t a_vo_n;                            // one-tile chunks: row 8 * wave + lane / 8
+    {
+      const int r = 8 * wave + (lane >> 3);
+      const int t = tok_s[r];
+      a_vo_n = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ (r & 7));
+    }
     float16_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -348,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
     const uint32_t mc = (uint32_t)(mat ? L.m[1].codes : L.m[0].codes);
     const uint32_t ms = (uint32_t)(mat ? L.m[1].sb : L.m[0].sb);
-    gemm_tiles<BITS>(in.n, S0, S1, S2, rX, a_vo, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
+    gemm_tiles<BITS>(in.n, S0, S1, S2, rX, a_vo, a_vo_n, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
                      (uint32_t)(o0 + colb + (lane & 31)), C, acc);
     // epilogue: up waves hand their tiles to the gate waves, one m-tile at a time
     const int mt_live = (in.n + 31) >> 5;
@@ -384,7 +489,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_down_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t S0[kStage<BITS>], S1[kStage<BITS>], S2[kStage<BITS>];
+  __shared__ __attribute__((aligned(16))) uint8_t SM[3 * kStage<BITS>];
+  uint8_t* S0 = SM;
+  uint8_t* S1 = SM + kStage<BITS>;
+  uint8_t* S2 = SM + 2 * kStage<BITS>;
   __shared__ int hrow_s[kPM], tok_s[kPM];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
@@ -427,12 +535,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int hr = hrow_s[r];
       a_vo[i] = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ (r & 7));
     }
+    uint32_t a_vo_n;                            // one-tile chunks: row 8 * wave + lane / 8
+    {
+      const int r = 8 * wave + (lane >> 3);
+      const int hr = hrow_s[r];
+      a_vo_n = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ (r & 7));
+    }
     float16_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-    gemm_tiles<BITS>(in.n, S0, S1, S2, rH, a_vo, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
+    gemm_tiles<BITS>(in.n, S0, S1, S2, rH, a_vo, a_vo_n, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
                      (uint32_t)L.m[2].sb, (uint32_t)a.d, (uint32_t)(n0 + 32 * wave + (lane & 31)), Iinst / kKS, acc);
     const int n = n0 + 32 * wave + (lane & 31);
 #pragma unroll
