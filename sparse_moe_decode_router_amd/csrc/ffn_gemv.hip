@@ -1462,7 +1462,7 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int E = f.pool.E;
     const size_t lds = (size_t)1 * G * kXPad * 4 +
                        (f.logits ? (size_t)(topk_scratch_words(E) + E + 2 * f.k) * 4 : 0);
-    void* fn = kf.gate_up(nk_for(E), G, xq == nullptr);
+    void* fn = kf.gate_up(f.logits ? nk_for(E) : 1, G, xq == nullptr);   // no selection: the smallest instance
     void* args[] = {&g};
     if (f.phase != 2 || f.pending > 0)   // multiple of 8: xcd_remap
       MOE_HIP(hipLaunchKernel(fn, dim3((items + 7) & ~7), dim3(256), args, lds, s));

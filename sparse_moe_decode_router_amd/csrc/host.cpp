@@ -652,10 +652,16 @@ int layer_forward(const moe_layer_desc* L, const uint16_t* x, int T, float* y, i
   if (!carve_layer(c, L, T, path, &lw)) return MOE_ERR_INVALID_ARG;
   const int d = L->sh.d;
   const bool f32 = shape_bits(&L->sh) == 32;
+  // one token: the decode FFN selects the experts in-kernel (its blocks all
+  // run at once, so the selection costs one pass); more tokens take several
+  // rounds of gate/up blocks, each of which would repeat it: one top-k
+  // kernel, then the FFN with the routing given
+  const bool sel_in_ffn = path == MOE_PATH_DECODE && !f32 && T == 1;
   if (path == MOE_PATH_DECODE && !f32) {
-    // logits here; the decode FFN selects the experts in-kernel
     MOE_TRY(router_logits_launch(x, T, d, L->w_router_dev, L->E, lw.r, s, true, io ? io->ssp_in : nullptr,
                                  io ? io->eps : 0.f));
+    if (!sel_in_ffn)
+      MOE_TRY(topk_launch(lw.r.logits, L->logit_bias_dev, T, d, L->E, L->k, idx, w, sgate, L->usage_dev, s));
   } else if (path == MOE_PATH_DECODE) {
     // f32 experts: top-k here, then the FFN with the routing given
     MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, L->k, idx, w, sgate,
@@ -675,10 +681,13 @@ int layer_forward(const moe_layer_desc* L, const uint16_t* x, int T, float* y, i
   a.T = T; a.k = L->k; a.idx = idx; a.w = w; a.sgate = sgate;
   if (path == MOE_PATH_DECODE) {
     a.y = y;
-    if (!f32) {
+    if (sel_in_ffn) {
       a.logits = lw.r.logits;
       a.bias = L->logit_bias_dev;
       a.usage = L->usage_dev;
+    } else if (!f32 && !io) {
+      a.xq = nullptr;                           // the gate/up blocks form the pairs from x (same bits)
+      a.xs = nullptr;
     }
     if (io) {
       a.res_in = io->res_in;
