@@ -601,34 +601,51 @@ struct Rows4 {                                  // up to four rows, named (no ar
 // addressing (so the compiler neither waits per piece nor sinks the loads
 // to their stores); pieces past the end reload and rewrite piece 0 of
 // record 0 (same value, same place).
+// One pass of it: the pieces in registers with their LDS destinations.
+struct HPass {
+  uint4 vp[4], vs;
+  int dp[4], ds;
+};
+template <int NT, class Rows>
+__device__ __forceinline__ void stage_h_load(const uint32_t* __restrict__ hq, const float* __restrict__ hs8, int Imax,
+                                             int nrec, Rows rows, int rec, int it, HPass& p) {
+  const int pp = Imax / 4, sp = Imax / 32;      // pair pieces and sum pieces per record
+  const int np = nrec * pp, ns = nrec * sp;
+#pragma unroll
+  for (int uu = 0; uu < 4; ++uu) {
+    int q = it * 4 * NT + NT * uu + (int)threadIdx.x;
+    q = q < np ? q : 0;
+    const int r = q / pp, c = q % pp;
+    p.vp[uu] = reinterpret_cast<const uint4*>(hq + (size_t)rows(r) * Imax)[c];
+    const int j = 4 * c, part = j >= Imax / 2 ? 1 : 0, jj = j - part * (Imax / 2);
+    p.dp[uu] = r * rec + (part * (Imax / 64) + (jj >> 5)) * kHG + (jj & 31);
+  }
+  int q = it * NT + (int)threadIdx.x;
+  q = q < ns ? q : 0;
+  const int r = q / sp, c = q % sp;
+  p.vs = reinterpret_cast<const uint4*>(hs8 + (size_t)rows(r) * (Imax / 8))[c];
+  p.ds = r * rec + 2 * (Imax / 64) * kHG + 4 * c;
+}
+__device__ __forceinline__ void stage_h_store(uint32_t* hst, const HPass& p) {
+#pragma unroll
+  for (int uu = 0; uu < 4; ++uu) *reinterpret_cast<uint4*>(hst + p.dp[uu]) = p.vp[uu];
+  *reinterpret_cast<uint4*>(hst + p.ds) = p.vs;
+}
+// Passes needed for nrec records by NT threads.
+template <int NT>
+__host__ __device__ inline int stage_h_passes(int nrec, int Imax) {
+  const int np = nrec * (Imax / 4), ns = nrec * (Imax / 32);
+  const int a = (np + 4 * NT - 1) / (4 * NT), b = (ns + NT - 1) / NT;
+  return a > b ? a : b;
+}
 template <int NT, class Rows>
 __device__ __forceinline__ void stage_h(const uint32_t* __restrict__ hq, const float* __restrict__ hs8, int Imax,
                                         int nrec, Rows rows, uint32_t* hst, int rec) {
-  const int pp = Imax / 4, sp = Imax / 32;      // pair pieces and sum pieces per record
-  const int np = nrec * pp, ns = nrec * sp;
-  const int K = max((np + 4 * NT - 1) / (4 * NT), (ns + NT - 1) / NT);
+  const int K = stage_h_passes<NT>(nrec, Imax);
   for (int it = 0; it < K; ++it) {
-    uint4 vp[4], vs;
-    int dp[4], ds;
-#pragma unroll
-    for (int uu = 0; uu < 4; ++uu) {
-      int q = it * 4 * NT + NT * uu + (int)threadIdx.x;
-      q = q < np ? q : 0;
-      const int r = q / pp, c = q % pp;
-      vp[uu] = reinterpret_cast<const uint4*>(hq + (size_t)rows(r) * Imax)[c];
-      const int j = 4 * c, part = j >= Imax / 2 ? 1 : 0, jj = j - part * (Imax / 2);
-      dp[uu] = r * rec + (part * (Imax / 64) + (jj >> 5)) * kHG + (jj & 31);
-    }
-    {
-      int q = it * NT + (int)threadIdx.x;
-      q = q < ns ? q : 0;
-      const int r = q / sp, c = q % sp;
-      vs = reinterpret_cast<const uint4*>(hs8 + (size_t)rows(r) * (Imax / 8))[c];
-      ds = r * rec + 2 * (Imax / 64) * kHG + 4 * c;
-    }
-#pragma unroll
-    for (int uu = 0; uu < 4; ++uu) *reinterpret_cast<uint4*>(hst + dp[uu]) = vp[uu];
-    *reinterpret_cast<uint4*>(hst + ds) = vs;
+    HPass p;
+    stage_h_load<NT>(hq, hs8, Imax, nrec, rows, rec, it, p);
+    stage_h_store(hst, p);
   }
 }
 
@@ -829,6 +846,152 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
       a.res_out[yi] = (uint16_t)b;
       const float r = __uint_as_float(b << 16);
       const float p = sum8_dpp(__fmul_rn(r, r));
+      if (rr == 0) a.ssp_out[(size_t)t * (a.d / 8) + jb] = p;
+    }
+  }
+}
+
+// Decode down for more than one round of instances: the same arithmetic,
+// with the next round's codes in flight while the current round computes
+// (every selection slot is staged in LDS at the start, so they wait for no
+// slot), and the next round's h records staged after the compute into the
+// second of two LDS buffers (held in registers across the compute they
+// would not fit).
+template <int BITS>
+struct DnInst {                                 // a wave's instance in one round
+  uint4 q[BITS / 2];
+  uint32_t sb;
+  bool miss, from_buf;
+  float obuf;
+  int Iinst;
+  const uint8_t* blob;
+};
+template <int BITS>
+__device__ __forceinline__ void dn_inst_load(const DownArgs& a, int i, bool active, int slot, int j, int gl,
+                                             DnInst<BITS>& s) {
+  constexpr int kNP = BITS / 2;
+  const int nR = a.T * a.k;
+  s.from_buf = false; s.obuf = 0.f; s.miss = true; s.Iinst = 0; s.blob = nullptr; s.sb = 0;
+  if (a.phase == 2 && active) {
+    s.from_buf = i >= nR || a.pend[i] >= 0;
+    if (s.from_buf) s.obuf = a.oi_buf[(size_t)i * a.d + j];
+  }
+  if (active && !s.from_buf) {
+    if (i < nR) {
+      s.miss = slot < 0;
+      s.blob = a.pool.slab + (uint64_t)(s.miss ? 0 : slot) * a.pool.stride;
+      s.Iinst = a.I;
+    } else {
+      s.miss = false;
+      s.blob = a.shared_blob;
+      s.Iinst = a.Ish;
+    }
+    if (!s.miss && gl < s.Iinst / 64) {
+      const BlobLayout L = blob_layout(a.d, s.Iinst, BITS);
+#pragma unroll
+      for (int p = 0; p < kNP; ++p)
+        s.q[p] = *reinterpret_cast<const uint4*>(s.blob + L.m[2].codes + ((uint64_t)(kNP * gl + p) * a.d + j) * 16);
+      s.sb = *reinterpret_cast<const uint32_t*>(s.blob + L.m[2].sb + ((uint64_t)gl * a.d + j) * 4);
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArgs a) {
+  constexpr int kNP = BITS / 2;
+  extern __shared__ float dyn[];                // oi[nI][8] | wk[nI] | slots[nR] | hst[2][kDnRound][rec]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane >> 3, gl = lane & 7;
+  const int jb = xcd_remap(blockIdx.x, gridDim.x);
+  const int j = jb * 8 + r;
+  const int nR = a.T * a.k, nI = nR + a.T;
+  const int rec = hrec_words(a.Imax);
+  float* oi = dyn;
+  float* wk = dyn + nI * 8;
+  int32_t* sl = reinterpret_cast<int32_t*>(wk + nI);
+  uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 9 + nR + 3) & ~3));
+  DnInst<BITS> cur;
+  {
+    // round 0: its slot straight from memory; the combine weights and every
+    // routed slot (nR <= 2048: two per thread, clamped) go to LDS
+    const bool active = wave < kDnRound && wave < nI;
+    const int slot0 = a.sel_slot[(active && wave < nR) ? wave : 0];
+    float wkv[2];
+    int32_t sv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 64 * kDnWaves * u;
+      const int qw = q < nI ? q : 0;
+      wkv[u] = *(qw < nR ? a.w + qw : a.sgate + (qw - nR));
+      sv[u] = a.sel_slot[q < nR ? q : 0];
+    }
+    dn_inst_load<BITS>(a, wave, active, slot0, j, gl, cur);
+    stage_h<64 * kDnWaves>(a.hq, a.hs8, a.Imax, min(kDnRound, nI), RowsFrom{0}, hst, rec);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 64 * kDnWaves * u;
+      wk[q < nI ? q : 0] = wkv[u];
+      sl[q < nR ? q : 0] = sv[u];
+    }
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int base = 0; base < nI; base += kDnRound) {
+    const int nr = min(kDnRound, nI - base);
+    const int i = base + wave;
+    const bool active = wave < nr;
+    const int nb = base + kDnRound, nnr = min(kDnRound, nI - nb);
+    // 1. the next round's codes, in flight during the compute
+    DnInst<BITS> nxt;
+    if (nnr > 0) {
+      const int i2 = nb + wave;
+      const bool act2 = wave < nnr;
+      dn_inst_load<BITS>(a, i2, act2, sl[(act2 && i2 < nR) ? i2 : 0], j, gl, nxt);
+    }
+    // 2. this round
+    if (active) {
+      const uint32_t* hrec = hst + (buf * kDnRound + wave) * rec;
+      const float* hs = hrec_sums(hrec, a.Imax);
+      float acc = 0.f;
+      if (!cur.miss) {
+        if (gl < cur.Iinst / 64)
+          acc = down_group_regs<BITS>(cur.q[0], cur.q[1], cur.q[kNP > 2 ? 2 : 0], cur.q[kNP > 3 ? 3 : 0], cur.sb, gl,
+                                      hrec, a.Imax, hs);
+        if (cur.Iinst > 512) {                  // wider intermediates: further groups
+          const BlobLayout L = blob_layout(a.d, cur.Iinst, BITS);
+          for (int g = gl + 8; g < cur.Iinst / 64; g += 8)
+            acc += down_group<BITS>(cur.blob, L, a.d, j, g, hrec, a.Imax, hs);
+        }
+      }
+      acc = sum8_dpp(acc);
+      if (gl == 0) oi[i * 8 + r] = cur.from_buf ? cur.obuf : acc;
+    }
+    // 3. the next round's records into the other buffer (every wave is past
+    //    its reads of it: the barrier that ended the previous round)
+    if (nnr > 0) {
+      stage_h<64 * kDnWaves>(a.hq, a.hs8, a.Imax, nnr, RowsFrom{nb}, hst + (buf ^ 1) * kDnRound * rec, rec);
+      cur = nxt;
+    }
+    buf ^= 1;
+    __syncthreads();
+  }
+  if (a.phase == 1) {                           // streamed step: hand the outputs to phase 2
+    for (int q2 = tid; q2 < nI * 8; q2 += 64 * kDnWaves)
+      a.oi_buf[(size_t)(q2 / 8) * a.d + jb * 8 + (q2 % 8)] = oi[q2];
+    return;
+  }
+  if (tid < 8 * a.T) {
+    const int t = tid / 8, rr = tid % 8;
+    float y = 0.f;
+    for (int q2 = 0; q2 < a.k; ++q2) y += wk[t * a.k + q2] * oi[(t * a.k + q2) * 8 + rr];
+    y += wk[nR + t] * oi[(nR + t) * 8 + rr];
+    const size_t yi = (size_t)t * a.d + jb * 8 + rr;
+    a.y[yi] = y;
+    if (a.res_out) {                            // chain hand-over (all 8 lanes of a token active)
+      const uint32_t b = f32_to_bf16(__uint_as_float((uint32_t)a.res_in[yi] << 16) + y);
+      a.res_out[yi] = (uint16_t)b;
+      const float rv = __uint_as_float(b << 16);
+      const float p = sum8_dpp(__fmul_rn(rv, rv));
       if (rr == 0) a.ssp_out[(size_t)t * (a.d / 8) + jb] = p;
     }
   }
@@ -1338,6 +1501,7 @@ struct GemvFns {
          : (void*)gate_up_batched_kernel<16, BITS>;
   }
   static void* down_decode() { return (void*)down_decode_kernel<BITS>; }
+  static void* down_decode_pipe() { return (void*)down_decode_pipe_kernel<BITS>; }
   static void* down_batched() { return (void*)down_batched_kernel<BITS>; }
 };
 
@@ -1345,12 +1509,13 @@ struct GemvSet {
   void* (*gate_up)(int, int, bool);
   void* (*gate_up_batched)(int);
   void* (*down_decode)();
+  void* (*down_decode_pipe)();
   void* (*down_batched)();
 };
 template <int BITS>
 GemvSet gemv_set() {
   return {GemvFns<BITS>::gate_up, GemvFns<BITS>::gate_up_batched, GemvFns<BITS>::down_decode,
-          GemvFns<BITS>::down_batched};
+          GemvFns<BITS>::down_decode_pipe, GemvFns<BITS>::down_batched};
 }
 
 }  // namespace
@@ -1469,8 +1634,13 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
+    // more than one round of instances: the pipelined kernel, when a round's
+    // records take one staging pass and both buffers fit the LDS
+    const size_t plds = (size_t)(((nI * 9 + f.T * f.k + 3) & ~3) + 2 * kDnRound * hrec_words(Imax)) * 4;
+    const bool pipe = nI > kDnRound && plds <= 160 * 1024;
     if (f.phase == 2 && f.down_wait) MOE_HIP(hipStreamWaitEvent(s, f.down_wait, 0));
-    MOE_HIP(hipLaunchKernel(kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves), dargs, dlds, s));
+    MOE_HIP(hipLaunchKernel(pipe ? kf.down_decode_pipe() : kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves),
+                            dargs, pipe ? plds : dlds, s));
     return MOE_OK;
   }
   // batched: bucketed instances of up to kTC tokens
