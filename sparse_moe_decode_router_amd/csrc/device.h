@@ -88,4 +88,17 @@ __device__ __forceinline__ float sq_tree8(const float* v) {
   return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return
+// zeros (no fault).  LDS DMA (buffer_load ... lds) takes its LDS address
+// block-uniform and opaque to the compiler's alias tracking.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ lds_void* lds_opaque(const void* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_void*)p;
+  return (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(a);
+}
+
 }  // namespace moe

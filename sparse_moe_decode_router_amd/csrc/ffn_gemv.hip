@@ -852,11 +852,16 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
 }
 
 // Decode down for more than one round of instances: the same arithmetic,
-// with the next round's codes in flight while the current round computes
-// (every selection slot is staged in LDS at the start, so they wait for no
-// slot), and the next round's h records staged after the compute into the
-// second of two LDS buffers (held in registers across the compute they
-// would not fit).
+// with the next round's inputs in flight while the current round computes.
+// Every selection slot is staged in LDS at the start (so no round's code
+// loads wait for a slot); the next round's codes go to registers and its h
+// records to the second of two LDS buffers by LDS DMA (no registers).  The
+// record there: the hi pairs, then the lo pairs, as groups of 32 words whose
+// 16-byte pieces are XOR-swizzled by the group (piece m of group g at word
+// 32 g + 4 (m ^ (g & 7)): the reads of one piece by 8 group lanes hit 8
+// different bank quads), then the per-8 sums.
+__host__ __device__ inline int hrec_sw_words(int Imax) { return (Imax / 64) * 64 + Imax / 8; }
+
 template <int BITS>
 struct DnInst {                                 // a wave's instance in one round
   uint4 q[BITS / 2];
@@ -896,6 +901,72 @@ __device__ __forceinline__ void dn_inst_load(const DownArgs& a, int i, bool acti
   }
 }
 
+// Record of h row hr into LDS at rec (swizzled layout) by one wave's DMAs.
+__device__ __forceinline__ void h_record_dma(rsrc_t rq, rsrc_t rs, int hr, int Imax, uint32_t* rec, int lane) {
+  const int npc = Imax / 8;                     // 16-byte pieces per part
+#pragma unroll
+  for (int part = 0; part < 2; ++part)
+    for (int p0 = 0; p0 < npc; p0 += 64) {
+      const int L = p0 + lane;
+      if (L < npc) {
+        const int g = L >> 3, m = (L & 7) ^ (g & 7);
+        const uint32_t src = ((uint32_t)hr * Imax + part * (Imax / 2) + 32 * g + 4 * m) * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, lds_opaque(rec + part * (Imax / 64) * 32 + 4 * p0), 16, src, 0,
+                                                 0, 0);
+      }
+    }
+  for (int p0 = 0; p0 < Imax / 8; p0 += 64) {   // the sums, a word per lane
+    const int L = p0 + lane;
+    if (L < Imax / 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_opaque(rec + 2 * (Imax / 64) * 32 + p0), 4,
+                                               ((uint32_t)hr * (Imax / 8) + L) * 4, 0, 0, 0);
+  }
+}
+
+// down_group_regs on the swizzled record.
+template <int BITS>
+__device__ __forceinline__ float down_group_sw(uint4 q0, uint4 q1, uint4 q2, uint4 q3, uint32_t sb, int g,
+                                               const uint32_t* hrec, int Imax) {
+  const float s = f16_to_f32(sb);
+  const float b = f16_to_f32(sb >> 16);
+  const uint32_t qw[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                           q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+  const uint32_t* gh = hrec + 32 * g;
+  const uint32_t* glo = hrec + (Imax / 64 + g) * 32;
+  const float* hs = reinterpret_cast<const float*>(hrec + 2 * (Imax / 64) * 32);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;      // four independent chains
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int pm = 4 * (m ^ (g & 7));
+    const uint4 vh = *reinterpret_cast<const uint4*>(gh + pm), vl = *reinterpret_cast<const uint4*>(glo + pm);
+    const uint32_t ph[4] = {vh.x, vh.y, vh.z, vh.w};
+    const uint32_t pl[4] = {vl.x, vl.y, vl.z, vl.w};
+#pragma unroll
+    for (int s2 = 0; s2 < BITS / 2; ++s2) {         // products u = 2 s2 and 2 s2 + 1
+      const uint32_t c0 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2)], 2 * s2);
+      const uint32_t c1 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2 + 1)], 2 * s2 + 1);
+      a0 = dot2_bf16(c0, ph[qx<BITS>(2 * s2)], a0);
+      a1 = dot2_bf16(c0, pl[qx<BITS>(2 * s2)], a1);
+      a2 = dot2_bf16(c1, ph[qx<BITS>(2 * s2 + 1)], a2);
+      a3 = dot2_bf16(c1, pl[qx<BITS>(2 * s2 + 1)], a3);
+    }
+  }
+  const float acc = (a0 + a2) + (a1 + a3);
+  float sh = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) sh += hs[8 * g + m];
+  return s * acc + (b - qoff<BITS>() * s) * sh;
+}
+
+// every DMA and load of this wave landed, then the block meets (no memory
+// access moves across)
+__device__ __forceinline__ void wait_all_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int BITS>
 __global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArgs a) {
   constexpr int kNP = BITS / 2;
@@ -905,15 +976,18 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArg
   const int jb = xcd_remap(blockIdx.x, gridDim.x);
   const int j = jb * 8 + r;
   const int nR = a.T * a.k, nI = nR + a.T;
-  const int rec = hrec_words(a.Imax);
+  const int rec = hrec_sw_words(a.Imax);
   float* oi = dyn;
   float* wk = dyn + nI * 8;
   int32_t* sl = reinterpret_cast<int32_t*>(wk + nI);
   uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 9 + nR + 3) & ~3));
+  const rsrc_t rq = make_rsrc(a.hq, (uint32_t)nI * a.Imax * 4);
+  const rsrc_t rs = make_rsrc(a.hs8, (uint32_t)nI * (a.Imax / 8) * 4);
   DnInst<BITS> cur;
   {
-    // round 0: its slot straight from memory; the combine weights and every
-    // routed slot (nR <= 2048: two per thread, clamped) go to LDS
+    // round 0: its slot straight from memory and its records by DMA; the
+    // combine weights and every routed slot (nR <= 2048: two per thread,
+    // clamped) go to LDS
     const bool active = wave < kDnRound && wave < nI;
     const int slot0 = a.sel_slot[(active && wave < nR) ? wave : 0];
     float wkv[2];
@@ -925,8 +999,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArg
       wkv[u] = *(qw < nR ? a.w + qw : a.sgate + (qw - nR));
       sv[u] = a.sel_slot[q < nR ? q : 0];
     }
+    if (active) h_record_dma(rq, rs, wave, a.Imax, hst + wave * rec, lane);
     dn_inst_load<BITS>(a, wave, active, slot0, j, gl, cur);
-    stage_h<64 * kDnWaves>(a.hq, a.hs8, a.Imax, min(kDnRound, nI), RowsFrom{0}, hst, rec);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = tid + 64 * kDnWaves * u;
@@ -934,46 +1008,46 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArg
       sl[q < nR ? q : 0] = sv[u];
     }
   }
-  __syncthreads();
+  wait_all_barrier();
   int buf = 0;
   for (int base = 0; base < nI; base += kDnRound) {
     const int nr = min(kDnRound, nI - base);
     const int i = base + wave;
     const bool active = wave < nr;
     const int nb = base + kDnRound, nnr = min(kDnRound, nI - nb);
-    // 1. the next round's codes, in flight during the compute
+    // 1. the next round's records (into the other buffer: every wave is past
+    //    its reads of it, the barrier that ended the previous round) and codes
     DnInst<BITS> nxt;
     if (nnr > 0) {
       const int i2 = nb + wave;
       const bool act2 = wave < nnr;
+      if (act2) h_record_dma(rq, rs, i2, a.Imax, hst + ((buf ^ 1) * kDnRound + wave) * rec, lane);
       dn_inst_load<BITS>(a, i2, act2, sl[(act2 && i2 < nR) ? i2 : 0], j, gl, nxt);
     }
     // 2. this round
     if (active) {
       const uint32_t* hrec = hst + (buf * kDnRound + wave) * rec;
-      const float* hs = hrec_sums(hrec, a.Imax);
       float acc = 0.f;
       if (!cur.miss) {
         if (gl < cur.Iinst / 64)
-          acc = down_group_regs<BITS>(cur.q[0], cur.q[1], cur.q[kNP > 2 ? 2 : 0], cur.q[kNP > 3 ? 3 : 0], cur.sb, gl,
-                                      hrec, a.Imax, hs);
+          acc = down_group_sw<BITS>(cur.q[0], cur.q[1], cur.q[kNP > 2 ? 2 : 0], cur.q[kNP > 3 ? 3 : 0], cur.sb, gl,
+                                    hrec, a.Imax);
         if (cur.Iinst > 512) {                  // wider intermediates: further groups
           const BlobLayout L = blob_layout(a.d, cur.Iinst, BITS);
-          for (int g = gl + 8; g < cur.Iinst / 64; g += 8)
-            acc += down_group<BITS>(cur.blob, L, a.d, j, g, hrec, a.Imax, hs);
+          for (int g = gl + 8; g < cur.Iinst / 64; g += 8) {
+            uint4 q[kNP];
+            uint32_t sb;
+            down_load<BITS>(cur.blob, L, a.d, j, g, q, &sb);
+            acc += down_group_sw<BITS>(q[0], q[1], q[kNP > 2 ? 2 : 0], q[kNP > 3 ? 3 : 0], sb, g, hrec, a.Imax);
+          }
         }
       }
       acc = sum8_dpp(acc);
       if (gl == 0) oi[i * 8 + r] = cur.from_buf ? cur.obuf : acc;
     }
-    // 3. the next round's records into the other buffer (every wave is past
-    //    its reads of it: the barrier that ended the previous round)
-    if (nnr > 0) {
-      stage_h<64 * kDnWaves>(a.hq, a.hs8, a.Imax, nnr, RowsFrom{nb}, hst + (buf ^ 1) * kDnRound * rec, rec);
-      cur = nxt;
-    }
+    if (nnr > 0) cur = nxt;
     buf ^= 1;
-    __syncthreads();
+    wait_all_barrier();
   }
   if (a.phase == 1) {                           // streamed step: hand the outputs to phase 2
     for (int q2 = tid; q2 < nI * 8; q2 += 64 * kDnWaves)
@@ -1634,10 +1708,11 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
-    // more than one round of instances: the pipelined kernel, when a round's
-    // records take one staging pass and both buffers fit the LDS
-    const size_t plds = (size_t)(((nI * 9 + f.T * f.k + 3) & ~3) + 2 * kDnRound * hrec_words(Imax)) * 4;
-    const bool pipe = nI > kDnRound && plds <= 160 * 1024;
+    // several rounds of instances: the pipelined kernel when both record
+    // buffers fit the LDS (8-bit codes from three rounds: its registers
+    // spill, which measured slower than the plain kernel at two)
+    const size_t plds = (size_t)(((nI * 9 + f.T * f.k + 3) & ~3) + 2 * kDnRound * hrec_sw_words(Imax)) * 4;
+    const bool pipe = nI > (f.bits == 8 ? 2 : 1) * kDnRound && plds <= 160 * 1024;
     if (f.phase == 2 && f.down_wait) MOE_HIP(hipStreamWaitEvent(s, f.down_wait, 0));
     MOE_HIP(hipLaunchKernel(pipe ? kf.down_decode_pipe() : kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves),
                             dargs, pipe ? plds : dlds, s));

@@ -130,19 +130,6 @@ template <int BITS> constexpr int kStB = 4 * 1024 * kCodeDma<BITS>;
 template <int BITS> constexpr int kStage = kStA + kStB<BITS> + kStS;
 template <int BITS> constexpr int kDmaPerStage = 5 + kCodeDma<BITS>;
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Block-uniform LDS address of p, opaque to the compiler's alias tracking.
-__device__ __forceinline__ lds_void* lds_opaque(const uint8_t* p) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const lds_void*)p;
-  return (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(a);
-}
-
 // s_waitcnt vmcnt <= N, lgkmcnt == 0, then s_barrier; no code motion of
 // memory accesses across it.
 template <int N>
