@@ -17,15 +17,19 @@ constexpr int kRouterThreads = 256;
 
 // ---------------------------------------------------------------- x prep
 // One (token, group of 64 columns): the bf16 pairs (x[8m+i], x[8m+i+4]) the
-// int4 GEMVs consume, and the fp32 sum of the group (column order).
+// int4 GEMVs consume, and the fp32 sum of the group (column order).  The
+// group's eight loads are all issued before the first store.
 __device__ void xprep_group(const uint16_t* __restrict__ x, int d, int t, int g,
                             uint32_t* __restrict__ xq, float* __restrict__ xs) {
   const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d + 64 * g);
   uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)t * (d / 2) + 32 * g);
   float s = 0.0f;
+  uint4 vv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) vv[q] = src[q];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    uint4 v = src[q];
+    const uint4 v = vv[q];
     uint4 p;
     p.x = (v.x & 0xFFFFu) | (v.z << 16);
     p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
@@ -49,9 +53,12 @@ __device__ void xprep_group_scaled(const uint16_t* __restrict__ x, float scale, 
   const uint16_t* src = x + (size_t)t * d + 64 * g;
   uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)t * (d / 2) + 32 * g);
   float s = 0.0f;
+  uint4 vv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) vv[q] = reinterpret_cast<const uint4*>(src)[q];   // all loads first
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+    const uint4 v = vv[q];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t e[8];
 #pragma unroll
@@ -87,7 +94,8 @@ namespace {
 // shared gate) with 256 threads, each summing d/256 products in column
 // order, then a 64-lane butterfly and a two-level tree over the 4 waves:
 // depth d/256 + 8, plus one for the bias (added by the top-k).  Blocks also
-// prepare xq/xs.  No block waits for another.
+// prepare xq/xs, group q by thread q / gridDim of block q % gridDim (one
+// group per block while T d / 64 <= E + 1).  No block waits for another.
 struct DecodeArgs {
   const uint16_t* x; int T, d;
   const float* W; int E;
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   }
   {
     const int G = d / 64;
-    const int id = blockIdx.x * kRouterThreads + tid;
+    const int id = tid * gridDim.x + blockIdx.x;
     if (id < T * G) {
       const int t = id / G;
       if (chain) {
