@@ -31,7 +31,7 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_rounds_match_single_token_calls(name):
+def test_tokens_match_single_token_calls(name):
     cfg, Ts = CASES[name]
     L = DeviceLayer(cfg)
     for T in Ts:
