@@ -153,6 +153,62 @@ __global__ __launch_bounds__(kB) void bucket_scan_kernel(int32_t* __restrict__ b
   if (tid == 0) offsets[E] = part[kB - 1];
 }
 
+// The same scan with bc staged in LDS (when E nb entries fit): the loads
+// and the write-back are coalesced (kU loads per thread in flight), the
+// per-thread runs are scanned in LDS.  Same integers as bucket_scan_kernel.
+constexpr int kScanLdsMax = 24576;              // entries (96 KB)
+__global__ __launch_bounds__(kB) void bucket_scan_lds_kernel(int32_t* __restrict__ bc, int E, int nb,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             uint32_t* __restrict__ usage) {
+  extern __shared__ int sbc[];                  // [E nb]
+  __shared__ int part[kB];
+  const int tid = threadIdx.x;
+  const int N = E * nb;
+  for (int q0 = 0; q0 < N; q0 += kU * kB) {
+    int v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int q = q0 + u * kB + tid;
+      v[u] = bc[q < N ? q : 0];                 // clamped: loads stay unconditional
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int q = q0 + u * kB + tid;
+      if (q < N) sbc[q] = v[u];
+    }
+  }
+  __syncthreads();
+  const int per = (N + kB - 1) / kB;
+  const int lo = tid * per < N ? tid * per : N, hi = lo + per < N ? lo + per : N;
+  int s = 0;
+  for (int q = lo; q < hi; ++q) s += sbc[q];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < kB; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int q = lo; q < hi; ++q) {
+    const int v = sbc[q];
+    sbc[q] = run;
+    run += v;
+  }
+  __syncthreads();
+  for (int q = tid; q < N; q += kB) bc[q] = sbc[q];
+  for (int e = tid; e < E; e += kB) {
+    const int first = sbc[e * nb];
+    const int next = (e + 1 < E) ? sbc[(e + 1) * nb] : part[kB - 1];
+    offsets[e] = first;
+    counts[e] = next - first;
+    if (usage && next > first) atomicAdd(&usage[e], (uint32_t)(next - first));
+  }
+  if (tid == 0) offsets[E] = part[kB - 1];
+}
+
 __global__ __launch_bounds__(kB) void bucket_scatter_kernel(const int32_t* __restrict__ idx, int n, int E,
                                                             int nb, const int32_t* __restrict__ base,
                                                             int32_t* __restrict__ pair_ids) {
@@ -186,7 +242,10 @@ int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts, int3
   int32_t* bc = (int32_t*)ws;
   bucket_hist_kernel<<<nb, kB, (size_t)E * 4, s>>>(idx, (int)n, E, nb, bc);
   MOE_HIP(hipGetLastError());
-  bucket_scan_kernel<<<1, kB, 0, s>>>(bc, E, nb, counts, offsets, usage);
+  if ((long)E * nb <= kScanLdsMax)
+    bucket_scan_lds_kernel<<<1, kB, (size_t)E * nb * 4, s>>>(bc, E, nb, counts, offsets, usage);
+  else
+    bucket_scan_kernel<<<1, kB, 0, s>>>(bc, E, nb, counts, offsets, usage);
   MOE_HIP(hipGetLastError());
   bucket_scatter_kernel<<<nb, kB, (size_t)kW * E, s>>>(idx, (int)n, E, nb, bc, pair_ids);
   MOE_HIP(hipGetLastError());

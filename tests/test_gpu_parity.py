@@ -124,8 +124,10 @@ def test_router_k_extremes(k):
 
 
 # ---------------------------------------------------------------- bucketing
+# (the multi-block scan runs in LDS up to 24576 histogram entries: 4096 x 10
+# of 512 is 20480; 2048 x 16 of 1024 is 32768, the scan from global memory)
 @pytest.mark.parametrize("T,k,E", [(1, 10, 512), (4, 2, 16), (64, 10, 512), (100, 10, 512),
-                                   (700, 3, 1024), (4096, 10, 512), (5, 7, 7)])
+                                   (700, 3, 1024), (4096, 10, 512), (2048, 16, 1024), (5, 7, 7)])
 def test_bucket_bit_exact(T, k, E):
     g = np.random.default_rng(T * 1000 + k)
     idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
