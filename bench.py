@@ -508,7 +508,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--replicas", type=int, default=32)
-    ap.add_argument("--cpu-steps", type=int, default=40)
+    ap.add_argument("--cpu-steps", type=int, default=120)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="enqueue decode steps one by one (no HIP graph)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
