@@ -935,7 +935,7 @@ __device__ __forceinline__ float down_group_sw(uint4 q0, uint4 q1, uint4 q2, uin
   const uint32_t* glo = hrec + (Imax / 64 + g) * 32;
   const float* hs = reinterpret_cast<const float*>(hrec + 2 * (Imax / 64) * 32);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;      // four independent chains
-#pragma unroll
+#pragma unroll 2
   for (int m = 0; m < 8; ++m) {
     const int pm = 4 * (m ^ (g & 7));
     const uint4 vh = *reinterpret_cast<const uint4*>(gh + pm), vl = *reinterpret_cast<const uint4*>(glo + pm);
@@ -1709,10 +1709,9 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
     // several rounds of instances: the pipelined kernel when both record
-    // buffers fit the LDS (8-bit codes from three rounds: its registers
-    // spill, which measured slower than the plain kernel at two)
+    // buffers fit the LDS
     const size_t plds = (size_t)(((nI * 9 + f.T * f.k + 3) & ~3) + 2 * kDnRound * hrec_sw_words(Imax)) * 4;
-    const bool pipe = nI > (f.bits == 8 ? 2 : 1) * kDnRound && plds <= 160 * 1024;
+    const bool pipe = nI > kDnRound && plds <= 160 * 1024;
     if (f.phase == 2 && f.down_wait) MOE_HIP(hipStreamWaitEvent(s, f.down_wait, 0));
     MOE_HIP(hipLaunchKernel(pipe ? kf.down_decode_pipe() : kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves),
                             dargs, pipe ? plds : dlds, s));

@@ -3,9 +3,9 @@ the pipelined kernel (selection slots staged in LDS, the next round's codes
 and h records in flight during the compute, h records in a swizzled LDS
 layout) does the single-round kernel's arithmetic, so with the routing
 given a call on T tokens reproduces each token's own T = 1 call bit for
-bit.  4-bit experts take the pipelined kernel from two rounds (T = 2 at
-k = 10), 8-bit from three (T = 4); the 80B expert shape (64 experts, all
-resident), and a wide intermediate (groups past the eighth) on a small one."""
+bit.  The pipelined kernel runs from two rounds (T = 2 at k = 10); the 80B
+expert shape (64 experts, all resident) with 4- and 8-bit codes, and a
+wide intermediate (groups past the eighth) on a small one."""
 import numpy as np
 import pytest
 
@@ -24,7 +24,7 @@ def _np(t):
 
 CASES = {
     "80b_int4": (ms.scaled(ms.CONFIGS["decode80b"], E=64, n_slots=64), (2, 4, 8)),
-    "80b_int8": (ms.scaled(ms.CONFIGS["decode80b_int8"], E=64, n_slots=64), (4, 8)),
+    "80b_int8": (ms.scaled(ms.CONFIGS["decode80b_int8"], E=64, n_slots=64), (2, 4, 8)),
     "wide_I_int4": (ms.scaled(ms.CONFIGS["decode80b"], alpha=0.0, d=512, E=32, k=4, I=1024, I_shared=1024,
                               n_slots=32), (4, 8)),
 }
