@@ -262,7 +262,7 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
         "layer_expert_GBps": round(layer_gbs, 1),
         "layer_expert_frac_of_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": ("expert FFN: gate_up_kernel + down_decode_kernel" if cfg.bits != 32
+                     "kernel": ("expert FFN: gate_up_kernel + down_decode_pipe_kernel" if cfg.bits != 32
                                 else "expert FFN: gate_up_f32_kernel + down_decode_f32_kernel"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": ffn_traffic(name),

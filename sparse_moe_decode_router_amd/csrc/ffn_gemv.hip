@@ -737,7 +737,8 @@ struct DownArgs {
 // Decode: block = 8 output rows, all T*(k+1) instances, fused rank-order
 // combine.  16 waves; instances are taken in rounds of 16 (one per wave):
 // the round's code loads are issued first, its h records are staged in LDS
-// meanwhile.
+// meanwhile.  (down_decode_pipe_kernel below is used whenever its two
+// record buffers fit the LDS; this one otherwise.)
 constexpr int kDnWaves = 16;
 constexpr int kDnRound = kDnWaves;
 template <int BITS>
@@ -851,8 +852,10 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   }
 }
 
-// Decode down for more than one round of instances: the same arithmetic,
-// with the next round's inputs in flight while the current round computes.
+// Decode down (the kernel used whenever its two record buffers fit the
+// LDS): down_decode_kernel's arithmetic, with the h records fetched by LDS
+// DMA and, over several rounds of instances, the next round's inputs in
+// flight while the current round computes.
 // Every selection slot is staged in LDS at the start (so no round's code
 // loads wait for a slot); the next round's codes go to registers and its h
 // records to the second of two LDS buffers by LDS DMA (no registers).  The
@@ -1708,10 +1711,10 @@ int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_
     const int nI = f.T * (f.k + 1);
     void* dargs[] = {&dn};
     const size_t dlds = (size_t)(((nI * 9 + 3) & ~3) + kDnRound * hrec_words(Imax)) * 4;
-    // several rounds of instances: the pipelined kernel when both record
-    // buffers fit the LDS
+    // the pipelined kernel when both record buffers fit the LDS (also for
+    // one round: its DMA'd records measured faster than register staging)
     const size_t plds = (size_t)(((nI * 9 + f.T * f.k + 3) & ~3) + 2 * kDnRound * hrec_sw_words(Imax)) * 4;
-    const bool pipe = nI > kDnRound && plds <= 160 * 1024;
+    const bool pipe = plds <= 160 * 1024;
     if (f.phase == 2 && f.down_wait) MOE_HIP(hipStreamWaitEvent(s, f.down_wait, 0));
     MOE_HIP(hipLaunchKernel(pipe ? kf.down_decode_pipe() : kf.down_decode(), dim3(f.d / 8), dim3(64 * kDnWaves),
                             dargs, pipe ? plds : dlds, s));
