@@ -45,3 +45,28 @@ def test_tokens_match_single_token_calls(name):
             torch.cuda.synchronize()
             assert np.array_equal(_np(y1)[0], _np(y)[t]), (name, T, t)
         assert L.pool.check_error() == moe.MOE_OK
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wide_intermediate_fallback_kernel(bits):
+    """Intermediate 1536: the pipelined kernel's two record buffers exceed
+    the LDS, so the decode down pass takes down_decode_kernel (staged
+    records, one buffer).  Routing given from the router; outputs against
+    the fp64 oracle on that routing, and a T = 4 call against each token's
+    own call bit for bit."""
+    from gpu_support import assert_close_y
+    cfg = ms.scaled(ms.CONFIGS["tiny_int8" if bits == 8 else "tiny"], d=256, E=16, k=2, I=1536, I_shared=1536,
+                    n_slots=16)
+    L = DeviceLayer(cfg)
+    xb, x = L.x(7, 4)
+    idx, w, s = moe.moe_router_topk(x, L.Wr, L.bias, cfg.k)
+    y = moe.moe_expert_ffn(L.pool, L.shared_blob, cfg.I_shared, x, idx, w, s)
+    torch.cuda.synchronize()
+    ref = L.oracle(xb, idx=_np(idx))
+    for t in range(4):
+        assert_close_y(_np(y)[t:t + 1], ref["y"][t:t + 1])
+        y1 = moe.moe_expert_ffn(L.pool, L.shared_blob, cfg.I_shared, x[t:t + 1].contiguous(),
+                                idx[t:t + 1].contiguous(), w[t:t + 1].contiguous(), s[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(y1)[0], _np(y)[t])
+    assert L.pool.check_error() == moe.MOE_OK
