@@ -338,6 +338,8 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
                               out=(yt[i], it[i], torch.empty_like(w[i]), torch.empty_like(s[i])))
     torch.cuda.synchronize()
     identical = bool(torch.equal(yt, y) and torch.equal(it, idx))
+    # the workload's contract: every step bit-identical to the all-resident layer
+    assert identical, "refilled pool differs from the all-resident layer"
     hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
     ms_step = dt * 1e3 / K
     return {"metric": METRIC, "value": round(K / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,

@@ -57,7 +57,8 @@ enum {
   MOE_ERR_UNSUPPORTED = -2,    /* shape outside the kernels' envelope         */
   MOE_ERR_NOT_RESIDENT = -3,   /* a selected expert had no slot               */
   MOE_ERR_POOL_TOO_SMALL = -4, /* one step needs more distinct experts than slots */
-  MOE_ERR_HIP = -5             /* HIP runtime error; see moe_last_hip_error   */
+  MOE_ERR_HIP = -5,            /* HIP runtime error; see moe_last_hip_error   */
+  MOE_ERR_OUT_OF_MEMORY = -6   /* a host allocation of the library failed     */
 };
 
 /* Flags for moe_expert_ffn / moe_layer_forward. */
@@ -234,6 +235,19 @@ int moe_router_topk(const uint16_t* x_dev, int32_t T, int32_t d,
                     float* topk_w_dev, float* shared_gate_dev,
                     uint32_t* usage_dev, void* workspace_dev,
                     size_t workspace_bytes, hipStream_t stream);
+/* moe_router_topk that also copies out the logits its selection reads:
+ * logits_dev [T][E+1] fp32 (device; NULL = not wanted), row E the shared-gate
+ * logit, before the bias (the selection compares fp32(logit + bias)).  Same
+ * kernels, same bits; the export is one extra store per logit.  Lets a
+ * caller check each logit against the rounding bound of
+ * moe_router_sum_depth and the selection against its own logits. */
+int moe_router_topk_logits(const uint16_t* x_dev, int32_t T, int32_t d,
+                           const float* w_router_dev,
+                           const float* logit_bias_dev, int32_t E, int32_t k,
+                           int32_t* topk_idx_dev, float* topk_w_dev,
+                           float* shared_gate_dev, uint32_t* usage_dev,
+                           float* logits_dev, void* workspace_dev,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ bucketing
  * Stable counting sort of the T*k (token, rank) pairs by expert:

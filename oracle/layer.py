@@ -141,6 +141,21 @@ def logit_error_bound(x_bits: np.ndarray, w_router, bias, depth: int) -> np.ndar
     return r
 
 
+def logit_error_bounds(x_bits: np.ndarray, w_router, depth: int) -> np.ndarray:
+    """Elementwise bound on |fp32 logit - exact logit| for every router row
+    (the E routed rows and the shared-gate row E), before any bias, for a
+    device that forms each logit as an fp32 sum of the d products with at most
+    ``depth`` additions on any path: gamma_n * sum_j |x_j W_ej|, n = depth + 2
+    (the additions, the product's rounding and one spare), gamma_n =
+    n u / (1 - n u), u = 2^-24 (standard floating-point summation bound).
+    Returns [T, E+1]."""
+    x = np.abs(bf16_to_f64(x_bits))
+    W = np.abs(np.asarray(w_router, dtype=np.float64))
+    u = 2.0 ** -24
+    n = depth + 2
+    return (n * u / (1 - n * u)) * (x @ W.T)
+
+
 # ----------------------------------------------------------------- chains
 def bf16_round(v) -> np.ndarray:
     """bf16 bits of fp32 values, round to nearest, ties to even (written out

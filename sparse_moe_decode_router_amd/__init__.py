@@ -27,6 +27,7 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_NOT_RESIDENT = -3
 MOE_ERR_POOL_TOO_SMALL = -4
 MOE_ERR_HIP = -5
+MOE_ERR_OUT_OF_MEMORY = -6
 
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
@@ -97,6 +98,7 @@ _SIGS = {
     "moe_router_sum_depth": (_I, [_I, _I, _I]),
     "moe_router_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_router_topk": (C.c_int, [_P, _I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_router_topk_logits": (C.c_int, [_P, _I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_bucket_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_bucket_tokens": (C.c_int, [_P, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
     "moe_ffn_workspace_bytes": (_S, [_P, _P, _I, _I, _I, _I]),
@@ -378,6 +380,26 @@ def moe_router_topk(x, w_router, logit_bias, k: int, usage_ptr: Optional[int] = 
                               _ptr(s), usage_ptr, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "moe_router_topk")
     return idx, w, s
+
+
+def moe_router_topk_logits(x, w_router, logit_bias, k: int, usage_ptr: Optional[int] = None,
+                           workspace=None, stream=None):
+    """moe_router_topk plus the fp32 logits the selection read (before the
+    bias).  Returns (topk_idx [T,k], topk_w [T,k], shared_gate [T], logits [T,E+1])."""
+    import torch
+    T, d = x.shape
+    E = w_router.shape[0] - 1
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    s = torch.empty((T,), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E + 1), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _ws(moe_router_workspace_bytes(T, d, E))
+    st = _lib.moe_router_topk_logits(_ptr(x), T, d, _ptr(w_router), _ptr(logit_bias), E, k, _ptr(idx),
+                                     _ptr(w), _ptr(s), usage_ptr, _ptr(logits), _ptr(workspace),
+                                     workspace.numel(), _stream(stream))
+    _check(st, "moe_router_topk_logits")
+    return idx, w, s, logits
 
 
 # ---------------------------------------------------------------- bucketing

@@ -182,7 +182,8 @@ extern "C" int moe_chain_forward(const moe_layer_desc* layers, int32_t L, float 
   for (int l = 0; l < L && handover; ++l) {
     const moe_layer_desc* D = &layers[l];
     handover = shape_bits(&D->sh) != 32 && shape_bits(&D->shared_sh) != 32 &&
-               resolve_path(path, T, d, D->k, D->E, shape_bits(&D->sh)) == MOE_PATH_DECODE;
+               resolve_path(path, T, d, D->k, D->E, shape_bits(&D->sh),
+                            D->sh.I > D->shared_sh.I ? D->sh.I : D->shared_sh.I) == MOE_PATH_DECODE;
   }
   if (handover) {
     MOE_TRY(glue_launch(x, nullptr, T, d, eps, resid(0), w.u, s));        // x_0 and u_0

@@ -1602,14 +1602,20 @@ GemvSet gemv_set() {
 // from 2 tokens up (80B shape, 4- and 8-bit experts) even with a handful of
 // tokens per bucket; the bucketed GEMVs where the GEMM tiles do not fit
 // (d not a multiple of 128) and for unquantised f32 experts.
-int resolve_path(int path, int T, int d, int k, int E, int bits) {
+int resolve_path(int path, int T, int d, int k, int E, int bits, int Imax) {
   if (path != MOE_PATH_AUTO) return path;
   if (T <= 8 && (long)T * (k + 1) <= 2048) return MOE_PATH_DECODE;
-  return (d % 128 == 0 && bits != 32) ? MOE_PATH_PREFILL : MOE_PATH_BATCHED;
+  return (d % 128 == 0 && bits != 32 && prefill_fits(T, d, k, Imax)) ? MOE_PATH_PREFILL : MOE_PATH_BATCHED;
+}
+
+bool prefill_fits(int T, int d, int k, int Imax) {
+  const uint64_t lim = (uint64_t)1 << 32;
+  return (uint64_t)T * (uint64_t)d * 2 < lim && ((uint64_t)T * (uint64_t)k + (uint64_t)T) * (uint64_t)Imax * 2 < lim;
 }
 
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
-  if (path == MOE_PATH_PREFILL) return prefill_ws_bytes(d, I, Ish, T, k, E);
+  if (path == MOE_PATH_PREFILL)
+    return prefill_fits(T, d, k, I > Ish ? I : Ish) ? prefill_ws_bytes(d, I, Ish, T, k, E) : 0;
   Carver c(nullptr, (size_t)-1);
   FfnWs w;
   carve_ffn(c, d, I > Ish ? I : Ish, T, k, path, &w);

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nch = nR + a.n_shared_inst;
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
   const int C = a.d / kKS;
-  const rsrc_t rX = make_rsrc(a.xh, (uint32_t)a.T * a.d * 2);
+  const rsrc_t rX = make_rsrc(a.xh, (uint32_t)((uint64_t)a.T * a.d * 2));   // < 4 GiB: prefill_fits
   const int mat = wave >> 1;                    // waves 0,1: gate rows; 2,3: up rows
   const int colb = 32 * (wave & 1);
 
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nt = a.d / 128;
   const int nch = nR + a.n_shared_inst;
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
-  const rsrc_t rH = make_rsrc(a.hh, (uint32_t)(a.T * a.k + a.T) * a.Imax * 2);
+  const rsrc_t rH = make_rsrc(a.hh, (uint32_t)(((uint64_t)a.T * a.k + a.T) * a.Imax * 2));   // < 4 GiB: prefill_fits
 
   for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
     int ii, tile;
@@ -643,6 +643,7 @@ size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E) {
 
 int prefill_launch(const FfnArgs& f, void* ws, size_t ws_bytes, hipStream_t s) {
   const int Imax = f.I > f.Ish ? f.I : f.Ish;
+  if (!prefill_fits(f.T, f.d, f.k, Imax)) return MOE_ERR_UNSUPPORTED;
   Carver c(ws, ws_bytes);
   PrefillWs w;
   if (!carve_prefill(c, f.d, Imax, f.T, f.k, f.pool.E, &w)) return MOE_ERR_INVALID_ARG;

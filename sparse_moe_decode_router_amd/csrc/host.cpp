@@ -7,7 +7,9 @@
 // expert and a freshly loaded one give the same answer (correctness section).
 #include <algorithm>
 #include <cstring>
+#include <memory>
 #include <new>
+#include <stdexcept>
 #include <string>
 #include <vector>
 
@@ -20,6 +22,19 @@ static thread_local std::string g_last_hip;
 int hip_fail(hipError_t e) {
   g_last_hip = std::string(hipGetErrorName(e)) + ": " + hipGetErrorString(e);
   return MOE_ERR_HIP;
+}
+
+// Host entry points that grow std::vectors: an allocation failure comes back
+// as MOE_ERR_OUT_OF_MEMORY instead of an exception crossing the C ABI.
+template <class F>
+static int no_throw(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return MOE_ERR_OUT_OF_MEMORY;
+  } catch (...) {
+    return MOE_ERR_INVALID_ARG;
+  }
 }
 
 bool shape_ok(const moe_ffn_shape* sh) {
@@ -46,6 +61,7 @@ extern "C" const char* moe_status_string(int st) {
     case MOE_ERR_NOT_RESIDENT: return "selected expert not resident";
     case MOE_ERR_POOL_TOO_SMALL: return "pool too small for one step's experts";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_OUT_OF_MEMORY: return "host allocation failed";
     default: return "unknown status";
   }
 }
@@ -203,17 +219,19 @@ struct moe_lfu {
 };
 
 extern "C" int moe_lfu_create(int32_t E, int32_t n_slots, moe_lfu** out) {
-  if (!out || E < 1 || E > 1024 || n_slots < 1) return MOE_ERR_INVALID_ARG;
-  moe_lfu* l = new (std::nothrow) moe_lfu();
-  if (!l) return MOE_ERR_INVALID_ARG;
-  l->E = E;
-  l->n_slots = n_slots;
-  l->count.assign(E, 0);
-  l->last.assign(E, -1);
-  l->slot_of.assign(E, -1);
-  l->holder.assign(n_slots, -1);
-  *out = l;
-  return MOE_OK;
+  return no_throw([&]() -> int {
+    if (!out || E < 1 || E > 1024 || n_slots < 1) return MOE_ERR_INVALID_ARG;
+    std::unique_ptr<moe_lfu> l(new (std::nothrow) moe_lfu());
+    if (!l) return MOE_ERR_OUT_OF_MEMORY;
+    l->E = E;
+    l->n_slots = n_slots;
+    l->count.assign(E, 0);
+    l->last.assign(E, -1);
+    l->slot_of.assign(E, -1);
+    l->holder.assign(n_slots, -1);
+    *out = l.release();
+    return MOE_OK;
+  });
 }
 
 extern "C" int moe_lfu_destroy(moe_lfu* l) {
@@ -230,58 +248,60 @@ extern "C" int moe_lfu_get_stats(const moe_lfu* l, moe_pool_stats* st) {
 
 extern "C" int moe_lfu_plan(moe_lfu* p, const int32_t* sel, int32_t n, int32_t* le, int32_t* ls,
                             int32_t* lv, int32_t* n_loads) {
-  if (!p || n < 0 || (n > 0 && !sel) || !n_loads) return MOE_ERR_INVALID_ARG;
-  if (n > 0 && (!le || !ls || !lv)) return MOE_ERR_INVALID_ARG;
-  // distinct needed experts in first-appearance order
-  std::vector<int32_t> need;
-  std::vector<char> is_need(p->E, 0);
-  for (int q = 0; q < n; ++q) {
-    const int32_t e = sel[q];
-    if (e < 0 || e >= p->E) return MOE_ERR_INVALID_ARG;
-    if (!is_need[e]) {
-      is_need[e] = 1;
-      need.push_back(e);
-    }
-  }
-  if ((int)need.size() > p->n_slots) return MOE_ERR_POOL_TOO_SMALL;
-  for (int q = 0; q < n; ++q) {
-    p->count[sel[q]] += 1;
-    p->last[sel[q]] = p->step;
-  }
-  int nl = 0;
-  for (int32_t e : need) {
-    if (p->slot_of[e] >= 0) {
-      p->st.hits += 1;
-      continue;
-    }
-    p->st.misses += 1;
-    int32_t slot = -1, victim = -1;
-    for (int s = 0; s < p->n_slots; ++s)
-      if (p->holder[s] < 0) { slot = s; break; }
-    if (slot < 0) {
-      // least frequent, then least recent, then lowest id, among resident
-      // experts this step does not need
-      for (int32_t v = 0; v < p->E; ++v) {
-        if (p->slot_of[v] < 0 || is_need[v]) continue;
-        if (victim < 0 || p->count[v] < p->count[victim] ||
-            (p->count[v] == p->count[victim] && p->last[v] < p->last[victim]))
-          victim = v;
+  return no_throw([&]() -> int {
+    if (!p || n < 0 || (n > 0 && !sel) || !n_loads) return MOE_ERR_INVALID_ARG;
+    if (n > 0 && (!le || !ls || !lv)) return MOE_ERR_INVALID_ARG;
+    // distinct needed experts in first-appearance order
+    std::vector<int32_t> need;
+    std::vector<char> is_need(p->E, 0);
+    for (int q = 0; q < n; ++q) {
+      const int32_t e = sel[q];
+      if (e < 0 || e >= p->E) return MOE_ERR_INVALID_ARG;
+      if (!is_need[e]) {
+        is_need[e] = 1;
+        need.push_back(e);
       }
-      slot = p->slot_of[victim];
-      p->slot_of[victim] = -1;
-      p->st.evictions += 1;
     }
-    p->holder[slot] = e;
-    p->slot_of[e] = slot;
-    le[nl] = e;
-    ls[nl] = slot;
-    lv[nl] = victim;
-    ++nl;
-  }
-  p->step += 1;
-  p->st.steps += 1;
-  *n_loads = nl;
-  return MOE_OK;
+    if ((int)need.size() > p->n_slots) return MOE_ERR_POOL_TOO_SMALL;
+    for (int q = 0; q < n; ++q) {
+      p->count[sel[q]] += 1;
+      p->last[sel[q]] = p->step;
+    }
+    int nl = 0;
+    for (int32_t e : need) {
+      if (p->slot_of[e] >= 0) {
+        p->st.hits += 1;
+        continue;
+      }
+      p->st.misses += 1;
+      int32_t slot = -1, victim = -1;
+      for (int s = 0; s < p->n_slots; ++s)
+        if (p->holder[s] < 0) { slot = s; break; }
+      if (slot < 0) {
+        // least frequent, then least recent, then lowest id, among resident
+        // experts this step does not need
+        for (int32_t v = 0; v < p->E; ++v) {
+          if (p->slot_of[v] < 0 || is_need[v]) continue;
+          if (victim < 0 || p->count[v] < p->count[victim] ||
+              (p->count[v] == p->count[victim] && p->last[v] < p->last[victim]))
+            victim = v;
+        }
+        slot = p->slot_of[victim];
+        p->slot_of[victim] = -1;
+        p->st.evictions += 1;
+      }
+      p->holder[slot] = e;
+      p->slot_of[e] = slot;
+      le[nl] = e;
+      ls[nl] = slot;
+      lv[nl] = victim;
+      ++nl;
+    }
+    p->step += 1;
+    p->st.steps += 1;
+    *n_loads = nl;
+    return MOE_OK;
+  });
 }
 
 // ------------------------------------------------------------------- pool
@@ -313,34 +333,37 @@ bool pool_view(const moe_pool* p, PoolView* v) {
 }  // namespace moe
 
 extern "C" int moe_pool_create(int32_t E, int32_t n_slots, const moe_ffn_shape* sh, moe_pool** out) {
-  if (!out || E < 1 || E > 1024 || n_slots < 1 || !shape_ok(sh)) return MOE_ERR_INVALID_ARG;
-  *out = nullptr;
-  moe_pool* p = new (std::nothrow) moe_pool();
-  if (!p) return MOE_ERR_INVALID_ARG;
-  p->E = E;
-  p->n_slots = n_slots;
-  p->sh = *sh;
-  p->stride = blob_layout(sh->d, sh->I, shape_bits(sh)).stride;
-  p->lfu.E = E;
-  p->lfu.n_slots = n_slots;
-  p->lfu.count.assign(E, 0);
-  p->lfu.last.assign(E, -1);
-  p->lfu.slot_of.assign(E, -1);
-  p->lfu.holder.assign(n_slots, -1);
-  hipError_t e = hipMalloc(&p->slab, p->stride * (size_t)n_slots);
-  if (e == hipSuccess) e = hipMalloc(&p->table, sizeof(int32_t) * E);
-  if (e == hipSuccess) e = hipMalloc(&p->usage, sizeof(uint32_t) * E);
-  if (e == hipSuccess) e = hipMalloc(&p->err, 256);
-  if (e == hipSuccess) e = hipMemset(p->table, 0xFF, sizeof(int32_t) * E);
-  if (e == hipSuccess) e = hipMemset(p->usage, 0, sizeof(uint32_t) * E);
-  if (e == hipSuccess) e = hipMemset(p->err, 0, 256);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) {
-    moe_pool_destroy(p);
-    return hip_fail(e);
-  }
-  *out = p;
-  return MOE_OK;
+  return no_throw([&]() -> int {
+    if (!out || E < 1 || E > 1024 || n_slots < 1 || !shape_ok(sh)) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    std::unique_ptr<moe_pool> owner(new (std::nothrow) moe_pool());
+    if (!owner) return MOE_ERR_OUT_OF_MEMORY;
+    owner->lfu.count.assign(E, 0);               // host state first: may throw, nothing on the device yet
+    owner->lfu.last.assign(E, -1);
+    owner->lfu.slot_of.assign(E, -1);
+    owner->lfu.holder.assign(n_slots, -1);
+    moe_pool* p = owner.release();
+    p->E = E;
+    p->n_slots = n_slots;
+    p->sh = *sh;
+    p->stride = blob_layout(sh->d, sh->I, shape_bits(sh)).stride;
+    p->lfu.E = E;
+    p->lfu.n_slots = n_slots;
+    hipError_t e = hipMalloc(&p->slab, p->stride * (size_t)n_slots);
+    if (e == hipSuccess) e = hipMalloc(&p->table, sizeof(int32_t) * E);
+    if (e == hipSuccess) e = hipMalloc(&p->usage, sizeof(uint32_t) * E);
+    if (e == hipSuccess) e = hipMalloc(&p->err, 256);
+    if (e == hipSuccess) e = hipMemset(p->table, 0xFF, sizeof(int32_t) * E);
+    if (e == hipSuccess) e = hipMemset(p->usage, 0, sizeof(uint32_t) * E);
+    if (e == hipSuccess) e = hipMemset(p->err, 0, 256);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      moe_pool_destroy(p);
+      return hip_fail(e);
+    }
+    *out = p;
+    return MOE_OK;
+  });
 }
 
 extern "C" int moe_pool_destroy(moe_pool* p) {
@@ -393,12 +416,16 @@ static int load_common(moe_pool* p, int32_t e, int32_t slot, const void* blob, h
 }
 
 extern "C" int moe_pool_load(moe_pool* p, int32_t e, int32_t slot, const void* blob, hipStream_t s) {
-  return load_common(p, e, slot, blob, hipMemcpyHostToDevice, s);
+  return no_throw([&]() -> int {
+    return load_common(p, e, slot, blob, hipMemcpyHostToDevice, s);
+  });
 }
 
 extern "C" int moe_pool_load_device(moe_pool* p, int32_t e, int32_t slot, const void* blob,
                                     hipStream_t s) {
-  return load_common(p, e, slot, blob, hipMemcpyDeviceToDevice, s);
+  return no_throw([&]() -> int {
+    return load_common(p, e, slot, blob, hipMemcpyDeviceToDevice, s);
+  });
 }
 
 extern "C" int moe_pool_plan(moe_pool* p, const int32_t* sel, int32_t n, int32_t* le, int32_t* ls,
@@ -464,33 +491,37 @@ static int plan_and_copy(moe_pool* p, const int32_t* sel, int32_t n, const void*
 
 extern "C" int moe_pool_refill(moe_pool* p, const int32_t* sel, int32_t n, const void* host_blobs,
                                size_t host_stride, hipStream_t s) {
-  if (!p || !host_blobs || host_stride < p->stride) return MOE_ERR_INVALID_ARG;
-  std::vector<int32_t> te, ts;
-  int32_t nl = 0;
-  MOE_TRY(plan_and_copy(p, sel, n, host_blobs, host_stride, s, &te, &ts, &nl));
-  if (!te.empty()) MOE_TRY(table_edit_launch(p->table, te.data(), ts.data(), (int)te.size(), s));
-  return MOE_OK;
+  return no_throw([&]() -> int {
+    if (!p || !host_blobs || host_stride < p->stride) return MOE_ERR_INVALID_ARG;
+    std::vector<int32_t> te, ts;
+    int32_t nl = 0;
+    MOE_TRY(plan_and_copy(p, sel, n, host_blobs, host_stride, s, &te, &ts, &nl));
+    if (!te.empty()) MOE_TRY(table_edit_launch(p->table, te.data(), ts.data(), (int)te.size(), s));
+    return MOE_OK;
+  });
 }
 
 extern "C" int moe_pool_set_slot_table(moe_pool* p, const int32_t* table, hipStream_t s) {
-  if (!p || !table) return MOE_ERR_INVALID_ARG;
-  std::vector<char> used(p->n_slots, 0);
-  for (int e = 0; e < p->E; ++e) {
-    const int32_t sl = table[e];
-    if (sl < -1 || sl >= p->n_slots) return MOE_ERR_INVALID_ARG;
-    if (sl >= 0) {
-      if (used[sl]) return MOE_ERR_INVALID_ARG;
-      used[sl] = 1;
+  return no_throw([&]() -> int {
+    if (!p || !table) return MOE_ERR_INVALID_ARG;
+    std::vector<char> used(p->n_slots, 0);
+    for (int e = 0; e < p->E; ++e) {
+      const int32_t sl = table[e];
+      if (sl < -1 || sl >= p->n_slots) return MOE_ERR_INVALID_ARG;
+      if (sl >= 0) {
+        if (used[sl]) return MOE_ERR_INVALID_ARG;
+        used[sl] = 1;
+      }
     }
-  }
-  std::fill(p->lfu.holder.begin(), p->lfu.holder.end(), -1);
-  for (int e = 0; e < p->E; ++e) {
-    p->lfu.slot_of[e] = table[e];
-    if (table[e] >= 0) p->lfu.holder[table[e]] = e;
-  }
-  MOE_HIP(hipMemcpyAsync(p->table, table, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, s));
-  MOE_HIP(hipStreamSynchronize(s));
-  return MOE_OK;
+    std::fill(p->lfu.holder.begin(), p->lfu.holder.end(), -1);
+    for (int e = 0; e < p->E; ++e) {
+      p->lfu.slot_of[e] = table[e];
+      if (table[e] >= 0) p->lfu.holder[table[e]] = e;
+    }
+    MOE_HIP(hipMemcpyAsync(p->table, table, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, s));
+    MOE_HIP(hipStreamSynchronize(s));
+    return MOE_OK;
+  });
 }
 
 extern "C" int moe_pool_get_stats(const moe_pool* p, moe_pool_stats* st) {
@@ -529,7 +560,7 @@ extern "C" int moe_pool_reset_usage(moe_pool* p, hipStream_t s) {
 extern "C" size_t moe_ffn_workspace_bytes(const moe_ffn_shape* sh, const moe_ffn_shape* ssh, int32_t T,
                                           int32_t k, int32_t E, int32_t path) {
   if (!shape_ok(sh) || !shape_ok(ssh) || sh->d != ssh->d || T < 0 || k < 1 || E < 1) return 0;
-  path = resolve_path(path, T, sh->d, k, E, shape_bits(sh));
+  path = resolve_path(path, T, sh->d, k, E, shape_bits(sh), sh->I > ssh->I ? sh->I : ssh->I);
   return ffn_ws_bytes(sh->d, sh->I, ssh->I, T, k, E, path);
 }
 
@@ -551,7 +582,7 @@ extern "C" int moe_expert_ffn(const moe_pool* pool, const moe_ffn_shape* sh, con
                               size_t ws_bytes, hipStream_t s) {
   MOE_TRY(check_ffn(pool, sh, ssh, shared_blob, T, k));
   if (T == 0) return MOE_OK;
-  path = resolve_path(path, T, sh->d, k, pool->E, shape_bits(sh));
+  path = resolve_path(path, T, sh->d, k, pool->E, shape_bits(sh), sh->I > ssh->I ? sh->I : ssh->I);
   MOE_CHECK(x && idx && ws && aligned(x, 16) && aligned(ws, 256));
   FfnArgs a{};
   pool_view(pool, &a.pool);
@@ -616,6 +647,8 @@ static bool carve_layer(Carver& c, const moe_layer_desc* L, int T, int path, Lay
   return c.ok();
 }
 
+static int layer_imax(const moe_layer_desc* L) { return L->sh.I > L->shared_sh.I ? L->sh.I : L->shared_sh.I; }
+
 static int check_layer(const moe_layer_desc* L) {
   if (!L || !L->pool || !L->w_router_dev || !L->shared_blob_dev) return MOE_ERR_INVALID_ARG;
   if (!shape_ok(&L->sh) || !shape_ok(&L->shared_sh) || L->sh.d != L->shared_sh.d) return MOE_ERR_INVALID_ARG;
@@ -628,7 +661,7 @@ static int check_layer(const moe_layer_desc* L) {
 
 extern "C" size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int32_t T, int32_t path) {
   if (check_layer(L) != MOE_OK || T < 0) return 0;
-  path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh));
+  path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh), layer_imax(L));
   Carver c(nullptr, (size_t)-1);
   LayerWs w;
   carve_layer(c, L, T, path, &w);
@@ -643,7 +676,7 @@ int layer_forward(const moe_layer_desc* L, const uint16_t* x, int T, float* y, i
   if (T == 0) return MOE_OK;
   MOE_CHECK(x && y && idx && w && sgate && ws);
   MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
-  path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh));
+  path = resolve_path(path, T, L->sh.d, L->k, L->E, shape_bits(&L->sh), layer_imax(L));
   if (path == MOE_PATH_DECODE) MOE_CHECK(T <= 8 && (long)T * (L->k + 1) <= 2048);
   // the chain hand-over exists on the decode path of 4- and 8-bit experts
   if (io) MOE_CHECK(path == MOE_PATH_DECODE && shape_bits(&L->sh) != 32 && shape_bits(&L->shared_sh) != 32);
@@ -715,57 +748,59 @@ extern "C" int moe_layer_forward_streamed(const moe_layer_desc* L, const void* h
                                           const uint16_t* x, int32_t T, float* y, int32_t* idx, float* w,
                                           float* sgate, void* ws, size_t ws_bytes, hipStream_t s,
                                           hipStream_t copy_s, int32_t* n_loads) {
-  MOE_TRY(check_layer(L));
-  moe_pool* p = const_cast<moe_pool*>(L->pool);
-  MOE_CHECK(T >= 1 && T <= 8 && (long)T * (L->k + 1) <= 2048);
-  MOE_CHECK(shape_bits(&L->sh) != 32 && shape_bits(&L->shared_sh) != 32);
-  MOE_CHECK(x && y && idx && w && sgate && ws && host_blobs && host_stride >= p->stride);
-  MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
-  Carver c(ws, ws_bytes);
-  LayerWs lw;
-  if (!carve_layer(c, L, T, MOE_PATH_DECODE, &lw)) return MOE_ERR_INVALID_ARG;
-  if (!p->sel_host) {
-    MOE_HIP(hipHostMalloc((void**)&p->sel_host, sizeof(int32_t) * 8 * 1024, hipHostMallocDefault));
-    MOE_HIP(hipEventCreateWithFlags(&p->ev_sel, hipEventDisableTiming));
-    MOE_HIP(hipEventCreateWithFlags(&p->ev_gu, hipEventDisableTiming));
-    MOE_HIP(hipEventCreateWithFlags(&p->ev_copy, hipEventDisableTiming));
-  }
-  const int d = L->sh.d, k = L->k, n = T * k;
-  // 1. routing: selections, weights, shared gate, usage, and the activation
-  //    pairs for the GEMVs; the selections go to the host at once
-  MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, k, idx, w, sgate, L->usage_dev,
-                        lw.r, s, true));
-  MOE_HIP(hipMemcpyAsync(p->sel_host, idx, sizeof(int32_t) * n, hipMemcpyDeviceToHost, s));
-  MOE_HIP(hipEventRecord(p->ev_sel, s));
-  // 2. phase 1: the resident selections and the shared expert, queued now so
-  //    they run while the host plans and the missing blobs copy in
-  FfnArgs a{};
-  pool_view(p, &a.pool);
-  a.d = d; a.I = L->sh.I; a.Ish = L->shared_sh.I;
-  a.bits = shape_bits(&L->sh); a.bits_sh = shape_bits(&L->shared_sh);
-  a.shared_blob = static_cast<const uint8_t*>(L->shared_blob_dev);
-  a.x = x; a.xq = lw.r.xq; a.xs = lw.r.xs;
-  a.T = T; a.k = k; a.idx = idx; a.w = w; a.sgate = sgate; a.y = y;
-  a.phase = 1;
-  MOE_TRY(ffn_launch(a, MOE_PATH_DECODE, lw.ffn_ws, lw.ffn_bytes, s));
-  // 3. plan on the host, copy on copy_s (every blob's gate/up sections
-  //    first, then the down sections); the compute stream waits for the
-  //    gate/up sections before it publishes the new slots and runs the
-  //    phase-2 gate/up pass, and for the rest before the down pass
-  MOE_HIP(hipEventSynchronize(p->ev_sel));
-  std::vector<int32_t> te, ts;
-  int32_t nl = 0;
-  MOE_TRY(plan_and_copy(p, p->sel_host, n, host_blobs, host_stride, copy_s, &te, &ts, &nl, p->ev_gu));
-  if (nl > 0) {
-    MOE_HIP(hipEventRecord(p->ev_copy, copy_s));
-    MOE_HIP(hipStreamWaitEvent(s, p->ev_gu, 0));
-    MOE_TRY(table_edit_launch(p->table, te.data(), ts.data(), (int)te.size(), s));
-    a.down_wait = p->ev_copy;
-  }
-  // 4. phase 2: the deferred selections, then the rank-order combine
-  a.phase = 2;
-  a.pending = nl;
-  MOE_TRY(ffn_launch(a, MOE_PATH_DECODE, lw.ffn_ws, lw.ffn_bytes, s));
-  if (n_loads) *n_loads = nl;
-  return MOE_OK;
+  return no_throw([&]() -> int {
+    MOE_TRY(check_layer(L));
+    moe_pool* p = const_cast<moe_pool*>(L->pool);
+    MOE_CHECK(T >= 1 && T <= 8 && (long)T * (L->k + 1) <= 2048);
+    MOE_CHECK(shape_bits(&L->sh) != 32 && shape_bits(&L->shared_sh) != 32);
+    MOE_CHECK(x && y && idx && w && sgate && ws && host_blobs && host_stride >= p->stride);
+    MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
+    Carver c(ws, ws_bytes);
+    LayerWs lw;
+    if (!carve_layer(c, L, T, MOE_PATH_DECODE, &lw)) return MOE_ERR_INVALID_ARG;
+    if (!p->sel_host) {
+      MOE_HIP(hipHostMalloc((void**)&p->sel_host, sizeof(int32_t) * 8 * 1024, hipHostMallocDefault));
+      MOE_HIP(hipEventCreateWithFlags(&p->ev_sel, hipEventDisableTiming));
+      MOE_HIP(hipEventCreateWithFlags(&p->ev_gu, hipEventDisableTiming));
+      MOE_HIP(hipEventCreateWithFlags(&p->ev_copy, hipEventDisableTiming));
+    }
+    const int d = L->sh.d, k = L->k, n = T * k;
+    // 1. routing: selections, weights, shared gate, usage, and the activation
+    //    pairs for the GEMVs; the selections go to the host at once
+    MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, k, idx, w, sgate, L->usage_dev,
+                          lw.r, s, true));
+    MOE_HIP(hipMemcpyAsync(p->sel_host, idx, sizeof(int32_t) * n, hipMemcpyDeviceToHost, s));
+    MOE_HIP(hipEventRecord(p->ev_sel, s));
+    // 2. phase 1: the resident selections and the shared expert, queued now so
+    //    they run while the host plans and the missing blobs copy in
+    FfnArgs a{};
+    pool_view(p, &a.pool);
+    a.d = d; a.I = L->sh.I; a.Ish = L->shared_sh.I;
+    a.bits = shape_bits(&L->sh); a.bits_sh = shape_bits(&L->shared_sh);
+    a.shared_blob = static_cast<const uint8_t*>(L->shared_blob_dev);
+    a.x = x; a.xq = lw.r.xq; a.xs = lw.r.xs;
+    a.T = T; a.k = k; a.idx = idx; a.w = w; a.sgate = sgate; a.y = y;
+    a.phase = 1;
+    MOE_TRY(ffn_launch(a, MOE_PATH_DECODE, lw.ffn_ws, lw.ffn_bytes, s));
+    // 3. plan on the host, copy on copy_s (every blob's gate/up sections
+    //    first, then the down sections); the compute stream waits for the
+    //    gate/up sections before it publishes the new slots and runs the
+    //    phase-2 gate/up pass, and for the rest before the down pass
+    MOE_HIP(hipEventSynchronize(p->ev_sel));
+    std::vector<int32_t> te, ts;
+    int32_t nl = 0;
+    MOE_TRY(plan_and_copy(p, p->sel_host, n, host_blobs, host_stride, copy_s, &te, &ts, &nl, p->ev_gu));
+    if (nl > 0) {
+      MOE_HIP(hipEventRecord(p->ev_copy, copy_s));
+      MOE_HIP(hipStreamWaitEvent(s, p->ev_gu, 0));
+      MOE_TRY(table_edit_launch(p->table, te.data(), ts.data(), (int)te.size(), s));
+      a.down_wait = p->ev_copy;
+    }
+    // 4. phase 2: the deferred selections, then the rank-order combine
+    a.phase = 2;
+    a.pending = nl;
+    MOE_TRY(ffn_launch(a, MOE_PATH_DECODE, lw.ffn_ws, lw.ffn_bytes, s));
+    if (n_loads) *n_loads = nl;
+    return MOE_OK;
+  });
 }

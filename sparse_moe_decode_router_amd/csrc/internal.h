@@ -105,7 +105,7 @@ bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws);
 // prep_x: also fill ws.xq / ws.xs for T > 8 (T <= 8 always does, in-kernel)
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias,
                   int E, int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
-                  const RouterWs& ws, hipStream_t s, bool prep_x);
+                  const RouterWs& ws, hipStream_t s, bool prep_x, float* logits_out = nullptr);
 // moe_layer_forward with a chain's hand-over (decode path of 4- and 8-bit
 // experts only) or none (io == nullptr).
 int layer_forward(const moe_layer_desc* L, const uint16_t* x, int T, float* y, int32_t* idx, float* w,
@@ -116,7 +116,7 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
                          const RouterWs& ws, hipStream_t s, bool prep_x,
                          const float* ssp = nullptr, float eps = 0.f);
 int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx,
-                float* w, float* sgate, uint32_t* usage, hipStream_t s);
+                float* w, float* sgate, uint32_t* usage, hipStream_t s, float* logits_out = nullptr);
 
 // usage (optional): usage[e] += the pairs bucketed to e (one atomic per expert)
 int bucket_launch(const int32_t* idx, int T, int k, int E, int32_t* counts,
@@ -163,6 +163,10 @@ size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
 size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E);
 int prefill_launch(const FfnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 int ffn_launch(const FfnArgs& a, int path, void* ws, size_t ws_bytes, hipStream_t s);
-int resolve_path(int path, int T, int d, int k, int E, int bits);
+int resolve_path(int path, int T, int d, int k, int E, int bits, int Imax);
+// The matrix-core path addresses its activation and intermediate buffers
+// through 32-bit buffer descriptors: T d and (T k + T) Imax fp16 values must
+// stay below 4 GiB.
+bool prefill_fits(int T, int d, int k, int Imax);
 
 }  // namespace moe

@@ -302,12 +302,15 @@ int router_splits(int T, int d, int E) {
 
 // One wave per token.  With S > 1 the logits arrive as S split-K partials
 // [S][T][E+1], summed here in split order before the selection.
+// logits_out (optional, [T][E+1]): the logits the selection reads (the
+// split-K sum where S > 1, before the bias), copied out unchanged.
 template <int NK>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int S,
                                                    const float* __restrict__ bias,
                                                    int T, int E, int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ sgate,
-                                                   uint32_t* __restrict__ usage) {
+                                                   uint32_t* __restrict__ usage,
+                                                   float* __restrict__ logits_out) {
   extern __shared__ uint32_t dyn_lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
@@ -344,6 +347,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     row = lsum;
+  }
+  if (logits_out) {
+    for (int e = lane; e <= E; e += 64) logits_out[(size_t)t * (E + 1) + e] = row[e];
   }
   // one partial: the selection reads the logits where they are (its loads
   // are all issued before any use)
@@ -402,17 +408,17 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
 }
 
 int topk_launch(const float* logits, const float* bias, int T, int d, int E, int k, int32_t* idx, float* w,
-                float* sgate, uint32_t* usage, hipStream_t s) {
+                float* sgate, uint32_t* usage, hipStream_t s, float* logits_out) {
   if (T == 0) return MOE_OK;
   const int S = T <= 8 ? 1 : router_splits(T, d, E);
   const size_t lds = (size_t)4 * (2 * ((k + 3) & ~3) + topk_scratch_words(E) + ((E + 1 + 3) & ~3)) * 4;
   const dim3 tg((T + 3) / 4);
   switch (nk_for(E)) {
-    case 1: topk_kernel<1><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
-    case 2: topk_kernel<2><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
-    case 4: topk_kernel<4><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
-    case 8: topk_kernel<8><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
-    default: topk_kernel<16><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage); break;
+    case 1: topk_kernel<1><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage, logits_out); break;
+    case 2: topk_kernel<2><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage, logits_out); break;
+    case 4: topk_kernel<4><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage, logits_out); break;
+    case 8: topk_kernel<8><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage, logits_out); break;
+    default: topk_kernel<16><<<tg, 256, lds, s>>>(logits, S, bias, T, E, k, idx, w, sgate, usage, logits_out); break;
   }
   MOE_HIP(hipGetLastError());
   return MOE_OK;
@@ -420,9 +426,9 @@ int topk_launch(const float* logits, const float* bias, int T, int d, int E, int
 
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias, int E,
                   int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
-                  const RouterWs& ws, hipStream_t s, bool prep_x) {
+                  const RouterWs& ws, hipStream_t s, bool prep_x, float* logits_out) {
   MOE_TRY(router_logits_launch(x, T, d, W, E, ws, s, prep_x));
-  return topk_launch(ws.logits, bias, T, d, E, k, idx, w, sgate, usage, s);
+  return topk_launch(ws.logits, bias, T, d, E, k, idx, w, sgate, usage, s, logits_out);
 }
 
 }  // namespace moe
@@ -441,10 +447,10 @@ extern "C" int32_t moe_router_sum_depth(int32_t T, int32_t d, int32_t E) {
   return 32 + 2 + d / (32 * S) + (S - 1) + 1;
 }
 
-extern "C" int moe_router_topk(const uint16_t* x, int32_t T, int32_t d, const float* W,
-                               const float* bias, int32_t E, int32_t k, int32_t* idx, float* w,
-                               float* sgate, uint32_t* usage, void* ws, size_t ws_bytes,
-                               hipStream_t s) {
+extern "C" int moe_router_topk_logits(const uint16_t* x, int32_t T, int32_t d, const float* W,
+                                      const float* bias, int32_t E, int32_t k, int32_t* idx, float* w,
+                                      float* sgate, uint32_t* usage, float* logits_out, void* ws,
+                                      size_t ws_bytes, hipStream_t s) {
   MOE_CHECK(T >= 0 && d > 0 && d % 64 == 0 && d <= 8192);
   MOE_CHECK(E >= 1 && E <= 1024 && k >= 1 && k <= E);
   if (T == 0) return MOE_OK;
@@ -453,5 +459,12 @@ extern "C" int moe_router_topk(const uint16_t* x, int32_t T, int32_t d, const fl
   Carver c(ws, ws_bytes);
   RouterWs rw;
   if (!router_ws_carve(c, T, d, E, &rw)) return MOE_ERR_INVALID_ARG;
-  return router_launch(x, T, d, W, bias, E, k, idx, w, sgate, usage, rw, s, false);
+  return router_launch(x, T, d, W, bias, E, k, idx, w, sgate, usage, rw, s, false, logits_out);
+}
+
+extern "C" int moe_router_topk(const uint16_t* x, int32_t T, int32_t d, const float* W,
+                               const float* bias, int32_t E, int32_t k, int32_t* idx, float* w,
+                               float* sgate, uint32_t* usage, void* ws, size_t ws_bytes,
+                               hipStream_t s) {
+  return moe_router_topk_logits(x, T, d, W, bias, E, k, idx, w, sgate, usage, nullptr, ws, ws_bytes, s);
 }

@@ -96,3 +96,49 @@ def assert_close_y(y_dev, y_ref, rel=2e-3):
     scale = np.max(np.abs(y_ref))
     assert err <= rel * scale, f"max|err| {err:.3e} > {rel} * {scale:.3e}"
     return err / scale
+
+
+def check_device_logits(xb, Wr, bias, k, idx_dev, w_dev, l_dev, depth):
+    """The device's own logits (exported by moe_router_topk_logits, before the
+    bias) against the exact ones and its selection against its own logits:
+
+    * every logit, the shared-gate row included, within the elementwise fp32
+      rounding bound for the router's documented summation depth (this pins
+      the accumulation model the certified near-tie rule relies on, the matrix
+      cores' included);
+    * the selection is the exact top k of the device's own fp32 keys
+      fp32(logit + bias), ties to the lower index, in rank order: bit for bit
+      on every token, near-ties included;
+    * the weights are the softmax over those keys.
+    Returns the largest |error| / bound."""
+    E = Wr.shape[0] - 1
+    exact = olayer.bf16_to_f64(xb) @ np.asarray(Wr, np.float64).T
+    r = olayer.logit_error_bounds(xb, Wr, depth)
+    err = np.abs(l_dev.astype(np.float64) - exact)
+    bad = np.argwhere(err > r)
+    assert bad.size == 0, f"logit outside the rounding bound at {bad[:4].tolist()}"
+    keys = l_dev[:, :E].astype(np.float32)
+    if bias is not None:
+        keys = (keys + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
+    sel = olayer.select_topk(keys.astype(np.float64), k)
+    mism = np.nonzero((sel != idx_dev).any(1))[0]
+    assert mism.size == 0, f"selection differs from the top k of the device logits at tokens {mism[:4]}"
+    w_ref = olayer.topk_weights(keys.astype(np.float64), idx_dev)
+    assert np.allclose(w_dev, w_ref, rtol=0, atol=2e-6)
+    return float(np.max(err / np.maximum(r, 1e-300)))
+
+
+def predicted_near_ties(xb, Wr, bias, k, depth):
+    """Expected number of tokens the certified rule cannot separate, under the
+    exponential-spacing model of the top order statistics: at rank boundary
+    i the chance that the exact gap falls below 2 r_t is 1 - exp(-2 r_t / g_i),
+    g_i the mean gap at that boundary over these tokens."""
+    l, _ = olayer.router_logits(olayer.bf16_to_f64(xb), Wr, bias)
+    r = olayer.logit_error_bound(xb, Wr, bias, depth)
+    top = -np.sort(-l, axis=1)[:, :min(k + 1, l.shape[1])]
+    gaps = -np.diff(top, axis=1)
+    if gaps.shape[1] == 0:
+        return 0.0
+    g = np.maximum(gaps.mean(axis=0), 1e-30)
+    p = 1.0 - np.exp(-2.0 * r[:, None] / g[None, :])
+    return float((1.0 - np.prod(1.0 - p, axis=1)).sum())

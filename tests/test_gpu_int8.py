@@ -71,13 +71,6 @@ def test_prefill_int8_midsize_full_oracle():
     print(f"int8 prefill midsize rel err {rel:.2e}, near-ties {namb}")
 
 
-def test_prefill80b_int8_sampled():
-    cfg = ms.CONFIGS["prefill80b_int8"]
-    sample = np.sort(np.random.default_rng(11).choice(cfg.T, size=24, replace=False))
-    rel, namb = _check(DeviceLayer(cfg), 0, path=moe.MOE_PATH_PREFILL, T=cfg.T, sample=sample)
-    print(f"prefill80b int8: rel err {rel:.2e}, near-ties {namb}")
-
-
 def test_prefill_int8_matches_batched_path():
     cfg = ms.scaled(ms.CONFIGS["prefill80b_int8"], T=256, E=64, k=8, d=1024, I=256, I_shared=256,
                     n_slots=64)

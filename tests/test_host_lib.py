@@ -212,3 +212,30 @@ def test_workspace_sizes_monotone():
     a = moe.moe_ffn_workspace_bytes(2048, 512, 512, 1, 10, 512, moe.MOE_PATH_DECODE)
     b = moe.moe_ffn_workspace_bytes(2048, 512, 512, 64, 10, 512, moe.MOE_PATH_BATCHED)
     assert 0 < a < b
+
+
+def test_prefill_path_refuses_sizes_past_its_32bit_descriptors():
+    """The matrix-core path addresses activations (T d fp16) and the SwiGLU
+    intermediate ((T k + T) Imax fp16) through 32-bit buffer descriptors:
+    past 4 GiB it is refused (workspace size 0, the call MOE_ERR_UNSUPPORTED)
+    and MOE_PATH_AUTO takes the bucketed GEMVs instead."""
+    d, I, k, E = 2048, 512, 10, 512
+    ws = lambda T, path: moe.moe_ffn_workspace_bytes(d, I, I, T, k, E, path)
+    T_ok = 4096
+    T_big = (1 << 32) // ((k + 1) * I * 2) + 1          # first T whose intermediate reaches 4 GiB
+    assert ((T_big - 1) * (k + 1)) * I * 2 < (1 << 32) <= (T_big * (k + 1)) * I * 2
+    assert ws(T_ok, moe.MOE_PATH_PREFILL) > 0
+    assert ws(T_big - 1, moe.MOE_PATH_PREFILL) > 0
+    assert ws(T_big, moe.MOE_PATH_PREFILL) == 0
+    assert ws(T_big, moe.MOE_PATH_AUTO) == ws(T_big, moe.MOE_PATH_BATCHED) > 0
+    assert ws(T_big - 1, moe.MOE_PATH_AUTO) == ws(T_big - 1, moe.MOE_PATH_PREFILL)
+    # the activation descriptor alone: d = 8192, k = 1, I = 64 -> T d 2 bytes
+    T_x = (1 << 32) // (8192 * 2)
+    assert moe.moe_ffn_workspace_bytes(8192, 64, 64, T_x, 1, 16, moe.MOE_PATH_PREFILL) == 0
+    assert moe.moe_ffn_workspace_bytes(8192, 64, 64, T_x - 1, 1, 16, moe.MOE_PATH_PREFILL) > 0
+
+
+def test_out_of_memory_has_its_own_status():
+    assert moe.MOE_ERR_OUT_OF_MEMORY == -6
+    assert moe._lib.moe_status_string(moe.MOE_ERR_OUT_OF_MEMORY).decode() == "host allocation failed"
+    assert moe._lib.moe_status_string(moe.MOE_ERR_INVALID_ARG).decode() == "invalid argument"

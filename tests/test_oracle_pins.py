@@ -412,6 +412,37 @@ def test_logit_error_bound_holds_for_fp32_sums():
     assert np.max(np.abs(seq - exact[0])) <= r[0]
 
 
+def test_elementwise_logit_bounds_hold_for_fp32_sums():
+    """The elementwise bound covers every router row (the shared-gate row
+    included) of two real fp32 summation orders: a sequential sum (depth d)
+    and a pairwise tree (depth log2 d).  A bound with a dropped |.|, a wrong
+    row or a depth unit off by a factor fails on one of them."""
+    cfg = ms.CONFIGS["decode80b"]
+    Wr = ms.router_weight(cfg)
+    xb = ms.x_bits(cfg, 1, 3)
+    x32 = ms.bf16_bits_to_f32(xb)
+    exact = olayer.bf16_to_f64(xb) @ Wr.astype(np.float64).T              # [T, E+1]
+    for t in range(xb.shape[0]):
+        prod = (x32[t][None, :] * Wr).astype(np.float32)                  # [E+1, d], fp32 products
+        seq = np.zeros(cfg.E + 1, np.float32)
+        for j in range(cfg.d):
+            seq = (seq + prod[:, j]).astype(np.float32)
+        tree = prod.copy()
+        while tree.shape[1] > 1:
+            tree = (tree[:, 0::2] + tree[:, 1::2]).astype(np.float32)
+        r_seq = olayer.logit_error_bounds(xb[t:t + 1], Wr, depth=cfg.d)[0]
+        r_tree = olayer.logit_error_bounds(xb[t:t + 1], Wr, depth=int(np.log2(cfg.d)))[0]
+        assert np.all(np.abs(seq - exact[t]) <= r_seq)
+        assert np.all(np.abs(tree[:, 0] - exact[t]) <= r_tree)
+        # the pairwise tree is far inside the sequential bound: the depth matters
+        assert np.max(r_tree) < np.max(r_seq) / 100
+    # the per-token routed-row bound is the row maximum of the elementwise one
+    # (no bias)
+    r_all = olayer.logit_error_bounds(xb, Wr, depth=17)
+    r_tok = olayer.logit_error_bound(xb, Wr, None, depth=17)
+    assert np.allclose(r_all[:, :cfg.E].max(1), r_tok, rtol=1e-12, atol=0)
+
+
 # ---- chains of MoE layers: norm, residual, bf16 rounding -------------------
 def test_bf16_round_hand_values_and_generator_agree():
     """Round-to-nearest-even onto bf16 at hand-checked points (ties go to the
