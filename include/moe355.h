@@ -343,6 +343,28 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x_dev,
                       void* workspace_dev, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* ------------------------------------------- whole layer, no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * call as moe_layer_forward (same kernels, same bits), with the workspace
+ * taken from a scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory, one per GPU, for the life of the process (set up,
+ * and cleared once, by the first call on that GPU: a fill kernel on `stream`
+ * ahead of the call's own work).  Nothing is allocated, by this call or by
+ * the library routines it uses.  Calls whose workspace
+ * (moe_layer_workspace_bytes(L, T, path)) exceeds the scratch return
+ * MOE_ERR_UNSUPPORTED and do nothing: 32 MiB covers the decode path
+ * (T <= 8) at every supported shape and the 80B-shaped batched layer well
+ * past 64 tokens, not a 4096-token prefill.  Every call on one GPU shares
+ * that GPU's scratch, which keeps the last call's contents: calls that
+ * overlap on one GPU (two streams, two threads) race and must be ordered
+ * by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x_dev,
+                              int32_t T, float* y_dev, int32_t* topk_idx_dev,
+                              float* topk_w_dev, float* shared_gate_dev,
+                              int32_t path, hipStream_t stream);
+
 /* ------------------------------------------------- streamed decode step
  * One decode step (T <= 8, T*(k+1) <= 2048, 4- or 8-bit experts) on a pool
  * that holds only some experts, with the misses copied in while the resident

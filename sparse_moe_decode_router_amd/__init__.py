@@ -109,6 +109,7 @@ _SIGS = {
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_layer_workspace_bytes": (_S, [_P, _I, _I]),
     "moe_layer_forward": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
+    "moe_layer_forward_noalloc": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_layer_forward_streamed": (C.c_int, [_P, _P, _S, _P, _I, _P, _P, _P, _P, _P, _S, _P, _P, _P]),
     "moe_chain_workspace_bytes": (_S, [_P, _I, _I, _I]),
     "moe_chain_forward": (C.c_int, [_P, _I, C.c_float, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
@@ -508,6 +509,28 @@ def moe_layer_forward(layer: Layer, x, path: int = MOE_PATH_AUTO, workspace=None
     st = _lib.moe_layer_forward(C.byref(layer.desc), _ptr(x), T, _ptr(y), _ptr(idx), _ptr(w), _ptr(s),
                                 path, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "moe_layer_forward")
+    return y, idx, w, s
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_layer_forward_noalloc(layer: Layer, x, path: int = MOE_PATH_AUTO, out=None, stream=None):
+    """moe_layer_forward with the library's per-GPU scratch as the workspace
+    (the C call allocates nothing).  out: (y, topk_idx, topk_w, shared_gate),
+    allocated here when None."""
+    import torch
+    T, d = x.shape
+    k = layer.k
+    if out is None:
+        out = (torch.empty((T, d), dtype=torch.float32, device=x.device),
+               torch.empty((T, k), dtype=torch.int32, device=x.device),
+               torch.empty((T, k), dtype=torch.float32, device=x.device),
+               torch.empty((T,), dtype=torch.float32, device=x.device))
+    y, idx, w, s = out
+    st = _lib.moe_layer_forward_noalloc(C.byref(layer.desc), _ptr(x), T, _ptr(y), _ptr(idx), _ptr(w), _ptr(s),
+                                        path, _stream(stream))
+    _check(st, "moe_layer_forward_noalloc")
     return y, idx, w, s
 
 
