@@ -139,29 +139,138 @@ def graph_time(c, fn, lo, hi, stream):
     return e0.elapsed_time(e1) / (hi - lo)
 
 
-def cpu_baseline(c, cfg, sample_steps):
-    """The oracle as it stands, on the first `sample_steps` decode steps."""
+def cpu_info():
+    """Host cores this process may run on and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(c, cfg, steps=None, tokens=None):
+    """The oracle as it stands (numpy fp64, BLAS threads = the cores this
+    process may use) on a bounded sample of the workload: the first `steps`
+    seeded steps, or the first `tokens` tokens of step 0.  Expert weights are
+    generated before the timed region (they are inputs); dequantisation and
+    the products are timed."""
     import threadpoolctl
     ms, olayer = c.ms, c.olayer
+    cores, model = cpu_info()
     Wr = ms.router_weight(cfg)
     bias = ms.logit_bias(cfg)
     sh = ms.shared_raw(cfg)
-    xs = [ms.x_bits(cfg, s) for s in range(sample_steps)]
+    if steps is not None:
+        xs = [ms.x_bits(cfg, s) for s in range(steps)]
+        what = f"first {steps} of the {cfg.steps} seeded steps ({steps * cfg.T} tokens)"
+    else:
+        xs = [ms.x_bits(cfg, 0)[:tokens]]
+        what = f"first {tokens} of the {cfg.T} tokens of step 0"
     need = set()
     for xb in xs:
         idx, _, _, _ = olayer.route(xb, Wr, bias, cfg.k)
         need.update(int(e) for e in idx.ravel())
     raws = {e: ms.expert_raw(cfg, e) for e in sorted(need)}     # inputs, generated before timing
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
-    for xb in xs:
-        olayer.moe_layer(xb, Wr, bias, cfg.k, raws.__getitem__, sh)
-    dt = time.perf_counter() - t0
-    return {"value": round(sample_steps * cfg.T / dt, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"first {sample_steps} of the {cfg.steps} seeded decode steps, numpy fp64 "
-                      f"(dequantise + matmul per selected expert), {dt:.1f}s"}
+    ntok = sum(xb.shape[0] for xb in xs)
+    with threadpoolctl.threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for xb in xs:
+            olayer.moe_layer(xb, Wr, bias, cfg.k, raws.__getitem__, sh)
+        dt = time.perf_counter() - t0
+    return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": cores, "cpu": model, "kind": "oracle",
+            "sample": f"{what}, numpy fp64 (dequantise + matmul per selected expert, {len(need)} experts), "
+                      f"{dt:.1f}s; no dequantised-weight cache"}
+
+
+def chain_cpu_baseline(c, cfgs, expert_cfg):
+    """The oracle through a chain of layers (one residual block per layer)
+    for one token, as cpu_baseline: router and shared expert of layer l from
+    cfgs[l], the routed experts from expert_cfg (the chain workload packs
+    one set of expert blobs into every layer's pool)."""
+    import threadpoolctl
+    ms, olayer = c.ms, c.olayer
+    cores, model = cpu_info()
+    layers = []
+    xb = ms.x_bits(cfgs[0], 0)
+    for cl in cfgs:                                   # inputs first: router, shared and selected experts
+        Wr, bias, sh = ms.router_weight(cl), ms.logit_bias(cl), ms.shared_raw(cl)
+        layers.append(dict(w_router=Wr, bias=bias, k=cl.k, shared=sh, cfg=cl))
+    t_gen = 0.0
+    with threadpoolctl.threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for Ld in layers:
+            u = olayer.rms_norm_bf16(xb)
+            idx, _, _, _ = olayer.route(u, Ld["w_router"], Ld["bias"], Ld["k"])
+            tg = time.perf_counter()
+            raws = {int(e): ms.expert_raw(expert_cfg, int(e)) for e in np.unique(idx)}
+            t_gen += time.perf_counter() - tg
+            Ld["expert"] = raws.__getitem__
+            xb, _, _ = olayer.chain_layer(xb, Ld)
+        dt = time.perf_counter() - t0 - t_gen
+    return {"value": round(1.0 / dt, 4), "unit": "tokens/s", "cores": cores, "cpu": model, "kind": "oracle",
+            "sample": f"one token through the {len(cfgs)} layers, numpy fp64, {dt:.1f}s "
+                      f"(expert generation, {t_gen:.1f}s, not counted)"}
+
+
+def measure_ceilings(c, read_bytes=(), three=None, mfma=False):
+    """What this MI355X sustains: a one-launch streaming read of each size in
+    read_bytes (cold: every launch reads a different window of a 1 GiB
+    region, beyond the 256 MB last-level cache), three dependent launches
+    reading the sizes in `three` (the minimum a three-phase decode step
+    costs at the chip's own read rate and launch gaps), and a loop of dense
+    fp16 MFMAs.  HIP events on the launch stream around graph replays.
+    (A region of at least twice the largest read keeps every window cold.)"""
+    torch, moe = c.torch, c.moe
+    out = {}
+    stream = torch.cuda.Stream()
+    region = max([1 << 30] + [2 * ((nb + 4095) // 4096 * 4096) for nb in read_bytes])
+    buf = torch.empty(region, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    n = 40
+
+    def windows(size):
+        size = (size + 4095) // 4096 * 4096
+        k = region // size
+        return [buf[(i % k) * size:(i % k) * size + size] for i in range(n)], size
+
+    grids = (256, 512, 1024, 2048, 16384)        # the best of these workgroup counts
+    for nb in read_bytes:
+        ws, size = windows(nb)
+        best = min((graph_time(c, lambda i: moe.moe_probe_stream_read(ws[i], sink, g), 0, n, stream), g)
+                   for g in grids)
+        out.setdefault("stream_read", []).append({"bytes": size, "us": round(best[0] * 1e3, 3),
+                                                  "GBps": round(size / (best[0] * 1e-3) / 1e9, 1),
+                                                  "workgroups": best[1]})
+    if three:
+        parts = [windows(nb) for nb in three]
+
+        def skel_for(g):
+            def skel(i):
+                for ws, _ in parts:
+                    moe.moe_probe_stream_read(ws[i], sink, g)
+            return skel
+
+        best = min((graph_time(c, skel_for(g), 0, n, stream), g) for g in grids)
+        out["three_launch"] = {"bytes": [sz for _, sz in parts], "us": round(best[0] * 1e3, 3),
+                               "workgroups": best[1]}
+    if mfma:
+        fsink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+        flops = [0.0]
+
+        def mm(i):
+            flops[0] = moe.moe_probe_mfma_f16(4000, fsink, 1024)
+
+        ms_ = graph_time(c, mm, 0, 5, stream)
+        out["mfma_f16_TFLOPs"] = round(flops[0] / (ms_ * 1e-3) / 1e12, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def ffn_traffic(name):
@@ -247,6 +356,30 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
     router_bytes = (cfg.E + 1) * cfg.d * 4
     achieved = expert_bytes / (ffn_ms * 1e-3) / 1e9
     layer_gbs = expert_bytes / (ms_step * 1e-3) / 1e9
+    # single-step latency: one step, then a wait for it, 200 times (eager
+    # launches through the C ABI; and one-step graph replays)
+    lat_e, lat_g = [], []
+    with torch.cuda.stream(stream):
+        for i in range(200):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(W + i % K)
+            e1.record(stream)
+            e1.synchronize()
+            lat_e.append(e0.elapsed_time(e1) * 1e3)
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=stream):
+            step(W)
+        for i in range(200):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g1.replay()
+            e1.record(stream)
+            e1.synchronize()
+            lat_g.append(e0.elapsed_time(e1) * 1e3)
+    ceil = measure_ceilings(c, read_bytes=(expert_bytes, expert_bytes + router_bytes),
+                            three=(router_bytes, expert_bytes * 2 // 3, expert_bytes // 3))
+    read_gbs = ceil["stream_read"][0]["GBps"]
     metric, data, wdt = labels(cfg)
     out = {
         "metric": metric, "value": round(1000.0 / ms_step, 1), "unit": "tokens/s",
@@ -262,15 +395,24 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
         "layer_expert_GBps": round(layer_gbs, 1),
         "layer_expert_frac_of_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": ("expert FFN: gate_up_kernel + down_decode_pipe_kernel" if cfg.bits != 32
-                                else "expert FFN: gate_up_f32_kernel + down_decode_f32_kernel"),
+                     "kernel": ("expert FFN replayed with the routing given (one moe_expert_ffn call: "
+                                "gate_up_kernel RAW instance + down_decode_pipe_kernel; inside the layer the "
+                                "gate/up instance also selects the experts from the logits)" if cfg.bits != 32
+                                else "expert FFN replayed with the routing given (gate_up_f32_kernel + "
+                                     "down_decode_f32_kernel, the same kernels the layer runs)"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": ffn_traffic(name),
-                     "avg_us": round(ffn_ms * 1e3, 3)},
+                     "avg_us": round(ffn_ms * 1e3, 3),
+                     "measured_peak": read_gbs,
+                     "measured_peak_what": f"one-launch streaming read of the same {expert_bytes} bytes, cold",
+                     "frac_of_measured": round(achieved / read_gbs, 4)},
+        "layer_frac_of_measured_read": round(layer_gbs / read_gbs, 4),
+        "p50_step_us": {"eager": round(float(np.median(lat_e)), 2), "graph": round(float(np.median(lat_g)), 2)},
+        "ceilings": ceil,
     }
     if cpu_steps > 0:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(c, cfg, cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(c, cfg, steps=cpu_steps)
     return out
 
 
@@ -356,6 +498,41 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
             "bit_identical_to_all_resident": identical}
 
 
+def mfma_kernels(cfg, T):
+    """The launches of the matrix-core expert FFN for T tokens (the library
+    takes the weight-streaming GEMMs while T k <= 4 E and d <= 4096)."""
+    if T * cfg.k <= 4 * cfg.E and cfg.d <= 4096:
+        return "prefill_plan_kernel + stream_gate_up_kernel + stream_down_kernel"
+    return "prefill_xprep_kernel + prefill_plan_kernel + prefill_gate_up_kernel + prefill_down_kernel"
+
+
+def ffn_replay(c, cfg, layers, xall, idx, w, s, lo, hi, stream, path):
+    """The expert FFN of steps lo..hi-1 replayed alone from a graph (one
+    moe_expert_ffn call per step with that step's routing and bucketing, the
+    layer's replica), HIP events on the graph's stream; the last step's
+    partial outputs, combined, must equal the layer's output bit for bit.
+    Returns (ms per call, the launches of one call)."""
+    torch, moe = c.torch, c.moe
+    T = xall.shape[1]
+    R = len(layers)
+    buckets = [moe.moe_bucket_tokens(idx[i], cfg.E) for i in range(hi)]
+    rpath = moe.MOE_PATH_BATCHED if cfg.bits == 32 else moe.MOE_PATH_PREFILL
+    ws = torch.zeros(moe.moe_ffn_workspace_bytes(cfg.d, cfg.I, cfg.I_shared, T, cfg.k, cfg.E, rpath, cfg.bits),
+                     dtype=torch.uint8, device="cuda")
+    partial = torch.empty((T * cfg.k, cfg.d), dtype=torch.float32, device="cuda")
+    shared_out = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+
+    def ffn(i):
+        L = layers[i % R]
+        _, o, p = buckets[i]
+        moe.moe_expert_ffn(L.pool, L.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i], path=rpath,
+                           offsets=o, pair_ids=p, workspace=ws, out=(partial, shared_out))
+
+    ms = graph_time(c, ffn, lo, hi, stream)
+    return ms, partial, shared_out, (mfma_kernels(cfg, T) if cfg.bits != 32
+                                     else "plan_kernel + gate_up_f32_kernel + down_batched_f32_kernel")
+
+
 def run_batched(c, K, W, R, name="batch80b"):
     """T=64 independent tokens.  The layer runs on the path MOE_PATH_AUTO
     picks for 64 tokens (bucketing, then the grouped GEMMs on the matrix
@@ -387,6 +564,17 @@ def run_batched(c, K, W, R, name="batch80b"):
     distinct = float(np.mean([len(np.unique(ids[i])) for i in range(W, nsteps)]))
     expert_bytes = (distinct + 1) * moe.moe_blob_bytes(cfg.d, cfg.I, cfg.bits)
     gbs = expert_bytes / (ms_step * 1e-3) / 1e9
+    # dominant kernels: the expert FFN launch group of the AUTO path, replayed
+    # with every timed step's own routing and bucketing
+    ffn_ms, partial, shared_out, ffn_kernels = ffn_replay(c, cfg, layers, xall, idx, w, s, W, nsteps, stream,
+                                                          moe.MOE_PATH_AUTO)
+    yc = moe.moe_combine(partial, shared_out, w[nsteps - 1], s[nsteps - 1])
+    torch.cuda.synchronize()
+    assert torch.equal(yc, y[nsteps - 1]), "FFN-only replay differs from the layer"
+    ffn_kernels = "expert FFN replayed with the routing given: " + ffn_kernels
+    achieved = expert_bytes / (ffn_ms * 1e-3) / 1e9
+    ceil = measure_ceilings(c, read_bytes=(int(expert_bytes),))
+    read_gbs = ceil["stream_read"][0]["GBps"]
     metric, data, wdt = labels(cfg)
     return {"metric": metric, "value": round(T * 1000.0 / ms_step, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
@@ -400,7 +588,15 @@ def run_batched(c, K, W, R, name="batch80b"):
                                 else "auto: bucketing + bucketed f32 GEMVs")},
             "distinct_experts_per_step": round(distinct, 1),
             "layer_expert_GBps": round(gbs, 1), "layer_expert_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "gemv_path_ms_per_step": round(times[moe.MOE_PATH_BATCHED], 5)}
+            "gemv_path_ms_per_step": round(times[moe.MOE_PATH_BATCHED], 5),
+            "roofline": {"bound": "hbm", "kernel": ffn_kernels, "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": ffn_traffic(name), "avg_us": round(ffn_ms * 1e3, 3),
+                         "bytes_per_launch": int(expert_bytes),
+                         "measured_peak": read_gbs,
+                         "measured_peak_what": f"one-launch streaming read of {int(expert_bytes)} bytes, cold",
+                         "frac_of_measured": round(achieved / read_gbs, 4)},
+            "ceilings": ceil}
 
 
 def run_prefill(c, name, reps):
@@ -427,6 +623,17 @@ def run_prefill(c, name, reps):
     flops = 6.0 * cfg.d * (T * cfg.k * cfg.I + T * cfg.I_shared)
     router_flops = 2.0 * T * cfg.d * (cfg.E + 1)
     tf = flops / (ms_call * 1e-3) / 1e12
+    # dominant kernels: the grouped GEMMs' launch group replayed with the routing given
+    xs1, id1, w1, s1 = x.unsqueeze(0), out[1].unsqueeze(0), out[2].unsqueeze(0), out[3].unsqueeze(0)
+    xr = xs1.expand(reps, -1, -1)
+    ffn_ms, partial, shared_out, ffn_kernels = ffn_replay(c, cfg, [L], xr, id1.expand(reps, -1, -1),
+                                                          w1.expand(reps, -1, -1), s1.expand(reps, -1), 0, reps,
+                                                          stream, moe.MOE_PATH_PREFILL)
+    yc = moe.moe_combine(partial, shared_out, out[2], out[3])
+    torch.cuda.synchronize()
+    assert torch.equal(yc, out[0]), "FFN-only replay differs from the layer"
+    ffn_tf = flops / (ffn_ms * 1e-3) / 1e12
+    ceil = measure_ceilings(c, mfma=True)
     metric, data, wdt = labels(cfg)
     return {"metric": metric, "value": round(T * 1000.0 / ms_call, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": reps, "warmup": 2, "ms_per_step": round(ms_call, 4), "higher_is_better": True,
@@ -437,7 +644,16 @@ def run_prefill(c, name, reps):
                        "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "bits": cfg.bits},
             "expert_gflop": round(flops / 1e9, 1), "router_gflop": round(router_flops / 1e9, 2),
             "layer_expert_TFLOPs": round(tf, 1), "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-            "max_bucket": int(counts.max())}
+            "max_bucket": int(counts.max()),
+            "roofline": {"bound": "mfma",
+                         "kernel": "expert FFN replayed with the routing given: " + ffn_kernels,
+                         "achieved": round(ffn_tf, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ffn_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": ffn_traffic(name),
+                         "avg_us": round(ffn_ms * 1e3, 3), "flops_per_launch": flops,
+                         "measured_peak": ceil["mfma_f16_TFLOPs"],
+                         "measured_peak_what": "loop of dense v_mfma_f32_32x32x16_f16 on register operands",
+                         "frac_of_measured": round(ffn_tf / ceil["mfma_f16_TFLOPs"], 4)},
+            "ceilings": ceil}
 
 
 def run_chain(c, K, W, L=48):
@@ -518,7 +734,7 @@ def main():
     ap.add_argument("--workload", default="decode80b",
                     choices=["decode80b", "decode35b", "refill80b", "stream80b", "batch80b", "prefill80b",
                              "prefill80b_zipf", "decode80b_int8", "batch80b_int8", "prefill80b_int8",
-                             "decode80b_f32", "batch80b_f32", "chain80b", "all", "refill_sweep"])
+                             "decode80b_f32", "batch80b_f32", "chain80b", "all", "refill_sweep", "ceiling"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
@@ -534,15 +750,28 @@ def main():
             "decode80b_int8", "batch80b_int8", "prefill80b_int8", "decode80b_f32", "batch80b_f32",
             "chain80b"] \
         if args.workload == "all" else [args.workload]
+    ms = c.ms
     for wl in todo:
+        if wl == "ceiling":
+            res = {"metric": "measured ceilings of this MI355X", "n_gpus": 1,
+                   "ceilings": measure_ceilings(c, read_bytes=(19464192, 23666688, 605 << 20),
+                                                three=(4202496, 12976128, 6488064), mfma=True),
+                   "spec": {"hbm_GBps": HBM_PEAK_GBS, "mfma_f16_TFLOPs": MFMA_F16_PEAK_TFLOPS}}
+            print(json.dumps(res), flush=True)
+            continue
         if wl in ("decode80b", "decode35b", "decode80b_int8", "decode80b_f32"):
             # f32 blobs are 12.6 MB: 4 replicas already keep a step's 138 MB
             # out of the 256 MB last-level cache until its next use
             reps = min(args.replicas, 4) if wl.endswith("f32") else args.replicas
-            res = run_decode(c, wl, args.steps, args.warmup, reps,
-                             cpu if wl == "decode80b" else 0, args.eager)
+            # oracle sample: ~10 s of CPU (wider experts take longer per step)
+            csteps = 0 if cpu == 0 else (cpu if wl in ("decode80b", "decode35b")
+                                         else max(1, cpu // 2) if wl.endswith("int8") else max(1, cpu // 4))
+            res = run_decode(c, wl, args.steps, args.warmup, reps, csteps, args.eager)
         elif wl in ("refill80b", "stream80b"):
             res = run_refill(c, min(args.steps, 300), min(args.warmup, 50), streamed=wl == "stream80b")
+            if cpu:
+                log("timing the CPU oracle")
+                res["cpu_baseline"] = cpu_baseline(c, ms.CONFIGS["decode80b"], steps=cpu)
         elif wl == "refill_sweep":
             # hit rate and tokens/s against the pool size (the pages report that
             # pool size barely changes speed on their SSD-backed machine), the
@@ -556,10 +785,21 @@ def main():
             continue
         elif wl == "chain80b":
             res = run_chain(c, min(args.steps, 50), min(args.warmup, 5))
+            if cpu:
+                log("timing the CPU oracle")
+                base = ms.scaled(ms.CONFIGS["decode80b"], n_slots=512)
+                res["cpu_baseline"] = chain_cpu_baseline(c, [ms.scaled(base, seed=base.seed + 97 * l)
+                                                            for l in range(48)], base)
         elif wl in ("batch80b", "batch80b_int8", "batch80b_f32"):
             res = run_batched(c, min(args.steps, 100), min(args.warmup, 10), min(args.replicas, 4), wl)
+            if cpu:
+                log("timing the CPU oracle")
+                res["cpu_baseline"] = cpu_baseline(c, ms.CONFIGS[wl], steps=1)
         else:
             res = run_prefill(c, wl, 10)
+            if cpu:
+                log("timing the CPU oracle")
+                res["cpu_baseline"] = cpu_baseline(c, ms.CONFIGS[wl], tokens=64)
         print(json.dumps(res), flush=True)
         c.torch.cuda.empty_cache()
 

@@ -66,7 +66,9 @@ enum {
   MOE_PATH_AUTO = 0,       /* choose by token count (see moe_expert_ffn)      */
   MOE_PATH_DECODE = 1,     /* per-(token, rank) GEMV, fused combine (T <= 8)  */
   MOE_PATH_BATCHED = 2,    /* bucketed GEMV, partials + combine               */
-  MOE_PATH_PREFILL = 3     /* bucketed fp16 MFMA grouped GEMM + combine       */
+  MOE_PATH_PREFILL = 3,    /* bucketed fp16 MFMA grouped GEMM + combine       */
+  MOE_PATH_PREFILL_TILED = 4,  /* PREFILL with the tiled GEMMs forced         */
+  MOE_PATH_PREFILL_STREAM = 5  /* PREFILL with the weight-streaming GEMMs forced */
 };
 
 /* Expert FFN shape.  group must be 64; d and I multiples of 64. */
@@ -276,7 +278,16 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
  *                     to fp16 (one rounding of s*q + b), activations and the
  *                     SwiGLU intermediate in fp16 (|v| <= 65504, else the
  *                     pool error word reports MOE_ERR_UNSUPPORTED), fp32
- *                     accumulate.
+ *                     accumulate.  Two sets of kernels, same arithmetic in
+ *                     the same order (so the same bits): tiled (buckets in
+ *                     chunks of up to 128 tokens, activations and weights
+ *                     staged through LDS step by step) for many tokens per
+ *                     expert, and weight-streaming (chunks of up to 16
+ *                     tokens whose activations stay in LDS while the weights
+ *                     stream from HBM) for a few; PREFILL picks streaming
+ *                     when T*k <= 4*E and d <= 4096, and
+ *                     MOE_PATH_PREFILL_TILED / _STREAM force one (STREAM
+ *                     needs d <= 4096, else MOE_ERR_UNSUPPORTED).
  *   MOE_PATH_AUTO   : DECODE for T <= 8 (and T*(k+1) <= 2048), else PREFILL,
  *                     or BATCHED if d is not a multiple of 128 or the
  *                     experts are f32 (the caller must then supply every

@@ -33,6 +33,8 @@ MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
 MOE_PATH_BATCHED = 2
 MOE_PATH_PREFILL = 3
+MOE_PATH_PREFILL_TILED = 4
+MOE_PATH_PREFILL_STREAM = 5
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -111,6 +113,9 @@ _SIGS = {
     "moe_layer_forward": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
     "moe_layer_forward_noalloc": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_layer_forward_streamed": (C.c_int, [_P, _P, _S, _P, _I, _P, _P, _P, _P, _P, _S, _P, _P, _P]),
+    "moe_probe_stream_read": (C.c_int, [_P, _S, _P, _I, _P]),
+    "moe_probe_mfma_f16": (C.c_int, [_I, _P, _I, _P]),
+    "moe_probe_mfma_f16_flops": (C.c_double, [_I, _I]),
     "moe_chain_workspace_bytes": (_S, [_P, _I, _I, _I]),
     "moe_chain_forward": (C.c_int, [_P, _I, C.c_float, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
 }
@@ -435,7 +440,8 @@ def moe_expert_ffn_int4(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, 
 def moe_expert_ffn(pool: Pool, shared_blob, Ish: int, x, topk_idx, topk_w, shared_gate,
                    path: int = MOE_PATH_DECODE, offsets=None, pair_ids=None,
                    workspace=None, out=None, stream=None, shared_bits: Optional[int] = None):
-    """DECODE: returns y [T, d].  BATCHED/PREFILL: returns (partial [T*k, d], shared_out [T, d]).
+    """DECODE: returns y [T, d] (out: y).  BATCHED/PREFILL: returns (partial [T*k, d], shared_out [T, d])
+    (out: that pair).
     The routed experts' code width is the pool's; the shared expert's is shared_bits (default: the same)."""
     return _expert_ffn(_lib.moe_expert_ffn, pool, shared_blob, Ish, x, topk_idx, topk_w, shared_gate,
                        path, offsets, pair_ids, workspace, out, stream,
@@ -452,6 +458,8 @@ def _expert_ffn(fn, pool, shared_blob, Ish, x, topk_idx, topk_w, shared_gate, pa
     y = partial = shared_out = None
     if path == MOE_PATH_DECODE:
         y = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    elif out is not None:
+        partial, shared_out = out
     else:
         partial = torch.empty((T * k, d), dtype=torch.float32, device=x.device)
         shared_out = torch.empty((T, d), dtype=torch.float32, device=x.device)
@@ -597,3 +605,16 @@ def moe_chain_forward(chain: Chain, x, path: int = MOE_PATH_AUTO, trace: bool = 
                                 _ptr(ti), path, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "moe_chain_forward")
     return (x_out, tx, tu, ti) if trace else x_out
+
+
+# --------------------------------------------------------- measurement probes
+def moe_probe_stream_read(buf, sink, blocks: int = 2048, stream=None):
+    """One launch reading every byte of the CUDA tensor buf (16-byte multiple)."""
+    _check(_lib.moe_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), blocks,
+                                      _stream(stream)), "moe_probe_stream_read")
+
+
+def moe_probe_mfma_f16(iters: int, sink, blocks: int, stream=None) -> float:
+    """A loop of dense fp16 MFMAs; returns the flops of the launch."""
+    _check(_lib.moe_probe_mfma_f16(iters, sink.data_ptr(), blocks, _stream(stream)), "moe_probe_mfma_f16")
+    return float(_lib.moe_probe_mfma_f16_flops(iters, blocks))

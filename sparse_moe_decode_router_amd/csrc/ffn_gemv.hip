@@ -1614,7 +1614,7 @@ bool prefill_fits(int T, int d, int k, int Imax) {
 }
 
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path) {
-  if (path == MOE_PATH_PREFILL)
+  if (is_mfma_path(path))
     return prefill_fits(T, d, k, I > Ish ? I : Ish) ? prefill_ws_bytes(d, I, Ish, T, k, E) : 0;
   Carver c(nullptr, (size_t)-1);
   FfnWs w;
@@ -1665,10 +1665,11 @@ int f32_launch(const FfnArgs& f, int path, GateUpArgs& g, DownArgs& dn, const Ff
 int ffn_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_t s) {
   // one code width for routed and shared experts (4-bit, 8-bit or f32)
   if (f.bits != f.bits_sh || (f.bits != 4 && f.bits != 8 && f.bits != 32)) return MOE_ERR_UNSUPPORTED;
-  if (path == MOE_PATH_PREFILL) {
+  if (is_mfma_path(path)) {
     if (f.bits == 32) return MOE_ERR_UNSUPPORTED;   // f32 experts: decode and bucketed GEMVs
-    return prefill_launch(f, ws, ws_bytes, s);
+    return prefill_launch(f, path, ws, ws_bytes, s);
   }
+  if (path != MOE_PATH_DECODE && path != MOE_PATH_BATCHED) return MOE_ERR_INVALID_ARG;
   const int Imax = f.I > f.Ish ? f.I : f.Ish;
   Carver c(ws, ws_bytes);
   FfnWs w;

@@ -44,6 +44,7 @@ struct PrefillArgs {
   PoolView pool;
   const uint8_t* shared_blob;
   int d, I, Ish, Imax, T, k;
+  const uint16_t* x;            // bf16 x [T][d] (the streaming kernels convert it themselves)
   const uint16_t* xh;           // fp16 x [T][d], k order permuted per 8
   const PInst* inst;
   const int32_t* n_routed;
@@ -80,6 +81,19 @@ __device__ __forceinline__ uint4 dequant8_b(uint32_t wa, uint32_t wb, half2_t s2
     o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// h = silu(g) u = g / (1 + e^-g) * u, rounded to fp32 (the caller then
+// rounds it to fp16).  The empty asm pins the fp32 value: without it the
+// compiler may fold the last multiply into the fp16 conversion
+// (v_fma_mixlo_f16, one rounding straight to fp16) in one kernel and not in
+// another, and the two roundings differ for values next to an fp16 midpoint
+// (about one h in 10^4); the tiled and streaming kernels must agree bit for
+// bit.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  float h = __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
+  asm volatile("" : "+v"(h));
+  return h;
 }
 
 __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool routed, const uint8_t** blob,
@@ -461,7 +475,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int r = 32 * mt + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
           if (r < in.n) {
             const float g = acc[mt][i], u = xch[wave & 1][i][lane];
-            const float h = missing ? 0.f : g / (1.0f + expf(-g)) * u;
+            const float h = missing ? 0.f : swiglu(g, u);
             ovf |= !(fabsf(h) <= 65504.0f);
             a.hh[(size_t)hrow_s[r] * a.Imax + po] = __builtin_bit_cast(uint16_t, (_Float16)h);
           }
@@ -552,6 +566,309 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming grouped GEMMs for buckets of a few tokens (batched decode: 64
+// tokens over 512 experts is 1-10 tokens per bucket).  There the weights are
+// read once per bucket and the step is bound by how many weight bytes are in
+// flight, not by the matrix cores, so the activation side stays put and the
+// weights stream:
+//   * a chunk holds at most kSC tokens; its activation rows (gate/up: x in
+//     fp16, converted from bf16 here; down: the chunk's h rows) sit in LDS for
+//     the whole k range, loaded once per work item;
+//   * every wave owns 32 weight rows (gate/up: the same 32 rows of both
+//     matrices, so SwiGLU happens in registers) and streams their codes and
+//     (scale, bias) words straight into registers through the buffer unit,
+//     kSP steps of 64 inputs ahead, with no block barrier in the k loop;
+//   * the MFMA tiles are the tiled path's (v_mfma_f32_32x32x16_f16, tokens
+//     as the 32 rows of A, of which the first n are live; rows past the chunk
+//     read chunk rows again and are never stored), with the same dequantised
+//     fp16 weights and k order, and h / partial outputs in the same layouts.
+constexpr int kSC = 16;                         // tokens per chunk on the streaming path
+constexpr int kSP = 4;                          // steps of codes in flight per wave
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One k step (64 inputs) of a wave's NM matrices: this lane's code pieces and
+// its row's (scale, bias) word.
+template <int BITS, int NM>
+struct SStep {
+  u32x4 c[NM][BITS / 4];
+  uint32_t sb[NM];
+};
+
+// Loads of step s (zeros through the zero-size descriptor past the end).
+template <int BITS, int NM>
+__device__ __forceinline__ void sstep_load(SStep<BITS, NM>& st, int s, bool live, rsrc_t rB, rsrc_t rN,
+                                           const uint32_t (&b_vo)[BITS / 4], uint32_t s_vo,
+                                           const uint32_t (&co)[NM], const uint32_t (&so)[NM], uint32_t rows) {
+  constexpr int ND = BITS / 4;
+  const rsrc_t r = live ? rB : rN;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const uint32_t cs = __builtin_amdgcn_readfirstlane(co[m] + (uint32_t)(2 * ND) * (uint32_t)s * rows * 16);
+    const uint32_t ss = __builtin_amdgcn_readfirstlane(so[m] + (uint32_t)s * rows * 4);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) st.c[m][j] = __builtin_amdgcn_raw_buffer_load_b128(r, b_vo[j], cs, 0);
+    st.sb[m] = __builtin_amdgcn_raw_buffer_load_b32(r, s_vo, ss, 0);
+  }
+}
+
+// Dequantise step st's matrices and multiply them into acc against the four
+// 8-input A pieces of this lane's row (arow: the row's fp16 values at the
+// step's first input, k order permuted per 8).
+template <int BITS, int NM>
+__device__ __forceinline__ void sstep_mma(const SStep<BITS, NM>& st, const uint16_t* arow, int h,
+                                          float16_t (&acc)[NM]) {
+  half8_t av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const half8_t*>(arow + 32 * h + 8 * j);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const uint32_t sb = st.sb[m];
+    const half2_t s2 = __builtin_bit_cast(half2_t, (sb & 0xFFFFu) * 0x10001u);
+    const half2_t b2 = __builtin_bit_cast(half2_t, (sb >> 16) * 0x10001u);
+    half8_t bv[4];
+    if constexpr (BITS == 4) {
+      const u32x4 cw = st.c[m][0];
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+    } else {
+      const u32x4 c0 = st.c[m][0], c1 = st.c[m][1];
+      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[j], acc[m], 0, 0, 0);
+  }
+}
+
+// The k loop of one wave: C steps, a ring of kSP steps in flight.  live:
+// whether the wave's 32 rows exist (a tile's last wave may be past the
+// matrix); a dead wave loads zeros and its results are not stored.
+template <int BITS, int NM>
+__device__ __forceinline__ void stream_loop(const uint16_t* arow, rsrc_t rB, bool live, const uint32_t (&co)[NM],
+                                            const uint32_t (&so)[NM], uint32_t rows, uint32_t row, int C,
+                                            float16_t (&acc)[NM]) {
+  constexpr int ND = BITS / 4;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  uint32_t b_vo[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) b_vo[j] = ((ND * h + j) * rows + row) * 16;
+  const uint32_t s_vo = row * 4;
+  const rsrc_t rN = make_rsrc(nullptr, 0);
+  SStep<BITS, NM> ring[kSP];
+#pragma unroll
+  for (int p = 0; p < kSP; ++p) sstep_load<BITS, NM>(ring[p], p, live && p < C, rB, rN, b_vo, s_vo, co, so, rows);
+  for (int s0 = 0; s0 < C; s0 += kSP) {
+#pragma unroll
+    for (int p = 0; p < kSP; ++p) {
+      const int s = s0 + p;
+      if (s < C) {
+        const SStep<BITS, NM> cur = ring[p];
+        sstep_load<BITS, NM>(ring[p], s + kSP, live && s + kSP < C, rB, rN, b_vo, s_vo, co, so, rows);
+        sstep_mma<BITS, NM>(cur, arow + 64 * s, h, acc);
+      }
+    }
+  }
+}
+
+// Stage the fp16 rows of a chunk into LDS (row stride ld halfs): gate/up from
+// bf16 x (converted, k order permuted per 8, values beyond fp16 range
+// flagged), down from the fp16 h rows as they are.  All of a thread's loads
+// are issued before its first store.
+template <bool FROM_BF16>
+__device__ __forceinline__ bool stage_rows(const uint16_t* __restrict__ src, size_t src_ld, const int* rows_s, int n,
+                                           int width, uint16_t* dst, int ld) {
+  const int npc = width / 8;
+  const int total = n * npc;
+  bool ovf = false;
+  for (int q0 = threadIdx.x; q0 < total; q0 += 4 * 256) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * 256;
+      const int qq = q < total ? q : 0;             // clamped: unconditional loads
+      v[u] = reinterpret_cast<const uint4*>(src + (size_t)rows_s[qq / npc] * src_ld)[qq % npc];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * 256;
+      if (q >= total) break;
+      uint4 o = v[u];
+      if constexpr (FROM_BF16) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = bf16_lo(w[i]);
+          f[2 * i + 1] = bf16_hi(w[i]);
+        }
+        const int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        uint16_t hv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = f[order[t]];
+          ovf |= !(fabsf(x) <= 65504.0f);
+          hv[t] = __builtin_bit_cast(uint16_t, (_Float16)x);
+        }
+        o = make_uint4(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16),
+                       hv[4] | ((uint32_t)hv[5] << 16), hv[6] | ((uint32_t)hv[7] << 16));
+      }
+      *reinterpret_cast<uint4*>(dst + (q / npc) * ld + 8 * (q % npc)) = o;
+    }
+  }
+  return ovf;
+}
+
+// gate/up: item = (chunk, 128 intermediate rows); wave w takes rows
+// 32 w .. 32 w + 31 of both matrices.  LDS: the chunk's x rows.
+template <int BITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void stream_gate_up_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];   // [kSC][d + 8] fp16
+  __shared__ int tok_s[kSC], hrow_s[kSC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
+  const int ntR = (a.I + 127) / 128, ntS = (a.Ish + 127) / 128;
+  const int nt = ntR > ntS ? ntR : ntS;
+  const int nch = nR + a.n_shared_inst;
+  const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
+  const int ld = a.d + 8;
+  const int C = a.d / kKS;
+  for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
+    int ii, tile;
+    if (!xcd_item(wi, nch, nt, &ii, &tile)) continue;
+    const bool routed = ii < nR;
+    if (tile >= (routed ? ntR : ntS)) continue;
+    const uint8_t* blob;
+    int Iinst;
+    bool missing;
+    resolve_p(a, ii, routed, &blob, &Iinst, &missing);
+    PInst in = a.inst[ii];
+    in.start = __builtin_amdgcn_readfirstlane(in.start);
+    in.n = __builtin_amdgcn_readfirstlane(in.n);
+    if (tid < kSC) {
+      int t = 0, hr = 0;
+      if (tid < in.n) {
+        if (routed) {
+          const int p = a.pair_ids[in.start + tid];
+          t = p / a.k;
+          hr = p;
+        } else {
+          t = in.start + tid;
+          hr = a.T * a.k + t;
+        }
+      }
+      tok_s[tid] = t;
+      hrow_s[tid] = hr;
+    }
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
+    const int o = tile * 128 + 32 * wave + (lane & 31);
+    const bool live = !missing && tile * 128 + 32 * wave < Iinst;
+    const uint32_t co[2] = {(uint32_t)L.m[0].codes, (uint32_t)L.m[1].codes};
+    const uint32_t so[2] = {(uint32_t)L.m[0].sb, (uint32_t)L.m[1].sb};
+    __syncthreads();                            // tok_s; and every wave is past the previous item's LDS reads
+    bool ovf = stage_rows<true>(a.x, (size_t)a.d, tok_s, in.n, a.d, xl, ld);
+    __syncthreads();
+    float16_t acc[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
+    const uint16_t* arow = xl + ((lane & 31) % in.n) * ld;
+    stream_loop<BITS, 2>(arow, make_rsrc(blob, (uint32_t)L.bytes), live, co, so, (uint32_t)Iinst,
+                         (uint32_t)(live ? o : 0), C, acc);
+    if (live) {
+      const int po = (o & ~7) | (2 * (o & 3) + ((o >> 2) & 1));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {              // token rows 0..15 of the tile
+        const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (r < in.n) {
+          const float g = acc[0][i], u = acc[1][i];
+          const float hv = swiglu(g, u);
+          ovf |= !(fabsf(hv) <= 65504.0f);
+          a.hh[(size_t)hrow_s[r] * a.Imax + po] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+        }
+      }
+    } else if (missing && tile * 128 + 32 * wave < Iinst) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        const int po = (o & ~7) | (2 * (o & 3) + ((o >> 2) & 1));
+        if (r < in.n) a.hh[(size_t)hrow_s[r] * a.Imax + po] = 0;
+      }
+    }
+    if (ovf) atomicOr(a.pool.err, 2);
+    if (missing && tid == 0) atomicOr(a.pool.err, 1);
+  }
+}
+
+// down: item = (chunk, 128 output rows); wave w takes rows 32 w .. 32 w + 31.
+// LDS: the chunk's h rows.
+template <int BITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void stream_down_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t hl[];   // [kSC][Imax + 8] fp16
+  __shared__ int hrow_s[kSC], tok_s[kSC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
+  const int nt = (a.d + 127) / 128;
+  const int nch = nR + a.n_shared_inst;
+  const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
+  const int ld = a.Imax + 8;
+  for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
+    int ii, tile;
+    if (!xcd_item(wi, nch, nt, &ii, &tile)) continue;
+    const bool routed = ii < nR;
+    const uint8_t* blob;
+    int Iinst;
+    bool missing;
+    resolve_p(a, ii, routed, &blob, &Iinst, &missing);
+    PInst in = a.inst[ii];
+    in.start = __builtin_amdgcn_readfirstlane(in.start);
+    in.n = __builtin_amdgcn_readfirstlane(in.n);
+    if (tid < kSC) {
+      int t = 0, hr = 0;
+      if (tid < in.n) {
+        if (routed) {
+          hr = a.pair_ids[in.start + tid];
+        } else {
+          t = in.start + tid;
+          hr = a.T * a.k + t;
+        }
+      }
+      hrow_s[tid] = hr;
+      tok_s[tid] = t;
+    }
+    const BlobLayout L = blob_layout(a.d, Iinst, BITS);
+    const int n = tile * 128 + 32 * wave + (lane & 31);
+    const bool live = !missing && tile * 128 + 32 * wave < a.d;
+    const uint32_t co[1] = {(uint32_t)L.m[2].codes};
+    const uint32_t so[1] = {(uint32_t)L.m[2].sb};
+    __syncthreads();
+    stage_rows<false>(a.hh, (size_t)a.Imax, hrow_s, in.n, Iinst, hl, ld);
+    __syncthreads();
+    float16_t acc[1];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
+    const uint16_t* arow = hl + ((lane & 31) % in.n) * ld;
+    stream_loop<BITS, 1>(arow, make_rsrc(blob, (uint32_t)L.bytes), live, co, so, (uint32_t)a.d,
+                         (uint32_t)(live ? n : 0), Iinst / kKS, acc);
+    if (tile * 128 + 32 * wave < a.d) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (r < in.n) {
+          const float v = live ? acc[0][i] : 0.f;
+          if (routed) a.partial[(size_t)hrow_s[r] * a.d + n] = v;
+          else a.shared_out[(size_t)tok_s[r] * a.d + n] = v;
+        }
+      }
+    }
+  }
+}
+
 // x (bf16) -> fp16 with the k order permuted per 8 columns; flags values
 // outside the fp16 range.
 __global__ __launch_bounds__(256) void prefill_xprep_kernel(const uint16_t* __restrict__ x, long n8,
@@ -584,14 +901,16 @@ __global__ __launch_bounds__(256) void prefill_xprep_kernel(const uint16_t* __re
   if (ovf) atomicOr(err, 2);
 }
 
-// Bucket chunks of up to kPM tokens per expert, in expert order, then the
-// shared expert's chunks.  One block.
+// Bucket chunks of up to csz tokens per expert (kPM on the tiled path, kSC
+// on the streaming path), in expert order, then the shared expert's chunks.
+// One block.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t* __restrict__ offsets, int E, int T,
-                                                            PInst* __restrict__ inst, int32_t* __restrict__ n_routed) {
+                                                            int csz, PInst* __restrict__ inst,
+                                                            int32_t* __restrict__ n_routed) {
   __shared__ int sums[1024];
   const int tid = threadIdx.x;
   const int c = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
-  const int nch = (c + kPM - 1) / kPM;
+  const int nch = (c + csz - 1) / csz;
   sums[tid] = nch;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -604,18 +923,18 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t* __res
   for (int q = 0; q < nch; ++q) {
     PInst in;
     in.expert = tid;
-    in.start = offsets[tid] + q * kPM;
-    in.n = min(kPM, c - q * kPM);
+    in.start = offsets[tid] + q * csz;
+    in.n = min(csz, c - q * csz);
     inst[base + q] = in;
   }
   const int total = sums[1023];
   if (tid == 0) *n_routed = total;
-  const int nsh = (T + kPM - 1) / kPM;
+  const int nsh = (T + csz - 1) / csz;
   for (int q = tid; q < nsh; q += 1024) {
     PInst in;
     in.expert = -1;
-    in.start = q * kPM;
-    in.n = min(kPM, T - q * kPM);
+    in.start = q * csz;
+    in.n = min(csz, T - q * csz);
     inst[total + q] = in;
   }
 }
@@ -627,7 +946,7 @@ struct PrefillWs {
 bool carve_prefill(Carver& c, int d, int Imax, int T, int k, int E, PrefillWs* w) {
   w->xh = c.take<uint16_t>((size_t)T * d);
   w->hh = c.take<uint16_t>(((size_t)T * k + T) * Imax);
-  w->inst = c.take<PInst>((size_t)((long)T * k + E) / 1 + (T + kPM - 1) / kPM + 1);
+  w->inst = c.take<PInst>((size_t)((long)T * k + E) + (T + kSC - 1) / kSC + 1);   // chunks on either path
   w->n_routed = c.take<int32_t>(64);
   return c.ok();
 }
@@ -641,34 +960,54 @@ size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E) {
   return c.off + 256;
 }
 
-int prefill_launch(const FfnArgs& f, void* ws, size_t ws_bytes, hipStream_t s) {
+int prefill_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStream_t s) {
   const int Imax = f.I > f.Ish ? f.I : f.Ish;
   if (!prefill_fits(f.T, f.d, f.k, Imax)) return MOE_ERR_UNSUPPORTED;
+  if (f.d % 128 != 0) return MOE_ERR_UNSUPPORTED;
   Carver c(ws, ws_bytes);
   PrefillWs w;
   if (!carve_prefill(c, f.d, Imax, f.T, f.k, f.pool.E, &w)) return MOE_ERR_INVALID_ARG;
   if (!f.offsets || !f.pair_ids || !f.partial || !f.shared_out) return MOE_ERR_INVALID_ARG;
-  const long n8 = (long)f.T * f.d / 8;
-  prefill_xprep_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(f.x, n8, w.xh, f.pool.err);
-  MOE_HIP(hipGetLastError());
-  prefill_plan_kernel<<<1, 1024, 0, s>>>(f.offsets, f.pool.E, f.T, w.inst, w.n_routed);
+  // streaming GEMMs for a few tokens per expert (their activation rows stay
+  // in LDS: kSC rows of d fp16 values must fit beside a second block)
+  const bool stream_fits = f.d <= 4096;
+  if (path == MOE_PATH_PREFILL_STREAM && !stream_fits) return MOE_ERR_UNSUPPORTED;
+  const bool stream = path == MOE_PATH_PREFILL_STREAM ||
+                      (path == MOE_PATH_PREFILL && stream_fits && (long)f.T * f.k <= 4L * f.pool.E);
+  const int csz = stream ? kSC : kPM;
+  if (!stream) {
+    const long n8 = (long)f.T * f.d / 8;
+    prefill_xprep_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(f.x, n8, w.xh, f.pool.err);
+    MOE_HIP(hipGetLastError());
+  }
+  prefill_plan_kernel<<<1, 1024, 0, s>>>(f.offsets, f.pool.E, f.T, csz, w.inst, w.n_routed);
   MOE_HIP(hipGetLastError());
   PrefillArgs a{};
   a.pool = f.pool; a.shared_blob = f.shared_blob;
   a.d = f.d; a.I = f.I; a.Ish = f.Ish; a.Imax = Imax; a.T = f.T; a.k = f.k;
-  a.xh = w.xh; a.inst = w.inst; a.n_routed = w.n_routed;
-  a.n_shared_inst = (f.T + kPM - 1) / kPM;
+  a.x = f.x; a.xh = w.xh; a.inst = w.inst; a.n_routed = w.n_routed;
+  a.n_shared_inst = (f.T + csz - 1) / csz;
   a.pair_ids = f.pair_ids;
   a.hh = w.hh; a.partial = f.partial; a.shared_out = f.shared_out;
   // upper bounds on the work items; kernels stride over the device count
-  long chunks = ((long)f.T * f.k + kPM - 1) / kPM + f.pool.E + a.n_shared_inst;
+  long chunks = ((long)f.T * f.k + csz - 1) / csz + f.pool.E + a.n_shared_inst;
   chunks = (chunks + kXcd - 1) / kXcd * kXcd;   // grids stay multiples of 8
+  void* args[] = {&a};
+  if (stream) {
+    const long gu_items = chunks * ((Imax + 127) / 128);
+    const long dn_items = chunks * (f.d / 128);
+    const int gu_grid = (int)(gu_items < 8192 ? gu_items : 8192);
+    const int dn_grid = (int)(dn_items < 8192 ? dn_items : 8192);
+    void* gu = f.bits == 8 ? (void*)stream_gate_up_kernel<8> : (void*)stream_gate_up_kernel<4>;
+    void* dn = f.bits == 8 ? (void*)stream_down_kernel<8> : (void*)stream_down_kernel<4>;
+    MOE_HIP(hipLaunchKernel(gu, dim3(gu_grid), dim3(256), args, (size_t)kSC * (f.d + 8) * 2, s));
+    MOE_HIP(hipLaunchKernel(dn, dim3(dn_grid), dim3(256), args, (size_t)kSC * (Imax + 8) * 2, s));
+    return MOE_OK;
+  }
   const long gu_items = chunks * (Imax / 64);
   const long dn_items = chunks * (f.d / 128);
-  if (f.d % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const int gu_grid = (int)(gu_items < 4096 ? gu_items : 4096);
   const int dn_grid = (int)(dn_items < 4096 ? dn_items : 4096);
-  void* args[] = {&a};
   void* gu = f.bits == 8 ? (void*)prefill_gate_up_kernel<8> : (void*)prefill_gate_up_kernel<4>;
   void* dn = f.bits == 8 ? (void*)prefill_down_kernel<8> : (void*)prefill_down_kernel<4>;
   MOE_HIP(hipLaunchKernel(gu, dim3(gu_grid), dim3(256), args, 0, s));

@@ -596,7 +596,7 @@ extern "C" int moe_expert_ffn(const moe_pool* pool, const moe_ffn_shape* sh, con
   a.y = out; a.partial = partial; a.shared_out = shared_out;
   if (path == MOE_PATH_DECODE) {
     MOE_CHECK(T <= 8 && w && sgate && out && (long)T * (k + 1) <= 2048);
-  } else if (path == MOE_PATH_BATCHED || path == MOE_PATH_PREFILL) {
+  } else if (path == MOE_PATH_BATCHED || is_mfma_path(path)) {
     MOE_CHECK(offsets && pair_ids && partial && shared_out);
     MOE_CHECK(aligned(partial, 16) && aligned(shared_out, 16));
   } else {

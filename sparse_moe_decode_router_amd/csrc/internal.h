@@ -161,12 +161,17 @@ struct FfnArgs {
 };
 size_t ffn_ws_bytes(int d, int I, int Ish, int T, int k, int E, int path);
 size_t prefill_ws_bytes(int d, int I, int Ish, int T, int k, int E);
-int prefill_launch(const FfnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+int prefill_launch(const FfnArgs& a, int path, void* ws, size_t ws_bytes, hipStream_t s);
 int ffn_launch(const FfnArgs& a, int path, void* ws, size_t ws_bytes, hipStream_t s);
 int resolve_path(int path, int T, int d, int k, int E, int bits, int Imax);
 // The matrix-core path addresses its activation and intermediate buffers
 // through 32-bit buffer descriptors: T d and (T k + T) Imax fp16 values must
 // stay below 4 GiB.
 bool prefill_fits(int T, int d, int k, int Imax);
+// The matrix-core paths: PREFILL (the library picks tiled or streaming
+// GEMMs), or one of them forced.
+inline bool is_mfma_path(int p) {
+  return p == MOE_PATH_PREFILL || p == MOE_PATH_PREFILL_TILED || p == MOE_PATH_PREFILL_STREAM;
+}
 
 }  // namespace moe

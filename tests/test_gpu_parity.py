@@ -388,3 +388,64 @@ def test_usage_counters_bucketed_paths(l80, path):
         tot += np.bincount(_np(idx).ravel(), minlength=l80.cfg.E)
     _, usage = l80.pool.read_state()
     assert np.array_equal(usage.astype(np.int64), tot)
+
+
+# -------------------------------------------- matrix cores: streaming GEMMs
+# The two grouped-GEMM kernel sets of the matrix-core path (tiled: chunks of
+# up to 128 tokens staged step by step; streaming: chunks of up to 16 tokens
+# whose activations stay in LDS while the weights stream) do the same fp16
+# products in the same order, so they give the same bits; both are checked
+# against the oracle.  Cases: the 80B shape at 64 tokens, 200 Zipf tokens
+# (buckets above 16 tokens split into several chunks), intermediate 1024,
+# E = 1024 with k = 16, intermediate 64 (a half tile), a shared expert wider
+# than the routed ones, and 8-bit codes.
+STREAM = {
+    "80b_T64": (dict(), 64),
+    "80b_T200": (dict(), 200),
+    "wide_I": (dict(d=512, E=32, k=4, I=1024, I_shared=1024, n_slots=32, alpha=0.0), 24),
+    "max_E": (dict(d=512, E=1024, k=16, I=128, I_shared=128, n_slots=1024, alpha=0.0), 24),
+    "half_tile": (dict(d=256, E=16, k=16, I=64, I_shared=64, n_slots=16, alpha=0.0), 24),
+    "shared_wider": (dict(d=512, E=64, k=6, I=64, I_shared=192, n_slots=64, alpha=0.0), 40),
+}
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("name", sorted(STREAM))
+def test_stream_gemms_match_tiled_and_oracle(name, bits):
+    kw, T = STREAM[name]
+    base = ms.CONFIGS["decode80b" if bits == 4 else "decode80b_int8"]
+    cfg = ms.scaled(base, **{"n_slots": 512, **kw})
+    L = DeviceLayer(cfg)
+    _, x = L.x(7, T)
+    ys, i_s, ws_, ss = moe.moe_layer_forward(L.layer, x, path=moe.MOE_PATH_PREFILL_STREAM)
+    yt, it, wt, st = moe.moe_layer_forward(L.layer, x, path=moe.MOE_PATH_PREFILL_TILED)
+    torch.cuda.synchronize()
+    assert L.pool.check_error() == moe.MOE_OK
+    assert torch.equal(i_s, it) and torch.equal(ws_, wt) and torch.equal(ss, st)
+    rows = (ys != yt).any(1).nonzero().flatten().tolist()
+    if rows:
+        idx_np = _np(i_s)
+        xb, _ = L.x(7, T)
+        ref = L.oracle(xb, idx=idx_np)
+        es = np.abs(_np(ys) - ref["y"]).max(1) / np.abs(ref["y"]).max(1)
+        et = np.abs(_np(yt) - ref["y"]).max(1) / np.abs(ref["y"]).max(1)
+        cnt = np.bincount(idx_np.ravel(), minlength=cfg.E)
+        print(f"{name} {bits}-bit: {len(rows)} rows differ, e.g. {rows[:8]}; stream err {es[rows].max():.2e}, "
+              f"tiled err {et[rows].max():.2e}; their buckets {[cnt[idx_np[r]].tolist() for r in rows[:3]]}")
+    assert not rows
+    rel, namb, _, idx = _check_layer_step(L, 7, path=moe.MOE_PATH_PREFILL_STREAM, T=T)
+    biggest = np.bincount(idx.ravel(), minlength=cfg.E).max()
+    print(f"stream {name} {bits}-bit T={T}: rel err {rel:.2e}, near-ties {namb}, largest bucket {biggest}")
+
+
+def test_stream_path_is_the_choice_for_few_tokens_per_expert(l80):
+    """MOE_PATH_PREFILL (and AUTO above 8 tokens) take the streaming GEMMs
+    while T k <= 4 E: the same bits as the forced streaming path; beyond, the
+    tiled ones."""
+    for T, forced in ((64, moe.MOE_PATH_PREFILL_STREAM), (204, moe.MOE_PATH_PREFILL_STREAM),
+                      (206, moe.MOE_PATH_PREFILL_TILED)):
+        _, x = l80.x(50 + T, T)
+        ya, _, _, _ = moe.moe_layer_forward(l80.layer, x, path=moe.MOE_PATH_AUTO)
+        yf, _, _, _ = moe.moe_layer_forward(l80.layer, x, path=forced)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yf), T
