@@ -802,6 +802,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
     if (ovf) atomicOr(a.pool.err, 2);
     if (missing && tid == 0) atomicOr(a.pool.err, 1);
+    // every wave is past this item's reads of tok_s / hrow_s / xl before the
+    // next item rewrites them (a block takes several items when the grid is
+    // smaller than the work)
+    __syncthreads();
   }
 }
 
@@ -866,6 +870,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         }
       }
     }
+    // every wave is past this item's reads of hrow_s / tok_s / hl before the
+    // next item rewrites them
+    __syncthreads();
   }
 }
 
