@@ -155,10 +155,14 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// LDS position of the 16-byte piece `cc` (0..7) of activation row r: pieces
-// are XOR-swizzled by r mod 8 so the MFMA reads (32 rows, one piece) hit 32
-// distinct banks.
-__device__ __forceinline__ int a_pos(int r, int cc) { return r * 128 + 16 * (cc ^ (r & 7)); }
+// LDS position of the 16-byte piece `cc` (0..7) of activation row r (rows
+// of 128 B): pieces are XOR-swizzled by a_swz(r) = (r mod 8) ^ bit 3 of r,
+// so that an MFMA operand read (one piece of consecutive rows) hits distinct
+// banks both in any 8 consecutive rows (one 128-byte bank line) and in any
+// 16 (two rows per 256-byte bank line: plain r mod 8 made rows r and r + 8
+// collide there).
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int a_pos(int r, int cc) { return r * 128 + 16 * (cc ^ a_swz(r)); }
 
 // Grouped-GEMM main loop: C steps of 64 along k.
 //   S0, S1, S2: the stages, kStage bytes each (distinct arrays, used in a
@@ -439,13 +443,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * (4 * wave + i) + (lane >> 3);
       const int t = tok_s[r];
-      a_vo[i] = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ (r & 7));
+      a_vo[i] = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ a_swz(r));
     }
     uint32_t a_vo_n;                            // one-tile chunks: row 8 * wave + lane / 8
     {
       const int r = 8 * wave + (lane >> 3);
       const int t = tok_s[r];
-      a_vo_n = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ (r & 7));
+      a_vo_n = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ a_swz(r));
     }
     float16_t acc[4];
 #pragma unroll
@@ -534,13 +538,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * (4 * wave + i) + (lane >> 3);
       const int hr = hrow_s[r];
-      a_vo[i] = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ (r & 7));
+      a_vo[i] = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ a_swz(r));
     }
     uint32_t a_vo_n;                            // one-tile chunks: row 8 * wave + lane / 8
     {
       const int r = 8 * wave + (lane >> 3);
       const int hr = hrow_s[r];
-      a_vo_n = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ (r & 7));
+      a_vo_n = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ a_swz(r));
     }
     float16_t acc[4];
 #pragma unroll
