@@ -8,10 +8,12 @@
 //
 // Dequantisation: a 4-bit code word's nibbles i and i+4 (an 8-bit word
 // pair's bytes (0,2) and (1,3), which hold inputs i and i+4 of the block)
-// become the fp16 pair (1024+q_i, 1024+q_{i+4}) by OR-ing them into 0x6400
-// (fp16 1024.0 has a mantissa step of 1, exact for q < 1024), a packed
-// subtract gives q exactly, and one packed fma gives s*q + b rounded once to
-// fp16 (11-bit significand: |rel err| <= 2^-11).
+// become an fp16 pair (c+q_i, c+q_{i+4}) by OR-ing them into the mantissa of
+// an fp16 constant c whose mantissa step at that bit position is 1: 0x6400
+// (1024.0, step 1) for codes at bits 0.. of each half, 0x5400 (64.0, step
+// 1/16) for nibbles at bits 4..7, so a word needs one shift (by 8) rather
+// than three.  A packed subtract gives q exactly, and one packed fma gives
+// s*q + b rounded once to fp16 (11-bit significand: |rel err| <= 2^-11).
 // bf16 (8-bit significand) rounding of the weights would spend most of the
 // 2e-3 output tolerance; fp16 keeps it small.  Activations enter as fp16.
 // The k order inside every 8-column block is (0,4,1,5,2,6,3,7) in both
@@ -55,14 +57,32 @@ struct PrefillArgs {
   float* shared_out;            // [T][d]
 };
 
+// The masks and the fp16 constants enter through empty asm statements, so the
+// compiler keeps them in registers and forms each (code & mask) | constant as
+// one v_and_or_b32 (a VOP3 instruction takes no literal operand here; with
+// literals it emits a v_and and a v_or).
+struct DqConst {
+  uint32_t m4lo, m4hi, m8;        // nibble masks at bits 0.. / 4.. of each half; byte mask
+  uint32_t c1024, c64;            // 0x6400 (1024.0), 0x5400 (64.0) in both halves
+};
+__device__ __forceinline__ DqConst dq_const() {
+  DqConst k{0x000F000Fu, 0x00F000F0u, 0x00FF00FFu, 0x64006400u, 0x54005400u};
+  asm("" : "+s"(k.m4lo), "+s"(k.m4hi), "+s"(k.m8));
+  asm("" : "+v"(k.c1024), "+v"(k.c64));
+  return k;
+}
+
 // 8 nibbles -> 8 fp16 weights s*q + b, in (0,4,1,5,2,6,3,7) order.
-__device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t b2) {
+__device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t b2, const DqConst& k) {
   const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const half2_t m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const uint32_t w8 = w >> 8;
+  const uint32_t p[4] = {(w & k.m4lo) | k.c1024, (w & k.m4hi) | k.c64, (w8 & k.m4lo) | k.c1024,
+                         (w8 & k.m4hi) | k.c64};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t p = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-    const half2_t q = __builtin_bit_cast(half2_t, p) + m1024;
+    const half2_t q = __builtin_bit_cast(half2_t, p[i]) + ((i & 1) ? m64 : m1024);
     o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
@@ -70,13 +90,13 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t b2) {
 
 // 8-bit codes of one 8-input block (words wa = inputs (0,1,4,5), wb =
 // inputs (2,3,6,7), a byte each) -> 8 fp16 weights in (0,4,1,5,2,6,3,7) order.
-__device__ __forceinline__ uint4 dequant8_b(uint32_t wa, uint32_t wb, half2_t s2, half2_t b2) {
+__device__ __forceinline__ uint4 dequant8_b(uint32_t wa, uint32_t wb, half2_t s2, half2_t b2, const DqConst& k) {
   const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
   const uint32_t w[2] = {wa, wb};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t p = ((w[i >> 1] >> (8 * (i & 1))) & 0x00FF00FFu) | 0x64006400u;
+    const uint32_t p = ((w[i >> 1] >> (8 * (i & 1))) & k.m8) | k.c1024;
     const half2_t q = __builtin_bit_cast(half2_t, p) + m1024;
     o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
   }
@@ -181,6 +201,7 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
                                           rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
                                           uint32_t row, int C, float16_t* acc) {
   constexpr int ND = kCodeDma<BITS>;            // 16-byte code pieces per lane per step
+  const DqConst dq = dq_const();
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // piece (ND h + j) of the step's 2 ND pieces of this lane's row
@@ -222,17 +243,17 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
     half8_t bv[4];
     if constexpr (BITS == 4) {
       const uint4 cw = *reinterpret_cast<const uint4*>(st + kStA + wave * 1024 + 16 * lane);
-      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2, dq));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2, dq));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2, dq));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2, dq));
     } else {
       const uint4 c0 = *reinterpret_cast<const uint4*>(st + kStA + (2 * wave) * 1024 + 16 * lane);
       const uint4 c1 = *reinterpret_cast<const uint4*>(st + kStA + (2 * wave + 1) * 1024 + 16 * lane);
-      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2));
+      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2, dq));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2, dq));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2, dq));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2, dq));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -281,6 +302,7 @@ __device__ __forceinline__ void gemm_loop_narrow(uint8_t* SM, rsrc_t rA, uint32_
                                                  uint32_t codes_off, uint32_t sb_off, uint32_t rows, uint32_t row,
                                                  int C, float16_t* acc) {
   constexpr int ND = kCodeDma<BITS>;
+  const DqConst dq = dq_const();
   constexpr int kA = 4096, kB = 4096 * ND, kSt = kNarrowStage<BITS>, NS = kNarrowNS<BITS>;
   constexpr int kPer = 2 + ND;                  // DMAs per wave per stage
   static_assert(NS >= 3 && NS <= 7 && (NS - 2) * kPer < 64, "stages in flight");
@@ -333,17 +355,17 @@ __device__ __forceinline__ void gemm_loop_narrow(uint8_t* SM, rsrc_t rA, uint32_
     half8_t bv[4];
     if constexpr (BITS == 4) {
       const uint4 cw = *reinterpret_cast<const uint4*>(st + kA + wave * 1024 + 16 * lane);
-      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2, dq));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2, dq));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2, dq));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2, dq));
     } else {
       const uint4 c0 = *reinterpret_cast<const uint4*>(st + kA + (2 * wave) * 1024 + 16 * lane);
       const uint4 c1 = *reinterpret_cast<const uint4*>(st + kA + (2 * wave + 1) * 1024 + 16 * lane);
-      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2));
+      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2, dq));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2, dq));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2, dq));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2, dq));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -621,7 +643,7 @@ __device__ __forceinline__ void sstep_load(SStep<BITS, NM>& st, int s, bool live
 // step's first input, k order permuted per 8).
 template <int BITS, int NM>
 __device__ __forceinline__ void sstep_mma(const SStep<BITS, NM>& st, const uint16_t* arow, int h,
-                                          float16_t (&acc)[NM]) {
+                                          const DqConst& dq, float16_t (&acc)[NM]) {
   half8_t av[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const half8_t*>(arow + 32 * h + 8 * j);
@@ -633,16 +655,16 @@ __device__ __forceinline__ void sstep_mma(const SStep<BITS, NM>& st, const uint1
     half8_t bv[4];
     if constexpr (BITS == 4) {
       const u32x4 cw = st.c[m][0];
-      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2));
+      bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2, dq));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2, dq));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2, dq));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2, dq));
     } else {
       const u32x4 c0 = st.c[m][0], c1 = st.c[m][1];
-      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2));
-      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2));
-      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2));
-      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2));
+      bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2, dq));
+      bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2, dq));
+      bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2, dq));
+      bv[3] = __builtin_bit_cast(half8_t, dequant8_b(c1.z, c1.w, s2, b2, dq));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[j], acc[m], 0, 0, 0);
@@ -658,6 +680,7 @@ __device__ __forceinline__ void stream_loop(const uint16_t* arow, rsrc_t rB, boo
                                             float16_t (&acc)[NM]) {
   constexpr int ND = BITS / 4;
   const int lane = threadIdx.x & 63, h = lane >> 5;
+  const DqConst dq = dq_const();
   uint32_t b_vo[ND];
 #pragma unroll
   for (int j = 0; j < ND; ++j) b_vo[j] = ((ND * h + j) * rows + row) * 16;
@@ -673,7 +696,7 @@ __device__ __forceinline__ void stream_loop(const uint16_t* arow, rsrc_t rB, boo
       if (s < C) {
         const SStep<BITS, NM> cur = ring[p];
         sstep_load<BITS, NM>(ring[p], s + kSP, live && s + kSP < C, rB, rN, b_vo, s_vo, co, so, rows);
-        sstep_mma<BITS, NM>(cur, arow + 64 * s, h, acc);
+        sstep_mma<BITS, NM>(cur, arow + 64 * s, h, dq, acc);
       }
     }
   }
