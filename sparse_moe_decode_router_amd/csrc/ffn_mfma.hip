@@ -103,15 +103,19 @@ __device__ __forceinline__ uint4 dequant8_b(uint32_t wa, uint32_t wb, half2_t s2
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// h = silu(g) u = g / (1 + e^-g) * u, rounded to fp32 (the caller then
-// rounds it to fp16).  The empty asm pins the fp32 value: without it the
-// compiler may fold the last multiply into the fp16 conversion
-// (v_fma_mixlo_f16, one rounding straight to fp16) in one kernel and not in
-// another, and the two roundings differ for values next to an fp16 midpoint
-// (about one h in 10^4); the tiled and streaming kernels must agree bit for
-// bit.
+// h = silu(g) u = g / (1 + e^-g) * u in fp32 (the caller then rounds it to
+// fp16), from the hardware's base-2 exponential (v_exp_f32 of -g log2 e) and
+// reciprocal (v_rcp_f32), each within about one fp32 ulp: a few ulp in all,
+// far below the fp16 rounding of h (2^-11 relative).  Large |g| goes to the
+// right limits (e^-g -> inf: h -> 0; e^-g -> 0: h -> g u).  The empty asm
+// pins the fp32 value: without it the compiler may fold the last multiply
+// into the fp16 conversion (v_fma_mixlo_f16, one rounding straight to fp16)
+// in one kernel and not in another, and the two roundings differ for values
+// next to an fp16 midpoint (about one h in 10^4); the tiled and streaming
+// kernels must agree bit for bit.
 __device__ __forceinline__ float swiglu(float g, float u) {
-  float h = __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  float h = g * __builtin_amdgcn_rcpf(1.0f + e) * u;
   asm volatile("" : "+v"(h));
   return h;
 }
@@ -414,11 +418,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint8_t* S1 = SM + kStage<BITS>;
   uint8_t* S2 = SM + 2 * kStage<BITS>;
   __shared__ int tok_s[kPM], hrow_s[kPM];
-  // up tiles handed to the gate waves after the GEMM, one m-tile at a time;
-  // they reuse stage 0 (no DMA is in flight and no wave reads the stages
-  // once the GEMM has ended)
-  static_assert(sizeof(float) * 2 * 16 * 64 <= kStage<BITS>, "exchange fits a stage");
-  float (*xch)[16][64] = reinterpret_cast<float (*)[16][64]>(S0);
+  // half tiles swapped between gate and up waves after the GEMM, one m-tile
+  // at a time; they reuse stage 0 (no DMA is in flight and no wave reads the
+  // stages once the GEMM has ended)
+  static_assert(sizeof(float) * 2 * 2 * 8 * 64 <= kStage<BITS>, "exchange fits a stage");
+  float (*xch)[2][8][64] = reinterpret_cast<float (*)[2][8][64]>(S0);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
   const int ntR = a.I / 64, ntS = a.Ish / 64;
@@ -482,29 +486,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t ms = (uint32_t)(mat ? L.m[1].sb : L.m[0].sb);
     gemm_tiles<BITS>(in.n, S0, S1, S2, rX, a_vo, a_vo_n, make_rsrc(blob, (uint32_t)L.bytes), mc, ms, (uint32_t)Iinst,
                      (uint32_t)(o0 + colb + (lane & 31)), C, acc);
-    // epilogue: up waves hand their tiles to the gate waves, one m-tile at a time
+    // epilogue, one m-tile at a time: a gate wave and the up wave with the same
+    // 32 columns swap halves of their tiles through LDS (the gate wave gives
+    // rows i = 8..15 of its accumulators, the up wave rows 0..7), then each
+    // forms h for the half it kept
     const int mt_live = (in.n + 31) >> 5;
+    const int o = o0 + colb + (lane & 31);
+    const int po = (o & ~7) | (2 * (o & 3) + ((o >> 2) & 1));
     bool ovf = false;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= mt_live) break;
-      if (mat == 1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xch[wave & 1][i][lane] = acc[mt][i];
-      }
+      for (int i = 0; i < 8; ++i) xch[mat][wave & 1][i][lane] = mat ? acc[mt][i] : acc[mt][8 + i];
       __syncthreads();
-      if (mat == 0) {
-        const int o = o0 + colb + (lane & 31);
-        const int po = (o & ~7) | (2 * (o & 3) + ((o >> 2) & 1));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * mt + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-          if (r < in.n) {
-            const float g = acc[mt][i], u = xch[wave & 1][i][lane];
-            const float h = missing ? 0.f : swiglu(g, u);
-            ovf |= !(fabsf(h) <= 65504.0f);
-            a.hh[(size_t)hrow_s[r] * a.Imax + po] = __builtin_bit_cast(uint16_t, (_Float16)h);
-          }
+      for (int i = 0; i < 8; ++i) {
+        const int ii = mat ? 8 + i : i;
+        const int r = 32 * mt + (ii >> 2) * 8 + (lane >> 5) * 4 + (ii & 3);
+        if (r < in.n) {
+          const float mine = mat ? acc[mt][8 + i] : acc[mt][i];
+          const float other = xch[1 - mat][wave & 1][i][lane];
+          const float g = mat ? other : mine, u = mat ? mine : other;
+          const float h = missing ? 0.f : swiglu(g, u);
+          ovf |= !(fabsf(h) <= 65504.0f);
+          a.hh[(size_t)hrow_s[r] * a.Imax + po] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
       }
       __syncthreads();
