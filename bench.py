@@ -416,18 +416,64 @@ def run_decode(c, name, K, W, R, cpu_steps, eager=False):
     return out
 
 
+def prefetch_model(moe, trace, E, slots, budgets, lo):
+    """What a prefetcher driven by the usage counts could do on this routing
+    trace (trace[t] = step t's selections): the pool's own LFU + recency
+    policy (moe.Lfu) is replayed over the trace, and before every step t >= lo
+    the `b` non-resident experts with the most selections so far (ties: most
+    recent) are the candidates a prefetcher would copy into idle link time.
+    Reports, per budget b, the fraction of candidates that step t selects and
+    the misses of step t they would have covered.  The evictions such
+    prefetches would force are not charged, so the coverage is an upper bound."""
+    lfu = moe.Lfu(E, slots)
+    resident = np.zeros(E, bool)
+    count = np.zeros(E, np.int64)
+    last = np.full(E, -1, np.int64)
+    picked = {b: 0 for b in budgets}
+    covered = {b: 0 for b in budgets}
+    misses = 0
+    n = 0
+    for t, sel in enumerate(trace):
+        need = np.unique(sel)
+        if t >= lo:
+            miss = set(need[~resident[need]].tolist())
+            misses += len(miss)
+            n += 1
+            nonres = np.flatnonzero(~resident)
+            order = nonres[np.lexsort((-last[nonres], -count[nonres]))]
+            for b in budgets:
+                cand = set(order[:b].tolist())
+                picked[b] += len(cand & set(need.tolist()))
+                covered[b] += len(cand & miss)
+        for e, _, v in lfu.plan(sel):
+            resident[e] = True
+            if v >= 0:
+                resident[v] = False
+        np.add.at(count, sel, 1)
+        last[sel] = t
+    lfu.close()
+    return {"misses_per_step": round(misses / max(1, n), 3),
+            "by_budget": [{"experts_prefetched_per_step": b,
+                           "fraction_selected_next_step": round(picked[b] / max(1, n * b), 4),
+                           "misses_covered_per_step": round(covered[b] / max(1, n), 4)} for b in budgets]}
+
+
 def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     """A pool of n_slots (default 256) over 512 experts, refilled between
     router and experts by LFU + recency from pinned host memory; outputs
     checked bit-identical to an all-resident twin.  streamed: one
     moe_layer_forward_streamed call per step (the misses copy in on a second
     stream while the resident experts compute) instead of router -> refill
-    -> experts in sequence."""
+    -> experts in sequence.  The serial run adds X steps after the timed ones
+    with events around each refill (the pull kernel and the slot-table edit)
+    for the link's busy time, and models a usage-count prefetcher on the
+    step's routing trace (prefetch_model)."""
     torch, ms, moe = c.torch, c.ms, c.moe
     cfg = ms.CONFIGS["decode80b"]
     if n_slots is not None:
         cfg = ms.scaled(cfg, n_slots=n_slots)
-    nsteps = K + W
+    X = 0 if streamed else 50
+    nsteps = K + W + X
     log(f"refill80b: {cfg.n_slots} slots over {cfg.E} experts, steps={nsteps}")
     if host is None:
         host = packed_experts(c, cfg, pinned=True)
@@ -447,16 +493,22 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     wsl = torch.zeros(part.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
     copy_stream = torch.cuda.Stream()
 
-    def step(i):
+    def step(i, ev=None):
         if streamed:
             moe.moe_layer_forward_streamed(part, xall[i], host, copy_stream=copy_stream, workspace=wsl,
                                            out=(y[i], idx[i], w[i], s[i]))
             return
         moe.moe_router_topk(xall[i], twin.w_router, twin.logit_bias, cfg.k, workspace=wsr,
                             out=(idx[i], w[i], s[i]))
+        if ev:
+            ev[2].record()
         idx_host.copy_(idx[i, 0], non_blocking=True)
         torch.cuda.current_stream().synchronize()
+        if ev:
+            ev[0].record()
         pool.refill(idx_host.numpy(), host, stride)
+        if ev:
+            ev[1].record()
         moe.moe_expert_ffn_int4(pool, twin.shared_blob, cfg.I_shared, xall[i], idx[i], w[i], s[i],
                                 workspace=wsf, out=y[i])
 
@@ -465,11 +517,16 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     torch.cuda.synchronize()
     st0 = pool.stats()
     t0 = time.perf_counter()
-    for i in range(W, nsteps):
+    for i in range(W, W + K):
         step(i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     st1 = pool.stats()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(X)]
+    for i in range(W + K, nsteps):
+        step(i, evs[i - W - K])
+    torch.cuda.synchronize()
+    st2 = pool.stats()
     assert pool.check_error() == moe.MOE_OK
     # all-resident twin over the same steps: bit-identical outputs
     wst = torch.zeros(twin.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device="cuda")
@@ -484,6 +541,32 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     assert identical, "refilled pool differs from the all-resident layer"
     hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
     ms_step = dt * 1e3 / K
+    link = {}
+    if X:
+        # the link: busy while the pull kernel reads the missing blobs from
+        # pinned host memory; idle for the rest of the step
+        pull_us = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e3
+        # router done -> refill enqueued: selections to the host, the host's
+        # wake-up and plan, and the submission of the pull
+        host_us = float(np.mean([r.elapsed_time(a) for a, _, r in evs])) * 1e3
+        pulled = (st2["bytes_loaded"] - st1["bytes_loaded"]) / X
+        rate = pulled / (pull_us * 1e-6) if pull_us > 0 else 0.0
+        idle_us = max(0.0, ms_step * 1e3 - pull_us)
+        idle_blobs = idle_us * 1e-6 * rate / stride if rate else 0.0
+        blob_us = stride / rate * 1e6 if rate else 0.0
+        model = prefetch_model(moe, idx[:, 0].cpu().numpy(), cfg.E, cfg.n_slots, (1, 2, 4, 8), W)
+        best = max(model["by_budget"], key=lambda r: r["misses_covered_per_step"]
+                   if r["experts_prefetched_per_step"] <= max(1, int(idle_blobs)) else -1)
+        link = {"link": {"pull_us_per_step": round(pull_us, 1), "pull_GBps": round(rate / 1e9, 1),
+                         "host_round_trip_us_per_step": round(host_us, 1),
+                         "busy_frac_of_step": round(pull_us / (ms_step * 1e3), 3),
+                         "idle_us_per_step": round(idle_us, 1), "idle_blobs_per_step": round(idle_blobs, 2),
+                         "us_per_blob": round(blob_us, 1), "steps": X},
+                "usage_prefetch_model": {**model,
+                                         "best_within_idle_link": best,
+                                         "step_us_saved_at_most": round(best["misses_covered_per_step"] * blob_us, 2),
+                                         "perfect_predictor_step_us_saved_at_most":
+                                             round(min(idle_blobs, misses / max(1, K)) * blob_us, 1)}}
     return {"metric": METRIC, "value": round(K / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
             "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
@@ -495,7 +578,7 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
             "hit_rate": round(hits / max(1, hits + misses), 4),
             "hit_rate_all_steps": round(st1["hits"] / max(1, st1["hits"] + st1["misses"]), 4),
             "pcie_bytes_per_step": round((st1["bytes_loaded"] - st0["bytes_loaded"]) / K),
-            "bit_identical_to_all_resident": identical}
+            "bit_identical_to_all_resident": identical, **link}
 
 
 def mfma_kernels(cfg, T):
