@@ -458,13 +458,15 @@ def prefetch_model(moe, trace, E, slots, budgets, lo):
                            "misses_covered_per_step": round(covered[b] / max(1, n), 4)} for b in budgets]}
 
 
-def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
+def run_refill(c, K, W, n_slots=None, host=None, mode="serial"):
     """A pool of n_slots (default 256) over 512 experts, refilled between
     router and experts by LFU + recency from pinned host memory; outputs
-    checked bit-identical to an all-resident twin.  streamed: one
+    checked bit-identical to an all-resident twin.  mode "serial": router ->
+    host plan and refill -> experts in sequence; "streamed": one
     moe_layer_forward_streamed call per step (the misses copy in on a second
-    stream while the resident experts compute) instead of router -> refill
-    -> experts in sequence.  The serial run adds X steps after the timed ones
+    stream while the resident experts compute); "offload": one
+    moe_layer_forward_offload call per step (plan and copy on the GPU, no
+    host wait).  The serial run adds X steps after the timed ones
     with events around each refill (the pull kernel and the slot-table edit)
     for the link's busy time, and models a usage-count prefetcher on the
     step's routing trace (prefetch_model)."""
@@ -472,7 +474,8 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     cfg = ms.CONFIGS["decode80b"]
     if n_slots is not None:
         cfg = ms.scaled(cfg, n_slots=n_slots)
-    X = 0 if streamed else 50
+    streamed, offload = mode == "streamed", mode == "offload"
+    X = 50 if mode == "serial" else 0
     nsteps = K + W + X
     log(f"refill80b: {cfg.n_slots} slots over {cfg.E} experts, steps={nsteps}")
     if host is None:
@@ -494,6 +497,9 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
     copy_stream = torch.cuda.Stream()
 
     def step(i, ev=None):
+        if offload:
+            moe.moe_layer_forward_offload(part, xall[i], host, workspace=wsl, out=(y[i], idx[i], w[i], s[i]))
+            return
         if streamed:
             moe.moe_layer_forward_streamed(part, xall[i], host, copy_stream=copy_stream, workspace=wsl,
                                            out=(y[i], idx[i], w[i], s[i]))
@@ -572,9 +578,12 @@ def run_refill(c, K, W, n_slots=None, host=None, streamed=False):
             "vs_baseline": None, "dtype": "int4 weights, bf16 activations, fp32 accumulate", "data": DATA,
             "config": {"workload": f"80B-shape batch-1 decode, {cfg.n_slots}-slot HBM pool refilled by "
                                    "LFU+recency from pinned host memory (wall clock incl. PCIe and host policy)"
-                                   + (", misses copied on a second stream while the resident experts compute"
-                                      if streamed else ", router -> refill -> experts in sequence"),
-                       "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "slots": cfg.n_slots, "streamed": streamed},
+                                   + {"serial": ", router -> host plan and refill -> experts in sequence",
+                                      "streamed": ", misses copied on a second stream while the resident "
+                                                  "experts compute",
+                                      "offload": ", plan and copy on the GPU (router -> LFU plan kernel -> "
+                                                 "copy kernel -> experts, no host wait)"}[mode],
+                       "T": 1, "d": cfg.d, "E": cfg.E, "k": cfg.k, "slots": cfg.n_slots, "mode": mode},
             "hit_rate": round(hits / max(1, hits + misses), 4),
             "hit_rate_all_steps": round(st1["hits"] / max(1, st1["hits"] + st1["misses"]), 4),
             "pcie_bytes_per_step": round((st1["bytes_loaded"] - st0["bytes_loaded"]) / K),
@@ -815,7 +824,7 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only copy an MB-sized device buffer 5 times (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="decode80b",
-                    choices=["decode80b", "decode35b", "refill80b", "stream80b", "batch80b", "prefill80b",
+                    choices=["decode80b", "decode35b", "refill80b", "stream80b", "offload80b", "batch80b", "prefill80b",
                              "prefill80b_zipf", "decode80b_int8", "batch80b_int8", "prefill80b_int8",
                              "decode80b_f32", "batch80b_f32", "chain80b", "all", "refill_sweep", "ceiling"])
     args = ap.parse_args()
@@ -829,7 +838,7 @@ def main():
     c = Ctx()
     c.torch.cuda.set_device(0)
     cpu = 0 if args.no_cpu else args.cpu_steps
-    todo = ["decode80b", "decode35b", "refill80b", "stream80b", "batch80b", "prefill80b", "prefill80b_zipf",
+    todo = ["decode80b", "decode35b", "refill80b", "stream80b", "offload80b", "batch80b", "prefill80b", "prefill80b_zipf",
             "decode80b_int8", "batch80b_int8", "prefill80b_int8", "decode80b_f32", "batch80b_f32",
             "chain80b"] \
         if args.workload == "all" else [args.workload]
@@ -850,8 +859,9 @@ def main():
             csteps = 0 if cpu == 0 else (cpu if wl in ("decode80b", "decode35b")
                                          else max(1, cpu // 2) if wl.endswith("int8") else max(1, cpu // 4))
             res = run_decode(c, wl, args.steps, args.warmup, reps, csteps, args.eager)
-        elif wl in ("refill80b", "stream80b"):
-            res = run_refill(c, min(args.steps, 300), min(args.warmup, 50), streamed=wl == "stream80b")
+        elif wl in ("refill80b", "stream80b", "offload80b"):
+            res = run_refill(c, min(args.steps, 300), min(args.warmup, 50),
+                             mode={"refill80b": "serial", "stream80b": "streamed", "offload80b": "offload"}[wl])
             if cpu:
                 log("timing the CPU oracle")
                 res["cpu_baseline"] = cpu_baseline(c, ms.CONFIGS["decode80b"], steps=cpu)
@@ -861,8 +871,8 @@ def main():
             # serial and the streamed step for each size
             host = packed_experts(c, c.ms.CONFIGS["decode80b"], pinned=True)
             for slots in (64, 128, 192, 256, 384, 512):
-                for streamed in (False, True):
-                    res = run_refill(c, min(args.steps, 200), min(args.warmup, 50), slots, host, streamed)
+                for mode in ("serial", "streamed", "offload"):
+                    res = run_refill(c, min(args.steps, 200), min(args.warmup, 50), slots, host, mode)
                     print(json.dumps(res), flush=True)
                     c.torch.cuda.empty_cache()
             continue

@@ -409,6 +409,37 @@ int moe_layer_forward_streamed(const moe_layer_desc* L,
                                size_t workspace_bytes, hipStream_t stream,
                                hipStream_t copy_stream, int32_t* n_loads);
 
+/* The same decode step with the refill decided and copied by the GPU, so
+ * that no host wait sits between the router and the experts ("How it works":
+ * experts outside the bounded pool fetched on demand; the pages' streaming
+ * of experts from storage).  On `stream`, in order: router and top-k; the
+ * pool's LFU + recency plan (the rules and decisions of moe_pool_plan, on a
+ * device copy of the pool's policy state, by one wave); the missing blobs
+ * read over PCIe from host_blobs by a copy kernel that takes its work list
+ * from the plan; the experts and the combine.  The calling thread does not
+ * wait, and the outputs are bit-identical to the all-resident decode.
+ *   host_blobs: pinned host memory mapped for the device (hipHostMalloc or
+ *     torch's pin_memory), 16-byte aligned, blob e at host_blobs + e *
+ *     host_stride (host_stride >= the pool's stride, a multiple of 16);
+ *     MOE_ERR_INVALID_ARG if it is not mapped.
+ *   n_loads_dev: device int32 (may be NULL): blobs copied by this step.
+ * T <= 8, 4- or 8-bit experts.  MOE_ERR_UNSUPPORTED when T * k exceeds the
+ * pool's slots (a step could then need more experts than it holds; use
+ * moe_layer_forward_streamed, which reports MOE_ERR_POOL_TOO_SMALL) or when
+ * E or n_slots exceeds 1024.  The pool's policy state then lives on the
+ * device as well: the first call allocates its device copy (and copies the
+ * host state there), later host-side pool calls (moe_pool_plan, refill,
+ * load, set_slot_table, get_stats) first synchronise the device and bring
+ * the host copy up to date.  Offload steps on one pool must be issued in
+ * order on one stream. */
+int moe_layer_forward_offload(const moe_layer_desc* L,
+                              const void* host_blobs, size_t host_stride,
+                              const uint16_t* x_dev, int32_t T, float* y_dev,
+                              int32_t* topk_idx_dev, float* topk_w_dev,
+                              float* shared_gate_dev, void* workspace_dev,
+                              size_t workspace_bytes, int32_t* n_loads_dev,
+                              hipStream_t stream);
+
 /* ------------------------------------------------------------ layer chain
  * L layers applied one after the other to the same T tokens (the pages'
  * models stack dozens of MoE layers per token).  Each is a pre-norm residual

@@ -113,6 +113,7 @@ _SIGS = {
     "moe_layer_forward": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
     "moe_layer_forward_noalloc": (C.c_int, [_P, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_layer_forward_streamed": (C.c_int, [_P, _P, _S, _P, _I, _P, _P, _P, _P, _P, _S, _P, _P, _P]),
+    "moe_layer_forward_offload": (C.c_int, [_P, _P, _S, _P, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
     "moe_probe_stream_read": (C.c_int, [_P, _S, _P, _I, _P]),
     "moe_probe_mfma_f16": (C.c_int, [_I, _P, _I, _P]),
     "moe_probe_mfma_f16_flops": (C.c_double, [_I, _I]),
@@ -570,6 +571,37 @@ def moe_layer_forward_streamed(layer: Layer, x, host_blobs, copy_stream=None, wo
                                          C.byref(nl))
     _check(st, "moe_layer_forward_streamed")
     return y, idx, w, s, int(nl.value)
+
+
+def moe_layer_forward_offload(layer: Layer, x, host_blobs, workspace=None, out=None, n_loads=None, stream=None):
+    """One decode step on a partly resident pool with the refill planned and
+    copied by the GPU (router -> LFU + recency plan -> copy of the missing
+    blobs from host_blobs, pinned uint8 [E, stride], over PCIe -> experts),
+    all on `stream` and without waiting on the host.  n_loads: optional
+    device int32 tensor [1] that receives the blobs copied.  Returns
+    (y, topk_idx, topk_w, shared_gate)."""
+    import torch
+    T, d = x.shape
+    k = layer.k
+    if (host_blobs.dtype != torch.uint8 or host_blobs.dim() != 2 or host_blobs.is_cuda
+            or not host_blobs.is_pinned() or not host_blobs.is_contiguous()):
+        raise ValueError("host_blobs must be a contiguous pinned uint8 host tensor [E, stride]")
+    if n_loads is not None and (n_loads.dtype != torch.int32 or not n_loads.is_cuda or n_loads.numel() < 1):
+        raise ValueError("n_loads must be a device int32 tensor")
+    if out is None:
+        out = (torch.empty((T, d), dtype=torch.float32, device=x.device),
+               torch.empty((T, k), dtype=torch.int32, device=x.device),
+               torch.empty((T, k), dtype=torch.float32, device=x.device),
+               torch.empty((T,), dtype=torch.float32, device=x.device))
+    y, idx, w, s = out
+    if workspace is None:
+        workspace = _ws(layer.workspace_bytes(T, MOE_PATH_DECODE))
+    st = _lib.moe_layer_forward_offload(C.byref(layer.desc), host_blobs.data_ptr(), host_blobs.stride(0),
+                                        _ptr(x), T, _ptr(y), _ptr(idx), _ptr(w), _ptr(s), _ptr(workspace),
+                                        workspace.numel(), _ptr(n_loads) if n_loads is not None else None,
+                                        _stream(stream))
+    _check(st, "moe_layer_forward_offload")
+    return y, idx, w, s
 
 
 # -------------------------------------------------------------- layer chain

@@ -318,7 +318,74 @@ struct moe_pool {
   // selections and two events, made on first use
   int32_t* sel_host = nullptr;  // pinned [8 * 1024]
   hipEvent_t ev_sel = nullptr, ev_gu = nullptr, ev_copy = nullptr;
+  // refills planned on the device (moe_layer_forward_offload): a device copy
+  // of the policy state, made on first use.  One of the two copies is always
+  // current; the other is brought up to date before it is used.
+  DevLfu dev{};
+  void* dev_mem = nullptr;
+  bool dev_valid = false, host_valid = true;
 };
+
+// The host copy of the policy state, current (waits for the device's steps).
+static int lfu_on_host(moe_pool* p) {
+  if (p->host_valid) return MOE_OK;
+  MOE_HIP(hipDeviceSynchronize());
+  moe_lfu& l = p->lfu;
+  uint64_t meta[7];
+  MOE_HIP(hipMemcpy(l.count.data(), p->dev.count, sizeof(uint64_t) * p->E, hipMemcpyDeviceToHost));
+  MOE_HIP(hipMemcpy(l.last.data(), p->dev.last, sizeof(int64_t) * p->E, hipMemcpyDeviceToHost));
+  MOE_HIP(hipMemcpy(l.slot_of.data(), p->dev.slot_of, sizeof(int32_t) * p->E, hipMemcpyDeviceToHost));
+  MOE_HIP(hipMemcpy(l.holder.data(), p->dev.holder, sizeof(int32_t) * p->n_slots, hipMemcpyDeviceToHost));
+  MOE_HIP(hipMemcpy(meta, p->dev.meta, sizeof(meta), hipMemcpyDeviceToHost));
+  l.step = (int64_t)meta[0];
+  l.st.steps = meta[1];
+  l.st.hits = meta[2];
+  l.st.misses = meta[3];
+  l.st.loads = meta[4];
+  l.st.evictions = meta[5];
+  l.st.bytes_loaded = meta[6];
+  p->host_valid = true;
+  return MOE_OK;
+}
+
+// The device copy, current (allocated on first use).
+static int lfu_on_device(moe_pool* p) {
+  const size_t E = (size_t)p->E, S = (size_t)p->n_slots;
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t o_last = up(8 * E), o_slot = o_last + up(8 * E), o_holder = o_slot + up(4 * E),
+               o_meta = o_holder + up(4 * S), o_plan = o_meta + up(8 * 8), total = o_plan + up(4 * (1 + 3 * E));
+  if (!p->dev_mem) {
+    MOE_HIP(hipMalloc(&p->dev_mem, total));
+    uint8_t* b = static_cast<uint8_t*>(p->dev_mem);
+    p->dev.count = reinterpret_cast<uint64_t*>(b);
+    p->dev.last = reinterpret_cast<int64_t*>(b + o_last);
+    p->dev.slot_of = reinterpret_cast<int32_t*>(b + o_slot);
+    p->dev.holder = reinterpret_cast<int32_t*>(b + o_holder);
+    p->dev.meta = reinterpret_cast<uint64_t*>(b + o_meta);
+    p->dev.plan = reinterpret_cast<int32_t*>(b + o_plan);
+    p->dev_valid = false;
+  }
+  if (p->dev_valid) return MOE_OK;
+  MOE_TRY(lfu_on_host(p));
+  const moe_lfu& l = p->lfu;
+  const uint64_t meta[7] = {(uint64_t)l.step, l.st.steps, l.st.hits, l.st.misses,
+                            l.st.loads, l.st.evictions, l.st.bytes_loaded};
+  MOE_HIP(hipDeviceSynchronize());
+  MOE_HIP(hipMemcpy(p->dev.count, l.count.data(), sizeof(uint64_t) * E, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(p->dev.last, l.last.data(), sizeof(int64_t) * E, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(p->dev.slot_of, l.slot_of.data(), sizeof(int32_t) * E, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(p->dev.holder, l.holder.data(), sizeof(int32_t) * S, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(p->dev.meta, meta, sizeof(meta), hipMemcpyHostToDevice));
+  p->dev_valid = true;
+  return MOE_OK;
+}
+
+// A host-side policy call: the host copy first, and the device copy stale after.
+#define LFU_HOST_EDIT(p)        \
+  do {                          \
+    MOE_TRY(lfu_on_host(p));    \
+    (p)->dev_valid = false;     \
+  } while (0)
 
 namespace moe {
 bool pool_view(const moe_pool* p, PoolView* v) {
@@ -376,6 +443,7 @@ extern "C" int moe_pool_destroy(moe_pool* p) {
   if (p->ev_sel) (void)hipEventDestroy(p->ev_sel);
   if (p->ev_gu) (void)hipEventDestroy(p->ev_gu);
   if (p->ev_copy) (void)hipEventDestroy(p->ev_copy);
+  if (p->dev_mem) (void)hipFree(p->dev_mem);
   delete p;
   return MOE_OK;
 }
@@ -407,6 +475,7 @@ static void host_place(moe_lfu* p, int32_t e, int32_t slot, std::vector<int32_t>
 static int load_common(moe_pool* p, int32_t e, int32_t slot, const void* blob, hipMemcpyKind kind,
                        hipStream_t s) {
   if (!p || !blob || e < 0 || e >= p->E || slot < 0 || slot >= p->n_slots) return MOE_ERR_INVALID_ARG;
+  LFU_HOST_EDIT(p);
   MOE_HIP(hipMemcpyAsync(p->slab + (size_t)slot * p->stride, blob, p->stride, kind, s));
   std::vector<int32_t> te, ts;
   host_place(&p->lfu, e, slot, &te, &ts);
@@ -431,6 +500,7 @@ extern "C" int moe_pool_load_device(moe_pool* p, int32_t e, int32_t slot, const 
 extern "C" int moe_pool_plan(moe_pool* p, const int32_t* sel, int32_t n, int32_t* le, int32_t* ls,
                              int32_t* lv, int32_t* n_loads) {
   if (!p) return MOE_ERR_INVALID_ARG;
+  LFU_HOST_EDIT(p);
   return moe_lfu_plan(&p->lfu, sel, n, le, ls, lv, n_loads);
 }
 
@@ -504,6 +574,7 @@ extern "C" int moe_pool_refill(moe_pool* p, const int32_t* sel, int32_t n, const
 extern "C" int moe_pool_set_slot_table(moe_pool* p, const int32_t* table, hipStream_t s) {
   return no_throw([&]() -> int {
     if (!p || !table) return MOE_ERR_INVALID_ARG;
+    LFU_HOST_EDIT(p);
     std::vector<char> used(p->n_slots, 0);
     for (int e = 0; e < p->E; ++e) {
       const int32_t sl = table[e];
@@ -526,6 +597,7 @@ extern "C" int moe_pool_set_slot_table(moe_pool* p, const int32_t* table, hipStr
 
 extern "C" int moe_pool_get_stats(const moe_pool* p, moe_pool_stats* st) {
   if (!p || !st) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(lfu_on_host(const_cast<moe_pool*>(p)));
   *st = p->lfu.st;
   return MOE_OK;
 }
@@ -802,5 +874,49 @@ extern "C" int moe_layer_forward_streamed(const moe_layer_desc* L, const void* h
     MOE_TRY(ffn_launch(a, MOE_PATH_DECODE, lw.ffn_ws, lw.ffn_bytes, s));
     if (n_loads) *n_loads = nl;
     return MOE_OK;
+  });
+}
+
+extern "C" int moe_layer_forward_offload(const moe_layer_desc* L, const void* host_blobs, size_t host_stride,
+                                         const uint16_t* x, int32_t T, float* y, int32_t* idx, float* w,
+                                         float* sgate, void* ws, size_t ws_bytes, int32_t* n_loads_dev,
+                                         hipStream_t s) {
+  return no_throw([&]() -> int {
+    MOE_TRY(check_layer(L));
+    moe_pool* p = const_cast<moe_pool*>(L->pool);
+    MOE_CHECK(T >= 1 && T <= 8 && (long)T * (L->k + 1) <= 2048);
+    MOE_CHECK(shape_bits(&L->sh) != 32 && shape_bits(&L->shared_sh) != 32);
+    MOE_CHECK(x && y && idx && w && sgate && ws && host_blobs && host_stride >= p->stride);
+    MOE_CHECK(aligned(x, 16) && aligned(y, 16) && aligned(ws, 256) && aligned(L->w_router_dev, 16));
+    const int n = T * L->k;
+    // a step never needs more experts than the pool holds, and the plan's
+    // state fits one wave's LDS
+    if (n > p->n_slots || !lfu_plan_fits(p->E, p->n_slots, n)) return MOE_ERR_UNSUPPORTED;
+    void* src_dev = nullptr;
+    if (hipHostGetDevicePointer(&src_dev, const_cast<void*>(host_blobs), 0) != hipSuccess || !src_dev) {
+      (void)hipGetLastError();
+      return MOE_ERR_INVALID_ARG;                 // not pinned host memory mapped for the device
+    }
+    MOE_CHECK(aligned(src_dev, 16) && host_stride % 16 == 0);
+    Carver c(ws, ws_bytes);
+    LayerWs lw;
+    if (!carve_layer(c, L, T, MOE_PATH_DECODE, &lw)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(lfu_on_device(p));
+    const int d = L->sh.d, k = L->k;
+    // 1. routing; 2. the plan (slot table edited on the device); 3. the
+    // missing blobs over PCIe; 4. the experts and the combine
+    MOE_TRY(router_launch(x, T, d, L->w_router_dev, L->logit_bias_dev, L->E, k, idx, w, sgate, L->usage_dev,
+                          lw.r, s, true));
+    MOE_TRY(lfu_plan_launch(p->dev, p->E, p->n_slots, p->stride, p->table, p->err, idx, n, n_loads_dev, s));
+    p->host_valid = false;
+    MOE_TRY(plan_pull_launch(src_dev, host_stride, p->slab, p->stride, 0, p->stride, p->dev.plan, p->E, s));
+    FfnArgs a{};
+    pool_view(p, &a.pool);
+    a.d = d; a.I = L->sh.I; a.Ish = L->shared_sh.I;
+    a.bits = shape_bits(&L->sh); a.bits_sh = shape_bits(&L->shared_sh);
+    a.shared_blob = static_cast<const uint8_t*>(L->shared_blob_dev);
+    a.x = x; a.xq = lw.r.xq; a.xs = lw.r.xs;
+    a.T = T; a.k = k; a.idx = idx; a.w = w; a.sgate = sgate; a.y = y;
+    return ffn_launch(a, MOE_PATH_DECODE, lw.ffn_ws, lw.ffn_bytes, s);
   });
 }

@@ -103,6 +103,25 @@ struct ChainIO {
 size_t router_ws_bytes(int T, int d, int E);
 bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws);
 // prep_x: also fill ws.xq / ws.xs for T > 8 (T <= 8 always does, in-kernel)
+// Device copy of a pool's LFU + recency state, for refills planned on the GPU
+// (moe_layer_forward_offload); the same fields as the host-side policy.
+struct DevLfu {
+  uint64_t* count;      // [E] selections so far
+  int64_t* last;        // [E] step of the last selection, -1 = never
+  int32_t* slot_of;     // [E] slot or -1
+  int32_t* holder;      // [n_slots] expert or -1
+  uint64_t* meta;       // [0] step, [1..6] steps, hits, misses, loads, evictions, bytes loaded
+  int32_t* plan;        // the last step's loads: [0] count, then experts [E], slots [E], victims [E]
+};
+bool lfu_plan_fits(int E, int n_slots, int n);
+// One step's plan on the device: selections sel[0..n) (device), the pool's
+// slot table edited in place, n_loads_out (device, may be null) = loads.
+int lfu_plan_launch(const DevLfu& v, int E, int n_slots, size_t stride, int32_t* table, int32_t* err,
+                    const int32_t* sel, int n, int32_t* n_loads_out, hipStream_t s);
+// The planned loads' byte range [off, off + bytes) of every blob, host -> slots.
+int plan_pull_launch(const void* src_dev, size_t src_stride, void* dst, size_t dst_stride, size_t off,
+                     size_t bytes, const int32_t* plan, int E, hipStream_t s);
+
 int router_launch(const uint16_t* x, int T, int d, const float* W, const float* bias,
                   int E, int k, int32_t* idx, float* w, float* sgate, uint32_t* usage,
                   const RouterWs& ws, hipStream_t s, bool prep_x, float* logits_out = nullptr);

@@ -10,8 +10,9 @@ oracle.
   against the oracle (one prefill tensor: max|y - y_ref| <= 2e-3 max|y_ref|);
 * refill80b (T = 1, 256-slot pool over 512 experts refilled by LFU + recency
   from pinned host memory, Zipf router): all 1000 seeded steps bit-identical
-  to the all-resident layer, for the serial step (router, refill, experts)
-  and the streamed one, at 256 and 512 slots; hit rate inside the pages'
+  to the all-resident layer, for the serial step (router, refill, experts),
+  the streamed one and the offload one (refill planned and copied by the
+  GPU), at 256 and 512 slots, with the same policy statistics; hit rate inside the pages'
   43-70 % band at 256 slots; streamed outputs against the oracle.
 
 Routing bars everywhere: the device's exported logits within the fp32
@@ -127,15 +128,18 @@ def test_refill80b_1000_steps_bit_identical(c2, slots):
     ser = moe.Pool(cfg.E, slots, cfg.d, cfg.I)                 # router -> refill -> experts
     stp = moe.Pool(cfg.E, slots, cfg.d, cfg.I)                 # streamed step
     lst = moe.Layer(twin.Wr, twin.bias, stp, twin.shared_blob, cfg.I_shared, cfg.k, usage=False)
+    opl = moe.Pool(cfg.E, slots, cfg.d, cfg.I)                 # offload step (plan and copy on the GPU)
+    lof = moe.Layer(twin.Wr, twin.bias, opl, twin.shared_blob, cfg.I_shared, cfg.k, usage=False)
     wst = torch.zeros(twin.layer.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device=dev)
     wsl = torch.zeros(lst.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device=dev)
+    wso = torch.zeros(lof.workspace_bytes(1, moe.MOE_PATH_DECODE), dtype=torch.uint8, device=dev)
     wsr = torch.zeros(moe.moe_router_workspace_bytes(1, cfg.d, cfg.E), dtype=torch.uint8, device=dev)
     wsf = torch.zeros(moe.moe_ffn_workspace_bytes(cfg.d, cfg.I, cfg.I_shared, 1, cfg.k, cfg.E,
                                                   moe.MOE_PATH_DECODE), dtype=torch.uint8, device=dev)
     out = {key: (torch.empty((n, 1, cfg.d), dtype=torch.float32, device=dev),
                  torch.empty((n, 1, cfg.k), dtype=torch.int32, device=dev),
                  torch.empty((n, 1, cfg.k), dtype=torch.float32, device=dev),
-                 torch.empty((n, 1), dtype=torch.float32, device=dev)) for key in ("twin", "ser", "st")}
+                 torch.empty((n, 1), dtype=torch.float32, device=dev)) for key in ("twin", "ser", "st", "off")}
     cs = torch.cuda.Stream()
     idx_host = torch.empty((cfg.k,), dtype=torch.int32, pin_memory=True)
     snap = {}
@@ -154,21 +158,23 @@ def test_refill80b_1000_steps_bit_identical(c2, slots):
         moe.moe_expert_ffn_int4(ser, twin.shared_blob, cfg.I_shared, x, i, w, s, workspace=wsf, out=y)
         moe.moe_layer_forward_streamed(lst, x, host, copy_stream=cs, workspace=wsl,
                                        out=tuple(t[step] for t in out["st"]))
+        moe.moe_layer_forward_offload(lof, x, host, workspace=wso, out=tuple(t[step] for t in out["off"]))
         if step == 99:
             torch.cuda.synchronize()
             snap = {"ser": ser.stats(), "st": stp.stats()}
     torch.cuda.synchronize()
-    assert ser.check_error() == moe.MOE_OK and stp.check_error() == moe.MOE_OK
-    for key in ("ser", "st"):
+    assert ser.check_error() == moe.MOE_OK and stp.check_error() == moe.MOE_OK and opl.check_error() == moe.MOE_OK
+    for key in ("ser", "st", "off"):
         for a, b, what in zip(out["twin"], out[key], ("y", "idx", "w", "s")):
             diff = (a != b).reshape(n, -1).any(1).nonzero()
             assert diff.numel() == 0, f"{key}: {what} differs from the all-resident layer at steps {diff[:4].tolist()}"
-    s_ser, s_st = ser.stats(), stp.stats()
-    assert s_ser["hits"] == s_st["hits"] and s_ser["misses"] == s_st["misses"]   # one policy, same picks
+    s_ser, s_st, s_off = ser.stats(), stp.stats(), opl.stats()
+    for key in ("steps", "hits", "misses", "loads", "evictions", "bytes_loaded"):   # one policy, same picks
+        assert s_ser[key] == s_st[key] == s_off[key], (key, s_ser, s_st, s_off)
     late = (s_ser["hits"] - snap["ser"]["hits"]) / max(1, (s_ser["hits"] + s_ser["misses"]
                                                            - snap["ser"]["hits"] - snap["ser"]["misses"]))
     allr = s_ser["hits"] / max(1, s_ser["hits"] + s_ser["misses"])
-    print(f"{slots} slots: {n} steps bit-identical (serial and streamed); hit rate {allr:.3f} "
+    print(f"{slots} slots: {n} steps bit-identical (serial, streamed, offload); hit rate {allr:.3f} "
           f"(steps 100-999: {late:.3f}), loads {s_ser['loads']}")
     if slots == 256:
         assert 0.43 <= late <= 0.70
