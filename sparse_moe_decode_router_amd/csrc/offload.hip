@@ -15,6 +15,7 @@
 //   * stats: steps, hits, misses, loads, evictions, bytes loaded.
 #include "internal.h"
 #include "device.h"
+#include "pull.h"
 
 namespace moe {
 namespace {
@@ -212,34 +213,9 @@ __global__ __launch_bounds__(kPlanThreads) void lfu_plan_kernel(DevLfu v, int E,
   }
 }
 
-// The planned blobs' byte range [off, off + bytes) copied from host memory
-// (read by the CUs over PCIe) into their slots; the work list is the plan's
-// load list, read from device memory.  Four 16-byte pieces per thread in
-// flight, clamped loads and guarded stores as in the host-planned copy.
-__global__ __launch_bounds__(256) void plan_pull_kernel(const uint4* __restrict__ src, long src_stride16,
-                                                        uint4* __restrict__ dst, long dst_stride16, long off16,
-                                                        long n16, const int32_t* __restrict__ plan, int E) {
-  const int nb = plan[0];
-  const long total = n16 * nb;
-  const long stride = (long)gridDim.x * blockDim.x;
-  for (long q0 = (long)blockIdx.x * blockDim.x + threadIdx.x; q0 < total; q0 += 4 * stride) {
-    uint4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long q = q0 + u * stride < total ? q0 + u * stride : 0;
-      const int b = (int)(q / n16);
-      v[u] = src[(long)plan[1 + b] * src_stride16 + off16 + q % n16];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long q = q0 + u * stride;
-      if (q < total) {
-        const int b = (int)(q / n16);
-        dst[(long)plan[1 + E + b] * dst_stride16 + off16 + q % n16] = v[u];
-      }
-    }
-  }
-}
+// The planned blobs' byte range copied from host memory into their slots,
+// the work list read from the plan in device memory.
+__global__ __launch_bounds__(256) void plan_pull_kernel(PullJob j) { plan_pull_body(j, blockIdx.x); }
 
 }  // namespace
 
@@ -256,12 +232,19 @@ int lfu_plan_launch(const DevLfu& v, int E, int n_slots, size_t stride, int32_t*
 int plan_pull_launch(const void* src_dev, size_t src_stride, void* dst, size_t dst_stride, size_t off,
                      size_t bytes, const int32_t* plan, int E, hipStream_t s) {
   if ((uintptr_t)src_dev % 16 || (uintptr_t)dst % 16 || src_stride % 16 || dst_stride % 16 || bytes % 16 ||
-      off % 16)
+      off % 16 || !plan)
     return MOE_ERR_INVALID_ARG;
-  // 64 blocks keep the PCIe link full (as the host-planned copy)
-  plan_pull_kernel<<<64, 256, 0, s>>>(static_cast<const uint4*>(src_dev), (long)(src_stride / 16),
-                                      static_cast<uint4*>(dst), (long)(dst_stride / 16), (long)(off / 16),
-                                      (long)(bytes / 16), plan, E);
+  PullJob j;
+  j.src = static_cast<const uint4*>(src_dev);
+  j.dst = static_cast<uint4*>(dst);
+  j.src_stride16 = (long)(src_stride / 16);
+  j.dst_stride16 = (long)(dst_stride / 16);
+  j.off16 = (long)(off / 16);
+  j.n16 = (long)(bytes / 16);
+  j.plan = plan;
+  j.E = E;
+  j.blocks = 64;                        // 64 blocks keep the PCIe link full (as the host-planned copy)
+  plan_pull_kernel<<<j.blocks, 256, 0, s>>>(j);
   MOE_HIP(hipGetLastError());
   return MOE_OK;
 }
