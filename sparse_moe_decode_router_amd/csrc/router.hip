@@ -111,6 +111,19 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   const int row = blockIdx.x;
   const int d = a.d, T = a.T, E = a.E;
   const bool chain = a.ssp != nullptr;
+  const float4* Wr = reinterpret_cast<const float4*>(a.W + (size_t)row * d);
+  // kRU pieces of 4 columns per thread a step.  The first step's weight
+  // loads (all of the row's for d <= 2048) go out first: the chain's scale
+  // (a reduction of loaded partials) and the activation preparation (loads,
+  // then stores that later loads may not pass) would otherwise sit in front
+  // of them.
+  constexpr int kRU = 2;
+  float4 w_first[kRU];
+#pragma unroll
+  for (int u = 0; u < kRU; ++u) {
+    const int c = tid + u * kRouterThreads;
+    w_first[u] = Wr[c < d / 4 ? c : 0];          // clamped: unconditional loads
+  }
   float scale[TMAX];
   if (chain) {
     // x is a chain's residual stream: every block forms the same scale from
@@ -160,12 +173,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   float acc[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) acc[t] = 0.0f;
-  const float4* Wr = reinterpret_cast<const float4*>(a.W + (size_t)row * d);
-  // kRU pieces of 4 columns per thread: their weight and activation loads
-  // are all issued before the first product (a plain strided loop would wait
-  // for each piece's loads before issuing the next); columns are still added
-  // in the order c = tid, tid + 256, ...
-  constexpr int kRU = 2;
+  // a step's weight and activation loads are all issued before its first
+  // product (a plain strided loop would wait for each piece's loads before
+  // issuing the next); columns are still added in the order c = tid, tid +
+  // 256, ...
   for (int c0 = tid; c0 < d / 4; c0 += kRU * kRouterThreads) {
     float4 wv[kRU];
     uint2 xv[kRU][TMAX];
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
       const int c = c0 + u * kRouterThreads;
       const bool ok = c < d / 4;
       const int cc = ok ? c : 0;                 // clamped: unconditional loads
-      wv[u] = Wr[cc];
+      wv[u] = c0 == tid ? w_first[u] : Wr[cc];
 #pragma unroll
       for (int t = 0; t < TMAX; ++t)
         xv[u][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * d + 4 * cc);
