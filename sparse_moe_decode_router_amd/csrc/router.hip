@@ -112,17 +112,22 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   const int d = a.d, T = a.T, E = a.E;
   const bool chain = a.ssp != nullptr;
   const float4* Wr = reinterpret_cast<const float4*>(a.W + (size_t)row * d);
-  // kRU pieces of 4 columns per thread a step.  The first step's weight
-  // loads (all of the row's for d <= 2048) go out first: the chain's scale
-  // (a reduction of loaded partials) and the activation preparation (loads,
-  // then stores that later loads may not pass) would otherwise sit in front
-  // of them.
+  // kRU pieces of 4 columns per thread a step.  The first step's weight and
+  // activation loads (all of the row's for d <= 2048) go out first: the
+  // chain's scale (a reduction of loaded partials) and the activation
+  // preparation (loads, then stores that later loads may not pass) would
+  // otherwise sit in front of them.
   constexpr int kRU = 2;
   float4 w_first[kRU];
+  uint2 x_first[kRU][TMAX];
 #pragma unroll
   for (int u = 0; u < kRU; ++u) {
     const int c = tid + u * kRouterThreads;
-    w_first[u] = Wr[c < d / 4 ? c : 0];          // clamped: unconditional loads
+    const int cc = c < d / 4 ? c : 0;            // clamped: unconditional loads
+    w_first[u] = Wr[cc];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+      x_first[u][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * d + 4 * cc);
   }
   float scale[TMAX];
   if (chain) {
@@ -188,7 +193,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
       wv[u] = c0 == tid ? w_first[u] : Wr[cc];
 #pragma unroll
       for (int t = 0; t < TMAX; ++t)
-        xv[u][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * d + 4 * cc);
+        xv[u][t] = c0 == tid ? x_first[u][t]
+                             : *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * d + 4 * cc);
     }
 #pragma unroll
     for (int u = 0; u < kRU; ++u) {
