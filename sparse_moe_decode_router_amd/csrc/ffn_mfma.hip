@@ -35,6 +35,7 @@ constexpr int kPM = 128;        // tokens per bucket chunk (m-tile)
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct PInst {                  // bucket chunk
   int32_t expert;               // -1 = shared expert
@@ -200,6 +201,12 @@ __device__ __forceinline__ int a_pos(int r, int cc) { return r * 128 + 16 * (cc 
 //   rows: the matrix's output rows; row: this lane's weight row.
 // MT: live 32-token tiles of the chunk (a template so the inner loop has no
 // branches and LDS reads overlap the MFMAs).
+template <int BITS>
+struct CodeSlot {                               // one step's codes and (scale, bias) word of a lane
+  u32x4 c[BITS / 4];
+  uint32_t sb;
+};
+
 template <int MT, int BITS>
 __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2, rsrc_t rA, const uint32_t* a_vo,
                                           rsrc_t rB, uint32_t codes_off, uint32_t sb_off, uint32_t rows,
@@ -214,12 +221,15 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
   for (int j = 0; j < ND; ++j) b_vo[j] = ((ND * h + j) * rows + row) * 16;
   const uint32_t s_vo = row * 4;
   // Stages past the end read through a zero-size descriptor: no memory
-  // traffic, zeros land in a stage nobody reads, and the count stays six.
+  // traffic, zeros land in a stage nobody reads, and the count stays the same.
   const rsrc_t rN = make_rsrc(nullptr, 0);
   // Wave w fetches activation rows 32w..32w+31 (tile w): the waves past the
   // live tiles fetch through the zero-size descriptor as well.
   const bool a_live = wave < MT;
-  auto issue = [&](int s, uint8_t* st) {
+  // The codes and (scale, bias) words are the wave's own: they go straight
+  // into registers (a ring of three steps, as the stages), counted by the
+  // same vmcnt as the activation DMAs.
+  auto issue = [&](int s, uint8_t* st, CodeSlot<BITS>& cs) {
     const bool live = s < C;
     const rsrc_t ra = (live && a_live) ? rA : rN, rb = live ? rB : rN;
     const uint32_t ao = __builtin_amdgcn_readfirstlane(s * 128);
@@ -229,31 +239,28 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_opaque(st + (4 * wave + i) * 1024), 16, a_vo[i], ao, 0, 0);
 #pragma unroll
-    for (int j = 0; j < ND; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + (ND * wave + j) * 1024), 16, b_vo[j], co,
-                                               0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_opaque(st + kStA + kStB<BITS> + wave * 256), 4, s_vo, so, 0, 0);
+    for (int j = 0; j < ND; ++j) cs.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_vo[j], co, 0);
+    cs.sb = __builtin_amdgcn_raw_buffer_load_b32(rb, s_vo, so, 0);
   };
-  // One step on stage `st` while stage s+2 refills `nx` (the stage read in
-  // the previous step).
-  auto step = [&](int s, const uint8_t* st, uint8_t* nx) {
+  // One step on stage `st` with codes `cs` while stage s+2 refills `nx` and
+  // `nxs` (the stage and codes used in the previous step).
+  auto step = [&](int s, const uint8_t* st, const CodeSlot<BITS>& cs, uint8_t* nx, CodeSlot<BITS>& nxs) {
     // stage s landed for this wave (stage s+1 may be in flight) and this
     // wave's reads of the previous stage are done; then the block meets
     stage_barrier<kDmaPerStage<BITS>>();
-    issue(s + 2, nx);
-    const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kStA + kStB<BITS> + wave * 256 + 4 * (lane & 31));
-    const half2_t s2 = __builtin_bit_cast(half2_t, (sb & 0xFFFFu) * 0x10001u);
-    const half2_t b2 = __builtin_bit_cast(half2_t, (sb >> 16) * 0x10001u);
+    const CodeSlot<BITS> cur = cs;
+    issue(s + 2, nx, nxs);
+    const half2_t s2 = __builtin_bit_cast(half2_t, (cur.sb & 0xFFFFu) * 0x10001u);
+    const half2_t b2 = __builtin_bit_cast(half2_t, (cur.sb >> 16) * 0x10001u);
     half8_t bv[4];
     if constexpr (BITS == 4) {
-      const uint4 cw = *reinterpret_cast<const uint4*>(st + kStA + wave * 1024 + 16 * lane);
+      const u32x4 cw = cur.c[0];
       bv[0] = __builtin_bit_cast(half8_t, dequant8(cw.x, s2, b2, dq));
       bv[1] = __builtin_bit_cast(half8_t, dequant8(cw.y, s2, b2, dq));
       bv[2] = __builtin_bit_cast(half8_t, dequant8(cw.z, s2, b2, dq));
       bv[3] = __builtin_bit_cast(half8_t, dequant8(cw.w, s2, b2, dq));
     } else {
-      const uint4 c0 = *reinterpret_cast<const uint4*>(st + kStA + (2 * wave) * 1024 + 16 * lane);
-      const uint4 c1 = *reinterpret_cast<const uint4*>(st + kStA + (2 * wave + 1) * 1024 + 16 * lane);
+      const u32x4 c0 = cur.c[0], c1 = cur.c[1];
       bv[0] = __builtin_bit_cast(half8_t, dequant8_b(c0.x, c0.y, s2, b2, dq));
       bv[1] = __builtin_bit_cast(half8_t, dequant8_b(c0.z, c0.w, s2, b2, dq));
       bv[2] = __builtin_bit_cast(half8_t, dequant8_b(c1.x, c1.y, s2, b2, dq));
@@ -276,16 +283,17 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  issue(0, S0);
-  issue(1, S1);
+  CodeSlot<BITS> r0, r1, r2;
+  issue(0, S0, r0);
+  issue(1, S1, r1);
   for (int s = 0; s < C; s += 3) {
-    step(s, S0, S2);
+    step(s, S0, r0, S2, r2);
     if (s + 1 >= C) break;
-    step(s + 1, S1, S0);
+    step(s + 1, S1, r1, S0, r0);
     if (s + 2 >= C) break;
-    step(s + 2, S2, S1);
+    step(s + 2, S2, r2, S1, r1);
   }
-  // the (empty) DMAs still in flight land before anyone reuses the stages
+  // the (empty) loads still in flight land before anyone reuses the stages
   stage_barrier<0>();
 }
 
@@ -617,7 +625,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //     fp16 weights and k order, and h / partial outputs in the same layouts.
 constexpr int kSC = 16;                         // tokens per chunk on the streaming path
 constexpr int kSP = 4;                          // steps of codes in flight per wave
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // One k step (64 inputs) of a wave's NM matrices: this lane's code pieces and
 // its row's (scale, bias) word.
