@@ -624,7 +624,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //     read chunk rows again and are never stored), with the same dequantised
 //     fp16 weights and k order, and h / partial outputs in the same layouts.
 constexpr int kSC = 16;                         // tokens per chunk on the streaming path
-constexpr int kSP = 4;                          // steps of codes in flight per wave
+// steps of codes in flight per wave: 2 measured best on the 80B batched
+// shape (expert FFN 157.5 us, 8-bit 220.4) against 1 (160.7, 219.0), 4
+// (160.7, 228.7) and 8 (169.9, 241.7)
+constexpr int kSP = 2;
 
 // One k step (64 inputs) of a wave's NM matrices: this lane's code pieces and
 // its row's (scale, bias) word.
