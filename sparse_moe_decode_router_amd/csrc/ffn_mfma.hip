@@ -623,7 +623,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //     as the 32 rows of A, of which the first n are live; rows past the chunk
 //     read chunk rows again and are never stored), with the same dequantised
 //     fp16 weights and k order, and h / partial outputs in the same layouts.
-constexpr int kSC = 16;                         // tokens per chunk on the streaming path
+// tokens per chunk on the streaming path: its activation rows take kSC (d + 8)
+// x 2 B of LDS, so 8 lets four gate/up blocks share a CU at d = 2048; measured
+// on the 80B batched shape (1.9 tokens per active expert) against 16 and 4:
+// expert FFN 146.6 against 151.1 and 149.0 us (8-bit unchanged)
+constexpr int kSC = 8;
 // steps of codes in flight per wave: 2 measured best on the 80B batched
 // shape (expert FFN 157.5 us, 8-bit 220.4) against 1 (160.7, 219.0), 4
 // (160.7, 228.7) and 8 (169.9, 241.7)
