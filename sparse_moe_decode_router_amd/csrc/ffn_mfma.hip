@@ -286,13 +286,18 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
   CodeSlot<BITS> r0, r1, r2;
   issue(0, S0, r0);
   issue(1, S1, r1);
-  for (int s = 0; s < C; s += 3) {
+  // Whole rounds of three steps, then the last C mod 3 after the loop: exits
+  // from inside the round made the compiler give each of the three steps its
+  // own copy of the accumulators (up to 192 registers), copied across once a
+  // round while the MFMAs writing them drained.
+  int s = 0;
+  for (; s + 3 <= C; s += 3) {
     step(s, S0, r0, S2, r2);
-    if (s + 1 >= C) break;
     step(s + 1, S1, r1, S0, r0);
-    if (s + 2 >= C) break;
     step(s + 2, S2, r2, S1, r1);
   }
+  if (s < C) step(s, S0, r0, S2, r2);
+  if (s + 1 < C) step(s + 1, S1, r1, S0, r0);
   // the (empty) loads still in flight land before anyone reuses the stages
   stage_barrier<0>();
 }
