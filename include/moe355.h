@@ -282,7 +282,7 @@ int moe_bucket_tokens(const int32_t* topk_idx_dev, int32_t T, int32_t k,
  *                     the same order (so the same bits): tiled (buckets in
  *                     chunks of up to 128 tokens, activations and weights
  *                     staged through LDS step by step) for many tokens per
- *                     expert, and weight-streaming (chunks of up to 16
+ *                     expert, and weight-streaming (chunks of up to 8
  *                     tokens whose activations stay in LDS while the weights
  *                     stream from HBM) for a few; PREFILL picks streaming
  *                     when T*k <= 4*E and d <= 4096, and

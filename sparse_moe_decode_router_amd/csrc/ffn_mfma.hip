@@ -142,18 +142,23 @@ __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool rou
 // Pipeline of both GEMMs (one block = 4 waves, a chunk of <= 128 tokens x
 // 128 weight rows, k in steps of 64 = one quantisation group): every wave
 // owns 32 weight rows and all 128 tokens (up to four 32x32 MFMA tiles).
-// Each step's operands go global -> LDS by the buffer unit itself (LDS DMA,
-// no registers), three stages in flight: the activation tile (128 rows x
-// 128 B), every wave's codes (lanes 0-31 hold the first 32 k of the step for
-// their row, lanes 32-63 the second: one 16-byte piece per lane for 4-bit
-// codes, two for 8-bit) and its (scale, bias) words.  A wave dequantises its
-// own codes straight into the MFMA B operand, so each weight is dequantised
-// once.  The k order inside a step is (lane half, 8-input block, the
-// (0,4,1,5,2,6,3,7) order) on both operands.
+// Each step's activation tile (128 rows x 128 B) goes global -> LDS by the
+// buffer unit itself (LDS DMA, no registers), three stages in flight; every
+// wave's codes (lanes 0-31 hold the first 32 k of the step for their row,
+// lanes 32-63 the second: one 16-byte piece per lane for 4-bit codes, two
+// for 8-bit) and its (scale, bias) words go straight into registers, a ring
+// of three steps beside the stages.  A wave dequantises its own codes into
+// the MFMA B operand, so each weight is dequantised once.  The k order
+// inside a step is (lane half, 8-input block, the (0,4,1,5,2,6,3,7) order)
+// on both operands.  A stage is the activation tile alone (16 KB), so three
+// blocks share a CU (3 x 49 KB of LDS, 168 VGPRs a wave): against two blocks
+// with 21-25 KB stages, the 4096-token expert FFN went 581-591 -> 547-554 us
+// (8-bit 646-667 -> 630-634).
 //
-// Synchronisation is explicit: every step issues the same DMAs per wave (six
-// for 4-bit codes, seven for 8-bit), waits until at most the next stage's
-// are in flight (s_waitcnt vmcnt),
+// Synchronisation is explicit: every step issues the same loads per wave
+// (four DMAs, then the codes and the (scale, bias) word: six for 4-bit
+// codes, seven for 8-bit), waits until at most the next step's are in
+// flight (s_waitcnt vmcnt),
 // then meets the other waves at a bare s_barrier.  The DMA destinations are
 // passed as opaque LDS addresses, so the compiler adds no waits of its own
 // (a __syncthreads fence, or its alias tracking, would wait for every DMA in
@@ -161,12 +166,10 @@ __device__ __forceinline__ void resolve_p(const PrefillArgs& a, int ii, bool rou
 // clobber keep it from moving LDS accesses across the wait and barrier.
 constexpr int kKS = 64;                         // k per step
 constexpr int kStA = kPM * 128;                 // activation tile bytes
-constexpr int kStS = 4 * 256;                   // (scale, bias), 256 B per wave
-// per code width: 16-byte code DMAs per lane, codes bytes (1 KB per wave per
-// DMA), stage bytes and DMA instructions per wave per stage
+// per code width: 16-byte code loads per lane, stage bytes and loads per
+// wave per step (four activation DMAs, the codes, the (scale, bias) word)
 template <int BITS> constexpr int kCodeDma = BITS / 4;
-template <int BITS> constexpr int kStB = 4 * 1024 * kCodeDma<BITS>;
-template <int BITS> constexpr int kStage = kStA + kStB<BITS> + kStS;
+template <int BITS> constexpr int kStage = kStA;
 template <int BITS> constexpr int kDmaPerStage = 5 + kCodeDma<BITS>;
 
 // s_waitcnt vmcnt <= N, lgkmcnt == 0, then s_barrier; no code motion of
@@ -305,14 +308,17 @@ __device__ __forceinline__ void gemm_loop(uint8_t* S0, uint8_t* S1, uint8_t* S2,
 // The same GEMM for chunks of at most 32 tokens (one m-tile), with more
 // steps in flight: a stage holds only the live 32 activation rows (4 KB, one
 // 1 KB DMA per wave), the codes and the (scale, bias) words, so the LDS of
-// the three full stages takes NS of these and NS - 1 steps are in flight.
-// Used for 8-bit codes (batched 80B shape: gate/up 236 -> 219 us, down
-// 141 -> 121 us); with 4-bit codes it measured slower than the full-stage
-// loop (gate/up 131 -> 193 us at any depth from 3 to 7 stages), not yet
-// understood, so 4-bit keeps that loop.
+// the three full stages takes NS of these and NS - 1 steps are in flight
+// (three stages, two in flight, since a full stage holds only the
+// activation tile).  Used for 8-bit codes (batched 80B shape, with five of
+// these stages in the larger full stages of before: gate/up 236 -> 219 us,
+// down 141 -> 121 us); with 4-bit codes it measured slower than the
+// full-stage loop (gate/up 131 -> 193 us at any depth from 3 to 7 stages),
+// not yet understood, so 4-bit keeps that loop.
 // a_vo_n: this lane's activation offset for row 8 * wave + lane / 8.
 template <int BITS> constexpr int kNarrowStage = 4096 + 4096 * kCodeDma<BITS> + 1024;
 template <int BITS> constexpr int kNarrowNS = (3 * kStage<BITS>) / kNarrowStage<BITS>;
+static_assert(kNarrowNS<8> >= 3, "narrow stages in the LDS of three full stages");
 
 template <int BITS>
 __device__ __forceinline__ void gemm_loop_narrow(uint8_t* SM, rsrc_t rA, uint32_t a_vo_n, rsrc_t rB,
@@ -423,8 +429,9 @@ __device__ __forceinline__ bool xcd_item(long L, int nch, int nt, int* chunk, in
   return *chunk < nch;
 }
 
+// three blocks a CU: 168 VGPRs a wave (a few spills, outside the k loop)
 template <int BITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gate_up_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void prefill_gate_up_kernel(PrefillArgs a) {
   // three stages, contiguous (chunks of <= 32 tokens use the space as more, smaller stages)
   __shared__ __attribute__((aligned(16))) uint8_t SM[3 * kStage<BITS>];
   uint8_t* S0 = SM;
@@ -534,7 +541,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <int BITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_down_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void prefill_down_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t SM[3 * kStage<BITS>];
   uint8_t* S0 = SM;
   uint8_t* S1 = SM + kStage<BITS>;
