@@ -82,8 +82,6 @@ struct Carver {
 // Router pieces used by the layer driver (router.hip).
 struct RouterWs {
   float* logits;      // [S][T][E+1] (S split-K partials, S = 1 for T <= 8)
-  uint32_t* ticket;   // unused, kept zero
-  uint16_t* wsplit;   // [3][E+1][d] bf16 parts of the router weights (T > 8)
   uint32_t* xq;       // [T][d/2]  bf16 pairs (x[8m+i], x[8m+i+4])
   float* xs;          // [T][d/64] group sums of x
 };

@@ -231,69 +231,138 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
 // (d/(32 S) additions), so the summation depth stays near a plain tiled GEMM:
 // 32 + 2 + d/(32 S) per split, plus S-1 for the fixed-order sum of the S
 // split-K partials in the top-k kernel, plus one for the bias.
+//
+// Block: 128 tokens x 64 router rows, 8 waves of 32 x 32; k advances 64 at a
+// time (two of the 32-wide steps) through one LDS stage.  The x and fp32 W
+// pieces of the stages after it are loaded into registers, two stages ahead,
+// while the matrix cores work on the current one, and split and stored once
+// every wave has read it: the router weights are split as they are staged
+// (no separate pass over W).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W, long n,
-                                                           uint16_t* __restrict__ Wsplit) {
-  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= n) return;
-  const float w = W[id];
-  const uint32_t hi = f32_to_bf16(w);
-  const float r1 = w - __uint_as_float(hi << 16);
-  const uint32_t mid = f32_to_bf16(r1);
-  const float r2 = r1 - __uint_as_float(mid << 16);
-  const uint32_t lo = f32_to_bf16(r2);
-  Wsplit[id] = (uint16_t)hi;
-  Wsplit[n + id] = (uint16_t)mid;
-  Wsplit[2 * n + id] = (uint16_t)lo;
+// Two weights a, b as bf16 parts hi + mid + lo, each the bf16 rounding (to
+// nearest even, the hardware's packed conversion) of what is left; the pairs
+// are packed with a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float p, float q) {
+  const bf16x2_t v = {(__bf16)p, (__bf16)q};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16x2(a, b);
+  const float a1 = a - bf16_lo(hi), b1 = b - bf16_hi(hi);
+  mid = bf16x2(a1, b1);
+  const float a2 = a1 - bf16_lo(mid), b2 = b1 - bf16_hi(mid);
+  lo = bf16x2(a2, b2);
 }
 
-constexpr int kRtM = 128, kRtN = 64, kRtLds = 40;   // block tile, LDS row (bf16)
+constexpr int kRtM = 128, kRtN = 64, kRtK = 64, kRtLds = 72;   // block tile, k per stage, LDS row (bf16)
 
 __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __restrict__ x, int T, int d,
-                                                          const uint16_t* __restrict__ Wsplit, int R,
+                                                          const float* __restrict__ W, int R,
                                                           int S, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kRtM * kRtLds];
   __shared__ __attribute__((aligned(16))) uint16_t ws[3][kRtN * kRtLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * kRtM, n0 = blockIdx.x * kRtN, sp = blockIdx.z;
-  const int kspan = d / S, kbeg = sp * kspan;
-  const long nW = (long)R * d;
+  // Workgroups go to the 8 XCDs in turn; each XCD takes a contiguous range of
+  // tiles, ordered (split, token tile, row tile), so the row tiles of one
+  // token tile share its x rows in one L2 and one split's W columns stay there
+  const int nt = (R + kRtN - 1) / kRtN, mt = (T + kRtM - 1) / kRtM;
+  const int G = gridDim.x, tile = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (tile >= nt * mt * S) return;               // grid padded to a multiple of 8
+  const int m0 = (tile / nt) % mt * kRtM, n0 = tile % nt * kRtN, sp = tile / (nt * mt);
+  const int kspan = d / S, kbeg = sp * kspan, kend = kbeg + kspan;
   const int wm = 32 * (wave & 3), wn = 32 * (wave >> 2);
+  // this thread's pieces of a stage, two of each: x row xr (8 bf16 at column
+  // 8 xq), W row wr (4 fp32 at column 4 wq), read through buffer resources
+  // over the block's own rows (fixed offsets, the k position a scalar).  Rows
+  // past T or R read as zeros; they would feed only outputs that are never
+  // stored (an MFMA output row depends on its A row alone, a column on its B
+  // row).
+  const rsrc_t rX = make_rsrc(x + (size_t)m0 * d, (uint32_t)(min(kRtM, T - m0) * d * 2));
+  const rsrc_t rW = make_rsrc(W + (size_t)n0 * d, (uint32_t)(min(kRtN, R - n0) * d * 4));
+  uint32_t xv[2], wv[2];
+  int xo[2], wo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int id = tid + 512 * u;
+    const int xr = id >> 3, xq = id & 7, wr = id >> 4, wq = id & 15;
+    xv[u] = (uint32_t)(xr * d + 8 * xq) * 2;
+    wv[u] = (uint32_t)(wr * d + 4 * wq) * 4;
+    xo[u] = xr * kRtLds + 8 * xq;
+    wo[u] = wr * kRtLds + 4 * wq;
+  }
+  struct Piece {
+    u32x4 x[2];
+    u32x4 w[2];
+  };
+  auto load = [&](Piece& pc, int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pc.x[u] = __builtin_amdgcn_raw_buffer_load_b128(rX, xv[u], (uint32_t)k0 * 2, 0);
+      pc.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rW, wv[u], (uint32_t)k0 * 4, 0);
+    }
+  };
+  auto store = [&](const Piece& pc) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<u32x4*>(&xs[xo[u]]) = pc.x[u];
+      const float4 f = make_float4(__uint_as_float(pc.w[u].x), __uint_as_float(pc.w[u].y),
+                                   __uint_as_float(pc.w[u].z), __uint_as_float(pc.w[u].w));
+      uint32_t p[3][2];
+      split3x2(f.x, f.y, p[0][0], p[1][0], p[2][0]);
+      split3x2(f.z, f.w, p[0][1], p[1][1], p[2][1]);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) *reinterpret_cast<uint2*>(&ws[j][wo[u]]) = make_uint2(p[j][0], p[j][1]);
+    }
+  };
   float run[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) run[i] = 0.f;
-  for (int k0 = kbeg; k0 < kbeg + kspan; k0 += 32) {
-    {  // x tile: 128 tokens x 32, one uint4 (8 bf16) per thread
-      const int row = tid >> 2, q = tid & 3;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + row < T) v = *reinterpret_cast<const uint4*>(x + (size_t)(m0 + row) * d + k0 + 8 * q);
-      *reinterpret_cast<uint4*>(&xs[row * kRtLds + 8 * q]) = v;
-    }
-    for (int qq = tid; qq < 3 * kRtN * 4; qq += 512) {   // W parts: 3 x 64 rows x 32
-      const int j = qq / (kRtN * 4), rem = qq % (kRtN * 4), row = rem >> 2, q = rem & 3;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n0 + row < R) v = *reinterpret_cast<const uint4*>(Wsplit + j * nW + (size_t)(n0 + row) * d + k0 + 8 * q);
-      *reinterpret_cast<uint4*>(&ws[j][row * kRtLds + 8 * q]) = v;
-    }
-    __syncthreads();
-    f32x16_t acc[3];
+  // one stage of MFMAs from LDS: two 32-wide steps, fresh accumulators each
+  auto mma = [&]() {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x16_t acc[3];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xs[(wm + (lane & 31)) * kRtLds + 16 * kh + 8 * (lane >> 5)]);
+        for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&ws[j][(wn + (lane & 31)) * kRtLds + 16 * kh + 8 * (lane >> 5)]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[j], 0, 0, 0);
+      for (int kh = 0; kh < 2; ++kh) {
+        const int col = 32 * h2 + 16 * kh + 8 * (lane >> 5);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xs[(wm + (lane & 31)) * kRtLds + col]);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&ws[j][(wn + (lane & 31)) * kRtLds + col]);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[j], 0, 0, 0);
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) run[i] += (acc[0][i] + acc[1][i]) + acc[2][i];
+      for (int i = 0; i < 16; ++i) run[i] += (acc[0][i] + acc[1][i]) + acc[2][i];
+    }
+  };
+  // stages two ahead in registers (pa, pb in turn): the loads of stage t + 2
+  // are issued before stage t's MFMAs, stage t + 1 is stored after them
+  Piece pa, pb;
+  load(pa, kbeg);
+  if (kbeg + kRtK < kend) load(pb, kbeg + kRtK);
+  store(pa);
+  __syncthreads();
+  for (int k0 = kbeg; k0 < kend; k0 += 2 * kRtK) {
+    if (k0 + 2 * kRtK < kend) load(pa, k0 + 2 * kRtK);
+    mma();
+    __syncthreads();                             // every wave is done with the stage
+    if (k0 + kRtK >= kend) break;
+    store(pb);
+    __syncthreads();
+    if (k0 + 3 * kRtK < kend) load(pb, k0 + 3 * kRtK);
+    mma();
+    __syncthreads();
+    if (k0 + 2 * kRtK >= kend) break;
+    store(pa);
     __syncthreads();
   }
   float* out = part + (size_t)sp * T * R;
@@ -307,13 +376,13 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
 
 // split-K count for T > 8: the smallest power of two (<= 8) that gives the
 // launch about 1024 blocks of 128 tokens x 64 rows (at E = 512: 8 below 128
-// tokens, 4 at 4096 tokens); every split spans a multiple of 32 columns (d is
-// a multiple of 64)
+// tokens, 4 at 4096 tokens); every split spans a multiple of 64 columns (d is
+// a multiple of 64), whole stages of the MFMA kernel
 int router_splits(int T, int d, int E) {
   const long tiles = (long)((E + 1 + kRtN - 1) / kRtN) * ((T + kRtM - 1) / kRtM);
   int S = 1;
   while (S < 8 && tiles * S < 1024) S *= 2;
-  while (S > 1 && (d / 32) % S != 0) S /= 2;
+  while (S > 1 && (d / kRtK) % S != 0) S /= 2;
   return S;
 }
 
@@ -393,9 +462,7 @@ size_t router_ws_bytes(int T, int d, int E) {
 }
 
 bool router_ws_carve(Carver& c, int T, int d, int E, RouterWs* ws) {
-  ws->ticket = c.take<uint32_t>(64);
   ws->logits = c.take<float>((size_t)(T <= 8 ? 1 : router_splits(T, d, E)) * T * (E + 1));
-  ws->wsplit = T <= 8 ? nullptr : c.take<uint16_t>((size_t)3 * (E + 1) * d);
   ws->xq = c.take<uint32_t>((size_t)T * d / 2);
   ws->xs = c.take<float>((size_t)T * d / 64);
   return c.ok();
@@ -415,11 +482,8 @@ int router_logits_launch(const uint16_t* x, int T, int d, const float* W, int E,
   }
   if (prep_x) MOE_TRY(xprep_launch(x, T, d, ws.xq, ws.xs, s));
   const int R = E + 1, S = router_splits(T, d, E);
-  const long nW = (long)R * d;
-  router_split_kernel<<<(unsigned)((nW + 255) / 256), 256, 0, s>>>(W, nW, ws.wsplit);
-  MOE_HIP(hipGetLastError());
-  router_mfma_kernel<<<dim3((R + kRtN - 1) / kRtN, (T + kRtM - 1) / kRtM, S), 512, 0, s>>>(
-      x, T, d, ws.wsplit, R, S, ws.logits);
+  const int tiles = ((R + kRtN - 1) / kRtN) * ((T + kRtM - 1) / kRtM) * S;
+  router_mfma_kernel<<<(unsigned)((tiles + 7) & ~7), 512, 0, s>>>(x, T, d, W, R, S, ws.logits);
   MOE_HIP(hipGetLastError());
   return MOE_OK;
 }
