@@ -68,7 +68,20 @@ def test_router_parity(name, T):
     the selection the exact top k of the device's own logits on every token,
     and the selection equal to the exact one wherever the bound separates the
     exact logits (certified); usage counters equal the selections."""
-    cfg = ms.CONFIGS[name]
+    _router_parity(ms.CONFIGS[name], name, T)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(129, 192, 7, 2), (40, 64, 33, 4), (300, 320, 65, 8), (257, 640, 100, 6)])
+def test_router_mfma_ragged_shapes(T, d, E, k):
+    """The matrix-core router where its tiles are ragged: an odd number of
+    64-wide stages per split (3, 1, 5, and 5 with two splits), a last token
+    tile of 1 or 44 rows, router rows far short of a 64-row tile (E + 1 = 8)
+    or just past one (66), and tile grids that are not a multiple of 8."""
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], d=d, E=E, k=k)
+    _router_parity(cfg, f"d{d}_E{E}", T)
+
+
+def _router_parity(cfg, name, T):
     Wr = ms.router_weight(cfg)
     bias = ms.logit_bias(cfg)
     Wd = torch.from_numpy(Wr).cuda()
