@@ -197,9 +197,11 @@ __device__ __forceinline__ int a_pos(int r, int cc) { return r * 128 + 16 * (cc 
 //                 fixed rotation).
 //   rA / a_vo[i]: activation rows; a_vo[i] = byte offset of the row this
 //                 lane fetches for DMA i (row 8*(4*wave+i) + lane/8), plus
-//                 16 * the swizzled piece.  Rows past the chunk fetch row 0:
-//                 MFMA row r of C depends on row r of A only, and those
-//                 output rows are never stored.
+//                 16 * the swizzled piece.  Rows past the chunk read from
+//                 past the end of the buffer, i.e. zeros: MFMA row r of C
+//                 depends on row r of A only, and those output rows are
+//                 never stored (zeros rather than a copy of a real row: the
+//                 matrix cores draw less power on them).
 //   rB: the expert blob; codes_off / sb_off: the matrix's sections in it;
 //   rows: the matrix's output rows; row: this lane's weight row.
 // MT: live 32-token tiles of the chunk (a template so the inner loop has no
@@ -450,7 +452,8 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_kernel(PrefillArgs a) 
   const int nch = nR + a.n_shared_inst;
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
   const int C = a.d / kKS;
-  const rsrc_t rX = make_rsrc(a.xh, (uint32_t)((uint64_t)a.T * a.d * 2));   // < 4 GiB: prefill_fits
+  const uint32_t xbytes = (uint32_t)((uint64_t)a.T * a.d * 2);               // < 4 GiB: prefill_fits
+  const rsrc_t rX = make_rsrc(a.xh, xbytes);
   const int mat = wave >> 1;                    // waves 0,1: gate rows; 2,3: up rows
   const int colb = 32 * (wave & 1);
 
@@ -489,13 +492,13 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_kernel(PrefillArgs a) 
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * (4 * wave + i) + (lane >> 3);
       const int t = tok_s[r];
-      a_vo[i] = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ a_swz(r));
+      a_vo[i] = t >= 0 ? (uint32_t)t * a.d * 2 + 16 * ((lane & 7) ^ a_swz(r)) : xbytes;   // past the end: zeros
     }
     uint32_t a_vo_n;                            // one-tile chunks: row 8 * wave + lane / 8
     {
       const int r = 8 * wave + (lane >> 3);
       const int t = tok_s[r];
-      a_vo_n = (uint32_t)(t >= 0 ? t : 0) * a.d * 2 + 16 * ((lane & 7) ^ a_swz(r));
+      a_vo_n = t >= 0 ? (uint32_t)t * a.d * 2 + 16 * ((lane & 7) ^ a_swz(r)) : xbytes;
     }
     float16_t acc[4];
 #pragma unroll
@@ -552,7 +555,8 @@ __global__ __launch_bounds__(256, 3) void prefill_down_kernel(PrefillArgs a) {
   const int nt = a.d / 128;
   const int nch = nR + a.n_shared_inst;
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
-  const rsrc_t rH = make_rsrc(a.hh, (uint32_t)(((uint64_t)a.T * a.k + a.T) * a.Imax * 2));   // < 4 GiB: prefill_fits
+  const uint32_t hbytes = (uint32_t)(((uint64_t)a.T * a.k + a.T) * a.Imax * 2);   // < 4 GiB: prefill_fits
+  const rsrc_t rH = make_rsrc(a.hh, hbytes);
 
   for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
     int ii, tile;
@@ -586,13 +590,13 @@ __global__ __launch_bounds__(256, 3) void prefill_down_kernel(PrefillArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * (4 * wave + i) + (lane >> 3);
       const int hr = hrow_s[r];
-      a_vo[i] = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ a_swz(r));
+      a_vo[i] = hr >= 0 ? (uint32_t)hr * a.Imax * 2 + 16 * ((lane & 7) ^ a_swz(r)) : hbytes;   // past the end: zeros
     }
     uint32_t a_vo_n;                            // one-tile chunks: row 8 * wave + lane / 8
     {
       const int r = 8 * wave + (lane >> 3);
       const int hr = hrow_s[r];
-      a_vo_n = (uint32_t)(hr >= 0 ? hr : 0) * a.Imax * 2 + 16 * ((lane & 7) ^ a_swz(r));
+      a_vo_n = hr >= 0 ? (uint32_t)hr * a.Imax * 2 + 16 * ((lane & 7) ^ a_swz(r)) : hbytes;
     }
     float16_t acc[4];
 #pragma unroll
@@ -633,10 +637,13 @@ __global__ __launch_bounds__(256, 3) void prefill_down_kernel(PrefillArgs a) {
 //     kSP steps of 64 inputs ahead, with no block barrier in the k loop;
 //   * the MFMA tiles are the tiled path's (v_mfma_f32_32x32x16_f16, tokens
 //     as the 32 rows of A, of which the first n are live; rows past the chunk
-//     read chunk rows again and are never stored), with the same dequantised
-//     fp16 weights and k order, and h / partial outputs in the same layouts.
-// tokens per chunk on the streaming path: its activation rows take kSC (d + 8)
-// x 2 B of LDS, so 8 lets four gate/up blocks share a CU at d = 2048; measured
+//     read a row of zeros kept after the chunk's rows and are never stored:
+//     with at most 8 live rows, zeros instead of copies of live rows cut the
+//     matrix cores' power, 153-154 -> 145-149 us for the 80B batched expert
+//     FFN), with the same dequantised fp16 weights and k order, and h /
+//     partial outputs in the same layouts.
+// tokens per chunk on the streaming path: its activation rows take (kSC + 1)
+// (d + 8) x 2 B of LDS, so 8 lets four gate/up blocks share a CU at d = 2048; measured
 // on the 80B batched shape (1.9 tokens per active expert) against 16 and 4:
 // expert FFN 146.6 against 151.1 and 149.0 us (8-bit unchanged)
 constexpr int kSC = 8;
@@ -786,7 +793,7 @@ __device__ __forceinline__ bool stage_rows(const uint16_t* __restrict__ src, siz
 // 32 w .. 32 w + 31 of both matrices.  LDS: the chunk's x rows.
 template <int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void stream_gate_up_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];   // [kSC][d + 8] fp16
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];   // [kSC + 1][d + 8] fp16, the last row zeros
   __shared__ int tok_s[kSC], hrow_s[kSC];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
@@ -796,6 +803,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
   const int ld = a.d + 8;
   const int C = a.d / kKS;
+  for (int c = tid; c < ld / 8; c += 256) reinterpret_cast<uint4*>(xl + kSC * ld)[c] = make_uint4(0, 0, 0, 0);
   for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
     int ii, tile;
     if (!xcd_item(wi, nch, nt, &ii, &tile)) continue;
@@ -836,7 +844,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-    const uint16_t* arow = xl + ((lane & 31) % in.n) * ld;
+    const uint16_t* arow = xl + ((lane & 31) < in.n ? (lane & 31) : kSC) * ld;
     stream_loop<BITS, 2>(arow, make_rsrc(blob, (uint32_t)L.bytes), live, co, so, (uint32_t)Iinst,
                          (uint32_t)(live ? o : 0), C, acc);
     if (live) {
@@ -872,7 +880,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // LDS: the chunk's h rows.
 template <int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void stream_down_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t hl[];   // [kSC][Imax + 8] fp16
+  extern __shared__ __attribute__((aligned(16))) uint16_t hl[];   // [kSC + 1][Imax + 8] fp16, the last row zeros
   __shared__ int hrow_s[kSC], tok_s[kSC];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nR = __builtin_amdgcn_readfirstlane(*a.n_routed);
@@ -880,6 +888,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int nch = nR + a.n_shared_inst;
   const long Lend = (long)((nch + kXcd - 1) / kXcd) * kXcd * nt;
   const int ld = a.Imax + 8;
+  for (int c = tid; c < ld / 8; c += 256) reinterpret_cast<uint4*>(hl + kSC * ld)[c] = make_uint4(0, 0, 0, 0);
   for (long wi = blockIdx.x; wi < Lend; wi += gridDim.x) {
     int ii, tile;
     if (!xcd_item(wi, nch, nt, &ii, &tile)) continue;
@@ -915,7 +924,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     float16_t acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
-    const uint16_t* arow = hl + ((lane & 31) % in.n) * ld;
+    const uint16_t* arow = hl + ((lane & 31) < in.n ? (lane & 31) : kSC) * ld;
     stream_loop<BITS, 1>(arow, make_rsrc(blob, (uint32_t)L.bytes), live, co, so, (uint32_t)a.d,
                          (uint32_t)(live ? n : 0), Iinst / kKS, acc);
     if (tile * 128 + 32 * wave < a.d) {
@@ -1035,7 +1044,7 @@ int prefill_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStr
   if (!carve_prefill(c, f.d, Imax, f.T, f.k, f.pool.E, &w)) return MOE_ERR_INVALID_ARG;
   if (!f.offsets || !f.pair_ids || !f.partial || !f.shared_out) return MOE_ERR_INVALID_ARG;
   // streaming GEMMs for a few tokens per expert (their activation rows stay
-  // in LDS: kSC rows of d fp16 values must fit beside a second block)
+  // in LDS: kSC + 1 rows of d fp16 values must fit beside a second block)
   const bool stream_fits = f.d <= 4096;
   if (path == MOE_PATH_PREFILL_STREAM && !stream_fits) return MOE_ERR_UNSUPPORTED;
   const bool stream = path == MOE_PATH_PREFILL_STREAM ||
@@ -1066,8 +1075,8 @@ int prefill_launch(const FfnArgs& f, int path, void* ws, size_t ws_bytes, hipStr
     const int dn_grid = (int)(dn_items < 8192 ? dn_items : 8192);
     void* gu = f.bits == 8 ? (void*)stream_gate_up_kernel<8> : (void*)stream_gate_up_kernel<4>;
     void* dn = f.bits == 8 ? (void*)stream_down_kernel<8> : (void*)stream_down_kernel<4>;
-    MOE_HIP(hipLaunchKernel(gu, dim3(gu_grid), dim3(256), args, (size_t)kSC * (f.d + 8) * 2, s));
-    MOE_HIP(hipLaunchKernel(dn, dim3(dn_grid), dim3(256), args, (size_t)kSC * (Imax + 8) * 2, s));
+    MOE_HIP(hipLaunchKernel(gu, dim3(gu_grid), dim3(256), args, (size_t)(kSC + 1) * (f.d + 8) * 2, s));
+    MOE_HIP(hipLaunchKernel(dn, dim3(dn_grid), dim3(256), args, (size_t)(kSC + 1) * (Imax + 8) * 2, s));
     return MOE_OK;
   }
   const long gu_items = chunks * (Imax / 64);
