@@ -89,6 +89,7 @@ ENVELOPE = {
     "max_d": dict(d=8192, E=16, k=2, I=128, I_shared=128, n_slots=16),
     "k_eq_E": dict(d=256, E=16, k=16, I=64, I_shared=64, n_slots=16),
     "small_d": dict(d=192, E=16, k=3, I=64, I_shared=64, n_slots=16),
+    "steps_3n": dict(d=768, E=32, k=4, I=384, I_shared=384, n_slots=32),
 }
 
 

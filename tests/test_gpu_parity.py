@@ -227,6 +227,9 @@ ENVELOPE = {
     "max_E": dict(d=512, E=1024, k=16, I=128, I_shared=128, n_slots=1024),
     "max_d": dict(d=8192, E=16, k=2, I=128, I_shared=128, n_slots=16),
     "k_eq_E": dict(d=256, E=16, k=16, I=64, I_shared=64, n_slots=16),
+    # k steps of the tiled GEMMs a multiple of three (gate/up 12, down 6): the
+    # unrolled rounds of three steps with no remainder after them
+    "steps_3n": dict(d=768, E=32, k=4, I=384, I_shared=384, n_slots=32),
 }
 
 
