@@ -754,6 +754,9 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
   float* oi = dyn;
   float* wk = dyn + nI * 8;                     // combine weights: w[T*k] then sgate[T]
   uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 9 + 3) & ~3));
+  // a chain's residual rows, loaded now (they depend on nothing here) so
+  // the hand-over at the end does not wait for them
+  const uint32_t res_pre = (a.res_out && tid < 8 * a.T) ? a.res_in[(size_t)(tid / 8) * a.d + jb * 8 + tid % 8] : 0u;
   for (int base = 0; base < nI; base += kDnRound) {
     const int nr = min(kDnRound, nI - base);
     const int i = base + wave;
@@ -843,7 +846,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_kernel(DownArgs a) 
     const size_t yi = (size_t)t * a.d + jb * 8 + rr;
     a.y[yi] = y;
     if (a.res_out) {                            // chain hand-over (all 8 lanes of a token active)
-      const uint32_t b = f32_to_bf16(__uint_as_float((uint32_t)a.res_in[yi] << 16) + y);
+      const uint32_t b = f32_to_bf16(__uint_as_float(res_pre << 16) + y);
       a.res_out[yi] = (uint16_t)b;
       const float r = __uint_as_float(b << 16);
       const float p = sum8_dpp(__fmul_rn(r, r));
@@ -986,6 +989,9 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArg
   uint32_t* hst = reinterpret_cast<uint32_t*>(dyn + ((nI * 9 + nR + 3) & ~3));
   const rsrc_t rq = make_rsrc(a.hq, (uint32_t)nI * a.Imax * 4);
   const rsrc_t rs = make_rsrc(a.hs8, (uint32_t)nI * (a.Imax / 8) * 4);
+  // a chain's residual rows, loaded now (they depend on nothing here) so
+  // the hand-over at the end does not wait for them
+  const uint32_t res_pre = (a.res_out && tid < 8 * a.T) ? a.res_in[(size_t)(tid / 8) * a.d + jb * 8 + tid % 8] : 0u;
   DnInst<BITS> cur;
   {
     // round 0: its slot straight from memory and its records by DMA; the
@@ -1065,7 +1071,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void down_decode_pipe_kernel(DownArg
     const size_t yi = (size_t)t * a.d + jb * 8 + rr;
     a.y[yi] = y;
     if (a.res_out) {                            // chain hand-over (all 8 lanes of a token active)
-      const uint32_t b = f32_to_bf16(__uint_as_float((uint32_t)a.res_in[yi] << 16) + y);
+      const uint32_t b = f32_to_bf16(__uint_as_float(res_pre << 16) + y);
       a.res_out[yi] = (uint16_t)b;
       const float rv = __uint_as_float(b << 16);
       const float p = sum8_dpp(__fmul_rn(rv, rv));
