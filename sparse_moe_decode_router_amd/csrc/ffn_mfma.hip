@@ -543,6 +543,12 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_kernel(PrefillArgs a) 
   }
 }
 
+// Output staging of the down kernel: 64 tokens x 128 outputs fp32 a pass,
+// rows padded by 4 floats (the two token rows a store instruction writes
+// fall in different banks); it fits the stages.
+constexpr int kEpLd = 132;
+static_assert(64 * kEpLd * 4 <= 3 * kStA, "down output staging in the stages");
+
 template <int BITS>
 __global__ __launch_bounds__(256, 3) void prefill_down_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t SM[3 * kStage<BITS>];
@@ -605,20 +611,36 @@ __global__ __launch_bounds__(256, 3) void prefill_down_kernel(PrefillArgs a) {
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
     gemm_tiles<BITS>(in.n, S0, S1, S2, rH, a_vo, a_vo_n, make_rsrc(blob, (uint32_t)L.bytes), (uint32_t)L.m[2].codes,
                      (uint32_t)L.m[2].sb, (uint32_t)a.d, (uint32_t)(n0 + 32 * wave + (lane & 31)), Iinst / kKS, acc);
-    const int n = n0 + 32 * wave + (lane & 31);
+    // The outputs go out through LDS (the stages are idle now: every wave
+    // is past its last stage read and every DMA has landed) in two passes of
+    // 64 tokens, so each thread stores 16-byte pieces of one token's 128
+    // outputs, a quarter of the store instructions and address computations
+    // of storing the accumulators as they lie (one value a lane).
+    float* E = reinterpret_cast<float*>(SM);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int p = 0; p < 2; ++p) {
+      if (64 * p >= in.n) break;                // block-uniform
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 32 * mt + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rl = 32 * h + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);   // token within the pass
+          E[rl * kEpLd + 32 * wave + (lane & 31)] = missing ? 0.f : acc[2 * p + h][i];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = tid + 256 * u, rl = q >> 5, pc = q & 31;
+        const int r = 64 * p + rl;
         if (r < in.n) {
-          const float v = missing ? 0.f : acc[mt][i];
-          if (routed) a.partial[(size_t)hrow_s[r] * a.d + n] = v;
-          else a.shared_out[(size_t)tok_s[r] * a.d + n] = v;
+          const float4 v = *reinterpret_cast<const float4*>(&E[rl * kEpLd + 4 * pc]);
+          float* dst = routed ? a.partial + (size_t)hrow_s[r] * a.d : a.shared_out + (size_t)tok_s[r] * a.d;
+          *reinterpret_cast<float4*>(dst + n0 + 4 * pc) = v;
         }
       }
+      __syncthreads();                          // the next pass rewrites E
     }
-    __syncthreads();
+    __syncthreads();                            // every wave is past this item's hrow_s / tok_s reads
   }
 }
 
