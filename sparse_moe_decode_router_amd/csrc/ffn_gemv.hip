@@ -146,21 +146,35 @@ __device__ __forceinline__ uint32_t qword(const uint4 (&q)[NP], int i) {
 //   8-bit: u = 0..7, pair p = u/2: its inputs are bytes (0,2) (p even) or
 //          (1,3) (p odd) of word 2m + p/2; u even takes their low nibbles
 //          (128 + lo), u odd their high nibbles (2048 + 16 hi).
+// The nibble mask and the two bf16 constants, held in registers (the mask in
+// an SGPR, the constants in VGPRs) so that each (shifted word & mask) |
+// constant is one v_and_or_b32: a VOP3 instruction takes no literal operand
+// here, and with literals the compiler emits a v_and and a v_or.
+struct QConst {
+  uint32_t mask, mag, mag8;       // 0x000F000F; 0x4300 (128.0) and 0x4500 (2048.0) in both halves
+};
+__device__ __forceinline__ QConst q_const() {
+  QConst k{0x000F000Fu, 0x43004300u, 0x45004500u};
+  asm("" : "+s"(k.mask));
+  asm("" : "+v"(k.mag), "+v"(k.mag8));
+  return k;
+}
+
 template <int BITS, int NP>
-__device__ __forceinline__ uint32_t qpair(const uint4 (&q)[NP], int m, int u) {
+__device__ __forceinline__ uint32_t qpair(const uint4 (&q)[NP], int m, int u, const QConst& k) {
   static_assert(NP >= BITS / 2, "code pieces");
   const uint32_t w = qword(q, (BITS / 4) * m + (u >> 2));
-  const uint32_t mag = (BITS == 8 && (u & 1)) ? 0x45004500u : 0x43004300u;
-  return ((w >> (4 * (u & 3))) & 0x000F000Fu) | mag;
+  const uint32_t mag = (BITS == 8 && (u & 1)) ? k.mag8 : k.mag;
+  return ((w >> (4 * (u & 3))) & k.mask) | mag;
 }
 template <int BITS> __device__ __forceinline__ constexpr int qx(int u) { return BITS == 4 ? u : u >> 1; }
 // The same from the group's code words: word index of product u of block m,
 // and the pair from that word.
 template <int BITS> __device__ __forceinline__ constexpr int qwi(int m, int u) { return (BITS / 4) * m + (u >> 2); }
 template <int BITS>
-__device__ __forceinline__ uint32_t qpw(uint32_t w, int u) {
-  const uint32_t mag = (BITS == 8 && (u & 1)) ? 0x45004500u : 0x43004300u;
-  return ((w >> (4 * (u & 3))) & 0x000F000Fu) | mag;
+__device__ __forceinline__ uint32_t qpw(uint32_t w, int u, const QConst& k) {
+  const uint32_t mag = (BITS == 8 && (u & 1)) ? k.mag8 : k.mag;
+  return ((w >> (4 * (u & 3))) & k.mask) | mag;
 }
 template <int BITS> __device__ __forceinline__ constexpr float qoff() { return BITS == 4 ? 128.0f : 2176.0f; }
 
@@ -365,6 +379,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
     float vg[TC], vu[TC];
 #pragma unroll
     for (int tt = 0; tt < TC; ++tt) { vg[tt] = 0.f; vu[tt] = 0.f; }
+    const QConst qk = q_const();
     if (!missing) {
 #pragma unroll
       for (int gi = 0; gi < GPL; ++gi) {
@@ -389,10 +404,10 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 #pragma unroll
               for (int s2 = 0; s2 < BITS / 2; ++s2) {     // products u = 2 s2 and 2 s2 + 1
                 const int u0 = 2 * s2, u1 = 2 * s2 + 1;
-                ag0 = dot2_bf16(qpair<BITS>(cg[gi], m, u0), xw[qx<BITS>(u0)], ag0);
-                au0 = dot2_bf16(qpair<BITS>(cu[gi], m, u0), xw[qx<BITS>(u0)], au0);
-                ag1 = dot2_bf16(qpair<BITS>(cg[gi], m, u1), xw[qx<BITS>(u1)], ag1);
-                au1 = dot2_bf16(qpair<BITS>(cu[gi], m, u1), xw[qx<BITS>(u1)], au1);
+                ag0 = dot2_bf16(qpair<BITS>(cg[gi], m, u0, qk), xw[qx<BITS>(u0)], ag0);
+                au0 = dot2_bf16(qpair<BITS>(cu[gi], m, u0, qk), xw[qx<BITS>(u0)], au0);
+                ag1 = dot2_bf16(qpair<BITS>(cg[gi], m, u1, qk), xw[qx<BITS>(u1)], ag1);
+                au1 = dot2_bf16(qpair<BITS>(cu[gi], m, u1, qk), xw[qx<BITS>(u1)], au1);
               }
             }
             const float ag = ag0 + ag1, au = au0 + au1;
@@ -443,6 +458,7 @@ __global__ __launch_bounds__(256, (GPL <= 4 && BITS == 4) ? 3 : 1) void gate_up_
   const int nbR = a.I / 32, nbS = a.Ish / 32;   // items of 32 rows
   const int nR = *a.n_routed;
   const int items = nR * nbR + a.n_shared_inst * nbS;
+  const QConst qk = q_const();
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const bool routed = item < nR * nbR;
     const int rel = routed ? item : item - nR * nbR;
@@ -517,8 +533,9 @@ __global__ __launch_bounds__(256, (GPL <= 4 && BITS == 4) ? 3 : 1) void gate_up_
                                  : make_uint4(0, 0, 0, 0);
 #pragma unroll
             for (int s2 = 0; s2 < BITS / 2; ++s2) {       // products u = 2 s2 and 2 s2 + 1
-              const uint32_t qg0 = qpair<BITS>(cg[it][gi], m, 2 * s2), qu0 = qpair<BITS>(cu[it][gi], m, 2 * s2);
-              const uint32_t qg1 = qpair<BITS>(cg[it][gi], m, 2 * s2 + 1), qu1 = qpair<BITS>(cu[it][gi], m, 2 * s2 + 1);
+              const uint32_t qg0 = qpair<BITS>(cg[it][gi], m, 2 * s2, qk), qu0 = qpair<BITS>(cu[it][gi], m, 2 * s2, qk);
+              const uint32_t qg1 = qpair<BITS>(cg[it][gi], m, 2 * s2 + 1, qk);
+              const uint32_t qu1 = qpair<BITS>(cu[it][gi], m, 2 * s2 + 1, qk);
 #pragma unroll
               for (int tt = 0; tt < kTC; ++tt) {
                 if (tt < ntok) {
@@ -658,6 +675,7 @@ __device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint4 q2, u
   const float b = f16_to_f32(sb >> 16);
   const uint32_t qw[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                            q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+  const QConst qk = q_const();
   const uint4* hh = reinterpret_cast<const uint4*>(hrec + g * kHG);
   const uint4* hl = reinterpret_cast<const uint4*>(hrec + (Imax / 64 + g) * kHG);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;      // four independent chains
@@ -668,8 +686,8 @@ __device__ __forceinline__ float down_group_regs(uint4 q0, uint4 q1, uint4 q2, u
     const uint32_t pl[4] = {vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
     for (int s2 = 0; s2 < BITS / 2; ++s2) {         // products u = 2 s2 and 2 s2 + 1
-      const uint32_t c0 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2)], 2 * s2);
-      const uint32_t c1 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2 + 1)], 2 * s2 + 1);
+      const uint32_t c0 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2)], 2 * s2, qk);
+      const uint32_t c1 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2 + 1)], 2 * s2 + 1, qk);
       a0 = dot2_bf16(c0, ph[qx<BITS>(2 * s2)], a0);
       a1 = dot2_bf16(c0, pl[qx<BITS>(2 * s2)], a1);
       a2 = dot2_bf16(c1, ph[qx<BITS>(2 * s2 + 1)], a2);
@@ -937,6 +955,7 @@ __device__ __forceinline__ float down_group_sw(uint4 q0, uint4 q1, uint4 q2, uin
   const float b = f16_to_f32(sb >> 16);
   const uint32_t qw[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                            q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+  const QConst qk = q_const();
   const uint32_t* gh = hrec + 32 * g;
   const uint32_t* glo = hrec + (Imax / 64 + g) * 32;
   const float* hs = reinterpret_cast<const float*>(hrec + 2 * (Imax / 64) * 32);
@@ -949,8 +968,8 @@ __device__ __forceinline__ float down_group_sw(uint4 q0, uint4 q1, uint4 q2, uin
     const uint32_t pl[4] = {vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
     for (int s2 = 0; s2 < BITS / 2; ++s2) {         // products u = 2 s2 and 2 s2 + 1
-      const uint32_t c0 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2)], 2 * s2);
-      const uint32_t c1 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2 + 1)], 2 * s2 + 1);
+      const uint32_t c0 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2)], 2 * s2, qk);
+      const uint32_t c1 = qpw<BITS>(qw[qwi<BITS>(m, 2 * s2 + 1)], 2 * s2 + 1, qk);
       a0 = dot2_bf16(c0, ph[qx<BITS>(2 * s2)], a0);
       a1 = dot2_bf16(c0, pl[qx<BITS>(2 * s2)], a1);
       a2 = dot2_bf16(c1, ph[qx<BITS>(2 * s2 + 1)], a2);
