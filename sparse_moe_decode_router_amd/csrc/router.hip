@@ -94,8 +94,9 @@ namespace {
 // shared gate) with 256 threads, each summing d/256 products in column
 // order, then a 64-lane butterfly and a two-level tree over the 4 waves:
 // depth d/256 + 8, plus one for the bias (added by the top-k).  Blocks also
-// prepare xq/xs, group q by thread q / gridDim of block q % gridDim (one
-// group per block while T d / 64 <= E + 1).  No block waits for another.
+// prepare xq/xs, group q by thread (q / gridDim) % 256 of block q % gridDim
+// (one group per block while T d / 64 <= E + 1).  No block waits for
+// another.
 struct DecodeArgs {
   const uint16_t* x; int T, d;
   const float* W; int E;
@@ -161,8 +162,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_decode_kernel(DecodeArg
   }
   {
     const int G = d / 64;
-    const int id = tid * gridDim.x + blockIdx.x;
-    if (id < T * G) {
+    // grid-stride: a grid of fewer than T d / 64 / 256 blocks (few experts,
+    // wide d) still prepares every group
+    for (int id = tid * gridDim.x + blockIdx.x; id < T * G; id += kRouterThreads * gridDim.x) {
       const int t = id / G;
       if (chain) {
         float sc = 1.f;

@@ -250,6 +250,18 @@ def test_envelope_prefill(name):
     print(f"prefill {name}: rel err {rel:.2e}, near-ties {namb}")
 
 
+def test_decode_router_preps_every_group_with_few_experts():
+    """T = 8 tokens of d = 8192 make T d / 64 = 1024 activation groups, more than
+    the threads of the decode router's grid when E = 2 (three blocks): every
+    group is still prepared for the GEMVs.  Step 1 would read step 0's
+    activations in a group left unprepared."""
+    L = DeviceLayer(ms.scaled(ms.CONFIGS["decode80b"], alpha=0.0, d=8192, E=2, k=1, I=128,
+                              I_shared=128, n_slots=2))
+    for step in range(2):
+        _check_layer_step(L, step, path=moe.MOE_PATH_DECODE, T=8)
+    assert L.pool.check_error() == moe.MOE_OK
+
+
 # ------------------------------------------------------ placement invariance
 def test_placement_invariance_bit_identical():
     """Two pools holding the same experts at different slots, and a smaller
