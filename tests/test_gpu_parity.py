@@ -238,6 +238,7 @@ def test_envelope_decode_and_batched(name):
     L = DeviceLayer(ms.scaled(ms.CONFIGS["decode80b"], alpha=0.0, **ENVELOPE[name]))
     _check_layer_step(L, 0, path=moe.MOE_PATH_DECODE, T=1)
     _check_layer_step(L, 1, path=moe.MOE_PATH_DECODE, T=4)
+    _check_layer_step(L, 3, path=moe.MOE_PATH_DECODE, T=8)      # the decode router's widest instance
     _check_layer_step(L, 2, path=moe.MOE_PATH_BATCHED, T=24)
     assert L.pool.check_error() == moe.MOE_OK
 
