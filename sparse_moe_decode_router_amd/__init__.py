@@ -42,6 +42,13 @@ if not os.path.exists(LIB_PATH):
         "`python sparse_moe_decode_router_amd/build.py` (the HIP library is required; "
         "there is no CPU fallback)")
 
+# torch first: the library's HIP runtime dependency then resolves to the one
+# torch has already mapped, so the device memory and streams torch hands over
+# belong to the runtime the kernels launch on.  Loaded before torch, it
+# would map a second HIP and HSA runtime into the process, and one of the two
+# finds no device.
+import torch  # noqa: E402,F401
+
 _lib = C.CDLL(LIB_PATH)
 
 

@@ -6,6 +6,8 @@ validation rejects bad calls before any device work."""
 import ctypes as C
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -28,6 +30,25 @@ def _header_functions():
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
             names.update(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src))
     return sorted(names)
+
+
+_MAPPED_RUNTIMES = r"""
+import re, sys
+sys.path.insert(0, sys.argv[1])
+import sparse_moe_decode_router_amd  # the package before anything imports torch
+import torch  # then torch, for the tensors a caller hands over
+maps = open("/proc/self/maps").read()
+for lib in ("amdhip64", "hsa-runtime64"):
+    print(lib, len(set(re.findall(r"(/\S*lib" + lib + r"\S*)", maps))))
+"""
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Imported before torch, the package still maps one HIP and one HSA
+    runtime (torch's): two in one process leave one of them without a device."""
+    out = subprocess.run([sys.executable, "-c", _MAPPED_RUNTIMES, ROOT], capture_output=True, text=True,
+                         timeout=300, check=True).stdout.split()
+    assert out == ["amdhip64", "1", "hsa-runtime64", "1"], out
 
 
 def test_library_exports_every_declared_symbol():
