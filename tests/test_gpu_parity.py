@@ -149,6 +149,16 @@ def test_router_k_extremes(k):
         assert np.allclose(np.take_along_axis(p, idx.astype(np.int64), 1), w, atol=2e-6)
 
 
+@pytest.mark.parametrize("T", [3, 40])
+@pytest.mark.parametrize("E,k", [(256, 80), (1024, 100)])
+def test_router_k_above_64(E, k, T):
+    """k > 64: the top-k skips its threshold search and ranks every key as a
+    candidate; both routers (T = 3 on the per-row GEMVs, T = 40 on the matrix
+    cores), under the same certified comparison as test_router_parity."""
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], d=512, E=E, k=k, I=64, I_shared=64, n_slots=E)
+    _router_parity(cfg, f"E{E}_k{k}", T)
+
+
 # ---------------------------------------------------------------- bucketing
 # (the multi-block scan runs in LDS up to 24576 histogram entries: 4096 x 10
 # of 512 is 20480; 2048 x 16 of 1024 is 32768, the scan from global memory)
@@ -261,6 +271,20 @@ def test_decode_router_preps_every_group_with_few_experts():
     for step in range(2):
         _check_layer_step(L, step, path=moe.MOE_PATH_DECODE, T=8)
     assert L.pool.check_error() == moe.MOE_OK
+
+
+def test_layer_k_above_64():
+    """A layer that sends each token to 72 of 128 experts (the top-k's k > 64
+    branch inside the decode gate/up kernel, 584 down instances at T = 8) on
+    the decode, batched and prefill paths."""
+    cfg = ms.scaled(ms.CONFIGS["decode80b"], alpha=0.0, d=256, E=128, k=72, I=64, I_shared=64, n_slots=128)
+    L = DeviceLayer(cfg)
+    _check_layer_step(L, 0, path=moe.MOE_PATH_DECODE, T=1)
+    _check_layer_step(L, 1, path=moe.MOE_PATH_DECODE, T=8)
+    _check_layer_step(L, 2, path=moe.MOE_PATH_BATCHED, T=24)
+    assert L.pool.check_error() == moe.MOE_OK
+    rel, namb, _ = _prefill_check(L, 3, 160)
+    print(f"k = 72 prefill: rel err {rel:.2e}, near-ties {namb}")
 
 
 # ------------------------------------------------------ placement invariance
